@@ -1,0 +1,312 @@
+"""TEST INFRASTRUCTURE ONLY: ctypes wrapper around the plain C oracle (liboracle.so).
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
+import this package.  It never touches the GPU library and the GPU library
+never touches it.  Arrays are numpy; bf16 data travels as its raw uint16 bits.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+SRC_PATH = os.path.join(_HERE, "kvq_oracle.c")
+
+# -ffp-contract=off: every fp32 step is its own IEEE operation; no -ffast-math, no -march
+# (the default x86-64 target has no FMA); single-threaded.
+GCC_CMD = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
+           "-Wall", "-Wextra", "-o", LIB_PATH, SRC_PATH, "-lm"]
+
+
+def build() -> str:
+    subprocess.run(GCC_CMD, check=True)
+    return LIB_PATH
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            build()
+        _lib = C.CDLL(LIB_PATH)
+        _declare(_lib)
+    return _lib
+
+
+P = C.c_void_p
+I64 = C.c_int64
+
+
+def _declare(L):
+    L.orc_quant_sym.argtypes = [P, C.c_int, I64, I64, I64, C.c_int, P, P, P]
+    L.orc_quant_asym.argtypes = [P, C.c_int, I64, I64, I64, C.c_int, C.c_int, P, P, P]
+    L.orc_dequant_pc.argtypes = [P, P, P, I64, I64, I64, P]
+    L.orc_dequant_pc.restype = None
+    L.orc_err_stats.argtypes = [P, C.c_int, P, C.c_int, I64, P]
+    L.orc_err_stats.restype = None
+    L.orc_stats_finalize.argtypes = [P, I64, P, P, P]
+    L.orc_stats_finalize.restype = None
+    L.orc_int4_quant.argtypes = [P, P, I64, I64, I64, I64, I64, I64] + [P] * 8
+    L.orc_int4_dequant.argtypes = [C.c_int, P, P, P, P, I64, I64, I64, I64, I64, I64, P]
+    L.orc_int4_dequant.restype = None
+    L.orc_decode_attn.argtypes = [P] * 8 + [I64] * 6 + [P, I64, C.c_double, P]
+    L.orc_decode_attn_rows.argtypes = [P] * 8 + [I64] * 6 + [P, I64, C.c_double, P, P, I64, P]
+    L.orc_colsum.argtypes = [P, I64, I64, I64, P]
+    L.orc_colsum.restype = None
+    L.orc_keep_count.argtypes = [I64, I64, I64]
+    L.orc_keep_count.restype = I64
+    L.orc_select.argtypes = [P, I64, I64, I64, I64, P]
+    L.orc_h2o_select.argtypes = [P, I64, I64, I64, I64, I64, P, P]
+    L.orc_compact.argtypes = [P, I64, I64, I64, I64, P, I64, P]
+    L.orc_compact.restype = None
+    L.orc_int4_bytes.argtypes = [C.c_uint64, C.c_uint64]
+    L.orc_int4_bytes.restype = C.c_uint64
+    L.orc_int4_cache_sizes.argtypes = [I64] * 6 + [P, P]
+    L.orc_compression_ratio.argtypes = [C.c_uint64] * 4
+    L.orc_compression_ratio.restype = C.c_double
+    L.orc_token_ratio.argtypes = [I64, I64, P]
+    L.orc_total_gain.argtypes = [C.c_double, C.c_double, I64, I64]
+    L.orc_total_gain.restype = C.c_double
+    L.orc_kv_bytes.argtypes = [C.c_uint64] * 5
+    L.orc_kv_bytes.restype = C.c_uint64
+    L.orc_f32_to_bf16.argtypes = [C.c_float]
+    L.orc_f32_to_bf16.restype = C.c_uint16
+    L.orc_bf16_to_f32.argtypes = [C.c_uint16]
+    L.orc_bf16_to_f32.restype = C.c_float
+    L.orc_f32_to_bf16_array.argtypes = [P, I64, P]
+    L.orc_f32_to_bf16_array.restype = None
+
+
+def _p(a: np.ndarray):
+    assert a.flags["C_CONTIGUOUS"], "oracle arrays must be C-contiguous"
+    return a.ctypes.data_as(C.c_void_p)
+
+
+def _x(a: np.ndarray):
+    """Pointer + bf16 flag for an fp32 or bf16(uint16) array."""
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.float32:
+        return a, 0
+    if a.dtype == np.uint16:
+        return a, 1
+    raise TypeError(f"oracle takes float32 or bf16-as-uint16, got {a.dtype}")
+
+
+class OracleError(ValueError):
+    pass
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise OracleError(f"{what}: oracle rejected the arguments (rc={rc})")
+
+
+# ------------------------------------------------------------ per-channel --
+
+def quant_sym(x: np.ndarray, bits: int):
+    """x: [nb][R][C] or [R][C] fp32/bf16 -> (q int8, scale fp32 [nb][C], zp int8 [nb][C])."""
+    x3 = x.reshape((-1,) + x.shape[-2:]) if x.ndim >= 2 else x.reshape(1, -1, 1)
+    x3, isb = _x(x3)
+    nb, R, Cc = x3.shape
+    q = np.empty((nb, R, Cc), np.int8)
+    s = np.empty((nb, Cc), np.float32)
+    z = np.empty((nb, Cc), np.int8)
+    _check(lib().orc_quant_sym(_p(x3), isb, nb, R, Cc, bits, _p(q), _p(s), _p(z)), "quant_sym")
+    return q, s, z
+
+
+def quant_asym(x: np.ndarray, qmin: int, qmax: int):
+    x3 = x.reshape((-1,) + x.shape[-2:])
+    x3, isb = _x(x3)
+    nb, R, Cc = x3.shape
+    q = np.empty((nb, R, Cc), np.int8)
+    s = np.empty((nb, Cc), np.float32)
+    z = np.empty((nb, Cc), np.int8)
+    _check(lib().orc_quant_asym(_p(x3), isb, nb, R, Cc, qmin, qmax, _p(q), _p(s), _p(z)), "quant_asym")
+    return q, s, z
+
+
+def dequant_pc(q: np.ndarray, scale: np.ndarray, zp):
+    q = np.ascontiguousarray(q, np.int8)
+    nb, R, Cc = q.shape
+    scale = np.ascontiguousarray(scale, np.float32)
+    out = np.empty((nb, R, Cc), np.float32)
+    if zp is None:
+        lib().orc_dequant_pc(_p(q), _p(scale), None, nb, R, Cc, _p(out))
+    else:
+        zp = np.ascontiguousarray(zp, np.int8)
+        lib().orc_dequant_pc(_p(q), _p(scale), _p(zp), nb, R, Cc, _p(out))
+    return out
+
+
+def err_stats(x: np.ndarray, xh: np.ndarray):
+    """-> (sum_sq, sum_abs, max_abs) in fp64."""
+    x, xb = _x(x.reshape(-1))
+    xh, hb = _x(xh.reshape(-1))
+    assert x.size == xh.size
+    out = np.zeros(3, np.float64)
+    lib().orc_err_stats(_p(x), xb, _p(xh), hb, x.size, _p(out))
+    return float(out[0]), float(out[1]), float(out[2])
+
+
+def stats_finalize(raw, n: int):
+    a = np.asarray(raw, np.float64)
+    r, m, mean = C.c_double(), C.c_double(), C.c_double()
+    lib().orc_stats_finalize(_p(a), n, C.byref(r), C.byref(m), C.byref(mean))
+    return r.value, m.value, mean.value
+
+
+# ------------------------------------------------------------------ INT4 ----
+
+def int4_cache_sizes(B, T, H, d, g, R):
+    sect = np.zeros(8, np.uint64)
+    tot = C.c_uint64()
+    _check(lib().orc_int4_cache_sizes(B, T, H, d, g, R, _p(sect), C.byref(tot)), "int4_cache_sizes")
+    return [int(v) for v in sect], int(tot.value)
+
+
+def int4_quant(K: np.ndarray, V: np.ndarray, g: int, R: int):
+    """K, V bf16-as-uint16 [B][T][H][d] -> dict of the cache sections."""
+    K = np.ascontiguousarray(K, np.uint16)
+    V = np.ascontiguousarray(V, np.uint16)
+    B, T, H, d = K.shape
+    Tq = T - R
+    nKg = -(-Tq // g) if Tq > 0 else 0
+    c = dict(
+        k_codes=np.zeros((B, H, Tq, d // 2), np.uint8),
+        k_scale=np.zeros((B, H, nKg, d), np.uint16),
+        k_zero=np.zeros((B, H, nKg, d), np.uint16),
+        v_codes=np.zeros((B, H, Tq, d // 2), np.uint8),
+        v_scale=np.zeros((B, H, Tq, d // g), np.uint16),
+        v_zero=np.zeros((B, H, Tq, d // g), np.uint16),
+        k_res=np.zeros((B, H, R, d), np.uint16),
+        v_res=np.zeros((B, H, R, d), np.uint16),
+    )
+    rc = lib().orc_int4_quant(_p(K), _p(V), B, T, H, d, g, R,
+                              _p(c["k_codes"]), _p(c["k_scale"]), _p(c["k_zero"]),
+                              _p(c["v_codes"]), _p(c["v_scale"]), _p(c["v_zero"]),
+                              _p(c["k_res"]), _p(c["v_res"]))
+    _check(rc, "int4_quant")
+    c.update(B=B, T=T, H=H, d=d, g=g, R=R)
+    return c
+
+
+def int4_dequant(c: dict, side: str):
+    """side 'k' or 'v' -> fp32 [B][T][H][d]."""
+    B, T, H, d, g, R = (c[k] for k in ("B", "T", "H", "d", "g", "R"))
+    out = np.empty((B, T, H, d), np.float32)
+    s = side.lower()
+    lib().orc_int4_dequant(1 if s == "k" else 0, _p(c[s + "_codes"]), _p(c[s + "_scale"]),
+                           _p(c[s + "_zero"]), _p(c[s + "_res"]), B, T, H, d, g, R, _p(out))
+    return out
+
+
+def _cache_ptrs(c):
+    return [_p(np.ascontiguousarray(c[k])) for k in
+            ("k_codes", "k_scale", "k_zero", "v_codes", "v_scale", "v_zero", "k_res", "v_res")]
+
+
+def decode_attn(c: dict, q: np.ndarray, sm_scale: float = 1.0, rows=None):
+    """q bf16-as-uint16 [B][Hq][d] -> fp64 [B][Hq][d] (or [n_rows][d] for rows=[(b,hq),...])."""
+    q = np.ascontiguousarray(q, np.uint16)
+    B, Hq, d = q.shape
+    args = _cache_ptrs(c) + [c["B"], c["T"], c["H"], c["d"], c["g"], c["R"], _p(q), Hq, float(sm_scale)]
+    if rows is None:
+        out = np.empty((B, Hq, d), np.float64)
+        _check(lib().orc_decode_attn(*args, _p(out)), "decode_attn")
+        return out
+    rb = np.ascontiguousarray([r[0] for r in rows], np.int64)
+    rh = np.ascontiguousarray([r[1] for r in rows], np.int64)
+    out = np.empty((len(rows), d), np.float64)
+    _check(lib().orc_decode_attn_rows(*args, _p(rb), _p(rh), len(rows), _p(out)), "decode_attn_rows")
+    return out
+
+
+# -------------------------------------------------------------- selection ---
+
+def keep_count(T, budget, window) -> int:
+    return int(lib().orc_keep_count(T, budget, window))
+
+
+def colsum(hist: np.ndarray):
+    hist = np.ascontiguousarray(hist, np.float32)
+    rows, T_obs, T = hist.shape
+    out = np.empty((rows, T), np.float32)
+    lib().orc_colsum(_p(hist), rows, T_obs, T, _p(out))
+    return out
+
+
+def select(scores: np.ndarray, budget: int, window: int):
+    scores = np.ascontiguousarray(scores, np.float32)
+    if scores.ndim == 1:
+        scores = scores[None]
+    rows, T = scores.shape
+    K = keep_count(T, budget, window)
+    keep = np.empty((rows, K), np.int32)
+    _check(lib().orc_select(_p(scores), rows, T, budget, window, _p(keep)), "select")
+    return keep
+
+
+def h2o_select(hist: np.ndarray, budget: int, window: int):
+    hist = np.ascontiguousarray(hist, np.float32)
+    rows, T_obs, T = hist.shape
+    K = keep_count(T, budget, window)
+    keep = np.empty((rows, K), np.int32)
+    scores = np.empty((rows, T), np.float32)
+    _check(lib().orc_h2o_select(_p(hist), rows, T_obs, T, budget, window, _p(scores), _p(keep)), "h2o_select")
+    return keep, scores
+
+
+def compact(src: np.ndarray, keep: np.ndarray):
+    """src bf16-as-uint16 [B][T][H][d], keep int32 [B][H][K] -> [B][K][H][d]."""
+    src = np.ascontiguousarray(src, np.uint16)
+    keep = np.ascontiguousarray(keep, np.int32)
+    B, T, H, d = src.shape
+    K = keep.shape[-1]
+    dst = np.empty((B, K, H, d), np.uint16)
+    lib().orc_compact(_p(src), B, T, H, d, _p(keep), K, _p(dst))
+    return dst
+
+
+# ------------------------------------------------------------- accounting ---
+
+def int4_bytes(N, g) -> int:
+    return int(lib().orc_int4_bytes(N, g))
+
+
+def compression_ratio(orig, data, scale, zp) -> float:
+    return float(lib().orc_compression_ratio(orig, data, scale, zp))
+
+
+def token_ratio(T, K) -> float:
+    out = C.c_double()
+    _check(lib().orc_token_ratio(T, K, C.byref(out)), "token_ratio")
+    return out.value
+
+
+def total_gain(s_old, s_new, T, K) -> float:
+    return float(lib().orc_total_gain(s_old, s_new, T, K))
+
+
+def kv_bytes(L, T, Cst, b, metadata=0) -> int:
+    return int(lib().orc_kv_bytes(L, T, Cst, b, metadata))
+
+
+def f32_to_bf16(x: np.ndarray) -> np.ndarray:
+    x = np.ascontiguousarray(x, np.float32)
+    out = np.empty(x.shape, np.uint16)
+    lib().orc_f32_to_bf16_array(_p(x), x.size, _p(out))
+    return out
+
+
+def bf16_to_f32(b: np.ndarray) -> np.ndarray:
+    """Widening is exact: the bf16 bits become the top half of an fp32."""
+    b = np.ascontiguousarray(b, np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32)

@@ -1,0 +1,602 @@
+"""Pins of the CPU oracle against facts the pages fix, closed forms and brute force.
+
+None of these tests re-types the oracle's formula: each compares it with a value
+the pages print, a hand-derived closed form, an invariant of the method, or a
+brute-force search over a tiny input.
+"""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _gold(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+def bf16(x):
+    return oracle.f32_to_bf16(np.asarray(x, np.float32))
+
+
+def f32(b):
+    return oracle.bf16_to_f32(b)
+
+
+# ------------------------------------------------------------ worked example --
+
+def test_worked_example_4bit():
+    g = _gold("worked_example_4bit.json")
+    x = np.array(g["printed"]["x"], np.float32).reshape(4, 1)
+    q, s, z = oracle.quant_sym(x, bits=4)
+    assert q.ravel().tolist() == g["hand_computed"]["q"]
+    # s = 1/7 rounded once to fp32
+    assert s[0, 0] == np.float32(1.0) / np.float32(7.0)
+    assert s.view(np.uint32)[0, 0] == 0x3E124925
+    assert z.ravel().tolist() == [0]
+    xh = oracle.dequant_pc(q, s, None).ravel()
+    # x_hat = q / 7: the ends are recovered exactly, the middle within s/2
+    assert xh[0] == -1.0 and xh[3] == 1.0
+    assert np.all(np.abs(xh.astype(np.float64) - x.ravel()) <= float(s[0, 0]) / 2)
+    assert abs(float(xh[1]) - (-1 / 7)) < 1e-7 and abs(float(xh[2]) - 2 / 7) < 1e-7
+
+
+# --------------------------------------------------------- byte accounting ----
+
+def test_group_size_table():
+    for row in _gold("group_size_table.json")["rows"]:
+        g = row["g"]
+        N = g * 4096
+        b = oracle.int4_bytes(N, g)
+        assert Fraction(b, N) == Fraction(row["bytes_per_number"]).limit_denominator(1 << 20)
+        ratio = 2 * N / b
+        digits = len(row["ratio_printed"].split(".")[1])
+        assert f"{ratio:.{digits}f}" == row["ratio_printed"]
+    # the formula's ceilings on a ragged N
+    assert oracle.int4_bytes(65, 64) == 33 + 2 * 4
+    assert oracle.int4_bytes(1, 32) == 1 + 4
+
+
+def test_exercise_1_and_lab_line():
+    e = _gold("byte_budgets.json")["exercise_1"]
+    tot = oracle.int4_bytes(e["N"], e["g"])
+    assert tot == e["total_bytes"] == 576 * 1024
+    ratio = 2 * e["N"] / tot
+    assert f"metadata: {tot // 1024} KiB; ratio = {ratio:.3f}" == e["lab_printed"]
+    assert Fraction(2 * e["N"], tot) == Fraction(32, 9)
+
+
+def test_residual_example_299_5_MiB():
+    r = _gold("byte_budgets.json")["residual_example"]
+    L = r["layer"]
+    sect, tot = oracle.int4_cache_sizes(1, L["T"], L["Hkv"], L["d"], L["g"], L["R"])
+    assert f"{tot * r['layers'] / 2**20:.3f}" == r["lab_printed_MiB"]
+    # item by item: codes 8064*8*64, K metadata ceil(8064/64)*8*128*4, V metadata 8064*8*2*4, residual
+    assert sect[0] == sect[3] == 8064 * 8 * 64
+    assert sect[1] + sect[2] == 126 * 8 * 128 * 4
+    assert sect[4] + sect[5] == 8064 * 8 * 2 * 4
+    assert sect[6] + sect[7] == 2 * 8 * 128 * 128 * 2
+    assert tot == 9_814_016
+
+
+def test_bytes_accounting():
+    a = _gold("byte_budgets.json")["accounting"]
+    GiB = 2**30
+    assert oracle.kv_bytes(a["L"], a["T"], 2 * a["H"] * a["d"], 2) == a["bf16_GiB"] * GiB
+    assert oracle.kv_bytes(a["L"], a["T"], 2 * a["H_gqa"] * a["d"], 2) == a["gqa_GiB"] * GiB
+    # 4-bit payload of the GQA cache: the code sections of the per-layer INT4 cache, 32 layers
+    sect, _ = oracle.int4_cache_sizes(1, a["T"], a["H_gqa"], a["d"], 64, 0)
+    assert a["L"] * (sect[0] + sect[3]) == a["int4_payload_GiB"] * GiB
+
+
+# ------------------------------------------------------- per-channel quant ----
+
+def test_per_channel_round_half_even():
+    # absmax 7 at bits=4 gives s = 1 exactly, so x/s are exact halves
+    x = np.array([7, 0.5, 1.5, 2.5, -0.5, -1.5, -2.5, 3.5], np.float32).reshape(-1, 1)
+    q, s, _ = oracle.quant_sym(x, bits=4)
+    assert s[0, 0] == 1.0
+    assert q.ravel().tolist() == [7, 0, 2, 2, 0, -2, -2, 4]
+
+
+def test_asym_zero_point_added_after_rounding():
+    # mn=-127, mx=128 -> range 255 -> s = 1; zp = round(-128 + 127) = -1 (odd), so
+    # round(x/s) + zp and round(x/s + zp) differ at halves.
+    x = np.array([-127, 128, 0.5, 2.5, -3.5], np.float32).reshape(-1, 1)
+    q, s, z = oracle.quant_asym(x, -128, 127)
+    assert s[0, 0] == 1.0 and z[0, 0] == -1
+    assert q.ravel().tolist() == [-128, 127, 0 - 1, 2 - 1, -4 - 1]
+
+
+def test_per_channel_closed_forms():
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((64, 16)).astype(np.float32)
+    x[:, 5] = 0.0                     # all-zero channel
+    x[:, 6] = 0.75                    # constant positive channel
+    x[:, 7] = np.abs(x[:, 7]) + 1.0   # all-positive channel
+    q, s, z = oracle.quant_sym(x, bits=8)
+    for c in range(16):
+        col = x[:, c]
+        if c == 5:
+            assert s[0, c] == np.float32(1e-8) / np.float32(127)
+            assert np.all(q[0, :, c] == 0)
+            continue
+        i = int(np.argmax(np.abs(col)))
+        assert q[0, i, c] == (127 if col[i] > 0 else -127)
+        assert np.all(np.abs(q[0, :, c]) <= 127)
+    qa, sa, za = oracle.quant_asym(x, -128, 127)
+    for c in range(16):
+        col = x[:, c]
+        if c in (5, 6, 7):
+            continue
+        assert qa[0, int(np.argmin(col)), c] == -128
+        assert qa[0, int(np.argmax(col)), c] == 127
+    # constant channel: range floored at 1e-8
+    assert sa[0, 6] == np.float32(1e-8) / np.float32(255)
+    # all-positive channel: round(qmin - min/s) is far below -128 and saturates, then
+    # q = clip(round(x/s) - 128, -128, 127)
+    assert za[0, 7] == -128
+    for r in range(64):
+        t = Fraction(float(x[r, 7])) / Fraction(float(sa[0, 7]))
+        n = math.floor(t + Fraction(1, 2))
+        assert qa[0, r, 7] == min(127, max(-128, n - 128))
+
+
+def test_per_channel_nearest_integer():
+    """Each code is the integer nearest to x/s (exact rational arithmetic), clipped."""
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((40, 6)).astype(np.float32)
+    for bits in (2, 4, 8):
+        q, s, _ = oracle.quant_sym(x, bits)
+        qmax = (1 << (bits - 1)) - 1
+        for r in range(40):
+            for c in range(6):
+                t = Fraction(float(x[r, c])) / Fraction(float(s[0, c]))
+                n = int(q[0, r, c])
+                if abs(n) < qmax:
+                    assert abs(t - n) <= Fraction(1, 2) + Fraction(1, 1 << 20)
+
+
+def test_per_channel_axes_and_batches():
+    """Channels are columns; slices are independent: a column scaled by 2 gets a doubled scale."""
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((3, 32, 8)).astype(np.float32)
+    x2 = x.copy()
+    x2[1, :, 3] *= 2
+    q, s, _ = oracle.quant_sym(x, 8)
+    q2, s2, _ = oracle.quant_sym(x2, 8)
+    assert s2[1, 3] == np.float32(2) * s[1, 3]
+    assert np.array_equal(q2, q)
+    mask = np.ones_like(s, bool)
+    mask[1, 3] = False
+    assert np.array_equal(s2[mask], s[mask])
+
+
+def test_dequant_closed_form():
+    q = np.array([-7, -1, 2, 7], np.int8).reshape(1, 4, 1)
+    s = np.array([[0.5]], np.float32)
+    z = np.array([[3]], np.int8)
+    assert oracle.dequant_pc(q, s, z).ravel().tolist() == [-5.0, -2.0, -0.5, 2.0]
+    assert oracle.dequant_pc(q, s, None).ravel().tolist() == [-3.5, -0.5, 1.0, 3.5]
+
+
+def test_per_channel_round_trip_bound():
+    rng = np.random.default_rng(9)
+    x = rng.standard_normal((256, 128)).astype(np.float32)
+    for fn in ("sym", "asym"):
+        if fn == "sym":
+            q, s, z = oracle.quant_sym(x, 8)
+        else:
+            q, s, z = oracle.quant_asym(x, -128, 127)
+        xh = oracle.dequant_pc(q, s, z)[0]
+        err = np.abs(x.astype(np.float64) - xh)
+        # half a step, plus the fp32 rounding of x/s and of the product
+        assert np.all(err <= s.astype(np.float64) * (0.5 + 1e-5))
+
+
+def test_err_stats_closed_form():
+    x = np.array([3, 0, 1], np.float32)
+    xh = np.array([0, 4, 1], np.float32)
+    raw = oracle.err_stats(x, xh)
+    assert raw == (25.0, 7.0, 4.0)
+    rmse, mx, mean = oracle.stats_finalize(raw, 3)
+    assert rmse == math.sqrt(25 / 3) and mx == 4.0 and mean == 7 / 3
+    # bf16 operands are widened exactly
+    raw_b = oracle.err_stats(bf16(x), bf16(xh))
+    assert raw_b == raw
+
+
+def test_compression_ratio_config_1():
+    # fp32 [256][128]: data 32768 B int8, scale 128 fp32, zero point 128 int8
+    r = oracle.compression_ratio(256 * 128 * 4, 256 * 128, 128 * 4, 128)
+    assert r == 131072 / 33408
+    assert f"{r:.6f}" == "3.923372"
+
+
+# ------------------------------------------------------------- INT4 groups ----
+
+def _level_cache(B, T, H, d, g, R, seed):
+    """K, V whose every group is made of exactly the 16 levels (k - z0) * s0, with s0 a
+    power of two and z0 an integer in [0, 15], so scale, zero, codes and x_hat are known
+    in closed form.  K groups run over tokens per channel, V groups over channels per token."""
+    rng = np.random.default_rng(seed)
+    Tq = T - R
+    K = np.zeros((B, T, H, d), np.float32)
+    V = np.zeros((B, T, H, d), np.float32)
+    kcode = np.zeros((B, T, H, d), np.int64)
+    vcode = np.zeros((B, T, H, d), np.int64)
+    ks = np.zeros((B, H, -(-Tq // g), d))
+    kz = np.zeros_like(ks)
+    vs = np.zeros((B, H, Tq, d // g))
+    vz = np.zeros_like(vs)
+    for b in range(B):
+        for h in range(H):
+            for j in range(-(-Tq // g)):
+                t0, n = j * g, min(g, Tq - j * g)
+                for c in range(d):
+                    s0 = 2.0 ** int(rng.integers(-6, 3))
+                    z0 = int(rng.integers(0, 16))
+                    codes = rng.integers(0, 16, n)
+                    if n >= 2:
+                        codes[rng.choice(n, 2, replace=False)] = [0, 15]
+                    else:  # a one-token group: value 0 gives code 0 and zero 0
+                        codes[0], z0 = 0, 0
+                    kcode[b, t0:t0 + n, h, c] = codes
+                    K[b, t0:t0 + n, h, c] = (codes - z0) * s0
+                    ks[b, h, j, c] = s0 if n >= 2 else np.nan
+                    kz[b, h, j, c] = z0
+            for t in range(Tq):
+                for k in range(d // g):
+                    s0 = 2.0 ** int(rng.integers(-6, 3))
+                    z0 = int(rng.integers(0, 16))
+                    codes = rng.integers(0, 16, g)
+                    codes[rng.choice(g, 2, replace=False)] = [0, 15]
+                    vcode[b, t, h, k * g:(k + 1) * g] = codes
+                    V[b, t, h, k * g:(k + 1) * g] = (codes - z0) * s0
+                    vs[b, h, t, k] = s0
+                    vz[b, h, t, k] = z0
+    K[:, Tq:] = rng.standard_normal((B, R, H, d))
+    V[:, Tq:] = rng.standard_normal((B, R, H, d))
+    return bf16(K), bf16(V), kcode, vcode, ks, kz, vs, vz
+
+
+@pytest.mark.parametrize("T,R,g", [(64 * 3 + 17, 16, 64), (96, 0, 32), (128 + 5, 5, 128)])
+def test_int4_exact_levels(T, R, g):
+    B, H, d = 2, 3, 128 if g == 128 else 64
+    Kb, Vb, kcode, vcode, ks, kz, vs, vz = _level_cache(B, T, H, d, g, R, seed=T + g)
+    c = oracle.int4_quant(Kb, Vb, g, R)
+    Tq = T - R
+    full = ~np.isnan(ks)
+    assert np.array_equal(f32(c["k_scale"])[full], ks[full].astype(np.float32))
+    assert np.array_equal(f32(c["k_zero"])[full], kz[full].astype(np.float32))
+    assert np.array_equal(f32(c["v_scale"]), vs.astype(np.float32))
+    assert np.array_equal(f32(c["v_zero"]), vz.astype(np.float32))
+    # packed bytes: low nibble = even channel, high nibble = odd channel; [B][H][Tq][d/2]
+    kc = kcode[:, :Tq].transpose(0, 2, 1, 3)
+    vc = vcode[:, :Tq].transpose(0, 2, 1, 3)
+    assert np.array_equal(c["k_codes"], (kc[..., 0::2] | (kc[..., 1::2] << 4)).astype(np.uint8))
+    assert np.array_equal(c["v_codes"], (vc[..., 0::2] | (vc[..., 1::2] << 4)).astype(np.uint8))
+    # dequantization reproduces the levels exactly, and the residual verbatim
+    assert np.array_equal(oracle.int4_dequant(c, "k"), f32(Kb))
+    assert np.array_equal(oracle.int4_dequant(c, "v"), f32(Vb))
+    assert np.array_equal(c["k_res"], Kb[:, Tq:].transpose(0, 2, 1, 3))
+    assert np.array_equal(c["v_res"], Vb[:, Tq:].transpose(0, 2, 1, 3))
+
+
+def _c2_like(B, T, H, d, seed):
+    rng = np.random.default_rng(seed)
+    K = rng.standard_normal((B, T, H, d)).astype(np.float32)
+    K[..., rng.choice(d, 4, replace=False)] *= 10
+    V = rng.standard_normal((B, T, H, d)).astype(np.float32)
+    return bf16(K), bf16(V)
+
+
+def _levels_and_ids(c, side):
+    """Per element of the quantized region: (code, scale, zero) as fp64, [B][Tq][H][d]."""
+    B, T, H, d, g, R = (c[k] for k in ("B", "T", "H", "d", "g", "R"))
+    Tq = T - R
+    codes = c[side + "_codes"]
+    q = np.stack([codes & 15, codes >> 4], -1).reshape(B, H, Tq, d).transpose(0, 2, 1, 3)
+    s = f32(c[side + "_scale"]).astype(np.float64)
+    z = f32(c[side + "_zero"]).astype(np.float64)
+    if side == "k":
+        s = np.repeat(s, g, axis=2)[:, :, :Tq].transpose(0, 2, 1, 3)
+        z = np.repeat(z, g, axis=2)[:, :, :Tq].transpose(0, 2, 1, 3)
+    else:
+        s = np.repeat(s, g, axis=3).transpose(0, 2, 1, 3)
+        z = np.repeat(z, g, axis=3).transpose(0, 2, 1, 3)
+    return q.astype(np.int64), s, z
+
+
+@pytest.mark.parametrize("g", [32, 64, 128])
+def test_int4_round_trip_bound_and_nearest_level(g):
+    B, T, H, d, R = 1, 300, 2, 128, 44
+    Kb, Vb = _c2_like(B, T, H, d, seed=g)
+    c = oracle.int4_quant(Kb, Vb, g, R)
+    Tq = T - R
+    for side, X in (("k", Kb), ("v", Vb)):
+        x = f32(X)[:, :Tq].astype(np.float64)
+        xh = oracle.int4_dequant(c, side)[:, :Tq].astype(np.float64)
+        q, s, z = _levels_and_ids(c, side)
+        # round trip: every element within half a (stored, bf16) step
+        assert np.all(np.abs(x - xh) <= s / 2)
+        # brute force: the code is the nearest of the 16 levels (k - z) * s; exact ties go
+        # to the even (k - z); the levels are exact in fp64
+        levels = (np.arange(16)[None, None, None, None, :] - z[..., None]) * s[..., None]
+        dist = np.abs(x[..., None] - levels)
+        best = dist.min(-1, keepdims=True)
+        cand = dist == best
+        even = ((np.arange(16)[None, None, None, None, :] - z[..., None]) % 2) == 0
+        pick = np.where(cand.sum(-1) > 1, np.argmax(cand & even, -1), np.argmax(cand, -1))
+        assert np.array_equal(pick, q)
+        # the K outlier channels get their own (larger) per-channel scales
+        if side == "k":
+            ksc = f32(c["k_scale"])
+            big = np.argsort(ksc.mean(axis=(0, 1, 2)))[-4:]
+            assert ksc[..., big].min() > 3 * np.median(ksc)
+
+
+def test_int4_special_groups():
+    B, T, H, d, g = 1, 64, 1, 64, 64
+    K = np.zeros((B, T, H, d), np.float32)
+    V = np.zeros((B, T, H, d), np.float32)
+    K[..., 1] = 3.0                       # constant channel
+    K[0, :, 0, 2] = np.linspace(1, 2, T)  # all-positive channel
+    c = oracle.int4_quant(bf16(K), bf16(V), g, 0)
+    s0 = f32(c["k_scale"])[0, 0, 0]
+    z0 = f32(c["k_zero"])[0, 0, 0]
+    # all-zero channel: range floored at 1e-8, scale = smallest bf16 >= 1e-8/15, code 0, x_hat 0
+    want = np.float32(np.float32(1e-8) / np.float32(15))
+    assert s0[0] >= want and s0[0] < want * (1 + 2.0**-7)
+    assert z0[0] == 0 and np.all((c["k_codes"][0, 0, :, 0] & 15) == 0)
+    assert np.all(oracle.int4_dequant(c, "k")[..., 0] == 0)
+    # all-positive group: z negative, every value still within half a step
+    xh = oracle.int4_dequant(c, "k")[0, :, 0, 2].astype(np.float64)
+    x = f32(bf16(K))[0, :, 0, 2].astype(np.float64)
+    assert z0[2] < 0
+    assert np.all(np.abs(x - xh) <= float(s0[2]) / 2)
+    # V rows of zeros
+    assert np.all(oracle.int4_dequant(c, "v") == 0)
+
+
+# ---------------------------------------------------------- decode attention --
+
+def _all_residual_cache(K, V, g=64):
+    """A cache holding every token in the bf16 residual (Tq = 0): x_hat is the input."""
+    return oracle.int4_quant(K, V, g, K.shape[1])
+
+
+def test_attn_single_token_returns_its_value():
+    rng = np.random.default_rng(1)
+    K = bf16(rng.standard_normal((2, 1, 2, 64)))
+    V = bf16(rng.standard_normal((2, 1, 2, 64)))
+    q = bf16(rng.standard_normal((2, 4, 64)))
+    c = _all_residual_cache(K, V)
+    o = oracle.decode_attn(c, q, 0.125)
+    for b in range(2):
+        for hq in range(4):
+            assert np.array_equal(o[b, hq], f32(V)[b, 0, hq // 2].astype(np.float64))
+
+
+def test_attn_zero_query_is_mean_of_values():
+    Kb, Vb = _c2_like(1, 192, 2, 64, seed=4)
+    c = oracle.int4_quant(Kb, Vb, 64, 64)
+    q = np.zeros((1, 2, 64), np.uint16)
+    o = oracle.decode_attn(c, q)
+    vh = oracle.int4_dequant(c, "v").astype(np.float64)
+    for hq in range(2):
+        assert np.allclose(o[0, hq], vh[0, :, hq].mean(0), rtol=0, atol=1e-12)
+
+
+def test_attn_two_tokens_closed_form():
+    # q = e_0, k_0 = 0, k_1[0] = ln 3 (as bf16): weights 1/(1+e^a), e^a/(1+e^a)
+    d = 64
+    K = np.zeros((1, 2, 1, d), np.float32)
+    K[0, 1, 0, 0] = math.log(3.0)
+    V = np.zeros((1, 2, 1, d), np.float32)
+    V[0, 0, 0, :] = 1.0
+    V[0, 1, 0, :] = -2.0
+    Kb, Vb = bf16(K), bf16(V)
+    a = float(f32(Kb)[0, 1, 0, 0])
+    q = np.zeros((1, 1, d), np.float32)
+    q[0, 0, 0] = 1.0
+    o = oracle.decode_attn(_all_residual_cache(Kb, Vb), bf16(q))
+    w1 = math.exp(a) / (1 + math.exp(a))
+    assert np.allclose(o[0, 0], (1 - w1) * 1.0 + w1 * -2.0, rtol=0, atol=1e-14)
+    # the softmax scale multiplies the logits: weights exp(0.5 a) / (1 + exp(0.5 a))
+    o = oracle.decode_attn(_all_residual_cache(Kb, Vb), bf16(q), 0.5)
+    w1 = math.exp(0.5 * a) / (1 + math.exp(0.5 * a))
+    assert np.allclose(o[0, 0], (1 - w1) * 1.0 + w1 * -2.0, rtol=0, atol=1e-14)
+
+
+def test_attn_gqa_head_map():
+    # V of KV head h is the constant h + 1; query head hq must read KV head hq // (Hq/Hkv)
+    rng = np.random.default_rng(2)
+    B, T, Hkv, Hq, d = 2, 80, 3, 12, 64
+    K = bf16(rng.standard_normal((B, T, Hkv, d)))
+    V = np.zeros((B, T, Hkv, d), np.float32)
+    for h in range(Hkv):
+        V[:, :, h, :] = h + 1
+    # all tokens in the bf16 residual: a constant INT4 group cannot hold a nonzero
+    # constant exactly (see test_int4_constant_group_limit)
+    c = oracle.int4_quant(K, bf16(V), 64, T)
+    q = bf16(rng.standard_normal((B, Hq, d)))
+    o = oracle.decode_attn(c, q)
+    for hq in range(Hq):
+        assert np.allclose(o[:, hq], hq // (Hq // Hkv) + 1, rtol=0, atol=1e-12)
+    # the same map with INT4 K in front of the residual
+    c2 = oracle.int4_quant(K, bf16(V), 64, 16)
+    vh = oracle.int4_dequant(c2, "v")
+    o2 = oracle.decode_attn(c2, q)
+    for hq in range(Hq):
+        h = hq // (Hq // Hkv)
+        lo, hi = vh[:, :, h].min(), vh[:, :, h].max()
+        assert np.all((o2[:, hq] >= lo - 1e-12) & (o2[:, hq] <= hi + 1e-12))
+        assert abs(o2[:, hq].mean() - (h + 1)) < 1e-2
+
+
+def test_int4_constant_group_limit():
+    # A constant nonzero group has range 0, floored at 1e-8: s is tiny, z = round(-x/s) is
+    # huge and its bf16 rounding (8 significant bits) moves x_hat by up to |x| * 2^-8.
+    K = np.full((1, 64, 1, 64), 1.0, np.float32)
+    c = oracle.int4_quant(bf16(K), bf16(K), 64, 0)
+    xh = oracle.int4_dequant(c, "k")
+    assert np.all(np.abs(xh - 1.0) <= 2.0**-8)
+    assert np.abs(f32(c["k_zero"])).min() > 2**24
+
+
+def test_attn_dominant_logit_picks_its_value():
+    rng = np.random.default_rng(6)
+    d, T = 64, 40
+    K = rng.standard_normal((1, T, 1, d)).astype(np.float32) * 0.01
+    K[0, 17, 0, :] = 1.0
+    V = rng.standard_normal((1, T, 1, d)).astype(np.float32)
+    q = np.full((1, 1, d), 1.0, np.float32)
+    Kb, Vb = bf16(K), bf16(V)
+    o = oracle.decode_attn(_all_residual_cache(Kb, Vb), bf16(q))
+    assert np.allclose(o[0, 0], f32(Vb)[0, 17, 0], rtol=0, atol=1e-12)
+
+
+def test_attn_rows_match_full():
+    Kb, Vb = _c2_like(2, 130, 2, 64, seed=8)
+    c = oracle.int4_quant(Kb, Vb, 64, 2)
+    q = bf16(np.random.default_rng(8).standard_normal((2, 4, 64)))
+    full = oracle.decode_attn(c, q, 0.5)
+    rows = [(1, 3), (0, 0), (1, 1)]
+    part = oracle.decode_attn(c, q, 0.5, rows=rows)
+    for i, (b, hq) in enumerate(rows):
+        assert np.array_equal(part[i], full[b, hq])
+
+
+def test_attn_error_propagation_bounds():
+    """Explainer, 'K error changes the weights, V error changes the content': with the
+    weights fixed (K exact) the output moves by at most max_i ||dv_i||; a K error moves
+    logit i by at most ||q|| ||dk_i|| (scale folded into q)."""
+    rng = np.random.default_rng(12)
+    B, T, H, d, g = 1, 256, 1, 64, 32
+    Kl, _, _, _, _, _, _, _ = _level_cache(B, T, H, d, g, 0, seed=99)   # K exact under INT4
+    _, Vb = _c2_like(B, T, H, d, seed=12)
+    q = bf16(rng.standard_normal((B, 1, d)) / 8)
+    exact = oracle.int4_quant(Kl, Vb, g, T)              # every token bf16
+    quant = oracle.int4_quant(Kl, Vb, g, 0)              # every token INT4
+    assert np.array_equal(oracle.int4_dequant(quant, "k"), f32(Kl))
+    vx = f32(Vb).astype(np.float64)[0, :, 0]
+    vh = oracle.int4_dequant(quant, "v").astype(np.float64)[0, :, 0]
+    o_ref = oracle.decode_attn(exact, q)[0, 0]
+    o_v = oracle.decode_attn(quant, q)[0, 0]
+    dv = np.linalg.norm(vh - vx, axis=1).max()
+    assert 0 < np.linalg.norm(o_v - o_ref) <= dv
+    # K error on random K: Cauchy-Schwarz bound on each logit
+    Kb, _ = _c2_like(B, T, H, d, seed=13)
+    qk = oracle.int4_quant(Kb, Vb, g, 0)
+    kx = f32(Kb).astype(np.float64)[0, :, 0]
+    kh = oracle.int4_dequant(qk, "k").astype(np.float64)[0, :, 0]
+    qv = f32(q)[0, 0].astype(np.float64)
+    dlog = np.abs((kh - kx) @ qv)
+    assert np.all(dlog <= np.linalg.norm(qv) * np.linalg.norm(kh - kx, axis=1) + 1e-12)
+
+
+# ------------------------------------------------------------ selection -------
+
+def test_colsum_is_sequential_fp32():
+    # sequential fp32: (0 + 1e8) + 1 rounds back to 1e8, then - 1e8 gives 0
+    hist = np.array([[[1e8], [1.0], [-1e8]]], np.float32)
+    assert oracle.colsum(hist)[0, 0] == 0.0
+    # in step order 1 + 1e8 rounds to 1e8, then - 1e8 gives 0 (the reverse order gives 1)
+    hist = np.array([[[1.0], [1e8], [-1e8]]], np.float32)
+    assert oracle.colsum(hist)[0, 0] == 0.0
+    # exactly representable terms: exact sum
+    h = (np.arange(5 * 7, dtype=np.float32).reshape(1, 5, 7) / 8.0)
+    assert np.array_equal(oracle.colsum(h)[0], h[0].astype(np.float64).sum(0).astype(np.float32))
+
+
+def test_keep_count_closed_form():
+    for T in (1, 5, 100, 300):
+        for B in (0, 3, 64, 200, 400):
+            for W in (0, 1, 10, 256, 1000):
+                sc = np.random.default_rng(T + B + W).random((1, T)).astype(np.float32)
+                keep = oracle.select(sc, B, W)
+                assert keep.shape[1] == min(T, max(B, min(W, T)))
+
+
+def _rank_count_heavy(masked, k):
+    n = len(masked)
+    out = set()
+    for i in range(n):
+        better = sum(1 for j in range(n) if masked[j] > masked[i] or (masked[j] == masked[i] and j < i))
+        if better < k:
+            out.add(i)
+    return out
+
+
+def test_select_bruteforce_small():
+    rng = np.random.default_rng(21)
+    for trial in range(400):
+        T = int(rng.integers(1, 13))
+        B = int(rng.integers(0, 15))
+        W = int(rng.integers(0, 6))
+        sc = (rng.integers(0, 4, T) / 4.0).astype(np.float32)   # many ties
+        keep = oracle.select(sc[None], B, W)[0].tolist()
+        rs = max(0, T - W)
+        masked = [float(sc[j]) if j < rs else -math.inf for j in range(T)]
+        heavy = _rank_count_heavy(masked, min(max(0, B - (T - rs)), T))
+        want = sorted(set(range(rs, T)) | heavy)
+        assert keep == want, (T, B, W, sc.tolist())
+
+
+def test_select_ties_take_lower_index():
+    sc = np.full((1, 20), 0.5, np.float32)
+    assert oracle.select(sc, 8, 3)[0].tolist() == [0, 1, 2, 3, 4, 17, 18, 19]
+
+
+def test_select_invariants_and_snapkv_equals_h2o():
+    rng = np.random.default_rng(4)
+    hist = rng.random((3, 8, 500)).astype(np.float32)
+    keep, scores = oracle.h2o_select(hist, 96, 32)
+    assert np.array_equal(oracle.select(oracle.colsum(hist), 96, 32), keep)
+    for r in range(3):
+        k = keep[r]
+        assert np.all(np.diff(k) > 0)
+        assert set(range(500 - 32, 500)) <= set(k.tolist())
+        kept = [j for j in k if j < 468]
+        dropped = sorted(set(range(468)) - set(kept))
+        assert min(scores[r, kept]) >= max(scores[r, dropped])
+
+
+def test_token_ratio_and_total_gain():
+    assert oracle.token_ratio(32768, 2048) == 16.0
+    for T, K in ((0, 1), (10, 0), (10, 11), (-1, -1)):
+        with pytest.raises(ValueError):
+            oracle.token_ratio(T, K)
+    assert oracle.total_gain(2.0, 0.5625, 32768, 2048) == (2.0 / 0.5625) * 16.0
+
+
+def test_compact_gathers_labelled_rows():
+    B, T, H, d, K = 2, 50, 3, 8, 7
+    src = np.zeros((B, T, H, d), np.uint16)
+    for b in range(B):
+        for t in range(T):
+            for h in range(H):
+                src[b, t, h, :] = b * 10000 + t * 10 + h
+    rng = np.random.default_rng(0)
+    keep = np.sort(np.stack([[rng.choice(T, K, replace=False) for _ in range(H)] for _ in range(B)]), -1).astype(np.int32)
+    dst = oracle.compact(src, keep)
+    for b in range(B):
+        for k in range(K):
+            for h in range(H):
+                assert np.all(dst[b, k, h] == b * 10000 + keep[b, h, k] * 10 + h)
+
+
+def test_bf16_helpers():
+    # nearest-even on a tie: 1 + 2^-8 is halfway between 1 and 1 + 2^-7 -> 1 (even)
+    assert oracle.f32_to_bf16(np.float32(1 + 2.0**-8)).item() == 0x3F80
+    assert oracle.f32_to_bf16(np.float32(1 + 3 * 2.0**-8)).item() == 0x3F82
+    assert oracle.f32_to_bf16(np.float32(-1.5)).item() == 0xBFC0
+    assert float(oracle.bf16_to_f32(np.array([0x4049], np.uint16))[0]) == 3.140625
