@@ -1,0 +1,243 @@
+/* kvq.h -- C ABI of libkvq, KV-cache compression on AMD Instinct MI355X (gfx950).
+ *
+ * Sources (cited by page title and section):
+ *   [Walkthrough] "KV Compression 公式到源码对照", formula-to-code walkthrough of a
+ *                 per-channel quantizer and an H2O / SnapKV sparsifier (§1.1-§4).
+ *   [Explainer]   "KV cache 压缩：把历史装得更小", animated explainer of KV-cache
+ *                 compression: KIVI-style 4-bit groups, byte budgets, eviction,
+ *                 fused dequantization in the attention kernel.
+ *
+ * Conventions shared by every entry point
+ *   - Return value: KVQ_OK (0) or a negative status.  kvq_last_error() returns a
+ *     thread-local description of the last failure of the calling thread.
+ *   - Arguments are validated before anything is launched; on KVQ_EINVAL or
+ *     KVQ_EALIGN nothing is written and nothing is enqueued.
+ *   - Pointers named dev_* or documented as "device" are device (HBM) pointers;
+ *     everything else is host memory.  The caller owns and allocates every
+ *     buffer, including workspaces sized by the matching *_ws() query.  The
+ *     library never allocates device memory.
+ *   - Device work is enqueued asynchronously on `stream` (a hipStream_t; NULL
+ *     is the null stream); no entry point synchronizes the host.
+ *   - Device pointers must be 16-byte aligned; innermost dimensions are dense.
+ *   - bf16 data are raw 16-bit patterns (uint16_t).  fp32 -> bf16 rounds to
+ *     nearest even.
+ *   - Inputs are finite.  Codes, scales, zero points, packed bytes and kept
+ *     indices are bit-identical to the plain definitions given below (fp32 IEEE
+ *     division, round-half-to-even, no fused steps).
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVQ_OK 0
+#define KVQ_EINVAL (-1) /* a shape, size or parameter the operation does not define */
+#define KVQ_EALIGN (-2) /* a device pointer is not 16-byte aligned */
+#define KVQ_EHIP (-3)   /* the HIP runtime reported an error (launch, stream) */
+
+#define KVQ_FP32 0
+#define KVQ_BF16 1
+
+typedef void* kvq_stream; /* hipStream_t */
+
+const char* kvq_last_error(void);
+int kvq_abi_version(void); /* 1 */
+
+/* ======================================================================
+ * Per-channel quantization  [Walkthrough §1.1, §1.2]
+ *
+ * x holds nb slices, each a [R][C] matrix (rows = tokens, columns = channels;
+ * a multi-dimensional cache puts every non-token dimension into C).  Element
+ * (s, r, c) is at x + s*bsx + r*ldx + c (in elements of type xt).  Channel c of
+ * slice s is quantized with its own scale, reduced over the R rows.
+ *
+ * kvq_quant_sym:   qmax = 2^(bits-1) - 1, bits in [2, 8];
+ *                  scale = max(max_r |x|, fp32(1e-8)) / qmax;
+ *                  q = clip(round(x / scale), -qmax, qmax).
+ * kvq_quant_asym:  scale = max(max_r x - min_r x, fp32(1e-8)) / (qmax - qmin);
+ *                  zp = round(qmin - min_r x / scale) saturated to int8;
+ *                  q = clip(round(x / scale) + zp, qmin, qmax); -128 <= qmin < qmax <= 127.
+ * round() is round-half-to-even.
+ *
+ * Outputs (device): q int8 [nb][R][C] dense; scale fp32 [nb][C]; zp int8 [nb][C]
+ * (zp is optional for sym and then filled with 0 when given).
+ * Workspace (device): kvq_quant_pc_ws(nb, R, C) bytes.
+ * EINVAL: nb, R or C < 1; ldx < C; bsx < R*ldx (when nb > 1); bits or qmin/qmax
+ *         outside the ranges above; NULL x, q or scale (or zp for asym); a
+ *         workspace smaller than the query.
+ * ====================================================================== */
+size_t kvq_quant_pc_ws(int64_t nb, int64_t R, int64_t C);
+int kvq_quant_sym(const void* x, int xt, int64_t nb, int64_t R, int64_t C, int64_t ldx, int64_t bsx,
+                  int bits, int8_t* q, float* scale, int8_t* zp_or_null, void* ws, size_t ws_bytes,
+                  kvq_stream stream);
+int kvq_quant_asym(const void* x, int xt, int64_t nb, int64_t R, int64_t C, int64_t ldx, int64_t bsx,
+                   int qmin, int qmax, int8_t* q, float* scale, int8_t* zp, void* ws, size_t ws_bytes,
+                   kvq_stream stream);
+
+/* ======================================================================
+ * KIVI-style 4-bit group quantization of one layer  [Explainer: quantization,
+ * grouping axis, group-size table and residual-budget sections; integer steps of
+ * Walkthrough §1.2 with qmin = 0, qmax = 15]
+ *
+ * Inputs K, V: bf16 [B][T][H][d] (device).  The first Tq = T - R tokens are
+ * quantized, the last R tokens are kept verbatim as a bf16 residual.
+ *   K is grouped per channel across g consecutive tokens (the last group of a
+ *   channel is partial when g does not divide Tq); V is grouped per token across
+ *   g consecutive channels.  Per group:
+ *     s = smallest bf16 >= max(max - min, fp32(1e-8)) / 15   (stored bf16)
+ *     z = round(0 - min / s), stored as bf16 (exact while |z| <= 256)
+ *     q = clip(round(x / s) + z, 0, 15), using the stored s and z.
+ *   Dequantization: x_hat = (q - z) * s, rounded once (exact in fp32 for |z| < 2^15).
+ * Sections (device, caller-allocated, sizes from kvq_int4_cache_sizes):
+ *   [0] k_codes u8   [B][H][Tq][d/2]  byte j = code(2j) | code(2j+1) << 4
+ *   [1] k_scale bf16 [B][H][ceil(Tq/g)][d]
+ *   [2] k_zero  bf16 [B][H][ceil(Tq/g)][d]
+ *   [3] v_codes u8   [B][H][Tq][d/2]
+ *   [4] v_scale bf16 [B][H][Tq][d/g]
+ *   [5] v_zero  bf16 [B][H][Tq][d/g]
+ *   [6] k_res   bf16 [B][H][R][d]
+ *   [7] v_res   bf16 [B][H][R][d]
+ * Total bytes of the quantized region follow ceil(N/2) + ceil(N/g)*4 per group
+ * axis [Explainer, group-size table].
+ * EINVAL: any of B, T, H < 1; d not in {64, 128, 256}; g not in {32, 64, 128} or
+ *         g > d; R < 0 or R > T; a NULL section pointer of nonzero size.
+ * ====================================================================== */
+typedef struct {
+    int64_t B, T, H, d, g, R;
+    uint8_t* k_codes;
+    uint16_t* k_scale;
+    uint16_t* k_zero;
+    uint8_t* v_codes;
+    uint16_t* v_scale;
+    uint16_t* v_zero;
+    uint16_t* k_res;
+    uint16_t* v_res;
+} kvq_int4_cache;
+
+int kvq_int4_cache_sizes(int64_t B, int64_t T, int64_t H, int64_t d, int64_t g, int64_t R,
+                         size_t sect_bytes[8], size_t* total);
+int kvq_group_quant_int4(const void* K, const void* V, const kvq_int4_cache* c, kvq_stream stream);
+
+/* ======================================================================
+ * Dequantization  [Walkthrough §1.3: x_hat = (q - zero_point) * scale]
+ *
+ * kind KVQ_FMT_PER_CHANNEL: desc -> kvq_pc_tensor; out [nb][R][C] dense.
+ *      x_hat = ((float)(q - zp)) * scale, one fp32 rounding (zp NULL = 0).
+ * kind KVQ_FMT_INT4_K / KVQ_FMT_INT4_V: desc -> kvq_int4_cache; out is the
+ *      original [B][T][H][d] layout of K (resp. V); residual tokens are copied.
+ * ot: KVQ_FP32 or KVQ_BF16 (fp32 result rounded to nearest even).
+ * EINVAL: unknown kind or ot, NULL pointers, shapes as for the quantizers.
+ * ====================================================================== */
+#define KVQ_FMT_PER_CHANNEL 1
+#define KVQ_FMT_INT4_K 2
+#define KVQ_FMT_INT4_V 3
+
+typedef struct {
+    const int8_t* q;
+    const float* scale;
+    const int8_t* zp; /* may be NULL */
+    int64_t nb, R, C;
+} kvq_pc_tensor;
+
+typedef struct {
+    int kind;
+    const void* desc;
+} kvq_qdesc;
+
+int kvq_dequant(const kvq_qdesc* src, void* out, int ot, kvq_stream stream);
+
+/* ======================================================================
+ * Error statistics  [Walkthrough §1.3: RMSE, max_abs_error, mean_abs_error]
+ *
+ * dev_out (device, 3 doubles, 8-byte aligned): sum (x - x_hat)^2, sum |x - x_hat|, max |x - x_hat|
+ * over n elements, accumulated in fp64 with a fixed (run-to-run identical) order.
+ * kvq_stats_finalize (host): rmse = sqrt(sum_sq / n), mean = sum_abs / n.
+ * Workspace (device): kvq_err_stats_ws(n) bytes.
+ * EINVAL: n < 1, NULL pointers, unknown dtypes, short workspace.
+ * ====================================================================== */
+size_t kvq_err_stats_ws(int64_t n);
+int kvq_err_stats(const void* x, int xt, const void* xhat, int ht, int64_t n, double* dev_out,
+                  void* ws, size_t ws_bytes, kvq_stream stream);
+int kvq_stats_finalize(const double in[3], int64_t n, double* rmse, double* max_abs, double* mean_abs);
+
+/* Host-only accounting helpers (pure functions, no device access). */
+/* [Walkthrough §2] orig / (data + scale + zero_point); 0 when the denominator is 0. */
+double kvq_compression_ratio(uint64_t orig_bytes, uint64_t data, uint64_t scale, uint64_t zp);
+/* [Explainer, group-size table] ceil(N/2) + ceil(N/g) * 4; 0 when g == 0. */
+uint64_t kvq_int4_bytes(uint64_t N, uint64_t g);
+/* [Walkthrough §4] T / K; KVQ_EINVAL unless 0 < K <= T. */
+int kvq_token_ratio(int64_t T, int64_t K, double* out);
+/* [Walkthrough §4] (s_old / s_new) * (T / K); KVQ_EINVAL unless 0 < K <= T and s_new > 0. */
+int kvq_total_gain(double s_old, double s_new, int64_t T, int64_t K, double* out);
+/* [Explainer, "four kinds of smaller"] L * T_stored * C_stored * b + metadata. */
+uint64_t kvq_kv_bytes(uint64_t L, uint64_t T, uint64_t C, uint64_t b, uint64_t metadata);
+/* [Walkthrough §3.2] size of recent ∪ TopK: min(T, max(budget, min(window, T))); -1 on bad input. */
+int64_t kvq_keep_count(int64_t T, int64_t budget, int64_t window);
+
+/* ======================================================================
+ * GQA decode attention over the INT4 cache  [Explainer: "the attention kernel
+ * reads the low-bit cache and dequantizes it" (quantization section) and "let the
+ * kernel cash in the savings: compact layout, fused dequantization" (evaluation
+ * section); GQA head sharing from the GQA section]
+ *
+ * For every batch b and query head hq (one query token each):
+ *   h = hq / (Hq / H)   (consecutive query heads share a KV head)
+ *   out[b][hq] = softmax_t(sm_scale * q[b][hq] . k_hat[b][t][h]) . v_hat[b][t][h]
+ * over all T tokens: the INT4 tokens dequantized as in kvq_group_quant_int4 and
+ * the R residual tokens read as bf16.  Scores, softmax and accumulation are fp32.
+ * q is bf16 [B][Hq][d] (device); out is [B][Hq][d] (device) of type ot: KVQ_FP32, or
+ * KVQ_BF16 = the fp32 result rounded to nearest even.
+ * Workspace (device): kvq_decode_attn_int4_ws(c, Hq) bytes.
+ * EINVAL: cache shape as above, Hq < 1, Hq % H != 0, Hq / H not in {1, 2, 4, 8, 16},
+ *         unknown ot, NULL pointers, short workspace.
+ * ====================================================================== */
+size_t kvq_decode_attn_int4_ws(const kvq_int4_cache* c, int64_t Hq);
+int kvq_decode_attn_int4(const kvq_int4_cache* c, const void* q, int64_t Hq, float sm_scale, void* out,
+                         int ot, void* ws, size_t ws_bytes, kvq_stream stream);
+
+/* ======================================================================
+ * H2O / SnapKV token selection  [Walkthrough §3.1-§3.3]
+ *
+ * kvq_h2o_select: hist fp32 [rows][T_obs][T] (device).  score[j] = sum over t of
+ *   hist[t][j], fp32, added in t order from 0.0 (cumulative attention).  When
+ *   scores_or_null is given the scores are also written there ([rows][T]).
+ * kvq_snapkv_select: scores fp32 [rows][T] given (one-shot observation scores).
+ * Both then, per row: recent = [max(0, T - window), T); the recent scores are
+ *   replaced by -inf; TopK of the masked scores with k = max(0, budget - |recent|)
+ *   (larger first, equal scores -> lower index, NaN below every number); keep =
+ *   the sorted union of recent and TopK, int32 [rows][kvq_keep_count(T, budget,
+ *   window)] (device); when that count is 0, keep may be NULL and nothing is selected.
+ * Workspace (device): kvq_select_ws(rows, T) bytes (h2o needs room for the scores
+ *   when scores_or_null is NULL; snapkv needs none).
+ * EINVAL: rows, T_obs or T < 1, T > 2^31 - 1, budget < 0, window < 0, NULL
+ *   pointers, short workspace.
+ * ====================================================================== */
+size_t kvq_select_ws(int64_t rows, int64_t T);
+int kvq_h2o_select(const float* hist, int64_t rows, int64_t T_obs, int64_t T, int64_t budget,
+                   int64_t window, float* scores_or_null, int32_t* keep, void* ws, size_t ws_bytes,
+                   kvq_stream stream);
+int kvq_snapkv_select(const float* scores, int64_t rows, int64_t T, int64_t budget, int64_t window,
+                      int32_t* keep, void* ws, size_t ws_bytes, kvq_stream stream);
+
+/* ======================================================================
+ * Compaction of the kept rows  [Explainer, eviction: "keep only the selected KV"]
+ *
+ * k_dst[b][k][h][:] = k_src[b][keep[b][h][k]][h][:] (and the same for V when both
+ * v pointers are given).  k_src, v_src bf16 [B][T][H][d]; keep int32 [B][H][K] with
+ * entries in [0, T) (the output of the selectors with rows = B*H); dst [B][K][H][d].
+ * All device.  Indices are trusted (out-of-range indices are undefined behaviour).
+ * EINVAL: B, T, H, d or K < 1, K > T, d % 8 != 0, NULL k pointers, exactly one
+ *   of v_src / v_dst NULL.
+ * ====================================================================== */
+int kvq_compact(const void* k_src, const void* v_src_or_null, int64_t B, int64_t T, int64_t H, int64_t d,
+                const int32_t* keep, int64_t K, void* k_dst, void* v_dst_or_null, kvq_stream stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KVQ_H */

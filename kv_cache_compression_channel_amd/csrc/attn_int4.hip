@@ -1,0 +1,354 @@
+// attn_int4.hip -- GQA decode attention that reads the INT4 cache and dequantizes it in
+// registers (Explainer (KV cache 压缩：把历史装得更小): the attention kernel reads the
+// low-bit cache and dequantizes it; fusing the dequantization is what turns fewer bytes
+// into bandwidth savings; GQA: consecutive query heads share one KV head).
+//
+// out[b][hq] = softmax_t(sm_scale * q . k_hat_t) . v_hat_t over all T tokens of KV head
+// h = hq / (Hq / H); INT4 tokens dequantize as x_hat = (code - z) * s, residual tokens
+// are bf16.  Split-K: one block per (b, h, token split) handles all Hq/H query heads
+// that share the KV head (each KV byte is read once), then a combine kernel merges the
+// splits with log-sum-exp weights.
+//
+// Dequantization is folded into the arithmetic instead of materialised:
+//   K (scale per channel over a token group):  q . k_hat = sum_c (q_c s_c) code_c - sum_c q_c s_c z_c
+//   V (scale per token per channel group):     p v_hat = (p s) code - (p s) z
+// so each element costs one fused multiply-add on its 4-bit code.  Softmax runs in the
+// base-2 domain (q pre-multiplied by sm_scale * log2 e), fp32 throughout.
+//
+// Lane layout (VALU path): d/8 lanes per token, 8 channels per lane; a wave takes
+// 512/d tokens per step; dot products are finished with butterfly shuffles.
+#include <cmath>
+
+#include "kvq_internal.h"
+
+namespace kvq {
+int check_cache_shape(const kvq_int4_cache* c, const char* name);
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+constexpr float kNegBig = -3.0e38f;
+
+struct AttnArgs {
+    const uint8_t* k_codes;
+    const uint16_t* k_scale;
+    const uint16_t* k_zero;
+    const uint8_t* v_codes;
+    const uint16_t* v_scale;
+    const uint16_t* v_zero;
+    const uint16_t* k_res;
+    const uint16_t* v_res;
+    const uint16_t* q;
+    void* out;
+    int ot;
+    float* ws;
+    int64_t B, T, H, R, Tq, nKg, Hq;
+    int64_t split_len;
+    int nsplit;
+    float qscale;   // sm_scale * log2(e)
+};
+
+__device__ __forceinline__ void unpack8(const uint4 a, float (&v)[8]) {
+    v[0] = bf_lo(a.x); v[1] = bf_hi(a.x); v[2] = bf_lo(a.y); v[3] = bf_hi(a.y);
+    v[4] = bf_lo(a.z); v[5] = bf_hi(a.z); v[6] = bf_lo(a.w); v[7] = bf_hi(a.w);
+}
+
+template <int D, int GS, int NQ>
+__global__ void __launch_bounds__(kThreads) attn_split_kernel(const AttnArgs a) {
+    constexpr int LPT = D / 8;        // lanes per token
+    constexpr int TPW = 64 / LPT;     // tokens per wave step
+    constexpr int TPS = TPW * kWaves; // tokens per block step
+    constexpr int NGD = D / GS;
+    __shared__ float s_m[kWaves][NQ], s_l[kWaves][NQ];
+    __shared__ float s_acc[kWaves][NQ][D];
+
+    const int tid = threadIdx.x, lane = tid % 64, wv = tid / 64;
+    const int li = lane % LPT, tg = lane / LPT;
+    const int64_t bh = blockIdx.x / a.nsplit;
+    const int split = (int)(blockIdx.x % a.nsplit);
+    const int64_t b = bh / a.H, h = bh % a.H;
+    const int64_t t_begin = (int64_t)split * a.split_len;
+    const int64_t t_end = min(a.T, t_begin + a.split_len);
+    const int64_t Tq = a.Tq;
+
+    float qv[NQ][8];
+#pragma unroll
+    for (int qi = 0; qi < NQ; ++qi) {
+        const uint4 raw = *reinterpret_cast<const uint4*>(a.q + ((b * a.Hq + h * NQ + qi) * D + 8 * li));
+        unpack8(raw, qv[qi]);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) qv[qi][c] *= a.qscale;
+    }
+    float m[NQ], l[NQ], acc[NQ][8], zacc[NQ];
+#pragma unroll
+    for (int qi = 0; qi < NQ; ++qi) {
+        m[qi] = kNegBig; l[qi] = 0.0f; zacc[qi] = 0.0f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[qi][c] = 0.0f;
+    }
+    float qk[NQ][8], zb[NQ];
+    int64_t cur_grp = -1;
+    const uint8_t* kc = a.k_codes + (b * a.H + h) * Tq * (D / 2) + 4 * li;
+    const uint8_t* vc = a.v_codes + (b * a.H + h) * Tq * (D / 2) + 4 * li;
+    const int vgrp = (8 * li) / GS;
+
+    for (int64_t t0 = t_begin; t0 < t_end; t0 += TPS) {
+        const int64_t t = t0 + wv * TPW + tg;
+        const bool valid = t < t_end;
+        float logit[NQ];
+        if (valid && t < Tq) {
+            const int64_t grp = t / GS;
+            if (grp != cur_grp) {
+                const int64_t mi = ((b * a.H + h) * a.nKg + grp) * D + 8 * li;
+                float s[8], z[8];
+                unpack8(*reinterpret_cast<const uint4*>(a.k_scale + mi), s);
+                unpack8(*reinterpret_cast<const uint4*>(a.k_zero + mi), z);
+#pragma unroll
+                for (int qi = 0; qi < NQ; ++qi) {
+                    float zz = 0.0f;
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) {
+                        qk[qi][c] = qv[qi][c] * s[c];
+                        zz = __builtin_fmaf(qk[qi][c], z[c], zz);
+                    }
+                    zb[qi] = zz;
+                }
+                cur_grp = grp;
+            }
+            const uint32_t w = *reinterpret_cast<const uint32_t*>(kc + t * (D / 2));
+            float code[8];
+#pragma unroll
+            for (int c = 0; c < 8; ++c) code[c] = (float)((w >> (4 * c)) & 15u);
+#pragma unroll
+            for (int qi = 0; qi < NQ; ++qi) {
+                float p = -zb[qi];
+#pragma unroll
+                for (int c = 0; c < 8; ++c) p = __builtin_fmaf(qk[qi][c], code[c], p);
+                logit[qi] = p;
+            }
+        } else if (valid) {
+            float kv[8];
+            unpack8(*reinterpret_cast<const uint4*>(a.k_res + ((b * a.H + h) * a.R + (t - Tq)) * D + 8 * li), kv);
+#pragma unroll
+            for (int qi = 0; qi < NQ; ++qi) {
+                float p = 0.0f;
+#pragma unroll
+                for (int c = 0; c < 8; ++c) p = __builtin_fmaf(qv[qi][c], kv[c], p);
+                logit[qi] = p;
+            }
+        } else {
+#pragma unroll
+            for (int qi = 0; qi < NQ; ++qi) logit[qi] = 0.0f;
+        }
+        // finish the dot products across the LPT lanes of the token
+#pragma unroll
+        for (int off = 1; off < LPT; off *= 2)
+#pragma unroll
+            for (int qi = 0; qi < NQ; ++qi) logit[qi] += __shfl_xor(logit[qi], off);
+
+        float p[NQ];
+#pragma unroll
+        for (int qi = 0; qi < NQ; ++qi) {
+            if (valid && logit[qi] > m[qi]) {
+                const float alpha = exp2f(m[qi] - logit[qi]);
+                l[qi] *= alpha;
+                zacc[qi] *= alpha;
+#pragma unroll
+                for (int c = 0; c < 8; ++c) acc[qi][c] *= alpha;
+                m[qi] = logit[qi];
+            }
+            p[qi] = valid ? exp2f(logit[qi] - m[qi]) : 0.0f;
+            l[qi] += p[qi];
+        }
+        if (valid && t < Tq) {
+            const uint32_t w = *reinterpret_cast<const uint32_t*>(vc + t * (D / 2));
+            const int64_t mi = ((b * a.H + h) * Tq + t) * NGD + vgrp;
+            const float vs = bf_to_f(a.v_scale[mi]), vz = bf_to_f(a.v_zero[mi]);
+            float code[8];
+#pragma unroll
+            for (int c = 0; c < 8; ++c) code[c] = (float)((w >> (4 * c)) & 15u);
+#pragma unroll
+            for (int qi = 0; qi < NQ; ++qi) {
+                const float pv = p[qi] * vs;
+                zacc[qi] = __builtin_fmaf(pv, vz, zacc[qi]);
+#pragma unroll
+                for (int c = 0; c < 8; ++c) acc[qi][c] = __builtin_fmaf(pv, code[c], acc[qi][c]);
+            }
+        } else if (valid) {
+            float vv[8];
+            unpack8(*reinterpret_cast<const uint4*>(a.v_res + ((b * a.H + h) * a.R + (t - Tq)) * D + 8 * li), vv);
+#pragma unroll
+            for (int qi = 0; qi < NQ; ++qi)
+#pragma unroll
+                for (int c = 0; c < 8; ++c) acc[qi][c] = __builtin_fmaf(p[qi], vv[c], acc[qi][c]);
+        }
+    }
+
+    // acc - zacc: the V zero points (this lane's 8 channels share one V group)
+#pragma unroll
+    for (int qi = 0; qi < NQ; ++qi)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[qi][c] -= zacc[qi];
+
+    // merge the token groups of the wave (same channels, different tokens)
+#pragma unroll
+    for (int off = LPT; off < 64; off *= 2) {
+#pragma unroll
+        for (int qi = 0; qi < NQ; ++qi) {
+            const float mo = __shfl_xor(m[qi], off), lo = __shfl_xor(l[qi], off);
+            const float M = fmaxf(m[qi], mo);
+            const float sa = exp2f(m[qi] - M), sb = exp2f(mo - M);
+            l[qi] = l[qi] * sa + lo * sb;
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                const float ao = __shfl_xor(acc[qi][c], off);
+                acc[qi][c] = acc[qi][c] * sa + ao * sb;
+            }
+            m[qi] = M;
+        }
+    }
+    if (tg == 0) {
+#pragma unroll
+        for (int qi = 0; qi < NQ; ++qi) {
+            if (li == 0) { s_m[wv][qi] = m[qi]; s_l[wv][qi] = l[qi]; }
+#pragma unroll
+            for (int c = 0; c < 8; ++c) s_acc[wv][qi][8 * li + c] = acc[qi][c];
+        }
+    }
+    __syncthreads();
+    // merge the waves and write this split's (m, l, acc[D]) for every query head
+    for (int e = tid; e < NQ * D; e += kThreads) {
+        const int qi = e / D, c = e % D;
+        float M = s_m[0][qi];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w][qi]);
+        float L = 0.0f, A = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const float f = exp2f(s_m[w][qi] - M);
+            L += s_l[w][qi] * f;
+            A += s_acc[w][qi][c] * f;
+        }
+        float* dst = a.ws + ((b * a.Hq + h * NQ + qi) * a.nsplit + split) * (D + 2);
+        if (c == 0) { dst[0] = M; dst[1] = L; }
+        dst[2 + c] = A;
+    }
+}
+
+template <int D, int OT>
+__global__ void __launch_bounds__(D) attn_combine_kernel(const float* __restrict__ ws, int nsplit,
+                                                         void* __restrict__ out) {
+    const int64_t row = blockIdx.x;   // b * Hq + hq
+    const int c = threadIdx.x;
+    const float* base = ws + row * nsplit * (D + 2);
+    float M = kNegBig;
+    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, base[s * (D + 2)]);
+    float L = 0.0f, A = 0.0f;
+    for (int s = 0; s < nsplit; ++s) {
+        const float f = exp2f(base[s * (D + 2)] - M);
+        L += base[s * (D + 2) + 1] * f;
+        A += base[s * (D + 2) + 2 + c] * f;
+    }
+    const float o = A / L;
+    if constexpr (OT == KVQ_FP32)
+        static_cast<float*>(out)[row * D + c] = o;
+    else
+        static_cast<uint16_t*>(out)[row * D + c] = f_to_bf(o);
+}
+
+struct SplitPlan {
+    int nsplit;
+    int64_t split_len;
+};
+
+SplitPlan plan_splits(int64_t B, int64_t H, int64_t T, int64_t g) {
+    const int64_t unit = g > 64 ? g : 64;      // split boundaries stay on K-group and step boundaries
+    const int64_t want = cdiv(2048, B * H);    // aim for >= 2048 blocks
+    int64_t len = cdiv(cdiv(T, want), unit) * unit;
+    if (len < unit) len = unit;
+    return SplitPlan{(int)cdiv(T, len), len};
+}
+
+template <int D, int GS, int NQ>
+void launch_attn(const AttnArgs& a, hipStream_t st) {
+    hipLaunchKernelGGL((attn_split_kernel<D, GS, NQ>), dim3((unsigned)(a.B * a.H * a.nsplit)), dim3(kThreads), 0, st,
+                       a);
+    if (a.ot == KVQ_FP32)
+        hipLaunchKernelGGL((attn_combine_kernel<D, KVQ_FP32>), dim3((unsigned)(a.B * a.Hq)), dim3(D), 0, st, a.ws,
+                           a.nsplit, a.out);
+    else
+        hipLaunchKernelGGL((attn_combine_kernel<D, KVQ_BF16>), dim3((unsigned)(a.B * a.Hq)), dim3(D), 0, st, a.ws,
+                           a.nsplit, a.out);
+}
+
+template <int D, int GS>
+void dispatch_nq(const AttnArgs& a, int nq, hipStream_t st) {
+    switch (nq) {
+        case 1: launch_attn<D, GS, 1>(a, st); break;
+        case 2: launch_attn<D, GS, 2>(a, st); break;
+        case 4: launch_attn<D, GS, 4>(a, st); break;
+        case 8: launch_attn<D, GS, 8>(a, st); break;
+        default: launch_attn<D, GS, 16>(a, st); break;
+    }
+}
+
+void dispatch(const AttnArgs& a, int64_t d, int64_t g, int nq, hipStream_t st) {
+    if (d == 64 && g == 32) dispatch_nq<64, 32>(a, nq, st);
+    else if (d == 64) dispatch_nq<64, 64>(a, nq, st);
+    else if (d == 128 && g == 32) dispatch_nq<128, 32>(a, nq, st);
+    else if (d == 128 && g == 64) dispatch_nq<128, 64>(a, nq, st);
+    else if (d == 128) dispatch_nq<128, 128>(a, nq, st);
+    else if (g == 32) dispatch_nq<256, 32>(a, nq, st);
+    else if (g == 64) dispatch_nq<256, 64>(a, nq, st);
+    else dispatch_nq<256, 128>(a, nq, st);
+}
+
+}  // namespace
+}  // namespace kvq
+
+extern "C" {
+
+size_t kvq_decode_attn_int4_ws(const kvq_int4_cache* c, int64_t Hq) {
+    if (!c || c->B < 1 || c->H < 1 || c->T < 1 || c->g < 1 || Hq < 1) return 0;
+    const kvq::SplitPlan p = kvq::plan_splits(c->B, c->H, c->T, c->g);
+    return (size_t)(c->B * Hq * p.nsplit * (c->d + 2)) * sizeof(float);
+}
+
+int kvq_decode_attn_int4(const kvq_int4_cache* c, const void* q, int64_t Hq, float sm_scale, void* out, int ot,
+                         void* ws, size_t ws_bytes, kvq_stream stream) {
+    const int rc = kvq::check_cache_shape(c, "kvq_decode_attn_int4");
+    if (rc) return rc;
+    KVQ_REQUIRE(q && out, "kvq_decode_attn_int4: NULL q or out");
+    KVQ_REQUIRE(ot == KVQ_FP32 || ot == KVQ_BF16, "kvq_decode_attn_int4: ot must be KVQ_FP32 or KVQ_BF16");
+    KVQ_REQUIRE(Hq >= 1 && Hq % c->H == 0, "kvq_decode_attn_int4: Hq (%lld) must be a multiple of H (%lld)",
+                (long long)Hq, (long long)c->H);
+    const int64_t nq = Hq / c->H;
+    KVQ_REQUIRE(nq == 1 || nq == 2 || nq == 4 || nq == 8 || nq == 16,
+                "kvq_decode_attn_int4: Hq / H must be 1, 2, 4, 8 or 16 (got %lld)", (long long)nq);
+    KVQ_REQUIRE(ws && ws_bytes >= kvq_decode_attn_int4_ws(c, Hq), "kvq_decode_attn_int4: workspace of %zu bytes needed",
+                kvq_decode_attn_int4_ws(c, Hq));
+    KVQ_REQUIRE_ALIGNED(q, "q");
+    KVQ_REQUIRE_ALIGNED(out, "out");
+    KVQ_REQUIRE_ALIGNED(ws, "ws");
+    const kvq::SplitPlan p = kvq::plan_splits(c->B, c->H, c->T, c->g);
+    KVQ_REQUIRE(c->B * c->H * p.nsplit < ((int64_t)1 << 31), "kvq_decode_attn_int4: grid too large");
+    kvq::AttnArgs a;
+    a.k_codes = c->k_codes; a.k_scale = c->k_scale; a.k_zero = c->k_zero;
+    a.v_codes = c->v_codes; a.v_scale = c->v_scale; a.v_zero = c->v_zero;
+    a.k_res = c->k_res; a.v_res = c->v_res;
+    a.q = static_cast<const uint16_t*>(q);
+    a.out = out;
+    a.ot = ot;
+    a.ws = static_cast<float*>(ws);
+    a.B = c->B; a.T = c->T; a.H = c->H; a.R = c->R; a.Tq = c->T - c->R;
+    a.nKg = kvq::cdiv(a.Tq, c->g);
+    a.Hq = Hq;
+    a.split_len = p.split_len;
+    a.nsplit = p.nsplit;
+    a.qscale = sm_scale * 1.4426950408889634f;
+    kvq::dispatch(a, c->d, c->g, (int)nq, static_cast<hipStream_t>(stream));
+    return kvq::launch_status("kvq_decode_attn_int4");
+}
+
+}  // extern "C"

@@ -1,0 +1,74 @@
+// kvq_internal.h -- shared host/device plumbing of libkvq (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "../../include/kvq.h"
+
+namespace kvq {
+
+// ----------------------------------------------------------------- errors --
+
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+void clear_error();
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Checks the launch status of the kernels just enqueued.
+int launch_status(const char* what);
+
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+#define KVQ_REQUIRE(cond, ...)                               \
+    do {                                                     \
+        if (!(cond)) return ::kvq::fail(KVQ_EINVAL, __VA_ARGS__); \
+    } while (0)
+
+#define KVQ_REQUIRE_ALIGNED(p, name)                                              \
+    do {                                                                          \
+        if ((p) && !::kvq::aligned16(p))                                          \
+            return ::kvq::fail(KVQ_EALIGN, "%s must be 16-byte aligned", name);   \
+    } while (0)
+
+// ------------------------------------------------------------ device side --
+
+// bf16 <-> fp32.  Widening is exact (the 16 bits become the top half).
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf_to_f(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> two bf16 (round to nearest even, one v_cvt_pk_bf16_f32), low half = a.
+__device__ __forceinline__ uint32_t pack_bf2(float a, float b) {
+    bf16x2_t v;
+    v[0] = (__bf16)a;
+    v[1] = (__bf16)b;
+    return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ uint16_t f_to_bf(float a) { return (uint16_t)(pack_bf2(a, 0.0f) & 0xffffu); }
+
+// Smallest bf16 >= f for finite f > 0: adding 0xffff carries into the kept half
+// exactly when any dropped bit is set.
+__device__ __forceinline__ uint16_t bf_ceil_pos(float f) {
+    return (uint16_t)((__float_as_uint(f) + 0xffffu) >> 16);
+}
+
+// round(x / s) with IEEE division semantics (round-half-to-even of the correctly
+// rounded quotient).  Fast path: y = x * r with r = fl(1/s) (correctly rounded),
+// valid while |x / s| < 256: then |y - x/s| < 2^-14.9 and |fl(x/s) - x/s| < 2^-16, so
+// unless x/s lies within 2^-14 of a half-integer, y, fl(x/s) and x/s all round to
+// the same integer; otherwise |y - rint(y)| > 0.4999 and the true division decides.
+__device__ __forceinline__ float rint_div(float x, float s, float r) {
+    const float y = x * r;
+    float n = __builtin_rintf(y);
+    if (__builtin_fabsf(y - n) > 0.4999f) n = __builtin_rintf(x / s);
+    return n;
+}
+
+}  // namespace kvq

@@ -1,0 +1,463 @@
+// quant_int4.hip -- KIVI-style 4-bit affine group quantization of one layer of KV cache,
+// its dequantization, and the section sizing.
+//
+// Explainer (KV cache 压缩：把历史装得更小): quantization section (x ~ s (q - z), bf16 scale
+// and bf16 zero per group), grouping-axis section (K grouped per channel across tokens,
+// V per token across channels), group-size table (bytes = ceil(N/2) + ceil(N/g)*4) and the
+// residual-budget section (the most recent tokens stay bf16).  The integer steps are those
+// of the Walkthrough (KV Compression 公式到源码对照) §1.2 with qmin = 0, qmax = 15.
+//
+// One launch covers K tiles, V tiles and the residual copy.  A tile is one (b, h) and a
+// block of consecutive tokens (g tokens for K, 64 for V) across all d channels.  Lane
+// layout: d/8 lanes per token row, each owning 8 consecutive channels (one 16-byte load
+// of bf16, one 4-byte store of packed codes); the 256 threads cover 2048/d rows per pass.
+// Block order is (b, token block, h) with h fastest, so concurrently running blocks
+// read neighbouring token rows of the [B][T][H][d] input.
+#include <cfloat>
+
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kVTile = 64;   // tokens per V tile
+constexpr int kResTile = 64; // tokens per residual tile
+
+struct I4Geom {
+    int64_t B, T, H, d, g, R, Tq;
+    int64_t nKg;   // K groups per (b, h) = ceil(Tq / g)
+    int64_t nVt;   // V tiles per (b, h) = ceil(Tq / 64)
+    int64_t nRt;   // residual tiles per (b, h) = ceil(R / 64)
+};
+
+struct I4Ptrs {
+    uint8_t* k_codes;
+    uint16_t* k_scale;
+    uint16_t* k_zero;
+    uint8_t* v_codes;
+    uint16_t* v_scale;
+    uint16_t* v_zero;
+    uint16_t* k_res;
+    uint16_t* v_res;
+};
+
+__device__ __forceinline__ void unpack8(const uint4 a, float (&v)[8]) {
+    v[0] = bf_lo(a.x); v[1] = bf_hi(a.x); v[2] = bf_lo(a.y); v[3] = bf_hi(a.y);
+    v[4] = bf_lo(a.z); v[5] = bf_hi(a.z); v[6] = bf_lo(a.w); v[7] = bf_hi(a.w);
+}
+
+// Per-group parameters from the group's min and max:
+//   s = smallest bf16 >= max(max - min, 1e-8) / 15, z = bf16(round(0 - min / s)).
+struct GroupParams {
+    float s, r, z;
+    uint16_t sb, zb;
+};
+
+__device__ __forceinline__ GroupParams group_params(float mn, float mx) {
+    GroupParams p;
+    float range = mx - mn;
+    range = fmaxf(range, 1e-8f);
+    p.sb = bf_ceil_pos(range / 15.0f);
+    p.s = bf_to_f(p.sb);
+    // 0 - m: the backend lowers a subtraction from +0 to a negation, which turns m = +0 into
+    // -0; IEEE gives 0 - (+-0) = +0, so the zero quotient is handled explicitly
+    const float m = mn / p.s;
+    const float zr = (m == 0.0f) ? 0.0f : __builtin_rintf(-m);
+    p.zb = f_to_bf(zr);
+    p.z = bf_to_f(p.zb);
+    p.r = 1.0f / p.s;
+    return p;
+}
+
+// q = clip(round(x / s) + z, 0, 15) with IEEE-division semantics.
+// Fast path (z in [0, 15], so |x / s| <= 31 for every x of the group):
+// w = fma(x, 1/s, z) lies within 4e-6 of x/s + z and fl(x/s) within 2e-6 of x/s, so
+// unless x/s + z is within 1e-5 of a half-integer, rint(w) = rint(fl(x/s)) + z;
+// otherwise |w - rint(w)| > 0.4999 and the true division decides (this also settles
+// exact ties, which round half to even on x/s before z is added).
+__device__ __forceinline__ float code4(float x, float s, float r, float z, bool fast) {
+    float n;
+    if (fast) {
+        const float w = __builtin_fmaf(x, r, z);
+        n = __builtin_rintf(w);
+        if (__builtin_fabsf(w - n) > 0.4999f) n = __builtin_rintf(x / s) + z;
+    } else {
+        // integers: exact whenever the result can fall in [0, 15] (Sterbenz), else far outside
+        n = __builtin_rintf(x / s) + z;
+    }
+    return fminf(fmaxf(n, 0.0f), 15.0f);
+}
+
+// 8 codes (as floats in [0, 15]) -> one dword, byte j = code(2j) | code(2j+1) << 4.
+__device__ __forceinline__ uint32_t pack_codes(const float (&q)[8]) {
+    uint32_t even = 0, odd = 0;
+    even = __builtin_amdgcn_cvt_pk_u8_f32(q[0], 0, even);
+    even = __builtin_amdgcn_cvt_pk_u8_f32(q[2], 1, even);
+    even = __builtin_amdgcn_cvt_pk_u8_f32(q[4], 2, even);
+    even = __builtin_amdgcn_cvt_pk_u8_f32(q[6], 3, even);
+    odd = __builtin_amdgcn_cvt_pk_u8_f32(q[1], 0, odd);
+    odd = __builtin_amdgcn_cvt_pk_u8_f32(q[3], 1, odd);
+    odd = __builtin_amdgcn_cvt_pk_u8_f32(q[5], 2, odd);
+    odd = __builtin_amdgcn_cvt_pk_u8_f32(q[7], 3, odd);
+    return even | (odd << 4);
+}
+
+template <int D, int G>
+__global__ void __launch_bounds__(kThreads) int4_quant_kernel(const uint16_t* __restrict__ K,
+                                                              const uint16_t* __restrict__ V, I4Geom geo,
+                                                              I4Ptrs out) {
+    constexpr int LPR = D / 8;            // lanes per token row
+    constexpr int RPP = kThreads / LPR;   // rows per pass
+    constexpr int NW = kThreads / 64;     // waves
+    constexpr int NGD = D / G;            // V groups per token
+    static_assert(G % RPP == 0 && kVTile % RPP == 0, "tile shape");
+    constexpr int NP = kVTile * NGD > D ? kVTile * NGD : D;   // parameter slots
+    __shared__ float s_mn[NW * D > NP ? NW * D : NP], s_mx[NW * D > NP ? NW * D : NP];
+    __shared__ float s_ps[NP], s_pr[NP], s_pz[NP];
+
+    const int tid = threadIdx.x, lane = tid % LPR, rg = tid / LPR;
+    const int wave = tid / 64;
+    const int64_t H = geo.H, T = geo.T, Tq = geo.Tq;
+    int64_t bid = blockIdx.x;
+    const int64_t nK = geo.B * geo.nKg * H, nV = geo.B * geo.nVt * H;
+
+    if (bid < nK) {
+        // ---------------- K: one group of G tokens, every channel ----------------
+        constexpr int NR = G / RPP;
+        const int64_t h = bid % H, j = (bid / H) % geo.nKg, b = bid / (H * geo.nKg);
+        const int64_t t0 = j * G;
+        const int n = (int)min<int64_t>(G, Tq - t0);
+        uint4 raw[NR];
+        float mn[8], mx[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) { mn[k] = FLT_MAX; mx[k] = -FLT_MAX; }
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+            const int r = rg + RPP * i;
+            if (r < n) {
+                raw[i] = *reinterpret_cast<const uint4*>(K + ((b * T + t0 + r) * H + h) * D + 8 * lane);
+                float v[8];
+                unpack8(raw[i], v);
+#pragma unroll
+                for (int k = 0; k < 8; ++k) { mn[k] = fminf(mn[k], v[k]); mx[k] = fmaxf(mx[k], v[k]); }
+            }
+        }
+        // rows of the same channel lanes inside the wave: lanes differ by multiples of LPR
+#pragma unroll
+        for (int off = LPR; off < 64; off *= 2) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                mn[k] = fminf(mn[k], __shfl_xor(mn[k], off));
+                mx[k] = fmaxf(mx[k], __shfl_xor(mx[k], off));
+            }
+        }
+        if ((tid % 64) < LPR) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) { s_mn[wave * D + 8 * lane + k] = mn[k]; s_mx[wave * D + 8 * lane + k] = mx[k]; }
+        }
+        __syncthreads();
+        for (int c = tid; c < D; c += kThreads) {
+            float a = s_mn[c], z = s_mx[c];
+#pragma unroll
+            for (int w = 1; w < NW; ++w) { a = fminf(a, s_mn[w * D + c]); z = fmaxf(z, s_mx[w * D + c]); }
+            const GroupParams p = group_params(a, z);
+            const int64_t mi = ((b * H + h) * geo.nKg + j) * D + c;
+            out.k_scale[mi] = p.sb;
+            out.k_zero[mi] = p.zb;
+            s_ps[c] = p.s; s_pr[c] = p.r; s_pz[c] = p.z;
+        }
+        __syncthreads();
+        float ps[8], pr[8], pz[8];
+        bool fast = true;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            ps[k] = s_ps[8 * lane + k]; pr[k] = s_pr[8 * lane + k]; pz[k] = s_pz[8 * lane + k];
+            fast = fast && pz[k] >= 0.0f && pz[k] <= 15.0f;
+        }
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+            const int r = rg + RPP * i;
+            if (r < n) {
+                float v[8], q[8];
+                unpack8(raw[i], v);
+#pragma unroll
+                for (int k = 0; k < 8; ++k) q[k] = code4(v[k], ps[k], pr[k], pz[k], fast);
+                *reinterpret_cast<uint32_t*>(out.k_codes + ((b * H + h) * Tq + t0 + r) * (D / 2) + 4 * lane) =
+                    pack_codes(q);
+            }
+        }
+        return;
+    }
+    bid -= nK;
+    if (bid < nV) {
+        // ---------------- V: 64 tokens, groups of G channels per token ----------------
+        constexpr int NR = kVTile / RPP;
+        constexpr int LPG = G / 8;   // lanes per group
+        const int64_t h = bid % H, jt = (bid / H) % geo.nVt, b = bid / (H * geo.nVt);
+        const int64_t t0 = jt * kVTile;
+        const int n = (int)min<int64_t>(kVTile, Tq - t0);
+        const int grp = (8 * lane) / G;
+        uint4 raw[NR];
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+            const int r = rg + RPP * i;
+            float mn = FLT_MAX, mx = -FLT_MAX;
+            if (r < n) {
+                raw[i] = *reinterpret_cast<const uint4*>(V + ((b * T + t0 + r) * H + h) * D + 8 * lane);
+                float v[8];
+                unpack8(raw[i], v);
+#pragma unroll
+                for (int k = 0; k < 8; ++k) { mn = fminf(mn, v[k]); mx = fmaxf(mx, v[k]); }
+            }
+#pragma unroll
+            for (int off = 1; off < LPG; off *= 2) {
+                mn = fminf(mn, __shfl_xor(mn, off));
+                mx = fmaxf(mx, __shfl_xor(mx, off));
+            }
+            if (lane % LPG == 0) { s_mn[r * NGD + grp] = mn; s_mx[r * NGD + grp] = mx; }
+        }
+        __syncthreads();
+        for (int p = tid; p < n * NGD; p += kThreads) {
+            const GroupParams gp = group_params(s_mn[p], s_mx[p]);
+            const int64_t mi = ((b * H + h) * Tq + t0) * NGD + p;
+            out.v_scale[mi] = gp.sb;
+            out.v_zero[mi] = gp.zb;
+            s_ps[p] = gp.s; s_pr[p] = gp.r; s_pz[p] = gp.z;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+            const int r = rg + RPP * i;
+            if (r < n) {
+                const float ps = s_ps[r * NGD + grp], pr = s_pr[r * NGD + grp], pz = s_pz[r * NGD + grp];
+                const bool fast = pz >= 0.0f && pz <= 15.0f;
+                float v[8], q[8];
+                unpack8(raw[i], v);
+#pragma unroll
+                for (int k = 0; k < 8; ++k) q[k] = code4(v[k], ps, pr, pz, fast);
+                *reinterpret_cast<uint32_t*>(out.v_codes + ((b * H + h) * Tq + t0 + r) * (D / 2) + 4 * lane) =
+                    pack_codes(q);
+            }
+        }
+        return;
+    }
+    bid -= nV;
+    {
+        // ---------------- residual: the last R tokens, verbatim ----------------
+        const int64_t h = bid % H, jr = (bid / H) % geo.nRt, b = bid / (H * geo.nRt);
+        const int64_t r0 = jr * kResTile;
+        const int n = (int)min<int64_t>(kResTile, geo.R - r0);
+        for (int r = rg; r < n; r += RPP) {
+            const int64_t src = ((b * T + Tq + r0 + r) * H + h) * D + 8 * lane;
+            const int64_t dst = ((b * H + h) * geo.R + r0 + r) * D + 8 * lane;
+            *reinterpret_cast<uint4*>(out.k_res + dst) = *reinterpret_cast<const uint4*>(K + src);
+            *reinterpret_cast<uint4*>(out.v_res + dst) = *reinterpret_cast<const uint4*>(V + src);
+        }
+    }
+}
+
+// Dequantization of one side: x_hat = (q - z) * s rounded once.  q*s and z*s are exact
+// in fp32 (4-bit x 8-bit and 8-bit x 8-bit significands), so fma(q, s, -z*s) rounds the
+// exact value once.  Residual tokens are copied (bf16) or widened (fp32).
+template <int D, int G, bool IS_K, int OT>
+__global__ void __launch_bounds__(kThreads) int4_dequant_kernel(const uint8_t* __restrict__ codes,
+                                                                const uint16_t* __restrict__ scale,
+                                                                const uint16_t* __restrict__ zero,
+                                                                const uint16_t* __restrict__ res, I4Geom geo,
+                                                                void* __restrict__ out) {
+    constexpr int LPR = D / 8;
+    constexpr int RPP = kThreads / LPR;
+    constexpr int TILE = IS_K ? G : kVTile;
+    constexpr int NGD = D / G;
+    const int tid = threadIdx.x, lane = tid % LPR, rg = tid / LPR;
+    const int64_t H = geo.H, T = geo.T, Tq = geo.Tq;
+    const int64_t ntile = IS_K ? geo.nKg : geo.nVt;
+    int64_t bid = blockIdx.x;
+    const int64_t nQ = geo.B * ntile * H;
+
+    auto store8 = [&](int64_t t, int64_t b, int64_t h, const float (&v)[8]) {
+        const int64_t o = ((b * T + t) * H + h) * D + 8 * lane;
+        if constexpr (OT == KVQ_FP32) {
+            float* p = static_cast<float*>(out) + o;
+            *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+            *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+        } else {
+            uint16_t* p = static_cast<uint16_t*>(out) + o;
+            *reinterpret_cast<uint4*>(p) =
+                make_uint4(pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]), pack_bf2(v[4], v[5]), pack_bf2(v[6], v[7]));
+        }
+    };
+
+    if (bid < nQ) {
+        const int64_t h = bid % H, j = (bid / H) % ntile, b = bid / (H * ntile);
+        const int64_t t0 = j * TILE;
+        const int n = (int)min<int64_t>(TILE, Tq - t0);
+        float s8[8], zs8[8];
+        if constexpr (IS_K) {
+            const int64_t mi = ((b * H + h) * geo.nKg + j) * D + 8 * lane;
+            const uint4 sv = *reinterpret_cast<const uint4*>(scale + mi);
+            const uint4 zv = *reinterpret_cast<const uint4*>(zero + mi);
+            float zf[8];
+            unpack8(sv, s8);
+            unpack8(zv, zf);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) zs8[k] = -zf[k] * s8[k];
+        }
+        for (int r = rg; r < n; r += RPP) {
+            const int64_t t = t0 + r;
+            const uint32_t w = *reinterpret_cast<const uint32_t*>(codes + ((b * H + h) * Tq + t) * (D / 2) + 4 * lane);
+            float v[8];
+            if constexpr (IS_K) {
+#pragma unroll
+                for (int k = 0; k < 8; ++k) v[k] = __builtin_fmaf((float)((w >> (4 * k)) & 15u), s8[k], zs8[k]);
+            } else {
+                const int64_t mi = ((b * H + h) * Tq + t) * NGD + (8 * lane) / G;
+                const float s = bf_to_f(scale[mi]);
+                const float zs = -bf_to_f(zero[mi]) * s;
+#pragma unroll
+                for (int k = 0; k < 8; ++k) v[k] = __builtin_fmaf((float)((w >> (4 * k)) & 15u), s, zs);
+            }
+            store8(t, b, h, v);
+        }
+        return;
+    }
+    bid -= nQ;
+    const int64_t h = bid % H, jr = (bid / H) % geo.nRt, b = bid / (H * geo.nRt);
+    const int64_t r0 = jr * kResTile;
+    const int n = (int)min<int64_t>(kResTile, geo.R - r0);
+    for (int r = rg; r < n; r += RPP) {
+        const uint4 a = *reinterpret_cast<const uint4*>(res + ((b * H + h) * geo.R + r0 + r) * D + 8 * lane);
+        if constexpr (OT == KVQ_BF16) {
+            *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + ((b * T + Tq + r0 + r) * H + h) * D + 8 * lane) = a;
+        } else {
+            float v[8];
+            unpack8(a, v);
+            store8(Tq + r0 + r, b, h, v);
+        }
+    }
+}
+
+I4Geom geom_of(const kvq_int4_cache* c) {
+    I4Geom g;
+    g.B = c->B; g.T = c->T; g.H = c->H; g.d = c->d; g.g = c->g; g.R = c->R;
+    g.Tq = c->T - c->R;
+    g.nKg = cdiv(g.Tq, g.g);
+    g.nVt = cdiv(g.Tq, kVTile);
+    g.nRt = cdiv(g.R, kResTile);
+    return g;
+}
+
+template <int D, int G>
+void launch_quant(const uint16_t* K, const uint16_t* V, const I4Geom& g, const I4Ptrs& p, int64_t nblk,
+                  hipStream_t st) {
+    hipLaunchKernelGGL((int4_quant_kernel<D, G>), dim3((unsigned)nblk), dim3(kThreads), 0, st, K, V, g, p);
+}
+
+template <int D, int G>
+void launch_dequant(bool is_k, int ot, const kvq_int4_cache* c, const I4Geom& g, void* out, hipStream_t st) {
+    const int64_t nblk = g.B * g.H * ((is_k ? g.nKg : g.nVt) + g.nRt);
+    const dim3 grid((unsigned)nblk), blk(kThreads);
+    if (is_k) {
+        if (ot == KVQ_FP32)
+            hipLaunchKernelGGL((int4_dequant_kernel<D, G, true, KVQ_FP32>), grid, blk, 0, st, c->k_codes, c->k_scale,
+                               c->k_zero, c->k_res, g, out);
+        else
+            hipLaunchKernelGGL((int4_dequant_kernel<D, G, true, KVQ_BF16>), grid, blk, 0, st, c->k_codes, c->k_scale,
+                               c->k_zero, c->k_res, g, out);
+    } else {
+        if (ot == KVQ_FP32)
+            hipLaunchKernelGGL((int4_dequant_kernel<D, G, false, KVQ_FP32>), grid, blk, 0, st, c->v_codes, c->v_scale,
+                               c->v_zero, c->v_res, g, out);
+        else
+            hipLaunchKernelGGL((int4_dequant_kernel<D, G, false, KVQ_BF16>), grid, blk, 0, st, c->v_codes, c->v_scale,
+                               c->v_zero, c->v_res, g, out);
+    }
+}
+
+#define KVQ_DISPATCH_DG(d, g, FN, ...)                                        \
+    do {                                                                      \
+        if (d == 64 && g == 32) FN<64, 32>(__VA_ARGS__);                      \
+        else if (d == 64 && g == 64) FN<64, 64>(__VA_ARGS__);                 \
+        else if (d == 128 && g == 32) FN<128, 32>(__VA_ARGS__);               \
+        else if (d == 128 && g == 64) FN<128, 64>(__VA_ARGS__);               \
+        else if (d == 128 && g == 128) FN<128, 128>(__VA_ARGS__);             \
+        else if (d == 256 && g == 32) FN<256, 32>(__VA_ARGS__);               \
+        else if (d == 256 && g == 64) FN<256, 64>(__VA_ARGS__);               \
+        else FN<256, 128>(__VA_ARGS__);                                       \
+    } while (0)
+
+}  // namespace
+
+int check_cache_shape(const kvq_int4_cache* c, const char* name) {
+    KVQ_REQUIRE(c, "%s: NULL cache descriptor", name);
+    KVQ_REQUIRE(c->B >= 1 && c->T >= 1 && c->H >= 1, "%s: B, T, H must be >= 1", name);
+    KVQ_REQUIRE(c->d == 64 || c->d == 128 || c->d == 256, "%s: d must be 64, 128 or 256 (got %lld)", name,
+                (long long)c->d);
+    KVQ_REQUIRE((c->g == 32 || c->g == 64 || c->g == 128) && c->g <= c->d,
+                "%s: g must be 32, 64 or 128 and <= d (got %lld)", name, (long long)c->g);
+    KVQ_REQUIRE(c->R >= 0 && c->R <= c->T, "%s: need 0 <= R <= T", name);
+    KVQ_REQUIRE(c->B * c->T * c->H * c->d < ((int64_t)1 << 40), "%s: cache too large", name);
+    const int64_t Tq = c->T - c->R;
+    const void* ptrs[8] = {c->k_codes, c->k_scale, c->k_zero, c->v_codes, c->v_scale, c->v_zero, c->k_res, c->v_res};
+    const char* names[8] = {"k_codes", "k_scale", "k_zero", "v_codes", "v_scale", "v_zero", "k_res", "v_res"};
+    for (int i = 0; i < 8; ++i) {
+        const bool needed = (i < 6) ? Tq > 0 : c->R > 0;
+        KVQ_REQUIRE(!needed || ptrs[i], "%s: NULL %s", name, names[i]);
+        KVQ_REQUIRE_ALIGNED(ptrs[i], names[i]);
+    }
+    return KVQ_OK;
+}
+
+int dequant_int4(const kvq_int4_cache* c, bool is_k, void* out, int ot, hipStream_t st) {
+    const int rc = check_cache_shape(c, "kvq_dequant");
+    if (rc) return rc;
+    KVQ_REQUIRE(out, "kvq_dequant: NULL out");
+    KVQ_REQUIRE(ot == KVQ_FP32 || ot == KVQ_BF16, "kvq_dequant: ot must be KVQ_FP32 or KVQ_BF16");
+    KVQ_REQUIRE_ALIGNED(out, "out");
+    const I4Geom g = geom_of(c);
+    KVQ_DISPATCH_DG(c->d, c->g, launch_dequant, is_k, ot, c, g, out, st);
+    return launch_status("INT4 dequantization");
+}
+
+}  // namespace kvq
+
+extern "C" {
+
+int kvq_int4_cache_sizes(int64_t B, int64_t T, int64_t H, int64_t d, int64_t g, int64_t R, size_t sect_bytes[8],
+                         size_t* total) {
+    KVQ_REQUIRE(sect_bytes && total, "kvq_int4_cache_sizes: NULL output");
+    KVQ_REQUIRE(B >= 1 && T >= 1 && H >= 1 && d >= 2 && d % 2 == 0 && g >= 1 && d % g == 0 && R >= 0 && R <= T,
+                "kvq_int4_cache_sizes: invalid shape");
+    const size_t bh = (size_t)(B * H), Tq = (size_t)(T - R);
+    sect_bytes[0] = bh * Tq * (size_t)(d / 2);
+    sect_bytes[1] = bh * (size_t)kvq::cdiv((int64_t)Tq, g) * (size_t)d * 2;
+    sect_bytes[2] = sect_bytes[1];
+    sect_bytes[3] = sect_bytes[0];
+    sect_bytes[4] = bh * Tq * (size_t)(d / g) * 2;
+    sect_bytes[5] = sect_bytes[4];
+    sect_bytes[6] = bh * (size_t)R * (size_t)d * 2;
+    sect_bytes[7] = sect_bytes[6];
+    size_t t = 0;
+    for (int i = 0; i < 8; ++i) t += sect_bytes[i];
+    *total = t;
+    return KVQ_OK;
+}
+
+int kvq_group_quant_int4(const void* K, const void* V, const kvq_int4_cache* c, kvq_stream stream) {
+    const int rc = kvq::check_cache_shape(c, "kvq_group_quant_int4");
+    if (rc) return rc;
+    KVQ_REQUIRE(K && V, "kvq_group_quant_int4: NULL K or V");
+    KVQ_REQUIRE_ALIGNED(K, "K");
+    KVQ_REQUIRE_ALIGNED(V, "V");
+    const kvq::I4Geom g = kvq::geom_of(c);
+    const kvq::I4Ptrs p{c->k_codes, c->k_scale, c->k_zero, c->v_codes, c->v_scale, c->v_zero, c->k_res, c->v_res};
+    const int64_t nblk = g.B * g.H * (g.nKg + g.nVt + g.nRt);
+    KVQ_REQUIRE(nblk < ((int64_t)1 << 31), "kvq_group_quant_int4: grid too large");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    KVQ_DISPATCH_DG(c->d, c->g, kvq::launch_quant, static_cast<const uint16_t*>(K), static_cast<const uint16_t*>(V),
+                    g, p, nblk, st);
+    return kvq::launch_status("INT4 group quantization");
+}
+
+}  // extern "C"

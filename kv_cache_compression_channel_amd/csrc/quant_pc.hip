@@ -1,0 +1,363 @@
+// quant_pc.hip -- per-channel symmetric / asymmetric quantization and its dequantization.
+//
+// Walkthrough (KV Compression 公式到源码对照) §1.1 and §1.2: one scale (and zero point)
+// per channel, reduced over the token rows of each slice; §1.3 for the dequantization.
+//
+// Layout: x is nb slices of [R][C]; each thread owns VEC (8 or 1) consecutive channels
+// and walks rows, so a wave reads whole rows with 16-byte (bf16) / 32-byte (fp32) loads.
+// Three launches: (1) per (slice, row chunk, channel) min/max into the workspace,
+// (2) per (slice, channel) parameters, (3) codes.  Each launch reads x once; pass (3)
+// follows pass (1) on the same stream, so slices small enough to stay in the MALL are
+// read from HBM once.
+#include <cfloat>
+
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kRowsPerChunk = 256;
+
+struct PcParams {
+    float s;     // scale
+    float r;     // fl(1 / s)
+    float zf;    // zero point as float (0 for sym)
+    float fast;  // 1 when every |x / s| of the channel is < 256
+};
+
+struct PcGeom {
+    int64_t nb, R, C, ldx, bsx;
+    int lpr;   // lanes per row (power of two, <= 64)
+    int rpp;   // rows per pass = kThreads / lpr
+    int64_t ncb, nrc;  // column blocks, row chunks
+};
+
+template <int XT, int VEC>
+__device__ __forceinline__ void load_x(const void* x, int64_t off, float (&v)[VEC]) {
+    if constexpr (XT == KVQ_FP32) {
+        const float* p = static_cast<const float*>(x) + off;
+        if constexpr (VEC == 8) {
+            const float4 a = *reinterpret_cast<const float4*>(p);
+            const float4 b = *reinterpret_cast<const float4*>(p + 4);
+            v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+            v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+        } else {
+            v[0] = *p;
+        }
+    } else {
+        const uint16_t* p = static_cast<const uint16_t*>(x) + off;
+        if constexpr (VEC == 8) {
+            const uint4 a = *reinterpret_cast<const uint4*>(p);
+            v[0] = bf_lo(a.x); v[1] = bf_hi(a.x); v[2] = bf_lo(a.y); v[3] = bf_hi(a.y);
+            v[4] = bf_lo(a.z); v[5] = bf_hi(a.z); v[6] = bf_lo(a.w); v[7] = bf_hi(a.w);
+        } else {
+            v[0] = bf_to_f(*p);
+        }
+    }
+}
+
+// Pass 1: min and max of every channel over one chunk of rows.
+template <int XT, int VEC>
+__global__ void __launch_bounds__(kThreads) pc_minmax_kernel(const void* __restrict__ x, PcGeom g,
+                                                             float2* __restrict__ part) {
+    __shared__ float smn[kThreads * VEC];
+    __shared__ float smx[kThreads * VEC];
+    int64_t bid = blockIdx.x;
+    const int64_t cb = bid % g.ncb; bid /= g.ncb;
+    const int64_t rc = bid % g.nrc;
+    const int64_t s = bid / g.nrc;
+    const int lane = threadIdx.x % g.lpr, rl = threadIdx.x / g.lpr;
+    const int64_t c0 = (cb * g.lpr + lane) * VEC;
+    float mn[VEC], mx[VEC];
+#pragma unroll
+    for (int k = 0; k < VEC; ++k) { mn[k] = FLT_MAX; mx[k] = -FLT_MAX; }
+    if (c0 < g.C) {
+        const int64_t r_end = min(g.R, (rc + 1) * kRowsPerChunk);
+        for (int64_t r = rc * kRowsPerChunk + rl; r < r_end; r += g.rpp) {
+            float v[VEC];
+            load_x<XT, VEC>(x, s * g.bsx + r * g.ldx + c0, v);
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) { mn[k] = fminf(mn[k], v[k]); mx[k] = fmaxf(mx[k], v[k]); }
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < VEC; ++k) {
+        smn[threadIdx.x * VEC + k] = mn[k];
+        smx[threadIdx.x * VEC + k] = mx[k];
+    }
+    __syncthreads();
+    // column j of the block (lane = j / VEC, element = j % VEC) reduced over the row lanes
+    const int ncol = g.lpr * VEC;
+    for (int j = threadIdx.x; j < ncol; j += kThreads) {
+        const int ln = j / VEC, k = j % VEC;
+        float a = FLT_MAX, b = -FLT_MAX;
+        for (int q = 0; q < g.rpp; ++q) {
+            a = fminf(a, smn[(q * g.lpr + ln) * VEC + k]);
+            b = fmaxf(b, smx[(q * g.lpr + ln) * VEC + k]);
+        }
+        const int64_t c = cb * ncol + j;
+        if (c < g.C) part[(s * g.nrc + rc) * g.C + c] = make_float2(a, b);
+    }
+}
+
+// Pass 2: per (slice, channel) scale / zero point (Walkthrough §1.1, §1.2).
+template <bool SYM>
+__global__ void __launch_bounds__(kThreads) pc_params_kernel(const float2* __restrict__ part, int64_t nb,
+                                                             int64_t nrc, int64_t C, int qmin, int qmax,
+                                                             float* __restrict__ scale, int8_t* __restrict__ zp,
+                                                             PcParams* __restrict__ prm) {
+    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (i >= nb * C) return;
+    const int64_t s = i / C, c = i % C;
+    float mn = FLT_MAX, mx = -FLT_MAX;
+    for (int64_t k = 0; k < nrc; ++k) {
+        const float2 p = part[(s * nrc + k) * C + c];
+        mn = fminf(mn, p.x);
+        mx = fmaxf(mx, p.y);
+    }
+    PcParams P;
+    int z = 0;
+    if constexpr (SYM) {
+        float a = fmaxf(mx, -mn);           // max |x|
+        a = fmaxf(a, 1e-8f);
+        P.s = a / (float)qmax;
+    } else {
+        float range = mx - mn;
+        range = fmaxf(range, 1e-8f);
+        P.s = range / (float)(qmax - qmin);
+        const float m = mn / P.s;   // qmin - m with an explicit zero case (see group_params of the INT4 path)
+        const float zr = (qmin == 0 && m == 0.0f) ? 0.0f : __builtin_rintf((float)qmin - m);
+        z = (int)fminf(fmaxf(zr, -128.0f), 127.0f);
+    }
+    P.r = 1.0f / P.s;
+    P.zf = (float)z;
+    P.fast = (fmaxf(fabsf(mn), fabsf(mx)) * P.r <= 250.0f) ? 1.0f : 0.0f;
+    scale[i] = P.s;
+    if (zp) zp[i] = (int8_t)z;
+    prm[i] = P;
+}
+
+// Pass 3: codes q = clip(round(x / s) + zp, qmin, qmax).
+template <int XT, int VEC>
+__global__ void __launch_bounds__(kThreads) pc_code_kernel(const void* __restrict__ x, PcGeom g,
+                                                           const PcParams* __restrict__ prm, int qmin, int qmax,
+                                                           int8_t* __restrict__ q) {
+    int64_t bid = blockIdx.x;
+    const int64_t cb = bid % g.ncb; bid /= g.ncb;
+    const int64_t rc = bid % g.nrc;
+    const int64_t s = bid / g.nrc;
+    const int lane = threadIdx.x % g.lpr, rl = threadIdx.x / g.lpr;
+    const int64_t c0 = (cb * g.lpr + lane) * VEC;
+    if (c0 >= g.C) return;
+    PcParams P[VEC];
+    bool fast = true;
+#pragma unroll
+    for (int k = 0; k < VEC; ++k) {
+        P[k] = prm[s * g.C + c0 + k];
+        fast = fast && (P[k].fast != 0.0f);
+    }
+    const float lo = (float)qmin, hi = (float)qmax;
+    const int64_t r_end = min(g.R, (rc + 1) * kRowsPerChunk);
+    for (int64_t r = rc * kRowsPerChunk + rl; r < r_end; r += g.rpp) {
+        float v[VEC];
+        load_x<XT, VEC>(x, s * g.bsx + r * g.ldx + c0, v);
+        int8_t o[VEC];
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) {
+            const float n = fast ? rint_div(v[k], P[k].s, P[k].r) : __builtin_rintf(v[k] / P[k].s);
+            // n and zf are integers: the fp32 sum is exact whenever the result can land in
+            // [qmin, qmax] (Sterbenz), and far outside otherwise, so the clip is exact.
+            o[k] = (int8_t)(int)fminf(fmaxf(n + P[k].zf, lo), hi);
+        }
+        int8_t* dst = q + (s * g.R + r) * g.C + c0;
+        if constexpr (VEC == 8) {
+            uint2 w;
+            w.x = (uint32_t)(uint8_t)o[0] | ((uint32_t)(uint8_t)o[1] << 8) | ((uint32_t)(uint8_t)o[2] << 16) |
+                  ((uint32_t)(uint8_t)o[3] << 24);
+            w.y = (uint32_t)(uint8_t)o[4] | ((uint32_t)(uint8_t)o[5] << 8) | ((uint32_t)(uint8_t)o[6] << 16) |
+                  ((uint32_t)(uint8_t)o[7] << 24);
+            *reinterpret_cast<uint2*>(dst) = w;
+        } else {
+            dst[0] = o[0];
+        }
+    }
+}
+
+// Dequantization x_hat = ((float)(q - zp)) * s (Walkthrough §1.3).  Same geometry as the
+// code pass: each thread owns VEC channels (scales loaded once) and walks rows.
+template <int OT, int VEC>
+__global__ void __launch_bounds__(kThreads) pc_dequant_kernel(const int8_t* __restrict__ q,
+                                                              const float* __restrict__ scale,
+                                                              const int8_t* __restrict__ zp, PcGeom g,
+                                                              void* __restrict__ out) {
+    int64_t bid = blockIdx.x;
+    const int64_t cb = bid % g.ncb; bid /= g.ncb;
+    const int64_t rc = bid % g.nrc;
+    const int64_t s = bid / g.nrc;
+    const int lane = threadIdx.x % g.lpr, rl = threadIdx.x / g.lpr;
+    const int64_t c0 = (cb * g.lpr + lane) * VEC;
+    if (c0 >= g.C) return;
+    float sc[VEC], zf[VEC];
+#pragma unroll
+    for (int k = 0; k < VEC; ++k) {
+        sc[k] = scale[s * g.C + c0 + k];
+        zf[k] = zp ? (float)zp[s * g.C + c0 + k] : 0.0f;
+    }
+    const int64_t r_end = min(g.R, (rc + 1) * kRowsPerChunk);
+    for (int64_t r = rc * kRowsPerChunk + rl; r < r_end; r += g.rpp) {
+        const int64_t e = (s * g.R + r) * g.C + c0;
+        float v[VEC];
+        if constexpr (VEC == 8) {
+            const uint2 w = *reinterpret_cast<const uint2*>(q + e);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                v[k] = ((float)(int8_t)(w.x >> (8 * k)) - zf[k]) * sc[k];
+                v[k + 4] = ((float)(int8_t)(w.y >> (8 * k)) - zf[k + 4]) * sc[k + 4];
+            }
+        } else {
+            v[0] = ((float)q[e] - zf[0]) * sc[0];
+        }
+        if constexpr (OT == KVQ_FP32) {
+            float* o = static_cast<float*>(out) + e;
+            if constexpr (VEC == 8) {
+                *reinterpret_cast<float4*>(o) = make_float4(v[0], v[1], v[2], v[3]);
+                *reinterpret_cast<float4*>(o + 4) = make_float4(v[4], v[5], v[6], v[7]);
+            } else {
+                o[0] = v[0];
+            }
+        } else {
+            uint16_t* o = static_cast<uint16_t*>(out) + e;
+            if constexpr (VEC == 8) {
+                *reinterpret_cast<uint4*>(o) = make_uint4(pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]),
+                                                          pack_bf2(v[4], v[5]), pack_bf2(v[6], v[7]));
+            } else {
+                o[0] = f_to_bf(v[0]);
+            }
+        }
+    }
+}
+
+PcGeom geom_of(int64_t nb, int64_t R, int64_t C, int64_t ldx, int64_t bsx, bool vec8);
+
+int64_t nrc_of(int64_t R) { return cdiv(R, kRowsPerChunk); }
+
+PcGeom geom_of(int64_t nb, int64_t R, int64_t C, int64_t ldx, int64_t bsx, bool vec8) {
+    const int64_t cols = vec8 ? C / 8 : C;
+    int lpr = 1;
+    while (lpr < 64 && lpr < cols) lpr *= 2;
+    return PcGeom{nb, R, C, ldx, nb == 1 ? 0 : bsx, lpr, kThreads / lpr, cdiv(cols, lpr), nrc_of(R)};
+}
+
+size_t ws_bytes_for(int64_t nb, int64_t R, int64_t C) {
+    const size_t part = (size_t)(nb * nrc_of(R) * C) * sizeof(float2);
+    const size_t prm = (size_t)(nb * C) * sizeof(PcParams);
+    return ((part + 255) / 256) * 256 + prm;
+}
+
+template <int XT>
+int launch_pc(const void* x, PcGeom g, bool vec8, bool sym, int qmin, int qmax, int8_t* q, float* scale,
+              int8_t* zp, void* ws, hipStream_t st) {
+    float2* part = static_cast<float2*>(ws);
+    const size_t part_bytes = (size_t)(g.nb * g.nrc * g.C) * sizeof(float2);
+    PcParams* prm = reinterpret_cast<PcParams*>(static_cast<char*>(ws) + ((part_bytes + 255) / 256) * 256);
+    const int64_t nblk = g.nb * g.nrc * g.ncb;
+    if (vec8)
+        hipLaunchKernelGGL((pc_minmax_kernel<XT, 8>), dim3((unsigned)nblk), dim3(kThreads), 0, st, x, g, part);
+    else
+        hipLaunchKernelGGL((pc_minmax_kernel<XT, 1>), dim3((unsigned)nblk), dim3(kThreads), 0, st, x, g, part);
+    const unsigned pblk = (unsigned)cdiv(g.nb * g.C, kThreads);
+    if (sym)
+        hipLaunchKernelGGL((pc_params_kernel<true>), dim3(pblk), dim3(kThreads), 0, st, part, g.nb, g.nrc, g.C,
+                           qmin, qmax, scale, zp, prm);
+    else
+        hipLaunchKernelGGL((pc_params_kernel<false>), dim3(pblk), dim3(kThreads), 0, st, part, g.nb, g.nrc, g.C,
+                           qmin, qmax, scale, zp, prm);
+    if (vec8)
+        hipLaunchKernelGGL((pc_code_kernel<XT, 8>), dim3((unsigned)nblk), dim3(kThreads), 0, st, x, g, prm, qmin,
+                           qmax, q);
+    else
+        hipLaunchKernelGGL((pc_code_kernel<XT, 1>), dim3((unsigned)nblk), dim3(kThreads), 0, st, x, g, prm, qmin,
+                           qmax, q);
+    return launch_status("per-channel quantization");
+}
+
+int quant_pc(const void* x, int xt, int64_t nb, int64_t R, int64_t C, int64_t ldx, int64_t bsx, bool sym,
+             int qmin, int qmax, int8_t* q, float* scale, int8_t* zp, void* ws, size_t ws_bytes,
+             kvq_stream stream, const char* name) {
+    KVQ_REQUIRE(x && q && scale, "%s: NULL x, q or scale", name);
+    KVQ_REQUIRE(sym || zp, "%s: zp is required", name);
+    KVQ_REQUIRE(xt == KVQ_FP32 || xt == KVQ_BF16, "%s: xt must be KVQ_FP32 or KVQ_BF16", name);
+    KVQ_REQUIRE(nb >= 1 && R >= 1 && C >= 1, "%s: nb, R, C must be >= 1", name);
+    KVQ_REQUIRE(ldx >= C, "%s: ldx (%lld) < C (%lld)", name, (long long)ldx, (long long)C);
+    KVQ_REQUIRE(nb == 1 || bsx >= R * ldx, "%s: bsx < R*ldx", name);
+    KVQ_REQUIRE(nb * R * C < ((int64_t)1 << 40), "%s: tensor too large", name);
+    KVQ_REQUIRE(ws != nullptr && ws_bytes >= ws_bytes_for(nb, R, C), "%s: workspace of %zu bytes needed", name,
+                ws_bytes_for(nb, R, C));
+    KVQ_REQUIRE_ALIGNED(x, "x");
+    KVQ_REQUIRE_ALIGNED(q, "q");
+    KVQ_REQUIRE_ALIGNED(scale, "scale");
+    KVQ_REQUIRE_ALIGNED(zp, "zp");
+    KVQ_REQUIRE_ALIGNED(ws, "ws");
+    const bool vec8 = (C % 8 == 0) && (ldx % 8 == 0) && (nb == 1 || bsx % 8 == 0);
+    const PcGeom g = geom_of(nb, R, C, ldx, bsx, vec8);
+    KVQ_REQUIRE(g.nb * g.nrc * g.ncb < ((int64_t)1 << 31), "%s: grid too large", name);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (xt == KVQ_FP32) return launch_pc<KVQ_FP32>(x, g, vec8, sym, qmin, qmax, q, scale, zp, ws, st);
+    return launch_pc<KVQ_BF16>(x, g, vec8, sym, qmin, qmax, q, scale, zp, ws, st);
+}
+
+}  // namespace
+
+int dequant_pc(const kvq_pc_tensor* t, void* out, int ot, hipStream_t st) {
+    KVQ_REQUIRE(t && t->q && t->scale && out, "kvq_dequant: NULL pointer");
+    KVQ_REQUIRE(t->nb >= 1 && t->R >= 1 && t->C >= 1, "kvq_dequant: nb, R, C must be >= 1");
+    KVQ_REQUIRE(ot == KVQ_FP32 || ot == KVQ_BF16, "kvq_dequant: ot must be KVQ_FP32 or KVQ_BF16");
+    KVQ_REQUIRE_ALIGNED(t->q, "q");
+    KVQ_REQUIRE_ALIGNED(t->scale, "scale");
+    KVQ_REQUIRE_ALIGNED(out, "out");
+    const bool vec8 = t->C % 8 == 0;
+    const PcGeom g = geom_of(t->nb, t->R, t->C, t->C, t->R * t->C, vec8);
+    const int64_t nblk = g.nb * g.nrc * g.ncb;
+    KVQ_REQUIRE(nblk < ((int64_t)1 << 31), "kvq_dequant: grid too large");
+    const dim3 grid((unsigned)nblk), blk(kThreads);
+    if (ot == KVQ_FP32) {
+        if (vec8)
+            hipLaunchKernelGGL((pc_dequant_kernel<KVQ_FP32, 8>), grid, blk, 0, st, t->q, t->scale, t->zp, g, out);
+        else
+            hipLaunchKernelGGL((pc_dequant_kernel<KVQ_FP32, 1>), grid, blk, 0, st, t->q, t->scale, t->zp, g, out);
+    } else {
+        if (vec8)
+            hipLaunchKernelGGL((pc_dequant_kernel<KVQ_BF16, 8>), grid, blk, 0, st, t->q, t->scale, t->zp, g, out);
+        else
+            hipLaunchKernelGGL((pc_dequant_kernel<KVQ_BF16, 1>), grid, blk, 0, st, t->q, t->scale, t->zp, g, out);
+    }
+    return launch_status("per-channel dequantization");
+}
+
+}  // namespace kvq
+
+extern "C" {
+
+size_t kvq_quant_pc_ws(int64_t nb, int64_t R, int64_t C) {
+    if (nb < 1 || R < 1 || C < 1) return 0;
+    return kvq::ws_bytes_for(nb, R, C);
+}
+
+int kvq_quant_sym(const void* x, int xt, int64_t nb, int64_t R, int64_t C, int64_t ldx, int64_t bsx, int bits,
+                  int8_t* q, float* scale, int8_t* zp_or_null, void* ws, size_t ws_bytes, kvq_stream stream) {
+    KVQ_REQUIRE(bits >= 2 && bits <= 8, "kvq_quant_sym: bits must be in [2, 8] (got %d)", bits);
+    const int qmax = (1 << (bits - 1)) - 1;
+    return kvq::quant_pc(x, xt, nb, R, C, ldx, bsx, true, -qmax, qmax, q, scale, zp_or_null, ws, ws_bytes, stream,
+                         "kvq_quant_sym");
+}
+
+int kvq_quant_asym(const void* x, int xt, int64_t nb, int64_t R, int64_t C, int64_t ldx, int64_t bsx, int qmin,
+                   int qmax, int8_t* q, float* scale, int8_t* zp, void* ws, size_t ws_bytes, kvq_stream stream) {
+    KVQ_REQUIRE(qmin >= -128 && qmax <= 127 && qmin < qmax,
+                "kvq_quant_asym: need -128 <= qmin < qmax <= 127 (got %d, %d)", qmin, qmax);
+    return kvq::quant_pc(x, xt, nb, R, C, ldx, bsx, false, qmin, qmax, q, scale, zp, ws, ws_bytes, stream,
+                         "kvq_quant_asym");
+}
+
+}  // extern "C"

@@ -1,0 +1,61 @@
+"""Helpers shared by the GPU parity tests (tensor <-> numpy marshalling, tolerances)."""
+import sys
+
+import numpy as np
+import torch
+
+DEV = "cuda:0"
+
+# dequantized values: one IEEE multiply on both sides -> identical; the stated bound is 1e-6
+DEQUANT_RTOL = 1e-6
+# error statistics: fp64 sums in a different order
+STATS_RTOL = 1e-5
+# decode attention output: per (b, hq) row, max |o - ref| / max |ref|
+ATTN_ROW_RTOL = 2e-3
+
+
+def need_gpu():
+    if not torch.cuda.is_available():
+        raise RuntimeError("GPU tests need a ROCm GPU (torch.cuda.is_available() is False)")
+
+
+def say(*a):
+    """Name the case before a GPU step, flushed, so a fault can be attributed."""
+    print("[gpu-case]", *a, file=sys.stderr, flush=True)
+
+
+def u16(t: torch.Tensor) -> np.ndarray:
+    """bf16 tensor -> its raw bits as numpy uint16 (host)."""
+    return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def np_(t: torch.Tensor) -> np.ndarray:
+    return t.detach().contiguous().cpu().numpy()
+
+
+def gpu_bf16(a: np.ndarray) -> torch.Tensor:
+    """numpy uint16 bf16 bits -> bf16 tensor on the GPU."""
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(DEV)
+
+
+def cache_np(cache) -> dict:
+    d = {s: (u16(getattr(cache, s)) if getattr(cache, s).dtype == torch.bfloat16 else np_(getattr(cache, s)))
+         for s in cache.SECTIONS}
+    d.update(B=cache.B, T=cache.T, H=cache.H, d=cache.d, g=cache.g, R=cache.R)
+    return d
+
+
+def assert_bits_equal(got: np.ndarray, want: np.ndarray, what: str):
+    assert got.shape == want.shape, f"{what}: shape {got.shape} != {want.shape}"
+    if not np.array_equal(got, want):
+        bad = np.argwhere(got != want)
+        i = tuple(bad[0])
+        raise AssertionError(f"{what}: {len(bad)} of {got.size} differ; first at {i}: got {got[i]!r} want {want[i]!r}")
+
+
+def assert_rel(got, want, rtol, what):
+    got = np.asarray(got, np.float64)
+    want = np.asarray(want, np.float64)
+    den = np.maximum(np.abs(want), 1e-300)
+    rel = np.abs(got - want) / den
+    assert np.all(rel <= rtol), f"{what}: max rel err {rel.max():.3e} > {rtol} (got {got}, want {want})"
