@@ -59,6 +59,37 @@ __device__ __forceinline__ uint16_t bf_ceil_pos(float f) {
     return (uint16_t)((__float_as_uint(f) + 0xffffu) >> 16);
 }
 
+// min / max / clamp on finite values.  fminf/fmaxf follow IEEE-754 NaN rules, for which the
+// compiler quiets every operand it cannot prove canonical with an extra v_max_f32 x, x, x;
+// the inputs here are finite by contract, so the hardware min3/max3/med3 are used directly.
+__device__ __forceinline__ float vmin3(float a, float b, float c) {
+    float r;
+    asm("v_min3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+__device__ __forceinline__ float vmax3(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+__device__ __forceinline__ float vmin2(float a, float b) {
+    float r;
+    asm("v_min_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+__device__ __forceinline__ float vmax2(float a, float b) {
+    float r;
+    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+__device__ __forceinline__ float vclamp(float x, float lo, float hi) { return __builtin_amdgcn_fmed3f(x, lo, hi); }
+
+// min and max of 8 values folded into running (mn, mx).
+__device__ __forceinline__ void minmax8(const float (&v)[8], float& mn, float& mx) {
+    mn = vmin3(vmin3(vmin3(mn, v[0], v[1]), v[2], v[3]), vmin3(v[4], v[5], v[6]), v[7]);
+    mx = vmax3(vmax3(vmax3(mx, v[0], v[1]), v[2], v[3]), vmax3(v[4], v[5], v[6]), v[7]);
+}
+
 // round(x / s) with IEEE division semantics (round-half-to-even of the correctly
 // rounded quotient).  Fast path: y = x * r with r = fl(1/s) (correctly rounded),
 // valid while |x / s| < 256: then |y - x/s| < 2^-14.9 and |fl(x/s) - x/s| < 2^-16, so
@@ -69,6 +100,26 @@ __device__ __forceinline__ float rint_div(float x, float s, float r) {
     float n = __builtin_rintf(y);
     if (__builtin_fabsf(y - n) > 0.4999f) n = __builtin_rintf(x / s);
     return n;
+}
+
+// rint_div for 8 values, with the exact-division fallback taken behind one branch.
+template <int N>
+__device__ __forceinline__ void rint_div_n(const float (&x)[N], const float (&s)[N], const float (&r)[N],
+                                           float (&n)[N]) {
+    bool slow = false;
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+        const float y = x[k] * r[k];
+        n[k] = __builtin_rintf(y);
+        slow |= __builtin_fabsf(y - n[k]) > 0.4999f;
+    }
+    if (slow) {
+#pragma unroll
+        for (int k = 0; k < N; ++k) {
+            const float y = x[k] * r[k];
+            if (__builtin_fabsf(y - __builtin_rintf(y)) > 0.4999f) n[k] = __builtin_rintf(x[k] / s[k]);
+        }
+    }
 }
 
 }  // namespace kvq

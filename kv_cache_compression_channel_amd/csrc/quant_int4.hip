@@ -57,7 +57,7 @@ struct GroupParams {
 __device__ __forceinline__ GroupParams group_params(float mn, float mx) {
     GroupParams p;
     float range = mx - mn;
-    range = fmaxf(range, 1e-8f);
+    range = vmax2(range, 1e-8f);
     p.sb = bf_ceil_pos(range / 15.0f);
     p.s = bf_to_f(p.sb);
     // 0 - m: the backend lowers a subtraction from +0 to a negation, which turns m = +0 into
@@ -70,23 +70,36 @@ __device__ __forceinline__ GroupParams group_params(float mn, float mx) {
     return p;
 }
 
-// q = clip(round(x / s) + z, 0, 15) with IEEE-division semantics.
+// q = clip(round(x / s) + z, 0, 15) with IEEE-division semantics, for 8 elements.
 // Fast path (z in [0, 15], so |x / s| <= 31 for every x of the group):
 // w = fma(x, 1/s, z) lies within 4e-6 of x/s + z and fl(x/s) within 2e-6 of x/s, so
 // unless x/s + z is within 1e-5 of a half-integer, rint(w) = rint(fl(x/s)) + z;
 // otherwise |w - rint(w)| > 0.4999 and the true division decides (this also settles
-// exact ties, which round half to even on x/s before z is added).
-__device__ __forceinline__ float code4(float x, float s, float r, float z, bool fast) {
-    float n;
-    if (fast) {
-        const float w = __builtin_fmaf(x, r, z);
-        n = __builtin_rintf(w);
-        if (__builtin_fabsf(w - n) > 0.4999f) n = __builtin_rintf(x / s) + z;
-    } else {
-        // integers: exact whenever the result can fall in [0, 15] (Sterbenz), else far outside
-        n = __builtin_rintf(x / s) + z;
+// exact ties, which round half to even on x/s before z is added).  The fallback sits
+// behind one branch per 8 elements; groups with z outside [0, 15] always take it:
+// rint(x/s) + z is then an fp32 sum of two integers, exact whenever the result can
+// fall in [0, 15] (Sterbenz) and far outside otherwise.
+template <bool UNIFORM>
+__device__ __forceinline__ void codes8(const float (&x)[8], const float (&s)[8], const float (&r)[8],
+                                       const float (&z)[8], bool fast, float (&q)[8]) {
+    float n[8];
+    bool slow = !fast;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const float w = __builtin_fmaf(x[k], r[k], z[k]);
+        n[k] = __builtin_rintf(w);
+        slow |= __builtin_fabsf(w - n[k]) > 0.4999f;
     }
-    return fminf(fmaxf(n, 0.0f), 15.0f);
+    if (slow) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const float w = __builtin_fmaf(x[k], r[k], z[k]);
+            if (!fast || __builtin_fabsf(w - __builtin_rintf(w)) > 0.4999f)
+                n[k] = __builtin_rintf(x[k] / s[k]) + z[k];
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) q[k] = vclamp(n[k], 0.0f, 15.0f);
 }
 
 // 8 codes (as floats in [0, 15]) -> one dword, byte j = code(2j) | code(2j+1) << 4.
@@ -132,24 +145,33 @@ __global__ void __launch_bounds__(kThreads) int4_quant_kernel(const uint16_t* __
         float mn[8], mx[8];
 #pragma unroll
         for (int k = 0; k < 8; ++k) { mn[k] = FLT_MAX; mx[k] = -FLT_MAX; }
+        if (n == G) {
 #pragma unroll
-        for (int i = 0; i < NR; ++i) {
-            const int r = rg + RPP * i;
-            if (r < n) {
-                raw[i] = *reinterpret_cast<const uint4*>(K + ((b * T + t0 + r) * H + h) * D + 8 * lane);
-                float v[8];
-                unpack8(raw[i], v);
+            for (int i = 0; i < NR; ++i)
+                raw[i] = *reinterpret_cast<const uint4*>(K + ((b * T + t0 + rg + RPP * i) * H + h) * D + 8 * lane);
+        } else {
 #pragma unroll
-                for (int k = 0; k < 8; ++k) { mn[k] = fminf(mn[k], v[k]); mx[k] = fmaxf(mx[k], v[k]); }
+            for (int i = 0; i < NR; ++i) {
+                const int r = rg + RPP * i;
+                // rows past the group repeat row 0 of this lane, which leaves min and max unchanged
+                raw[i] = *reinterpret_cast<const uint4*>(K + ((b * T + t0 + (r < n ? r : 0)) * H + h) * D + 8 * lane);
             }
+        }
+#pragma unroll
+        for (int i = 0; i < NR; i += 2) {
+            float v[8], u[8];
+            unpack8(raw[i], v);
+            if (i + 1 < NR) unpack8(raw[i + 1], u); else unpack8(raw[i], u);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) { mn[k] = vmin3(mn[k], v[k], u[k]); mx[k] = vmax3(mx[k], v[k], u[k]); }
         }
         // rows of the same channel lanes inside the wave: lanes differ by multiples of LPR
 #pragma unroll
         for (int off = LPR; off < 64; off *= 2) {
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
-                mn[k] = fminf(mn[k], __shfl_xor(mn[k], off));
-                mx[k] = fmaxf(mx[k], __shfl_xor(mx[k], off));
+                mn[k] = vmin2(mn[k], __shfl_xor(mn[k], off));
+                mx[k] = vmax2(mx[k], __shfl_xor(mx[k], off));
             }
         }
         if ((tid % 64) < LPR) {
@@ -160,7 +182,7 @@ __global__ void __launch_bounds__(kThreads) int4_quant_kernel(const uint16_t* __
         for (int c = tid; c < D; c += kThreads) {
             float a = s_mn[c], z = s_mx[c];
 #pragma unroll
-            for (int w = 1; w < NW; ++w) { a = fminf(a, s_mn[w * D + c]); z = fmaxf(z, s_mx[w * D + c]); }
+            for (int w = 1; w < NW; ++w) { a = vmin2(a, s_mn[w * D + c]); z = vmax2(z, s_mx[w * D + c]); }
             const GroupParams p = group_params(a, z);
             const int64_t mi = ((b * H + h) * geo.nKg + j) * D + c;
             out.k_scale[mi] = p.sb;
@@ -181,8 +203,7 @@ __global__ void __launch_bounds__(kThreads) int4_quant_kernel(const uint16_t* __
             if (r < n) {
                 float v[8], q[8];
                 unpack8(raw[i], v);
-#pragma unroll
-                for (int k = 0; k < 8; ++k) q[k] = code4(v[k], ps[k], pr[k], pz[k], fast);
+                codes8<false>(v, ps, pr, pz, fast, q);
                 *reinterpret_cast<uint32_t*>(out.k_codes + ((b * H + h) * Tq + t0 + r) * (D / 2) + 4 * lane) =
                     pack_codes(q);
             }
@@ -207,13 +228,12 @@ __global__ void __launch_bounds__(kThreads) int4_quant_kernel(const uint16_t* __
                 raw[i] = *reinterpret_cast<const uint4*>(V + ((b * T + t0 + r) * H + h) * D + 8 * lane);
                 float v[8];
                 unpack8(raw[i], v);
-#pragma unroll
-                for (int k = 0; k < 8; ++k) { mn = fminf(mn, v[k]); mx = fmaxf(mx, v[k]); }
+                minmax8(v, mn, mx);
             }
 #pragma unroll
             for (int off = 1; off < LPG; off *= 2) {
-                mn = fminf(mn, __shfl_xor(mn, off));
-                mx = fmaxf(mx, __shfl_xor(mx, off));
+                mn = vmin2(mn, __shfl_xor(mn, off));
+                mx = vmax2(mx, __shfl_xor(mx, off));
             }
             if (lane % LPG == 0) { s_mn[r * NGD + grp] = mn; s_mx[r * NGD + grp] = mx; }
         }
@@ -232,10 +252,11 @@ __global__ void __launch_bounds__(kThreads) int4_quant_kernel(const uint16_t* __
             if (r < n) {
                 const float ps = s_ps[r * NGD + grp], pr = s_pr[r * NGD + grp], pz = s_pz[r * NGD + grp];
                 const bool fast = pz >= 0.0f && pz <= 15.0f;
+                const float ps8[8] = {ps, ps, ps, ps, ps, ps, ps, ps}, pr8[8] = {pr, pr, pr, pr, pr, pr, pr, pr};
+                const float pz8[8] = {pz, pz, pz, pz, pz, pz, pz, pz};
                 float v[8], q[8];
                 unpack8(raw[i], v);
-#pragma unroll
-                for (int k = 0; k < 8; ++k) q[k] = code4(v[k], ps, pr, pz, fast);
+                codes8<true>(v, ps8, pr8, pz8, fast, q);
                 *reinterpret_cast<uint32_t*>(out.v_codes + ((b * H + h) * Tq + t0 + r) * (D / 2) + 4 * lane) =
                     pack_codes(q);
             }

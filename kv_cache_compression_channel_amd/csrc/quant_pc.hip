@@ -74,11 +74,19 @@ __global__ void __launch_bounds__(kThreads) pc_minmax_kernel(const void* __restr
     for (int k = 0; k < VEC; ++k) { mn[k] = FLT_MAX; mx[k] = -FLT_MAX; }
     if (c0 < g.C) {
         const int64_t r_end = min(g.R, (rc + 1) * kRowsPerChunk);
-        for (int64_t r = rc * kRowsPerChunk + rl; r < r_end; r += g.rpp) {
+        int64_t r = rc * kRowsPerChunk + rl;
+        for (; r + g.rpp < r_end; r += 2 * g.rpp) {
+            float v[VEC], u[VEC];
+            load_x<XT, VEC>(x, s * g.bsx + r * g.ldx + c0, v);
+            load_x<XT, VEC>(x, s * g.bsx + (r + g.rpp) * g.ldx + c0, u);
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) { mn[k] = vmin3(mn[k], v[k], u[k]); mx[k] = vmax3(mx[k], v[k], u[k]); }
+        }
+        if (r < r_end) {
             float v[VEC];
             load_x<XT, VEC>(x, s * g.bsx + r * g.ldx + c0, v);
 #pragma unroll
-            for (int k = 0; k < VEC; ++k) { mn[k] = fminf(mn[k], v[k]); mx[k] = fmaxf(mx[k], v[k]); }
+            for (int k = 0; k < VEC; ++k) { mn[k] = vmin2(mn[k], v[k]); mx[k] = vmax2(mx[k], v[k]); }
         }
     }
 #pragma unroll
@@ -93,8 +101,8 @@ __global__ void __launch_bounds__(kThreads) pc_minmax_kernel(const void* __restr
         const int ln = j / VEC, k = j % VEC;
         float a = FLT_MAX, b = -FLT_MAX;
         for (int q = 0; q < g.rpp; ++q) {
-            a = fminf(a, smn[(q * g.lpr + ln) * VEC + k]);
-            b = fmaxf(b, smx[(q * g.lpr + ln) * VEC + k]);
+            a = vmin2(a, smn[(q * g.lpr + ln) * VEC + k]);
+            b = vmax2(b, smx[(q * g.lpr + ln) * VEC + k]);
         }
         const int64_t c = cb * ncol + j;
         if (c < g.C) part[(s * g.nrc + rc) * g.C + c] = make_float2(a, b);
@@ -113,26 +121,26 @@ __global__ void __launch_bounds__(kThreads) pc_params_kernel(const float2* __res
     float mn = FLT_MAX, mx = -FLT_MAX;
     for (int64_t k = 0; k < nrc; ++k) {
         const float2 p = part[(s * nrc + k) * C + c];
-        mn = fminf(mn, p.x);
-        mx = fmaxf(mx, p.y);
+        mn = vmin2(mn, p.x);
+        mx = vmax2(mx, p.y);
     }
     PcParams P;
     int z = 0;
     if constexpr (SYM) {
-        float a = fmaxf(mx, -mn);           // max |x|
-        a = fmaxf(a, 1e-8f);
+        float a = vmax2(mx, -mn);           // max |x|
+        a = vmax2(a, 1e-8f);
         P.s = a / (float)qmax;
     } else {
         float range = mx - mn;
-        range = fmaxf(range, 1e-8f);
+        range = vmax2(range, 1e-8f);
         P.s = range / (float)(qmax - qmin);
         const float m = mn / P.s;   // qmin - m with an explicit zero case (see group_params of the INT4 path)
         const float zr = (qmin == 0 && m == 0.0f) ? 0.0f : __builtin_rintf((float)qmin - m);
-        z = (int)fminf(fmaxf(zr, -128.0f), 127.0f);
+        z = (int)vclamp(zr, -128.0f, 127.0f);
     }
     P.r = 1.0f / P.s;
     P.zf = (float)z;
-    P.fast = (fmaxf(fabsf(mn), fabsf(mx)) * P.r <= 250.0f) ? 1.0f : 0.0f;
+    P.fast = (vmax2(fabsf(mn), fabsf(mx)) * P.r <= 250.0f) ? 1.0f : 0.0f;
     scale[i] = P.s;
     if (zp) zp[i] = (int8_t)z;
     prm[i] = P;
@@ -150,12 +158,13 @@ __global__ void __launch_bounds__(kThreads) pc_code_kernel(const void* __restric
     const int lane = threadIdx.x % g.lpr, rl = threadIdx.x / g.lpr;
     const int64_t c0 = (cb * g.lpr + lane) * VEC;
     if (c0 >= g.C) return;
-    PcParams P[VEC];
+    float ps[VEC], pr[VEC], pz[VEC];
     bool fast = true;
 #pragma unroll
     for (int k = 0; k < VEC; ++k) {
-        P[k] = prm[s * g.C + c0 + k];
-        fast = fast && (P[k].fast != 0.0f);
+        const PcParams P = prm[s * g.C + c0 + k];
+        ps[k] = P.s; pr[k] = P.r; pz[k] = P.zf;
+        fast = fast && (P.fast != 0.0f);
     }
     const float lo = (float)qmin, hi = (float)qmax;
     const int64_t r_end = min(g.R, (rc + 1) * kRowsPerChunk);
@@ -163,12 +172,18 @@ __global__ void __launch_bounds__(kThreads) pc_code_kernel(const void* __restric
         float v[VEC];
         load_x<XT, VEC>(x, s * g.bsx + r * g.ldx + c0, v);
         int8_t o[VEC];
+        float n[VEC];
+        if (fast) {
+            rint_div_n<VEC>(v, ps, pr, n);
+        } else {
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) n[k] = __builtin_rintf(v[k] / ps[k]);
+        }
 #pragma unroll
         for (int k = 0; k < VEC; ++k) {
-            const float n = fast ? rint_div(v[k], P[k].s, P[k].r) : __builtin_rintf(v[k] / P[k].s);
             // n and zf are integers: the fp32 sum is exact whenever the result can land in
             // [qmin, qmax] (Sterbenz), and far outside otherwise, so the clip is exact.
-            o[k] = (int8_t)(int)fminf(fmaxf(n + P[k].zf, lo), hi);
+            o[k] = (int8_t)(int)vclamp(n[k] + pz[k], lo, hi);
         }
         int8_t* dst = q + (s * g.R + r) * g.C + c0;
         if constexpr (VEC == 8) {

@@ -60,17 +60,31 @@ __global__ void __launch_bounds__(kThreads) stats_partial_kernel(const void* __r
     __shared__ double sh[3 * (kThreads / 64)];
     const int64_t lo = (int64_t)blockIdx.x * chunk, hi = min(n, lo + chunk);
     double sq = 0.0, ab = 0.0, mx = 0.0;
-    for (int64_t i = lo + (int64_t)threadIdx.x * VEC; i < hi; i += (int64_t)kThreads * VEC) {
-        double a[VEC], b[VEC];
-        ld<XT, VEC>(x, i, a);
-        ld<HT, VEC>(xh, i, b);
+    auto acc = [&](const double (&a)[VEC], const double (&b)[VEC]) {
 #pragma unroll
         for (int k = 0; k < VEC; ++k) {
             const double e = a[k] - b[k];
             sq = __builtin_fma(e, e, sq);
-            ab += fabs(e);
-            mx = fmax(mx, fabs(e));
+            ab += __builtin_fabs(e);
+            mx = __builtin_fmax(mx, __builtin_fabs(e));
         }
+    };
+    constexpr int64_t step = (int64_t)kThreads * VEC;
+    int64_t i = lo + (int64_t)threadIdx.x * VEC;
+    for (; i + step < hi; i += 2 * step) {   // two independent load pairs in flight
+        double a0[VEC], b0[VEC], a1[VEC], b1[VEC];
+        ld<XT, VEC>(x, i, a0);
+        ld<HT, VEC>(xh, i, b0);
+        ld<XT, VEC>(x, i + step, a1);
+        ld<HT, VEC>(xh, i + step, b1);
+        acc(a0, b0);
+        acc(a1, b1);
+    }
+    if (i < hi) {
+        double a0[VEC], b0[VEC];
+        ld<XT, VEC>(x, i, a0);
+        ld<HT, VEC>(xh, i, b0);
+        acc(a0, b0);
     }
     block_reduce3(sq, ab, mx, sh);
     if (threadIdx.x == 0) {
