@@ -23,6 +23,8 @@
 
 namespace kvq {
 int check_cache_shape(const kvq_int4_cache* c, const char* name);
+void launch_attn_mfma(const kvq_int4_cache* c, const void* q, int64_t Hq, float qscale, float* ws, int nsplit,
+                      int64_t split_len, int nslot, hipStream_t st);
 
 namespace {
 
@@ -44,8 +46,10 @@ struct AttnArgs {
     int ot;
     float* ws;
     int64_t B, T, H, R, Tq, nKg, Hq;
+    int64_t range_lo, range_hi;   // token range this launch covers
     int64_t split_len;
-    int nsplit;
+    int nsplit;                   // splits of this launch per (b, h)
+    int nslot, slot_off;          // ws slots per (b, hq) and this launch's first slot
     float qscale;   // sm_scale * log2(e)
 };
 
@@ -68,8 +72,8 @@ __global__ void __launch_bounds__(kThreads) attn_split_kernel(const AttnArgs a) 
     const int64_t bh = blockIdx.x / a.nsplit;
     const int split = (int)(blockIdx.x % a.nsplit);
     const int64_t b = bh / a.H, h = bh % a.H;
-    const int64_t t_begin = (int64_t)split * a.split_len;
-    const int64_t t_end = min(a.T, t_begin + a.split_len);
+    const int64_t t_begin = a.range_lo + (int64_t)split * a.split_len;
+    const int64_t t_end = min(a.range_hi, t_begin + a.split_len);
     const int64_t Tq = a.Tq;
 
     float qv[NQ][8];
@@ -230,7 +234,7 @@ __global__ void __launch_bounds__(kThreads) attn_split_kernel(const AttnArgs a) 
             L += s_l[w][qi] * f;
             A += s_acc[w][qi][c] * f;
         }
-        float* dst = a.ws + ((b * a.Hq + h * NQ + qi) * a.nsplit + split) * (D + 2);
+        float* dst = a.ws + ((b * a.Hq + h * NQ + qi) * a.nslot + a.slot_off + split) * (D + 2);
         if (c == 0) { dst[0] = M; dst[1] = L; }
         dst[2 + c] = A;
     }
@@ -257,29 +261,59 @@ __global__ void __launch_bounds__(D) attn_combine_kernel(const float* __restrict
         static_cast<uint16_t*>(out)[row * D + c] = f_to_bf(o);
 }
 
+// How the token axis is cut: the INT4 tokens [0, Tq) go to the matrix-core kernel when
+// d = 128 (splits on multiples of 128 tokens), everything else to the VALU kernel (splits on
+// multiples of max(g, 64) tokens); each split writes one partial slot per (b, hq).
 struct SplitPlan {
-    int nsplit;
-    int64_t split_len;
+    bool mfma;
+    int nsplit_q;           // matrix-core splits over [0, Tq)
+    int64_t len_q;
+    int nsplit_v;           // VALU splits over [v_lo, T)
+    int64_t len_v, v_lo;
+    int nslot;
 };
 
-SplitPlan plan_splits(int64_t B, int64_t H, int64_t T, int64_t g) {
-    const int64_t unit = g > 64 ? g : 64;      // split boundaries stay on K-group and step boundaries
+int64_t split_len_for(int64_t n, int64_t want, int64_t unit) {
+    int64_t len = cdiv(cdiv(n, want), unit) * unit;
+    return len < unit ? unit : len;
+}
+
+SplitPlan plan_splits(int64_t B, int64_t H, int64_t T, int64_t R, int64_t d, int64_t g) {
+    SplitPlan p{};
+    const int64_t Tq = T - R;
     const int64_t want = cdiv(2048, B * H);    // aim for >= 2048 blocks
-    int64_t len = cdiv(cdiv(T, want), unit) * unit;
-    if (len < unit) len = unit;
-    return SplitPlan{(int)cdiv(T, len), len};
+    p.mfma = (d == 128) && Tq > 0;
+    if (p.mfma) {
+        p.len_q = split_len_for(Tq, want, 128);
+        p.nsplit_q = (int)cdiv(Tq, p.len_q);
+        p.v_lo = Tq;
+    } else {
+        p.v_lo = 0;
+    }
+    const int64_t nv = T - p.v_lo;
+    if (nv > 0) {
+        p.len_v = split_len_for(nv, p.mfma ? 1 : want, g > 64 ? g : 64);
+        p.len_v = p.mfma ? (p.len_v < 256 ? p.len_v : 256) : p.len_v;
+        p.nsplit_v = (int)cdiv(nv, p.len_v);
+    }
+    p.nslot = p.nsplit_q + p.nsplit_v;
+    return p;
 }
 
 template <int D, int GS, int NQ>
 void launch_attn(const AttnArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((attn_split_kernel<D, GS, NQ>), dim3((unsigned)(a.B * a.H * a.nsplit)), dim3(kThreads), 0, st,
                        a);
+}
+
+template <int D>
+void launch_combine(const AttnArgs& a, hipStream_t st) {
     if (a.ot == KVQ_FP32)
         hipLaunchKernelGGL((attn_combine_kernel<D, KVQ_FP32>), dim3((unsigned)(a.B * a.Hq)), dim3(D), 0, st, a.ws,
-                           a.nsplit, a.out);
+                           a.nslot, a.out);
     else
         hipLaunchKernelGGL((attn_combine_kernel<D, KVQ_BF16>), dim3((unsigned)(a.B * a.Hq)), dim3(D), 0, st, a.ws,
-                           a.nsplit, a.out);
+                           a.nslot, a.out);
 }
 
 template <int D, int GS>
@@ -291,6 +325,12 @@ void dispatch_nq(const AttnArgs& a, int nq, hipStream_t st) {
         case 8: launch_attn<D, GS, 8>(a, st); break;
         default: launch_attn<D, GS, 16>(a, st); break;
     }
+}
+
+void dispatch_combine(const AttnArgs& a, int64_t d, hipStream_t st) {
+    if (d == 64) launch_combine<64>(a, st);
+    else if (d == 128) launch_combine<128>(a, st);
+    else launch_combine<256>(a, st);
 }
 
 void dispatch(const AttnArgs& a, int64_t d, int64_t g, int nq, hipStream_t st) {
@@ -310,9 +350,9 @@ void dispatch(const AttnArgs& a, int64_t d, int64_t g, int nq, hipStream_t st) {
 extern "C" {
 
 size_t kvq_decode_attn_int4_ws(const kvq_int4_cache* c, int64_t Hq) {
-    if (!c || c->B < 1 || c->H < 1 || c->T < 1 || c->g < 1 || Hq < 1) return 0;
-    const kvq::SplitPlan p = kvq::plan_splits(c->B, c->H, c->T, c->g);
-    return (size_t)(c->B * Hq * p.nsplit * (c->d + 2)) * sizeof(float);
+    if (!c || c->B < 1 || c->H < 1 || c->T < 1 || c->g < 1 || Hq < 1 || c->R < 0 || c->R > c->T) return 0;
+    const kvq::SplitPlan p = kvq::plan_splits(c->B, c->H, c->T, c->R, c->d, c->g);
+    return (size_t)(c->B * Hq * p.nslot * (c->d + 2)) * sizeof(float);
 }
 
 int kvq_decode_attn_int4(const kvq_int4_cache* c, const void* q, int64_t Hq, float sm_scale, void* out, int ot,
@@ -331,8 +371,8 @@ int kvq_decode_attn_int4(const kvq_int4_cache* c, const void* q, int64_t Hq, flo
     KVQ_REQUIRE_ALIGNED(q, "q");
     KVQ_REQUIRE_ALIGNED(out, "out");
     KVQ_REQUIRE_ALIGNED(ws, "ws");
-    const kvq::SplitPlan p = kvq::plan_splits(c->B, c->H, c->T, c->g);
-    KVQ_REQUIRE(c->B * c->H * p.nsplit < ((int64_t)1 << 31), "kvq_decode_attn_int4: grid too large");
+    const kvq::SplitPlan p = kvq::plan_splits(c->B, c->H, c->T, c->R, c->d, c->g);
+    KVQ_REQUIRE(c->B * c->H * p.nslot < ((int64_t)1 << 31), "kvq_decode_attn_int4: grid too large");
     kvq::AttnArgs a;
     a.k_codes = c->k_codes; a.k_scale = c->k_scale; a.k_zero = c->k_zero;
     a.v_codes = c->v_codes; a.v_scale = c->v_scale; a.v_zero = c->v_zero;
@@ -344,10 +384,20 @@ int kvq_decode_attn_int4(const kvq_int4_cache* c, const void* q, int64_t Hq, flo
     a.B = c->B; a.T = c->T; a.H = c->H; a.R = c->R; a.Tq = c->T - c->R;
     a.nKg = kvq::cdiv(a.Tq, c->g);
     a.Hq = Hq;
-    a.split_len = p.split_len;
-    a.nsplit = p.nsplit;
+    a.nslot = p.nslot;
     a.qscale = sm_scale * 1.4426950408889634f;
-    kvq::dispatch(a, c->d, c->g, (int)nq, static_cast<hipStream_t>(stream));
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (p.mfma)
+        kvq::launch_attn_mfma(c, q, Hq, a.qscale, a.ws, p.nsplit_q, p.len_q, p.nslot, st);
+    if (p.nsplit_v > 0) {
+        a.range_lo = p.v_lo;
+        a.range_hi = c->T;
+        a.split_len = p.len_v;
+        a.nsplit = p.nsplit_v;
+        a.slot_off = p.nsplit_q;
+        kvq::dispatch(a, c->d, c->g, (int)nq, st);
+    }
+    kvq::dispatch_combine(a, c->d, st);
     return kvq::launch_status("kvq_decode_attn_int4");
 }
 
