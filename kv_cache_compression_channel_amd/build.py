@@ -27,6 +27,9 @@ FLAGS = [
     "-fno-gpu-flush-denormals-to-zero",
     # no packed fp32 instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core accumulators in ordinary VGPRs: the loop-carried sums of the attention
+    # kernel are also rescaled by VALU code, and AGPR homes cost a copy each way per tile
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall",
     "-I" + os.path.join(ROOT, "include"),
 ]

@@ -368,6 +368,7 @@ int kvq_decode_attn_int4(const kvq_int4_cache* c, const void* q, int64_t Hq, flo
                 "kvq_decode_attn_int4: Hq / H must be 1, 2, 4, 8 or 16 (got %lld)", (long long)nq);
     KVQ_REQUIRE(ws && ws_bytes >= kvq_decode_attn_int4_ws(c, Hq), "kvq_decode_attn_int4: workspace of %zu bytes needed",
                 kvq_decode_attn_int4_ws(c, Hq));
+    KVQ_REQUIRE(c->T <= ((int64_t)1 << 30), "kvq_decode_attn_int4: T must be at most 2^30 tokens");
     KVQ_REQUIRE_ALIGNED(q, "q");
     KVQ_REQUIRE_ALIGNED(out, "out");
     KVQ_REQUIRE_ALIGNED(ws, "ws");

@@ -4,32 +4,45 @@
 //
 // Per (b, KV head h, token split) block of 4 waves; each wave streams 32-token tiles of its
 // own contiguous token range and keeps an online softmax for the Hq/H query heads of h.
-// Both products are v_mfma_f32_16x16x32_f16 (16 rows x 16 columns x 32-deep):
+// Both products are v_mfma_f32_16x16x32_f16 (16 rows x 16 columns x 32-deep).
 //
-//   scores  S[t][n]  = sum_c code_K[t][c] * Q'[n][c],   Q' = q * s_K * log2(e) as fp16 hi + lo
-//           logit    = S - bias[n],  bias[n] = sum_c Q'[n][c] * z_K[c]
+// Codes enter the matrix cores as fp16(64 + code): with 0x54 as the high byte and the nibble
+// in mantissa bits 4..7, one v_and_or_b32 turns a pair of nibbles into a pair of fp16 values
+// (no convert, no subtract).  The constant 64 is removed on the other side of each product:
+//
+//   scores  S'[t][n] = sum_c (64 + code_K[t][c]) * Q'[n][c],   Q' = q * s_K (fp16 hi + lo)
+//           logit    = (S' - bias[n]) * lscale,   bias[n] = sum_c q'[n][c] * (z_K[c] + 64)
 //           (K scales and zeros are per channel over a token group, so they fold into Q'; Q' is
-//           split into two fp16 parts, two MFMAs each, so it carries ~22 significant bits)
-//   values  O[c][n] += sum_t code_V[t][c] * P'[t][n],            P' = p * s_V[t][grp(c)] (fp16)
-//           O[c][n] -= sum_t P'[t][n] * z_V[t][grp(c)]
-//           (V scales and zeros are per token per channel group, so they fold into P')
+//           split into two fp16 parts, two MFMAs each, so it carries ~22 significant bits; the
+//           bias is formed in fp32 from the unrounded q')
+//   values  O[c][n] = sum_t (64 + code_V[t][c]) * P'[t][n]  -  sum_t 64 * P'[t][n]
+//                     - sum_t (p s_V)[t][n] * z_V[t][grp(c)],      P' = fp16(p * s_V)
+//           (the middle term is one more MFMA per V group against a constant-64 operand; the
+//           zero-point term is accumulated in fp32 from the unrounded p * s_V, so groups with a
+//           tiny scale and a huge zero point -- constant groups -- keep their value)
 //
-// Codes become fp16 without a convert instruction: (0x6400 | n) is fp16(1024 + n), so after
-// masking nibbles into bytes one v_perm_b32 (against a register holding 0x64006400) yields two
-// fp16(1024 + code) values, and one packed fp16 add of -1024 leaves the exact codes.
+// The fp16 range is kept by the softmax reference: p = 2^(logit - ref) with
+// ref = Mlog + E - 15, where Mlog bounds every logit seen so far and 2^E bounds every V scale
+// seen so far, so P' = p * s_V < 2^15.  The reference only moves (with the usual rescale of
+// the running sums) when a tile holds a logit above Mlog or a scale at or above 2^E, which
+// after the first tiles is rare; the partial it writes is (ref, l, O), which the log-sum-exp
+// combine merges like any other.  A K group whose q * s_K would leave the fp16 range is
+// scaled by a power of two per query, undone in lscale.
 //
 // Lane layouts (verified for this builtin): A[m][k] in lane m%16 + 16*(k/8), element k%8;
 // B[k][n] in lane n + 16*(k/8), element k%8; D[m][n] in lane n + 16*(m/4), element m%4.
 //   QK: A = K codes, m = token (16 per MFMA), k = channel; lane group G = lane/16 owns the 32
 //       channels 32G..32G+31 (one 16-byte load), element j of chunk kk is channel
-//       32G + 8kk + perm[j] with perm = 0,2,4,6,1,3,5,7 (the order the byte pairing yields);
-//       B = Q'^T with the same channel order; D gives lane (n, G) the scores of tokens
-//       4G..4G+3 and 16+4G..16+4G+3 for query n.
+//       32G + 8kk + kPerm[j] (the order the nibble extraction yields); B = Q'^T in the same
+//       channel order; D gives lane (n, G) the scores of tokens 4G..4G+3 and 16+4G..16+4G+3.
 //   PV: B = P'^T straight from those registers (k = token slots in that same order, n = query);
 //       A = V codes^T, m = channel row, k = token; channel row m of block nb is channel
 //       g*(nb/BPG) + BPG*m + nb%BPG (BPG = g/16 blocks per V group), so each MFMA's 16
 //       channels share one V group (one P') and a lane's channels are adjacent nibbles.
-//       The V code tile is staged through LDS to transpose tokens into the k dimension.
+//       The V code tile is staged through LDS to bring tokens into the k dimension.
+//   Q' for a new K group: with NQ query heads, lane (n, G) computes query n % NQ on 8-channel
+//       chunk(s) of its 32 channels and the chunks are exchanged through LDS, so the work is
+//       spread over all 16 lanes of a group instead of the NQ lanes that own real queries.
 #include "kvq_internal.h"
 
 namespace kvq {
@@ -40,6 +53,8 @@ constexpr int kWaves = 4;
 constexpr int kTile = 32;           // tokens per wave iteration
 constexpr int D = 128;
 constexpr float kNegBig = -3.0e38f;
+constexpr float kMargin = 2.0f;     // head-room put above the largest logit when the reference moves
+constexpr int kEmin = -64, kEmax = 64;
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
@@ -55,8 +70,9 @@ struct MfmaArgs {
     const uint16_t* v_zero;
     const uint16_t* q;
     float* ws;
-    int64_t B, H, Tq, nKg, Hq;
-    int64_t split_len;   // tokens per split (multiple of 4 * kTile and of g)
+    int64_t B, H, Hq;
+    int Tq, nKg;
+    int split_len;       // tokens per split (multiple of 4 * kTile)
     int nsplit;          // INT4 splits per (b, h)
     int nslot;           // partial slots per (b, hq) in ws (INT4 splits + residual splits)
     float qscale;        // sm_scale * log2(e)
@@ -72,201 +88,300 @@ __device__ __forceinline__ uint32_t pack_h2(float a, float b) {
     return __builtin_bit_cast(uint32_t, h);
 }
 
-// two fp16(1024 + n) -> two exact fp16(n)
-__device__ __forceinline__ uint32_t sub1024(uint32_t w) {
-    const half2v off = {(_Float16)-1024.0f, (_Float16)-1024.0f};
-    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, w) + off);
+// fp16 0x5400 | (n << 4) = 64 + n for a nibble n in mantissa bits 4..7.
+constexpr uint32_t kMagic = 0x54005400u;
+constexpr uint32_t kNib = 0x00f000f0u;
+__device__ __forceinline__ uint32_t nib_pair(uint32_t x) {
+    return __builtin_amdgcn_bitop3_b32(x, kNib, kMagic, 0xEA);   // (x & kNib) | kMagic in one op
 }
 
-// Byte select that places a 0x64 exponent byte above each selected nibble byte: with
-// c64 = 0x64006400 as the high source, perm(c64, x, sel) builds fp16(1024 + x.byte) pairs.
-__device__ __forceinline__ uint32_t perm64(uint32_t x, uint32_t c64, uint32_t sel) {
-    return __builtin_amdgcn_perm(c64, x, sel);
+// One dword of K codes (byte j = c(2j) | c(2j+1) << 4) -> fp16(64 + c) in the element order
+// c0 c4 c2 c6 c1 c5 c3 c7: each pair takes the nibbles sitting in bits 4..7 and 20..23.
+constexpr int kPerm[8] = {0, 4, 2, 6, 1, 5, 3, 7};
+__device__ __forceinline__ half8 nib8(uint32_t w) {
+    return as_half8(nib_pair(w << 4), nib_pair(w >> 4), nib_pair(w), nib_pair(w >> 8));
 }
-constexpr uint32_t kSelB0B1 = 0x07010500u;   // bytes 0, 1 of x -> fp16 pair
-constexpr uint32_t kSelB2B3 = 0x07030502u;   // bytes 2, 3 of x
-constexpr uint32_t kSelB0B2 = 0x07020500u;   // bytes 0, 2
-constexpr uint32_t kSelB1B3 = 0x07030501u;   // bytes 1, 3
 
-// 8 nibbles of a dword (byte j = c(2j) | c(2j+1) << 4) -> fp16(code) in the order
-// c0,c2,c4,c6,c1,c3,c5,c7: mask the low and high nibbles into bytes, then pair bytes.
-__device__ __forceinline__ half8 nib8(uint32_t w, uint32_t c64) {
-    const uint32_t e = w & 0x0f0f0f0fu, o = (w >> 4) & 0x0f0f0f0fu;
-    return as_half8(sub1024(perm64(e, c64, kSelB0B1)), sub1024(perm64(e, c64, kSelB2B3)),
-                    sub1024(perm64(o, c64, kSelB0B1)), sub1024(perm64(o, c64, kSelB2B3)));
+// Butterfly exchange across lanes: xor distances below 32 go through ds_swizzle's bit mode.
+template <int OFF>
+__device__ __forceinline__ float xor_lane(float x) {
+    if constexpr (OFF < 32) {
+        return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x1f | (OFF << 10)));
+    } else {
+        return __shfl_xor(x, OFF);
+    }
 }
 
 template <int GS, int NQ>
-__global__ void __launch_bounds__(kThreads) attn_mfma_kernel(const MfmaArgs a) {
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+attn_mfma_kernel(const MfmaArgs a) {
     constexpr int NG = D / GS;          // V groups per token
     constexpr int BPG = GS / 16;        // MFMA channel blocks per V group
     constexpr int PB = GS / 32;         // bytes of one V group piece per lane per token
+    constexpr int PASS = NQ >= 16 ? 4 : (NQ == 8 ? 2 : 1);   // Q' chunks each lane computes
+    // tiles whose loads are in flight per wave: three where the registers allow two waves per SIMD
+    constexpr int kBuf = (GS == 32 || NQ == 16) ? 2 : 3;
     static_assert(NQ <= 16, "at most 16 query heads per KV head");
 
-    // per-wave V code tile (32 tokens x 64 bytes) and its scales/zeros; reused for the merge
-    __shared__ __attribute__((aligned(16))) uint8_t s_v[kWaves][kTile * D / 2];
-    __shared__ __attribute__((aligned(16))) uint16_t s_vs[kWaves][kTile * NG];
-    __shared__ __attribute__((aligned(16))) uint16_t s_vz[kWaves][kTile * NG];
-    __shared__ __attribute__((aligned(16))) uint16_t s_kp[kWaves][2 * D];   // K group scale, zero
-    __shared__ float s_m[kWaves][16], s_l[kWaves][16];
-    __shared__ float s_o[kWaves][16][D + 1];
+    // per-wave V code tile (32 tokens x 64 bytes), V (scale, zero) pairs in fp32, K group
+    // scale/zero rows, the Q' exchange; the merge at the end reuses the same memory
+    struct Loop {
+        uint8_t k[kWaves][kTile * D / 2];
+        uint8_t v[kWaves][kTile * D / 2];
+        float sz[kWaves][kTile * NG * 2];
+        uint16_t kp[kWaves][2 * D];
+        uint32_t qx[kWaves][64][PASS < 4 ? PASS * 8 : 1];
+    };
+    struct Merge {
+        float m[kWaves][16], l[kWaves][16];
+        float o[kWaves][16][D + 1];
+    };
+    __shared__ __attribute__((aligned(16))) union {
+        Loop lp;
+        Merge mg;
+    } sm;
 
-    const int tid = threadIdx.x, lane = tid % 64, wv = tid / 64;
+    const int tid = threadIdx.x, lane = tid % 64;
+    const int wv = __builtin_amdgcn_readfirstlane(tid / 64);
     const int n = lane % 16, G = lane / 16;
     const int64_t bh = blockIdx.x / a.nsplit;
     const int split = (int)(blockIdx.x % a.nsplit);
     const int64_t b = bh / a.H, h = bh % a.H;
-    const int64_t Tq = a.Tq;
+    const int Tq = a.Tq;
     // this wave's contiguous token range inside the split
-    const int64_t s_lo = (int64_t)split * a.split_len;
-    const int64_t s_hi = min(Tq, s_lo + a.split_len);
-    const int64_t per_wave = a.split_len / kWaves;
-    const int64_t t_lo = min(s_hi, s_lo + per_wave * wv);
-    const int64_t t_hi = min(s_hi, t_lo + per_wave);
+    const int s_lo = split * a.split_len;
+    const int s_hi = min(Tq, s_lo + a.split_len);
+    const int per_wave = a.split_len / kWaves;
+    const int t_lo = min(s_hi, s_lo + per_wave * wv);
+    const int t_hi = min(s_hi, t_lo + per_wave);
 
-    // query n, channels 32G..32G+31 (zero for padding columns n >= NQ); sm_scale * log2(e) is
-    // applied to the finished logits
-    float qv[32];
+    // the query values this lane turns into Q': query n % NQ, channels 32G + 8 kc(p) + 0..7
+    auto chunk_of = [&](int p) -> int {
+        if constexpr (NQ >= 16) return p;
+        else if constexpr (NQ == 8) return n / 8 + 2 * p;
+        else return (n / NQ) % 4;
+    };
+    float qv[PASS][8];
     {
-        const bool real = n < NQ;
-        const uint16_t* qp = a.q + ((b * a.Hq + h * NQ + (real ? n : 0)) * D + 32 * G);
+        const uint16_t* qp = a.q + (b * a.Hq + h * NQ + n % NQ) * D + 32 * G;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const uint4 r = *reinterpret_cast<const uint4*>(qp + 8 * u);
+        for (int p = 0; p < PASS; ++p) {
+            const u32x4 r = *reinterpret_cast<const u32x4*>(qp + 8 * chunk_of(p));
             const uint32_t w[4] = {r.x, r.y, r.z, r.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                qv[8 * u + 2 * e] = real ? bf_lo(w[e]) : 0.0f;
-                qv[8 * u + 2 * e + 1] = real ? bf_hi(w[e]) : 0.0f;
+                qv[p][2 * e] = bf_lo(w[e]);
+                qv[p][2 * e + 1] = bf_hi(w[e]);
             }
         }
     }
-    const uint32_t c64 = 0x64006400u;
 
-    floatx4 acc_o[8];
+    floatx4 acc_o[8], acc_off[NG];
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb) acc_o[nb] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-    float m_run = kNegBig, l_part = 0.0f;
-    float zterm[NG];
 #pragma unroll
-    for (int gI = 0; gI < NG; ++gI) zterm[gI] = 0.0f;
+    for (int gI = 0; gI < NG; ++gI) acc_off[gI] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+    float zsum[NG];
+#pragma unroll
+    for (int gI = 0; gI < NG; ++gI) zsum[gI] = 0.0f;
+    float l_part = 0.0f;
+    // softmax reference (per query column) and its bounds
+    float ref = 0.0f;            // p = 2^(logit - ref)
+    float thr = kNegBig;         // largest logit - ref allowed without moving ref (= 15 - E once started)
+    int e_s = kEmin;             // every V scale seen is below 2^e_s
+    float s_lim = 0.0f;          // 2^e_s (0 before the first tile)
+    bool started = false;
 
-    half8 bq[4], bql[4];   // Q'^T operand of the current K group: fp16 hi and lo parts
-    float bias = 0.0f;
+    half8 bq[4], bql[4];         // Q'^T operand of the current K group: fp16 hi and lo parts
+    float lscale = a.qscale, c0 = 0.0f;   // logit - ref = S' * lscale - c0
 
-    const uint8_t* kc = a.k_codes + (b * a.H + h) * Tq * (D / 2);
-    const uint8_t* vc = a.v_codes + (b * a.H + h) * Tq * (D / 2);
-    const uint16_t* vsp = a.v_scale + (b * a.H + h) * Tq * NG;
-    const uint16_t* vzp = a.v_zero + (b * a.H + h) * Tq * NG;
-    const uint16_t* kscale = a.k_scale + (b * a.H + h) * a.nKg * D;
-    const uint16_t* kzero = a.k_zero + (b * a.H + h) * a.nKg * D;
-    uint8_t* sv = s_v[wv];
+    const uint8_t* kc = a.k_codes + bh * (int64_t)Tq * (D / 2);
+    const uint8_t* vc = a.v_codes + bh * (int64_t)Tq * (D / 2);
+    const uint16_t* vsp = a.v_scale + bh * (int64_t)Tq * NG;
+    const uint16_t* vzp = a.v_zero + bh * (int64_t)Tq * NG;
+    const uint16_t* kscale = a.k_scale + bh * (int64_t)a.nKg * D;
+    const uint16_t* kzero = a.k_zero + bh * (int64_t)a.nKg * D;
+    uint8_t* sk = sm.lp.k[wv];
+    uint8_t* sv = sm.lp.v[wv];
+    float* ssz = sm.lp.sz[wv];
+    uint16_t* skp = sm.lp.kp[wv];
 
-    // ---- one tile of global loads, issued one tile ahead of its use ----
+    // ---- tile loads: kBuf tiles in flight per wave, in registers until staged ----
     // K codes: token 16*hf + n, bytes 16G..16G+15.  V codes: 16-byte unit lane + 64j of the
-    // 2 KB tile.  V scale/zero: one dword (two bf16) for lanes < 32*NG/2.  K group scale/zero:
+    // 2 KB tile.  V scale/zero: one dword (two bf16) for lanes < 16*NG.  K group scale/zero:
     // lanes 0..15 the scale row, 16..31 the zero row (16 bytes each), when the tile opens a group.
-    uint4 kr[2], vr[2], kp = make_uint4(0u, 0u, 0u, 0u);
-    uint32_t vs2 = 0u, vz2 = 0u;
-    auto fetch = [&](int64_t tt0) {
-        const int nv = (int)min<int64_t>(kTile, t_hi - tt0);
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-            const int tt = min(16 * hf + n, nv - 1);
-            kr[hf] = *reinterpret_cast<const uint4*>(kc + (tt0 + tt) * (D / 2) + 16 * G);
-        }
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int u = lane + 64 * j;
-            const int row = min(u / 4, nv - 1);
-            vr[j] = *reinterpret_cast<const uint4*>(vc + (tt0 + row) * (D / 2) + 16 * (u % 4));
-        }
-        if (lane < kTile * NG / 2) {
-            const int e0 = 2 * lane;
-            const int row = min(e0 / NG, nv - 1);
-            const int64_t off = (tt0 + row) * NG + e0 % NG;
-            if (NG == 1) {
-                const int row1 = min(e0 + 1, nv - 1);
-                vs2 = (uint32_t)vsp[off] | ((uint32_t)vsp[tt0 + row1] << 16);
-                vz2 = (uint32_t)vzp[off] | ((uint32_t)vzp[tt0 + row1] << 16);
-            } else {
-                vs2 = *reinterpret_cast<const uint32_t*>(vsp + off);
-                vz2 = *reinterpret_cast<const uint32_t*>(vzp + off);
+    // Rows at or past the end of the sequence read as zero (their logits are masked).
+    struct TileRegs {
+        u32x4 k[2], v[2], kp;
+        uint32_t vs, vz;
+    };
+    const uint32_t koff = (uint32_t)(n * (D / 2) + 16 * G);
+    const uint32_t voff = (uint32_t)(16 * lane);
+    auto fetch = [&](TileRegs& r, int tt0) {
+        const uint8_t* kt = kc + (int64_t)tt0 * (D / 2);
+        const uint8_t* vt = vc + (int64_t)tt0 * (D / 2);
+        const uint16_t* st = vsp + (int64_t)tt0 * NG;
+        const uint16_t* zt = vzp + (int64_t)tt0 * NG;
+        if (tt0 + kTile <= Tq) {
+            r.k[0] = *reinterpret_cast<const u32x4*>(kt + koff);
+            r.k[1] = *reinterpret_cast<const u32x4*>(kt + koff + 16 * (D / 2));
+            r.v[0] = *reinterpret_cast<const u32x4*>(vt + voff);
+            r.v[1] = *reinterpret_cast<const u32x4*>(vt + voff + 1024);
+            if (lane < 16 * NG) {
+                if constexpr (NG == 1) {   // one bf16 per token: the (b, h) row may be only 2-byte aligned
+                    r.vs = (uint32_t)st[2 * lane] | ((uint32_t)st[2 * lane + 1] << 16);
+                    r.vz = (uint32_t)zt[2 * lane] | ((uint32_t)zt[2 * lane + 1] << 16);
+                } else {
+                    r.vs = reinterpret_cast<const uint32_t*>(st)[lane];
+                    r.vz = reinterpret_cast<const uint32_t*>(zt)[lane];
+                }
+            }
+        } else {
+            const int nmem = Tq - tt0;
+            const u32x4 z4 = u32x4{0u, 0u, 0u, 0u};
+            r.k[0] = n < nmem ? *reinterpret_cast<const u32x4*>(kt + koff) : z4;
+            r.k[1] = 16 + n < nmem ? *reinterpret_cast<const u32x4*>(kt + koff + 16 * (D / 2)) : z4;
+            r.v[0] = lane / 4 < nmem ? *reinterpret_cast<const u32x4*>(vt + voff) : z4;
+            r.v[1] = 16 + lane / 4 < nmem ? *reinterpret_cast<const u32x4*>(vt + voff + 1024) : z4;
+            r.vs = 0u;
+            r.vz = 0u;
+            if (lane < 16 * NG) {
+                const int e0 = 2 * lane;
+                if (e0 / NG < nmem) { r.vs = st[e0]; r.vz = zt[e0]; }
+                if ((e0 + 1) / NG < nmem) { r.vs |= (uint32_t)st[e0 + 1] << 16; r.vz |= (uint32_t)zt[e0 + 1] << 16; }
             }
         }
         if ((tt0 % GS == 0 || tt0 == t_lo) && lane < 32) {
-            const uint16_t* src = (lane < 16 ? kscale : kzero) + (tt0 / GS) * D + 8 * (lane % 16);
-            kp = *reinterpret_cast<const uint4*>(src);
+            const uint16_t* src = (lane < 16 ? kscale : kzero) + (int64_t)(tt0 / GS) * D + 8 * (lane % 16);
+            r.kp = *reinterpret_cast<const u32x4*>(src);
         }
     };
-    if (t_lo < t_hi) fetch(t_lo);
-
-    for (int64_t t0 = t_lo; t0 < t_hi; t0 += kTile) {
-        const int nvalid = (int)min<int64_t>(kTile, t_hi - t0);
-        const bool new_grp = (t0 % GS == 0) || (t0 == t_lo);
-        // ---- stage this tile (V codes, V params, K group params) in LDS; keep K codes ----
-        *reinterpret_cast<uint4*>(sv + 16 * lane) = vr[0];
-        *reinterpret_cast<uint4*>(sv + 16 * (lane + 64)) = vr[1];
-        if (lane < kTile * NG / 2) {
-            reinterpret_cast<uint32_t*>(s_vs[wv])[lane] = vs2;
-            reinterpret_cast<uint32_t*>(s_vz[wv])[lane] = vz2;
+    // stage a tile in this wave's LDS: K and V codes, V (scale, zero) as fp32, K group params;
+    // returns whether this lane holds a V scale at or above the current bound 2^e_s
+    auto stage = [&](const TileRegs& r, bool new_grp) -> bool {
+        *reinterpret_cast<u32x4*>(sk + 16 * lane) = r.k[0];
+        *reinterpret_cast<u32x4*>(sk + 16 * lane + 1024) = r.k[1];
+        *reinterpret_cast<u32x4*>(sv + 16 * lane) = r.v[0];
+        *reinterpret_cast<u32x4*>(sv + 16 * lane + 1024) = r.v[1];
+        bool big = false;
+        if (lane < 16 * NG) {
+            const float s0 = bf_lo(r.vs), s1 = bf_hi(r.vs);
+            *reinterpret_cast<float4*>(ssz + 4 * lane) = make_float4(s0, bf_lo(r.vz), s1, bf_hi(r.vz));
+            big = vmax2(s0, s1) >= s_lim;
         }
-        if (new_grp && lane < 32) reinterpret_cast<uint4*>(s_kp[wv])[lane] = kp;
-        const uint4 kcur0 = kr[0], kcur1 = kr[1];
-        if (t0 + kTile < t_hi) fetch(t0 + kTile);
-        __builtin_amdgcn_wave_barrier();
+        if (new_grp && lane < 32) reinterpret_cast<u32x4*>(skp)[lane] = r.kp;
+        return big;
+    };
 
+    // ---- one 32-token tile from the staged LDS copy ----
+    auto compute = [&](int t0, bool new_grp, bool big_s) {
+        const int nvalid = min(kTile, t_hi - t0);
         // ---- K group parameters -> Q'^T operand (fp16 hi + lo) and bias ----
         if (new_grp) {
-            constexpr int perm[8] = {0, 2, 4, 6, 1, 3, 5, 7};
-            const uint32_t* ksw = reinterpret_cast<const uint32_t*>(s_kp[wv]) + 16 * G;        // scale, 32 bf16
-            const uint32_t* kzw = reinterpret_cast<const uint32_t*>(s_kp[wv]) + 64 + 16 * G;   // zero, 32 bf16
-            float bpart = 0.0f;
+            float qs[PASS][8];
+            float qmax = 0.0f;
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                uint32_t w[4], wl[4];
+            for (int p = 0; p < PASS; ++p) {
+                const u32x4 sw = *reinterpret_cast<const u32x4*>(skp + 32 * G + 8 * chunk_of(p));
+                const uint32_t s4[4] = {sw.x, sw.y, sw.z, sw.w};
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int c0 = 8 * kk + perm[2 * e], c1 = 8 * kk + perm[2 * e + 1];
-                    const uint32_t sw0 = ksw[c0 / 2], sw1 = ksw[c1 / 2], zw0 = kzw[c0 / 2], zw1 = kzw[c1 / 2];
-                    const float s0 = (c0 & 1) ? bf_hi(sw0) : bf_lo(sw0), s1 = (c1 & 1) ? bf_hi(sw1) : bf_lo(sw1);
-                    const float z0 = (c0 & 1) ? bf_hi(zw0) : bf_lo(zw0), z1 = (c1 & 1) ? bf_hi(zw1) : bf_lo(zw1);
-                    const float q0 = qv[c0] * s0, q1 = qv[c1] * s1;
-                    w[e] = pack_h2(q0, q1);
-                    const half2v hq = __builtin_bit_cast(half2v, w[e]);
-                    wl[e] = pack_h2(q0 - (float)hq[0], q1 - (float)hq[1]);
-                    bpart = __builtin_fmaf(q0, z0, bpart);
-                    bpart = __builtin_fmaf(q1, z1, bpart);
+                    qs[p][2 * e] = qv[p][2 * e] * bf_lo(s4[e]);
+                    qs[p][2 * e + 1] = qv[p][2 * e + 1] * bf_hi(s4[e]);
                 }
-                bq[kk] = as_half8(w[0], w[1], w[2], w[3]);
-                bql[kk] = as_half8(wl[0], wl[1], wl[2], wl[3]);
+#pragma unroll
+                for (int j = 0; j < 8; j += 2) qmax = vmax3(qmax, __builtin_fabsf(qs[p][j]), __builtin_fabsf(qs[p][j + 1]));
             }
-            bpart += __shfl_xor(bpart, 16);
-            bpart += __shfl_xor(bpart, 32);
-            bias = bpart;
+            lscale = a.qscale;
+            if (__any(qmax >= 16384.0f)) {
+                // out of the fp16 range: scale this query's Q' by 2^-tau, tau from the largest
+                // |q * s_K| over its 128 channels (lanes that hold the same query)
+#pragma unroll
+                for (int off = NQ; off < 4 * NQ && off < 16; off *= 2) qmax = vmax2(qmax, __shfl_xor(qmax, off));
+                qmax = vmax2(qmax, xor_lane<16>(qmax));
+                qmax = vmax2(qmax, xor_lane<32>(qmax));
+                const int tau = __builtin_amdgcn_frexp_expf(qmax) - 14;
+#pragma unroll
+                for (int p = 0; p < PASS; ++p)
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) qs[p][j] = __builtin_ldexpf(qs[p][j], -tau);
+                lscale = __builtin_ldexpf(a.qscale, tau);
+            }
+            float bz = 0.0f, bsum = 0.0f;
+            uint32_t hw[PASS][4], lw[PASS][4];
+#pragma unroll
+            for (int p = 0; p < PASS; ++p) {
+                const u32x4 zw = *reinterpret_cast<const u32x4*>(skp + D + 32 * G + 8 * chunk_of(p));
+                const uint32_t z4[4] = {zw.x, zw.y, zw.z, zw.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    bz = __builtin_fmaf(qs[p][2 * e], bf_lo(z4[e]), bz);
+                    bz = __builtin_fmaf(qs[p][2 * e + 1], bf_hi(z4[e]), bz);
+                    bsum += qs[p][2 * e] + qs[p][2 * e + 1];
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float x0 = qs[p][kPerm[2 * e]], x1 = qs[p][kPerm[2 * e + 1]];
+                    hw[p][e] = pack_h2(x0, x1);
+                    const half2v hh = __builtin_bit_cast(half2v, hw[p][e]);
+                    lw[p][e] = pack_h2(x0 - (float)hh[0], x1 - (float)hh[1]);
+                }
+            }
+            float bpart = __builtin_fmaf(64.0f, bsum, bz);
+            if constexpr (PASS == 4) {
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    bq[kk] = as_half8(hw[kk][0], hw[kk][1], hw[kk][2], hw[kk][3]);
+                    bql[kk] = as_half8(lw[kk][0], lw[kk][1], lw[kk][2], lw[kk][3]);
+                }
+            } else {
+                uint32_t* qx = sm.lp.qx[wv][0];
+#pragma unroll
+                for (int p = 0; p < PASS; ++p) {
+                    *reinterpret_cast<u32x4*>(qx + lane * PASS * 8 + 8 * p) = u32x4{hw[p][0], hw[p][1], hw[p][2], hw[p][3]};
+                    *reinterpret_cast<u32x4*>(qx + lane * PASS * 8 + 8 * p + 4) = u32x4{lw[p][0], lw[p][1], lw[p][2], lw[p][3]};
+                }
+                __builtin_amdgcn_wave_barrier();
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    // chunk kk of query n % NQ was computed by lane src, pass ps
+                    const int src = 16 * G + n % NQ + (NQ == 8 ? 8 * (kk % 2) : NQ * kk);
+                    const int ps = NQ == 8 ? kk / 2 : 0;
+                    const u32x4 hi = *reinterpret_cast<const u32x4*>(qx + src * PASS * 8 + 8 * ps);
+                    const u32x4 lo = *reinterpret_cast<const u32x4*>(qx + src * PASS * 8 + 8 * ps + 4);
+                    bq[kk] = as_half8(hi.x, hi.y, hi.z, hi.w);
+                    bql[kk] = as_half8(lo.x, lo.y, lo.z, lo.w);
+                }
+            }
+            // bias: sum over the distinct chunks of this query, then over the 4 lane groups
+#pragma unroll
+            for (int off = NQ; off < 4 * NQ && off < 16; off *= 2) bpart += __shfl_xor(bpart, off);
+            bpart += xor_lane<16>(bpart);
+            bpart += xor_lane<32>(bpart);
+            c0 = __builtin_fmaf(bpart, lscale, ref);
         }
 
         // ---- scores ----
         floatx4 sc[2];
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
-            const uint4 kraw = hf ? kcur1 : kcur0;
+            const u32x4 kraw = *reinterpret_cast<const u32x4*>(sk + 1024 * hf + 16 * lane);
             const uint32_t kw[4] = {kraw.x, kraw.y, kraw.z, kraw.w};
             floatx4 c = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
-                const half8 ak = nib8(kw[kk], c64);
+                const half8 ak = nib8(kw[kk]);
                 c = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak, bq[kk], c, 0, 0, 0);
                 c = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak, bql[kk], c, 0, 0, 0);
             }
             sc[hf] = c;
         }
-        // lane (n, G): tokens 4G+i (half 0) and 16+4G+i (half 1), i = 0..3
+        // lane (n, G): tokens 4G+i (half 0) and 16+4G+i (half 1), i = 0..3; lg = logit - ref
         float lg[8];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            lg[i] = (sc[0][i] - bias) * a.qscale;
-            lg[4 + i] = (sc[1][i] - bias) * a.qscale;
+            lg[i] = __builtin_fmaf(sc[0][i], lscale, -c0);
+            lg[4 + i] = __builtin_fmaf(sc[1][i], lscale, -c0);
         }
         if (nvalid < kTile) {   // only the last tile of a range is partial
 #pragma unroll
@@ -275,40 +390,54 @@ __global__ void __launch_bounds__(kThreads) attn_mfma_kernel(const MfmaArgs a) {
                 if (16 + 4 * G + i >= nvalid) lg[4 + i] = kNegBig;
             }
         }
-        float tmax = vmax3(vmax3(lg[0], lg[1], lg[2]), vmax3(lg[3], lg[4], lg[5]), vmax2(lg[6], lg[7]));
-        tmax = vmax2(tmax, __shfl_xor(tmax, 16));
-        tmax = vmax2(tmax, __shfl_xor(tmax, 32));
-        const float m_new = vmax2(m_run, tmax);
-        if (__any(m_new != m_run)) {          // rescale only when some running max moved
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        const float lmax = vmax3(vmax3(lg[0], lg[1], lg[2]), vmax3(lg[3], lg[4], lg[5]), vmax2(lg[6], lg[7]));
+        if (__any(lmax > thr || big_s)) {
+            // move the reference: largest logit of the tile (+ margin) and largest V scale
+            float tmax = vmax2(lmax, xor_lane<16>(lmax));
+            tmax = vmax2(tmax, xor_lane<32>(tmax));
+            float sm2 = 0.0f;
+            if (lane < 16 * NG) sm2 = vmax2(ssz[4 * lane], ssz[4 * lane + 2]);
+            sm2 = vmax2(sm2, xor_lane<1>(sm2));
+            sm2 = vmax2(sm2, xor_lane<2>(sm2));
+            sm2 = vmax2(sm2, xor_lane<4>(sm2));
+            sm2 = vmax2(sm2, xor_lane<8>(sm2));
+            sm2 = vmax2(sm2, xor_lane<16>(sm2));
+            sm2 = vmax2(sm2, xor_lane<32>(sm2));
+            int e_new = max(e_s, __builtin_amdgcn_frexp_expf(sm2));   // sm2 < 2^frexp_exp
+            e_new = min(max(e_new, kEmin), kEmax);
+            const float d = vmax2(thr, tmax + kMargin) + (float)(e_new - 15);
+            const float alpha = started ? __builtin_amdgcn_exp2f(-d) : 0.0f;
             l_part *= alpha;
 #pragma unroll
             for (int nb = 0; nb < 8; ++nb) acc_o[nb] *= alpha;
 #pragma unroll
-            for (int gI = 0; gI < NG; ++gI) zterm[gI] *= alpha;
-            m_run = m_new;
+            for (int gI = 0; gI < NG; ++gI) {
+                acc_off[gI] *= alpha;
+                zsum[gI] *= alpha;
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) lg[i] -= d;
+            ref += d;
+            c0 += d;
+            e_s = e_new;
+            s_lim = __builtin_ldexpf(1.0f, e_s);
+            thr = (float)(15 - e_s);
+            started = true;
         }
         float p[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            p[i] = __builtin_amdgcn_exp2f(lg[i] - m_run);
+            p[i] = __builtin_amdgcn_exp2f(lg[i]);
             l_part += p[i];
         }
 
-        // ---- P' = p * s_V per V group (fp16), and the zero-point term ----
+        // ---- P' = fp16(p * s_V) per V group, and the zero-point term in fp32 ----
         half8 bp[NG];
         {
-            // scales / zeros of tokens 4G..4G+3 and 16+4G..16+4G+3: 4*NG contiguous bf16 each
-            uint32_t sv4[2][2 * NG], zv4[2][2 * NG];
-#pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-                const int t4 = 16 * hf + 4 * G;
-#pragma unroll
-                for (int e = 0; e < 2 * NG; ++e) {
-                    sv4[hf][e] = reinterpret_cast<const uint32_t*>(s_vs[wv] + t4 * NG)[e];
-                    zv4[hf][e] = reinterpret_cast<const uint32_t*>(s_vz[wv] + t4 * NG)[e];
-                }
-            }
+            // (scale, zero) of token 16*hf + 4G + i, group gI: float2 at (16*hf + 4G + i) * NG + gI
+            auto sz2 = [&](int hf, int x) -> float2 {
+                return reinterpret_cast<const float2*>(ssz)[(16 * hf + 4 * G) * NG + x];
+            };
 #pragma unroll
             for (int gI = 0; gI < NG; ++gI) {
                 uint32_t w[4];
@@ -316,75 +445,96 @@ __global__ void __launch_bounds__(kThreads) attn_mfma_kernel(const MfmaArgs a) {
                 for (int e = 0; e < 4; ++e) {
                     // token slots 2e, 2e+1 -> half hf = e / 2, tokens i = 2(e%2), 2(e%2)+1 of that half
                     const int hf = e / 2, i0 = 2 * (e % 2), i1 = i0 + 1;
-                    const int x0 = i0 * NG + gI, x1 = i1 * NG + gI;   // bf16 index within the 4-token run
-                    const float sa = (x0 & 1) ? bf_hi(sv4[hf][x0 / 2]) : bf_lo(sv4[hf][x0 / 2]);
-                    const float sb = (x1 & 1) ? bf_hi(sv4[hf][x1 / 2]) : bf_lo(sv4[hf][x1 / 2]);
-                    const float za = (x0 & 1) ? bf_hi(zv4[hf][x0 / 2]) : bf_lo(zv4[hf][x0 / 2]);
-                    const float zb = (x1 & 1) ? bf_hi(zv4[hf][x1 / 2]) : bf_lo(zv4[hf][x1 / 2]);
-                    w[e] = pack_h2(p[2 * e] * sa, p[2 * e + 1] * sb);
-                    const half2v hp = __builtin_bit_cast(half2v, w[e]);
-                    zterm[gI] = __builtin_fmaf((float)hp[0], za, zterm[gI]);
-                    zterm[gI] = __builtin_fmaf((float)hp[1], zb, zterm[gI]);
+                    const float2 a0 = sz2(hf, i0 * NG + gI), a1 = sz2(hf, i1 * NG + gI);
+                    const float ps0 = p[2 * e] * a0.x, ps1 = p[2 * e + 1] * a1.x;
+                    w[e] = pack_h2(ps0, ps1);
+                    zsum[gI] = __builtin_fmaf(ps0, a0.y, zsum[gI]);
+                    zsum[gI] = __builtin_fmaf(ps1, a1.y, zsum[gI]);
                 }
                 bp[gI] = as_half8(w[0], w[1], w[2], w[3]);
             }
         }
 
-        // ---- values: transpose the code tile through LDS, 8 MFMAs ----
+        // ---- values: V codes^T from the LDS tile, 8 + NG MFMAs ----
         {
             const int tok[8] = {4 * G, 4 * G + 1, 4 * G + 2, 4 * G + 3,
                                 16 + 4 * G, 16 + 4 * G + 1, 16 + 4 * G + 2, 16 + 4 * G + 3};
+            const half8 c64 = as_half8(kMagic, kMagic, kMagic, kMagic);
 #pragma unroll
             for (int gI = 0; gI < NG; ++gI) {
                 // this lane's piece of group gI: PB bytes at byte offset (GS/2)*gI + PB*n
                 const int boff = (GS / 2) * gI + PB * n;
-                const uint32_t o = (uint32_t)(boff & 3);
-                uint32_t wd[8];
-#pragma unroll
-                for (int j = 0; j < 8; ++j) wd[j] = *reinterpret_cast<const uint32_t*>(sv + tok[j] * (D / 2) + (boff & ~3));
                 // dword per token pair: the pair's pieces side by side (token a low, token b high)
                 uint32_t P[4][2];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
+                    const uint8_t* ra = sv + tok[2 * e] * (D / 2) + boff;
+                    const uint8_t* rb = sv + tok[2 * e + 1] * (D / 2) + boff;
                     if constexpr (PB == 1) {
-                        P[e][0] = __builtin_amdgcn_perm(wd[2 * e + 1], wd[2 * e], o | ((4u + o) << 8));   // [a, b]
+                        P[e][0] = (uint32_t)*ra | ((uint32_t)*rb << 16);                        // [a 0 b 0]
                     } else if constexpr (PB == 2) {
-                        P[e][0] = __builtin_amdgcn_perm(wd[2 * e + 1], wd[2 * e], o | ((o + 1u) << 8) | ((4u + o) << 16) | ((5u + o) << 24));
+                        P[e][0] = (uint32_t)*reinterpret_cast<const uint16_t*>(ra) |
+                                  ((uint32_t)*reinterpret_cast<const uint16_t*>(rb) << 16);     // [a0 a1 b0 b1]
                     } else {
-                        P[e][0] = __builtin_amdgcn_perm(wd[2 * e + 1], wd[2 * e], 0x05040100u);
-                        P[e][1] = __builtin_amdgcn_perm(wd[2 * e + 1], wd[2 * e], 0x07060302u);
+                        const uint32_t wa = *reinterpret_cast<const uint32_t*>(ra);
+                        const uint32_t wb = *reinterpret_cast<const uint32_t*>(rb);
+                        P[e][0] = __builtin_amdgcn_perm(wb, wa, 0x05040100u);                  // [a0 a1 b0 b1]
+                        P[e][1] = __builtin_amdgcn_perm(wb, wa, 0x07060302u);                  // [a2 a3 b2 b3]
                     }
                 }
-                // nibble k of both tokens -> fp16 pair: mask nibbles into bytes, pair the bytes
+                // nibble k of both tokens -> fp16(64 + code) pair: move it to bits 4..7 / 20..23
 #pragma unroll
                 for (int k = 0; k < BPG; ++k) {
                     uint32_t w[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const uint32_t src = P[e][k / 4];
-                        const uint32_t nib = (k & 1) ? ((src >> 4) & 0x0f0f0f0fu) : (src & 0x0f0f0f0fu);
-                        uint32_t sel;
-                        if constexpr (PB == 1) sel = kSelB0B1;                                // bytes [a, b]
-                        else sel = ((k % 4) / 2) ? kSelB1B3 : kSelB0B2;                      // [a0 a1 b0 b1]
-                        w[e] = sub1024(perm64(nib, c64, sel));
+                        const int kb = k % 4;   // byte kb / 2 of each token, low nibble when kb is even
+                        const uint32_t x = kb == 0 ? (src << 4) : kb == 1 ? src : kb == 2 ? (src >> 4) : (src >> 8);
+                        w[e] = nib_pair(x);
                     }
                     const int nb = gI * BPG + k;
                     acc_o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(w[0], w[1], w[2], w[3]), bp[gI],
                                                                        acc_o[nb], 0, 0, 0);
                 }
+                acc_off[gI] = __builtin_amdgcn_mfma_f32_16x16x32_f16(c64, bp[gI], acc_off[gI], 0, 0, 0);
             }
         }
+    };
+
+    // one tile: stage it, refill its register set kBuf tiles ahead, compute it
+    auto step = [&](TileRegs& r, int tt) {
+        const bool new_grp = (tt % GS == 0) || (tt == t_lo);
+        const bool big_s = stage(r, new_grp);
+        if (tt + kBuf * kTile < t_hi) fetch(r, tt + kBuf * kTile);
+        __builtin_amdgcn_wave_barrier();
+        compute(tt, new_grp, big_s);
         __builtin_amdgcn_wave_barrier();     // LDS reads done before the next tile overwrites
+    };
+    // register sets as separate objects (not an array) so nothing is ever indexed dynamically
+    TileRegs r0, r1, r2;
+    if (t_lo < t_hi) fetch(r0, t_lo);
+    if (t_lo + kTile < t_hi) fetch(r1, t_lo + kTile);
+    if constexpr (kBuf == 3) {
+        if (t_lo + 2 * kTile < t_hi) fetch(r2, t_lo + 2 * kTile);
+    }
+    for (int t0 = t_lo; t0 < t_hi; t0 += kBuf * kTile) {
+        step(r0, t0);
+        if (t0 + kTile < t_hi) step(r1, t0 + kTile);
+        if constexpr (kBuf == 3) {
+            if (t0 + 2 * kTile < t_hi) step(r2, t0 + 2 * kTile);
+        }
     }
 
-    // ---------------- finish the wave: sums over the 4 lane groups, zero-point term ----------------
-    l_part += __shfl_xor(l_part, 16);
-    l_part += __shfl_xor(l_part, 32);
+    // ---------------- finish the wave: sums over the 4 lane groups, offset and zero terms ----------------
+    l_part += xor_lane<16>(l_part);
+    l_part += xor_lane<32>(l_part);
 #pragma unroll
     for (int gI = 0; gI < NG; ++gI) {
-        zterm[gI] += __shfl_xor(zterm[gI], 16);
-        zterm[gI] += __shfl_xor(zterm[gI], 32);
+        zsum[gI] += xor_lane<16>(zsum[gI]);
+        zsum[gI] += xor_lane<32>(zsum[gI]);
     }
+    __syncthreads();   // every wave is done with the loop buffers before the merge reuses them
     // acc_o[nb][i] is channel row m = 4G + i of block nb, query n
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb) {
@@ -393,23 +543,26 @@ __global__ void __launch_bounds__(kThreads) attn_mfma_kernel(const MfmaArgs a) {
         for (int i = 0; i < 4; ++i) {
             const int m = 4 * G + i;
             const int c = GS * gI + BPG * m + k;
-            s_o[wv][n][c] = acc_o[nb][i] - zterm[gI];
+            sm.mg.o[wv][n][c] = acc_o[nb][i] - acc_off[gI][i] - zsum[gI];
         }
     }
-    if (G == 0) { s_m[wv][n] = m_run; s_l[wv][n] = l_part; }
+    if (G == 0) {
+        sm.mg.m[wv][n] = started ? ref : kNegBig;
+        sm.mg.l[wv][n] = l_part;
+    }
     __syncthreads();
     // merge the 4 waves and write (m, l, acc[D]) for each real query
     for (int e = tid; e < NQ * D; e += kThreads) {
         const int qn = e / D, c = e % D;
-        float M = s_m[0][qn];
+        float M = sm.mg.m[0][qn];
 #pragma unroll
-        for (int w = 1; w < kWaves; ++w) M = vmax2(M, s_m[w][qn]);
+        for (int w = 1; w < kWaves; ++w) M = vmax2(M, sm.mg.m[w][qn]);
         float L = 0.0f, A = 0.0f;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
-            const float f = exp2f(s_m[w][qn] - M);
-            L = __builtin_fmaf(s_l[w][qn], f, L);
-            A = __builtin_fmaf(s_o[w][qn][c], f, A);
+            const float f = exp2f(sm.mg.m[w][qn] - M);
+            L = __builtin_fmaf(sm.mg.l[w][qn], f, L);
+            A = __builtin_fmaf(sm.mg.o[w][qn][c], f, A);
         }
         float* dst = a.ws + ((b * a.Hq + h * NQ + qn) * a.nslot + split) * (D + 2);
         if (c == 0) { dst[0] = M; dst[1] = L; }
@@ -440,8 +593,9 @@ void launch_attn_mfma(const kvq_int4_cache* c, const void* q, int64_t Hq, float 
     a.v_codes = c->v_codes; a.v_scale = c->v_scale; a.v_zero = c->v_zero;
     a.q = static_cast<const uint16_t*>(q);
     a.ws = ws;
-    a.B = c->B; a.H = c->H; a.Tq = c->T - c->R; a.nKg = cdiv(a.Tq, c->g); a.Hq = Hq;
-    a.split_len = split_len;
+    a.B = c->B; a.H = c->H; a.Hq = Hq;
+    a.Tq = (int)(c->T - c->R); a.nKg = (int)cdiv(a.Tq, c->g);
+    a.split_len = (int)split_len;
     a.nsplit = nsplit;
     a.nslot = nslot;
     a.qscale = qscale;

@@ -7,7 +7,8 @@ out of the arithmetic tolerance).
 
 Cases: the full-size configuration (batch 16, 32 query heads, 8 KV heads, d=128, context
 32768 with the 128-token residual, sampled rows), small ragged caches across every
-(d, g, heads-per-KV-head), residual 0 / all, one token, and peaked / flat softmaxes."""
+(d, g, heads-per-KV-head), residual 0 / all, one token, peaked / flat softmaxes, and
+groups whose scales and zero points sit far outside the usual range."""
 import math
 
 import numpy as np
@@ -43,7 +44,13 @@ def run_attn(B, T, H, Hq, d, g, R, seed, sm_scale=None, q_scale=1.0, k_gain=1.0)
     q = synth.decode_query(B, Hq, d, seed=seed + 1)
     if q_scale != 1.0:
         q = (q.float() * q_scale).to(torch.bfloat16)
-    sm = 1.0 if sm_scale is None else sm_scale
+    return check_attn(K, V, q, g, R, 1.0 if sm_scale is None else sm_scale)
+
+
+def check_attn(K, V, q, g, R, sm):
+    """Quantize bf16 K, V [B][T][H][d], attend with q [B][Hq][d] on the GPU, compare with the oracle."""
+    B, T, H, d = K.shape
+    Hq = q.shape[1]
     cache = kvq.group_quant_int4(K.to(DEV), V.to(DEV), g=g, R=R)
     out32 = kvq.decode_attn_int4(cache, q.to(DEV), sm, out_dtype=torch.float32)
     out16 = kvq.decode_attn_int4(cache, q.to(DEV), sm, out_dtype=torch.bfloat16)
@@ -76,6 +83,33 @@ def test_softmax_regimes():
     run_attn(B=2, T=999, H=2, Hq=8, d=128, g=64, R=128, seed=1, q_scale=0.0)
     run_attn(B=2, T=999, H=2, Hq=8, d=128, g=64, R=128, seed=2, q_scale=8.0)
     run_attn(B=2, T=999, H=2, Hq=8, d=128, g=64, R=128, seed=3, sm_scale=1 / math.sqrt(128), q_scale=math.sqrt(128))
+
+
+@pytest.mark.parametrize("g", [32, 64, 128])
+def test_scale_extremes(g):
+    """Groups whose scales leave the range where fp16 products are safe: V scaled down to
+    ~1e-5 and up to ~1e5 per quantization step, K scaled so q * s_K passes 65504 (with a small
+    sm_scale so the softmax stays soft), constant K and V groups (range floored at 1e-8: tiny
+    scale, huge zero point) and groups offset far from zero (large negative zero points)."""
+    B, T, H, Hq, d, R = 2, 700, 2, 8, 128, 64
+    K, V, _ = synth.kv_layer(B, T, H, d, seed=40 + g, n_outlier=0)
+    q = synth.decode_query(B, Hq, d, seed=41 + g)
+    Kf, Vf = K.float(), V.float()
+    cases = {
+        "v_tiny": (Kf, Vf * 1e-4, 1.0),
+        "v_huge": (Kf, Vf * 1e6, 1.0),
+        "k_huge": (Kf * 1e6, Vf, 1e-6),
+        "offset": (Kf + 100.0, Vf - 300.0, 0.05),
+    }
+    kc, vc = Kf.clone(), Vf.clone()
+    kc[:, g:2 * g, :, 0:48] = 1.5              # constant K channels over a whole token group
+    vc[:, 5:400:7, :, 0:g] = -2.25             # constant V groups on many tokens
+    c1 = g if 2 * g <= d else 0
+    vc[0, :, 0, c1:c1 + g] = 0.75              # one head: a V group constant on every token
+    cases["constant"] = (kc, vc, 1.0)
+    for name, (k, v, sm) in cases.items():
+        say("attn extreme", dict(case=name, g=g))
+        check_attn(k.to(torch.bfloat16), v.to(torch.bfloat16), q, g, R, sm)
 
 
 def test_config4_full_size_sampled_rows():
