@@ -51,6 +51,9 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
 constexpr int kTile = 32;           // tokens per wave iteration
+#ifndef KVQ_ATTN_BUF_OVERRIDE
+#define KVQ_ATTN_BUF_OVERRIDE 0
+#endif
 constexpr int D = 128;
 constexpr float kNegBig = -3.0e38f;
 constexpr float kMargin = 2.0f;     // head-room put above the largest logit when the reference moves
@@ -112,15 +115,15 @@ __device__ __forceinline__ float xor_lane(float x) {
     }
 }
 
-template <int GS, int NQ>
+template <int GS, int NQ, int KBUF>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 attn_mfma_kernel(const MfmaArgs a) {
     constexpr int NG = D / GS;          // V groups per token
     constexpr int BPG = GS / 16;        // MFMA channel blocks per V group
     constexpr int PB = GS / 32;         // bytes of one V group piece per lane per token
     constexpr int PASS = NQ >= 16 ? 4 : (NQ == 8 ? 2 : 1);   // Q' chunks each lane computes
-    // tiles whose loads are in flight per wave: three where the registers allow two waves per SIMD
-    constexpr int kBuf = (GS == 32 || NQ == 16) ? 2 : 3;
+    // KBUF: tiles whose loads are in flight per wave
+    constexpr int kBuf = KBUF;
     static_assert(NQ <= 16, "at most 16 query heads per KV head");
 
     // per-wave V code tile (32 tokens x 64 bytes), V (scale, zero) pairs in fp32, K group
@@ -130,7 +133,7 @@ attn_mfma_kernel(const MfmaArgs a) {
         uint8_t v[kWaves][kTile * D / 2];
         float sz[kWaves][kTile * NG * 2];
         uint16_t kp[kWaves][2 * D];
-        uint32_t qx[kWaves][64][PASS < 4 ? PASS * 8 : 1];
+        uint32_t qx[kWaves][64][PASS * 8];
     };
     struct Merge {
         float m[kWaves][16], l[kWaves][16];
@@ -192,7 +195,6 @@ attn_mfma_kernel(const MfmaArgs a) {
     float s_lim = 0.0f;          // 2^e_s (0 before the first tile)
     bool started = false;
 
-    half8 bq[4], bql[4];         // Q'^T operand of the current K group: fp16 hi and lo parts
     float lscale = a.qscale, c0 = 0.0f;   // logit - ref = S' * lscale - c0
 
     const uint8_t* kc = a.k_codes + bh * (int64_t)Tq * (D / 2);
@@ -205,6 +207,7 @@ attn_mfma_kernel(const MfmaArgs a) {
     uint8_t* sv = sm.lp.v[wv];
     float* ssz = sm.lp.sz[wv];
     uint16_t* skp = sm.lp.kp[wv];
+    uint32_t* sqx = sm.lp.qx[wv][0];   // Q'^T chunks of the current K group (fp16 hi, lo) per lane
 
     // ---- tile loads: kBuf tiles in flight per wave, in registers until staged ----
     // K codes: token 16*hf + n, bytes 16G..16G+15.  V codes: 16-byte unit lane + 64j of the
@@ -278,21 +281,25 @@ attn_mfma_kernel(const MfmaArgs a) {
         const int nvalid = min(kTile, t_hi - t0);
         // ---- K group parameters -> Q'^T operand (fp16 hi + lo) and bias ----
         if (new_grp) {
-            float qs[PASS][8];
+            // pass 1: largest |q * s_K| of this lane's chunks (the fp16 range check)
+            auto chunk_scaled = [&](int p, float (&qs)[8]) {
+                const u32x4 sw = *reinterpret_cast<const u32x4*>(skp + 32 * G + 8 * chunk_of(p));
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    qs[2 * e] = qv[p][2 * e] * bf_lo(sw[e]);
+                    qs[2 * e + 1] = qv[p][2 * e + 1] * bf_hi(sw[e]);
+                }
+            };
             float qmax = 0.0f;
 #pragma unroll
             for (int p = 0; p < PASS; ++p) {
-                const u32x4 sw = *reinterpret_cast<const u32x4*>(skp + 32 * G + 8 * chunk_of(p));
-                const uint32_t s4[4] = {sw.x, sw.y, sw.z, sw.w};
+                float qs[8];
+                chunk_scaled(p, qs);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    qs[p][2 * e] = qv[p][2 * e] * bf_lo(s4[e]);
-                    qs[p][2 * e + 1] = qv[p][2 * e + 1] * bf_hi(s4[e]);
-                }
-#pragma unroll
-                for (int j = 0; j < 8; j += 2) qmax = vmax3(qmax, __builtin_fabsf(qs[p][j]), __builtin_fabsf(qs[p][j + 1]));
+                for (int j = 0; j < 8; j += 2) qmax = vmax3(qmax, __builtin_fabsf(qs[j]), __builtin_fabsf(qs[j + 1]));
             }
             lscale = a.qscale;
+            int tau = 0;
             if (__any(qmax >= 16384.0f)) {
                 // out of the fp16 range: scale this query's Q' by 2^-tau, tau from the largest
                 // |q * s_K| over its 128 channels (lanes that hold the same query)
@@ -300,59 +307,39 @@ attn_mfma_kernel(const MfmaArgs a) {
                 for (int off = NQ; off < 4 * NQ && off < 16; off *= 2) qmax = vmax2(qmax, __shfl_xor(qmax, off));
                 qmax = vmax2(qmax, xor_lane<16>(qmax));
                 qmax = vmax2(qmax, xor_lane<32>(qmax));
-                const int tau = __builtin_amdgcn_frexp_expf(qmax) - 14;
-#pragma unroll
-                for (int p = 0; p < PASS; ++p)
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) qs[p][j] = __builtin_ldexpf(qs[p][j], -tau);
+                tau = __builtin_amdgcn_frexp_expf(qmax) - 14;
                 lscale = __builtin_ldexpf(a.qscale, tau);
             }
+            // pass 2: per chunk, Q' = q * s_K (* 2^-tau) as fp16 hi + lo, published to LDS for the
+            // score MFMAs, and the bias partial sum_c Q'_c (z_c + 64)
             float bz = 0.0f, bsum = 0.0f;
-            uint32_t hw[PASS][4], lw[PASS][4];
 #pragma unroll
             for (int p = 0; p < PASS; ++p) {
+                float qs[8];
+                chunk_scaled(p, qs);
+                if (tau != 0) {
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) qs[j] = __builtin_ldexpf(qs[j], -tau);
+                }
                 const u32x4 zw = *reinterpret_cast<const u32x4*>(skp + D + 32 * G + 8 * chunk_of(p));
-                const uint32_t z4[4] = {zw.x, zw.y, zw.z, zw.w};
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    bz = __builtin_fmaf(qs[p][2 * e], bf_lo(z4[e]), bz);
-                    bz = __builtin_fmaf(qs[p][2 * e + 1], bf_hi(z4[e]), bz);
-                    bsum += qs[p][2 * e] + qs[p][2 * e + 1];
+                    bz = __builtin_fmaf(qs[2 * e], bf_lo(zw[e]), bz);
+                    bz = __builtin_fmaf(qs[2 * e + 1], bf_hi(zw[e]), bz);
+                    bsum += qs[2 * e] + qs[2 * e + 1];
                 }
+                uint32_t hw[4], lw[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const float x0 = qs[p][kPerm[2 * e]], x1 = qs[p][kPerm[2 * e + 1]];
-                    hw[p][e] = pack_h2(x0, x1);
-                    const half2v hh = __builtin_bit_cast(half2v, hw[p][e]);
-                    lw[p][e] = pack_h2(x0 - (float)hh[0], x1 - (float)hh[1]);
+                    const float x0 = qs[kPerm[2 * e]], x1 = qs[kPerm[2 * e + 1]];
+                    hw[e] = pack_h2(x0, x1);
+                    const half2v hh = __builtin_bit_cast(half2v, hw[e]);
+                    lw[e] = pack_h2(x0 - (float)hh[0], x1 - (float)hh[1]);
                 }
+                *reinterpret_cast<u32x4*>(sqx + lane * PASS * 8 + 8 * p) = u32x4{hw[0], hw[1], hw[2], hw[3]};
+                *reinterpret_cast<u32x4*>(sqx + lane * PASS * 8 + 8 * p + 4) = u32x4{lw[0], lw[1], lw[2], lw[3]};
             }
             float bpart = __builtin_fmaf(64.0f, bsum, bz);
-            if constexpr (PASS == 4) {
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk) {
-                    bq[kk] = as_half8(hw[kk][0], hw[kk][1], hw[kk][2], hw[kk][3]);
-                    bql[kk] = as_half8(lw[kk][0], lw[kk][1], lw[kk][2], lw[kk][3]);
-                }
-            } else {
-                uint32_t* qx = sm.lp.qx[wv][0];
-#pragma unroll
-                for (int p = 0; p < PASS; ++p) {
-                    *reinterpret_cast<u32x4*>(qx + lane * PASS * 8 + 8 * p) = u32x4{hw[p][0], hw[p][1], hw[p][2], hw[p][3]};
-                    *reinterpret_cast<u32x4*>(qx + lane * PASS * 8 + 8 * p + 4) = u32x4{lw[p][0], lw[p][1], lw[p][2], lw[p][3]};
-                }
-                __builtin_amdgcn_wave_barrier();
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk) {
-                    // chunk kk of query n % NQ was computed by lane src, pass ps
-                    const int src = 16 * G + n % NQ + (NQ == 8 ? 8 * (kk % 2) : NQ * kk);
-                    const int ps = NQ == 8 ? kk / 2 : 0;
-                    const u32x4 hi = *reinterpret_cast<const u32x4*>(qx + src * PASS * 8 + 8 * ps);
-                    const u32x4 lo = *reinterpret_cast<const u32x4*>(qx + src * PASS * 8 + 8 * ps + 4);
-                    bq[kk] = as_half8(hi.x, hi.y, hi.z, hi.w);
-                    bql[kk] = as_half8(lo.x, lo.y, lo.z, lo.w);
-                }
-            }
             // bias: sum over the distinct chunks of this query, then over the 4 lane groups
 #pragma unroll
             for (int off = NQ; off < 4 * NQ && off < 16; off *= 2) bpart += __shfl_xor(bpart, off);
@@ -361,20 +348,24 @@ attn_mfma_kernel(const MfmaArgs a) {
             c0 = __builtin_fmaf(bpart, lscale, ref);
         }
 
-        // ---- scores ----
-        floatx4 sc[2];
+        // ---- scores: chunk kk of Q' for query n % NQ was computed by lane qsrc(kk), pass qpass(kk) ----
+        __builtin_amdgcn_wave_barrier();
+        floatx4 sc[2] = {floatx4{0.0f, 0.0f, 0.0f, 0.0f}, floatx4{0.0f, 0.0f, 0.0f, 0.0f}};
+        const u32x4 kraw0 = *reinterpret_cast<const u32x4*>(sk + 16 * lane);
+        const u32x4 kraw1 = *reinterpret_cast<const u32x4*>(sk + 1024 + 16 * lane);
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-            const u32x4 kraw = *reinterpret_cast<const u32x4*>(sk + 1024 * hf + 16 * lane);
-            const uint32_t kw[4] = {kraw.x, kraw.y, kraw.z, kraw.w};
-            floatx4 c = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int kk = 0; kk < 4; ++kk) {
+            const int src = PASS == 4 ? lane : 16 * G + n % NQ + (NQ == 8 ? 8 * (kk % 2) : NQ * kk);
+            const int ps = PASS == 4 ? kk : (NQ == 8 ? kk / 2 : 0);
+            const u32x4 hi = *reinterpret_cast<const u32x4*>(sqx + src * PASS * 8 + 8 * ps);
+            const u32x4 lo = *reinterpret_cast<const u32x4*>(sqx + src * PASS * 8 + 8 * ps + 4);
+            const half8 bh = __builtin_bit_cast(half8, hi), bl = __builtin_bit_cast(half8, lo);
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const half8 ak = nib8(kw[kk]);
-                c = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak, bq[kk], c, 0, 0, 0);
-                c = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak, bql[kk], c, 0, 0, 0);
+            for (int hf = 0; hf < 2; ++hf) {
+                const half8 ak = nib8((hf ? kraw1 : kraw0)[kk]);
+                sc[hf] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak, bh, sc[hf], 0, 0, 0);
+                sc[hf] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak, bl, sc[hf], 0, 0, 0);
             }
-            sc[hf] = c;
         }
         // lane (n, G): tokens 4G+i (half 0) and 16+4G+i (half 1), i = 0..3; lg = logit - ref
         float lg[8];
@@ -512,17 +503,24 @@ attn_mfma_kernel(const MfmaArgs a) {
         __builtin_amdgcn_wave_barrier();     // LDS reads done before the next tile overwrites
     };
     // register sets as separate objects (not an array) so nothing is ever indexed dynamically
-    TileRegs r0, r1, r2;
+    static_assert(kBuf >= 2 && kBuf <= 4, "two to four register sets");
+    TileRegs r0, r1, r2, r3;
     if (t_lo < t_hi) fetch(r0, t_lo);
     if (t_lo + kTile < t_hi) fetch(r1, t_lo + kTile);
-    if constexpr (kBuf == 3) {
+    if constexpr (kBuf >= 3) {
         if (t_lo + 2 * kTile < t_hi) fetch(r2, t_lo + 2 * kTile);
+    }
+    if constexpr (kBuf >= 4) {
+        if (t_lo + 3 * kTile < t_hi) fetch(r3, t_lo + 3 * kTile);
     }
     for (int t0 = t_lo; t0 < t_hi; t0 += kBuf * kTile) {
         step(r0, t0);
         if (t0 + kTile < t_hi) step(r1, t0 + kTile);
-        if constexpr (kBuf == 3) {
+        if constexpr (kBuf >= 3) {
             if (t0 + 2 * kTile < t_hi) step(r2, t0 + 2 * kTile);
+        }
+        if constexpr (kBuf >= 4) {
+            if (t0 + 3 * kTile < t_hi) step(r3, t0 + 3 * kTile);
         }
     }
 
@@ -570,15 +568,20 @@ attn_mfma_kernel(const MfmaArgs a) {
     }
 }
 
+// tiles in flight per wave for each variant: as many as fit two waves per SIMD without spilling
+constexpr int buf_for(int gs, int nq) {
+    return KVQ_ATTN_BUF_OVERRIDE > 0 ? KVQ_ATTN_BUF_OVERRIDE : (nq == 16 || (gs == 32 && nq == 8)) ? 3 : 4;
+}
+
 template <int GS>
 void launch_nq(const MfmaArgs& a, int nq, hipStream_t st) {
     const dim3 grid((unsigned)(a.B * a.H * a.nsplit)), blk(kThreads);
     switch (nq) {
-        case 1: hipLaunchKernelGGL((attn_mfma_kernel<GS, 1>), grid, blk, 0, st, a); break;
-        case 2: hipLaunchKernelGGL((attn_mfma_kernel<GS, 2>), grid, blk, 0, st, a); break;
-        case 4: hipLaunchKernelGGL((attn_mfma_kernel<GS, 4>), grid, blk, 0, st, a); break;
-        case 8: hipLaunchKernelGGL((attn_mfma_kernel<GS, 8>), grid, blk, 0, st, a); break;
-        default: hipLaunchKernelGGL((attn_mfma_kernel<GS, 16>), grid, blk, 0, st, a); break;
+        case 1: hipLaunchKernelGGL((attn_mfma_kernel<GS, 1, buf_for(GS, 1)>), grid, blk, 0, st, a); break;
+        case 2: hipLaunchKernelGGL((attn_mfma_kernel<GS, 2, buf_for(GS, 2)>), grid, blk, 0, st, a); break;
+        case 4: hipLaunchKernelGGL((attn_mfma_kernel<GS, 4, buf_for(GS, 4)>), grid, blk, 0, st, a); break;
+        case 8: hipLaunchKernelGGL((attn_mfma_kernel<GS, 8, buf_for(GS, 8)>), grid, blk, 0, st, a); break;
+        default: hipLaunchKernelGGL((attn_mfma_kernel<GS, 16, buf_for(GS, 16)>), grid, blk, 0, st, a); break;
     }
 }
 
