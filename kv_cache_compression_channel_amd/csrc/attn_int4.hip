@@ -25,6 +25,7 @@ namespace kvq {
 int check_cache_shape(const kvq_int4_cache* c, const char* name);
 void launch_attn_mfma(const kvq_int4_cache* c, const void* q, int64_t Hq, float qscale, float* ws, int nsplit,
                       int64_t split_len, int nslot, hipStream_t st);
+int res_splits(int64_t R);
 
 namespace {
 
@@ -240,38 +241,71 @@ __global__ void __launch_bounds__(kThreads) attn_split_kernel(const AttnArgs a) 
     }
 }
 
+// Log-sum-exp merge of the split partials (m, l, acc[D]) of one (b, hq) row per wave: lanes
+// read the slots' maxima and sums in parallel, then each lane sums its D/64 channels over the
+// slots with every slot's weight taken from the lane that holds it.
 template <int D, int OT>
-__global__ void __launch_bounds__(D) attn_combine_kernel(const float* __restrict__ ws, int nsplit,
-                                                         void* __restrict__ out) {
-    const int64_t row = blockIdx.x;   // b * Hq + hq
-    const int c = threadIdx.x;
-    const float* base = ws + row * nsplit * (D + 2);
+__global__ void __launch_bounds__(256) attn_combine_kernel(const float* __restrict__ ws, int nslot, int64_t rows,
+                                                          void* __restrict__ out) {
+    constexpr int CPL = D / 64;     // channels per lane
+    const int lane = threadIdx.x % 64;
+    const int64_t row = (int64_t)blockIdx.x * 4 + threadIdx.x / 64;   // b * Hq + hq
+    if (row >= rows) return;
+    const float* base = ws + row * nslot * (D + 2);
     float M = kNegBig;
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, base[s * (D + 2)]);
-    float L = 0.0f, A = 0.0f;
-    for (int s = 0; s < nsplit; ++s) {
-        const float f = exp2f(base[s * (D + 2)] - M);
-        L += base[s * (D + 2) + 1] * f;
-        A += base[s * (D + 2) + 2 + c] * f;
+    for (int s = lane; s < nslot; s += 64) M = fmaxf(M, base[(int64_t)s * (D + 2)]);
+#pragma unroll
+    for (int off = 32; off >= 1; off /= 2) M = fmaxf(M, __shfl_xor(M, off));
+    float L = 0.0f, A[CPL];
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) A[j] = 0.0f;
+    for (int s0 = 0; s0 < nslot; s0 += 64) {
+        const int s = s0 + lane;
+        float f = 0.0f;
+        if (s < nslot) {
+            const float* sp = base + (int64_t)s * (D + 2);
+            f = exp2f(sp[0] - M);
+            L = __builtin_fmaf(sp[1], f, L);
+        }
+        const int ns = min(64, nslot - s0);
+        for (int k = 0; k < ns; ++k) {
+            const float fk = __shfl(f, k);
+            const float* sp = base + (int64_t)(s0 + k) * (D + 2) + 2;
+#pragma unroll
+            for (int j = 0; j < CPL; ++j) A[j] = __builtin_fmaf(sp[lane + 64 * j], fk, A[j]);
+        }
     }
-    const float o = A / L;
-    if constexpr (OT == KVQ_FP32)
-        static_cast<float*>(out)[row * D + c] = o;
-    else
-        static_cast<uint16_t*>(out)[row * D + c] = f_to_bf(o);
+#pragma unroll
+    for (int off = 32; off >= 1; off /= 2) L += __shfl_xor(L, off);
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+        const int c = lane + 64 * j;
+        const float o = A[j] / L;
+        if constexpr (OT == KVQ_FP32)
+            static_cast<float*>(out)[row * D + c] = o;
+        else
+            static_cast<uint16_t*>(out)[row * D + c] = f_to_bf(o);
+    }
 }
 
-// How the token axis is cut: the INT4 tokens [0, Tq) go to the matrix-core kernel when
-// d = 128 (splits on multiples of 128 tokens), everything else to the VALU kernel (splits on
-// multiples of max(g, 64) tokens); each split writes one partial slot per (b, hq).
+// How the token axis is cut.  d = 128: the INT4 tokens [0, Tq) go to the matrix-core kernel
+// (splits on multiples of 512 tokens, so every wave's range starts on a 128-token boundary) and
+// the residual to blocks of the same launch (64 tokens each).  Otherwise everything goes to the
+// VALU kernel (splits on multiples of max(g, 64) tokens).  Each split writes one partial slot
+// per (b, hq); the combine merges them.
 struct SplitPlan {
     bool mfma;
     int nsplit_q;           // matrix-core splits over [0, Tq)
     int64_t len_q;
-    int nsplit_v;           // VALU splits over [v_lo, T)
-    int64_t len_v, v_lo;
+    int nres;               // residual splits inside the matrix-core launch
+    int nsplit_v;           // VALU splits over [0, T)
+    int64_t len_v;
     int nslot;
 };
+
+#ifndef KVQ_ATTN_BLOCKS
+#define KVQ_ATTN_BLOCKS 1024
+#endif
 
 int64_t split_len_for(int64_t n, int64_t want, int64_t unit) {
     int64_t len = cdiv(cdiv(n, want), unit) * unit;
@@ -281,22 +315,18 @@ int64_t split_len_for(int64_t n, int64_t want, int64_t unit) {
 SplitPlan plan_splits(int64_t B, int64_t H, int64_t T, int64_t R, int64_t d, int64_t g) {
     SplitPlan p{};
     const int64_t Tq = T - R;
-    const int64_t want = cdiv(2048, B * H);    // aim for >= 2048 blocks
+    const int64_t want = cdiv(KVQ_ATTN_BLOCKS, B * H);    // aim for about KVQ_ATTN_BLOCKS blocks
     p.mfma = (d == 128) && Tq > 0;
     if (p.mfma) {
-        p.len_q = split_len_for(Tq, want, 128);
+        p.len_q = split_len_for(Tq, want, 512);
         p.nsplit_q = (int)cdiv(Tq, p.len_q);
-        p.v_lo = Tq;
-    } else {
-        p.v_lo = 0;
+        p.nres = res_splits(R);
+        p.nslot = p.nsplit_q + p.nres;
+        return p;
     }
-    const int64_t nv = T - p.v_lo;
-    if (nv > 0) {
-        p.len_v = split_len_for(nv, p.mfma ? 1 : want, g > 64 ? g : 64);
-        p.len_v = p.mfma ? (p.len_v < 256 ? p.len_v : 256) : p.len_v;
-        p.nsplit_v = (int)cdiv(nv, p.len_v);
-    }
-    p.nslot = p.nsplit_q + p.nsplit_v;
+    p.len_v = split_len_for(T, want, g > 64 ? g : 64);
+    p.nsplit_v = (int)cdiv(T, p.len_v);
+    p.nslot = p.nsplit_v;
     return p;
 }
 
@@ -308,12 +338,12 @@ void launch_attn(const AttnArgs& a, hipStream_t st) {
 
 template <int D>
 void launch_combine(const AttnArgs& a, hipStream_t st) {
+    const int64_t rows = a.B * a.Hq;
+    const dim3 grid((unsigned)cdiv(rows, 4)), blk(256);
     if (a.ot == KVQ_FP32)
-        hipLaunchKernelGGL((attn_combine_kernel<D, KVQ_FP32>), dim3((unsigned)(a.B * a.Hq)), dim3(D), 0, st, a.ws,
-                           a.nslot, a.out);
+        hipLaunchKernelGGL((attn_combine_kernel<D, KVQ_FP32>), grid, blk, 0, st, a.ws, a.nslot, rows, a.out);
     else
-        hipLaunchKernelGGL((attn_combine_kernel<D, KVQ_BF16>), dim3((unsigned)(a.B * a.Hq)), dim3(D), 0, st, a.ws,
-                           a.nslot, a.out);
+        hipLaunchKernelGGL((attn_combine_kernel<D, KVQ_BF16>), grid, blk, 0, st, a.ws, a.nslot, rows, a.out);
 }
 
 template <int D, int GS>
@@ -373,7 +403,8 @@ int kvq_decode_attn_int4(const kvq_int4_cache* c, const void* q, int64_t Hq, flo
     KVQ_REQUIRE_ALIGNED(out, "out");
     KVQ_REQUIRE_ALIGNED(ws, "ws");
     const kvq::SplitPlan p = kvq::plan_splits(c->B, c->H, c->T, c->R, c->d, c->g);
-    KVQ_REQUIRE(c->B * c->H * p.nslot < ((int64_t)1 << 31), "kvq_decode_attn_int4: grid too large");
+    KVQ_REQUIRE(c->B * c->H * p.nslot < ((int64_t)1 << 31) && c->B * Hq * p.nslot < ((int64_t)1 << 31),
+                "kvq_decode_attn_int4: grid too large");
     kvq::AttnArgs a;
     a.k_codes = c->k_codes; a.k_scale = c->k_scale; a.k_zero = c->k_zero;
     a.v_codes = c->v_codes; a.v_scale = c->v_scale; a.v_zero = c->v_zero;
@@ -388,14 +419,14 @@ int kvq_decode_attn_int4(const kvq_int4_cache* c, const void* q, int64_t Hq, flo
     a.nslot = p.nslot;
     a.qscale = sm_scale * 1.4426950408889634f;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if (p.mfma)
+    if (p.mfma) {
         kvq::launch_attn_mfma(c, q, Hq, a.qscale, a.ws, p.nsplit_q, p.len_q, p.nslot, st);
-    if (p.nsplit_v > 0) {
-        a.range_lo = p.v_lo;
+    } else {
+        a.range_lo = 0;
         a.range_hi = c->T;
         a.split_len = p.len_v;
         a.nsplit = p.nsplit_v;
-        a.slot_off = p.nsplit_q;
+        a.slot_off = 0;
         kvq::dispatch(a, c->d, c->g, (int)nq, st);
     }
     kvq::dispatch_combine(a, c->d, st);

@@ -71,13 +71,17 @@ struct MfmaArgs {
     const uint8_t* v_codes;
     const uint16_t* v_scale;
     const uint16_t* v_zero;
+    const uint16_t* k_res;
+    const uint16_t* v_res;
     const uint16_t* q;
     float* ws;
     int64_t B, H, Hq;
     int Tq, nKg;
+    int R;               // residual (bf16) tokens per (b, h)
+    int nres;            // residual splits per (b, h), kResTile tokens each; their blocks come first
     int split_len;       // tokens per split (multiple of 4 * kTile)
     int nsplit;          // INT4 splits per (b, h)
-    int nslot;           // partial slots per (b, hq) in ws (INT4 splits + residual splits)
+    int nslot;           // partial slots per (b, hq) in ws: INT4 splits, then residual splits
     float qscale;        // sm_scale * log2(e)
 };
 
@@ -115,6 +119,79 @@ __device__ __forceinline__ float xor_lane(float x) {
     }
 }
 
+// ---- the bf16 residual window: one block per (b, h, split of up to kResTile tokens) ----
+// Plain fp32 arithmetic from an LDS copy of the rows: logits q . k (q pre-scaled by
+// sm_scale log2 e), base-2 softmax over the split, p-weighted sum of the V rows.  Writes the
+// split's partial (max logit, sum of p, sum of p v) like every other split.
+constexpr int kResTile = 64;
+constexpr int kResPad = D + 8;      // row stride of the LDS copies (16-byte reads spread over the banks)
+struct ResLds {
+    uint16_t k[kResTile][kResPad];
+    uint16_t v[kResTile][kResPad];
+    float q[16][D];
+    float p[kResTile][17];
+    float m[16], l[16];
+};
+
+template <int NQ>
+__device__ void residual_block(const MfmaArgs& a, ResLds& sr, int rb) {
+    const int tid = threadIdx.x, lane = tid % 64, wv = tid / 64;
+    const int64_t bh = rb / a.nres;
+    const int split = rb % a.nres;
+    const int64_t b = bh / a.H, h = bh % a.H;
+    const int r_lo = split * kResTile;
+    const int nt = min(kResTile, a.R - r_lo);
+    const uint16_t* kr = a.k_res + (bh * a.R + r_lo) * D;
+    const uint16_t* vr = a.v_res + (bh * a.R + r_lo) * D;
+    for (int i = tid; i < nt * (D / 8); i += kThreads) {
+        const int t = i / (D / 8), c8 = 8 * (i % (D / 8));
+        *reinterpret_cast<u32x4*>(&sr.k[t][c8]) = *reinterpret_cast<const u32x4*>(kr + t * D + c8);
+        *reinterpret_cast<u32x4*>(&sr.v[t][c8]) = *reinterpret_cast<const u32x4*>(vr + t * D + c8);
+    }
+    const uint16_t* qp = a.q + (b * a.Hq + h * NQ) * D;
+    for (int e = tid; e < NQ * D; e += kThreads) sr.q[e / D][e % D] = bf_to_f(qp[e]) * a.qscale;
+    __syncthreads();
+    // logits: token fastest across lanes, so a wave reads one query row (broadcast)
+    for (int e = tid; e < nt * NQ; e += kThreads) {
+        const int t = e % nt, n = e / nt;
+        float acc = 0.0f;
+#pragma unroll 4
+        for (int c8 = 0; c8 < D; c8 += 8) {
+            const u32x4 kw = *reinterpret_cast<const u32x4*>(&sr.k[t][c8]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                acc = __builtin_fmaf(sr.q[n][c8 + 2 * j], bf_lo(kw[j]), acc);
+                acc = __builtin_fmaf(sr.q[n][c8 + 2 * j + 1], bf_hi(kw[j]), acc);
+            }
+        }
+        sr.p[t][n] = acc;
+    }
+    __syncthreads();
+    // softmax over the split: one wave per query, lanes over tokens
+    for (int n = wv; n < NQ; n += kWaves) {
+        const float x = lane < nt ? sr.p[lane][n] : kNegBig;
+        float m = x;
+#pragma unroll
+        for (int off = 32; off >= 1; off /= 2) m = vmax2(m, __shfl_xor(m, off));
+        const float pv = lane < nt ? exp2f(x - m) : 0.0f;
+        float l = pv;
+#pragma unroll
+        for (int off = 32; off >= 1; off /= 2) l += __shfl_xor(l, off);
+        if (lane < nt) sr.p[lane][n] = pv;
+        if (lane == 0) { sr.m[n] = m; sr.l[n] = l; }
+    }
+    __syncthreads();
+    // partial output: channel fastest across lanes
+    for (int e = tid; e < NQ * D; e += kThreads) {
+        const int n = e / D, c = e % D;
+        float acc = 0.0f;
+        for (int t = 0; t < nt; ++t) acc = __builtin_fmaf(sr.p[t][n], bf_to_f(sr.v[t][c]), acc);
+        float* dst = a.ws + ((b * a.Hq + h * NQ + n) * a.nslot + (a.nslot - a.nres) + split) * (D + 2);
+        if (c == 0) { dst[0] = sr.m[n]; dst[1] = sr.l[n]; }
+        dst[2 + c] = acc;
+    }
+}
+
 template <int GS, int NQ, int KBUF>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 attn_mfma_kernel(const MfmaArgs a) {
@@ -142,13 +219,21 @@ attn_mfma_kernel(const MfmaArgs a) {
     __shared__ __attribute__((aligned(16))) union {
         Loop lp;
         Merge mg;
+        ResLds rs;
     } sm;
+
+    const int nres_blocks = (int)(a.B * a.H) * a.nres;
+    if ((int)blockIdx.x < nres_blocks) {      // uniform per block
+        residual_block<NQ>(a, sm.rs, (int)blockIdx.x);
+        return;
+    }
+    const int blk = (int)blockIdx.x - nres_blocks;
 
     const int tid = threadIdx.x, lane = tid % 64;
     const int wv = __builtin_amdgcn_readfirstlane(tid / 64);
     const int n = lane % 16, G = lane / 16;
-    const int64_t bh = blockIdx.x / a.nsplit;
-    const int split = (int)(blockIdx.x % a.nsplit);
+    const int64_t bh = blk / a.nsplit;
+    const int split = blk % a.nsplit;
     const int64_t b = bh / a.H, h = bh % a.H;
     const int Tq = a.Tq;
     // this wave's contiguous token range inside the split
@@ -211,53 +296,44 @@ attn_mfma_kernel(const MfmaArgs a) {
 
     // ---- tile loads: kBuf tiles in flight per wave, in registers until staged ----
     // K codes: token 16*hf + n, bytes 16G..16G+15.  V codes: 16-byte unit lane + 64j of the
-    // 2 KB tile.  V scale/zero: one dword (two bf16) for lanes < 16*NG.  K group scale/zero:
-    // lanes 0..15 the scale row, 16..31 the zero row (16 bytes each), when the tile opens a group.
-    // Rows at or past the end of the sequence read as zero (their logits are masked).
+    // 2 KB tile.  V scale/zero: elements 2l, 2l+1 of the tile's [token][group] arrays for
+    // l = lane % (16 NG).  K group scale/zero: the scale row (lanes with G even) or the zero
+    // row (G odd) of the group holding the tile's first token.
+    // Every lane issues the same loads for every tile, whatever the position: rows past the
+    // end of the cache are clamped to its last row (their logits are masked, so their values
+    // never count).  With no load behind a branch, the wait before staging a tile leaves the
+    // loads of the kBuf - 1 tiles behind it in flight.
     struct TileRegs {
         u32x4 k[2], v[2], kp;
         uint32_t vs, vz;
     };
-    const uint32_t koff = (uint32_t)(n * (D / 2) + 16 * G);
-    const uint32_t voff = (uint32_t)(16 * lane);
+    const int last_row = Tq - 1;
+    const int sl = lane % (16 * NG);
+    const uint16_t* kpsrc = (G % 2 ? kzero : kscale) + 8 * n;
+    // tt0 is at most the last row; rows of the tile past the last row are clamped to it.  Lane
+    // offsets are unsigned 32-bit so the loads take the scalar-base + vector-offset form.
     auto fetch = [&](TileRegs& r, int tt0) {
+        const int lim = last_row - tt0;
         const uint8_t* kt = kc + (int64_t)tt0 * (D / 2);
         const uint8_t* vt = vc + (int64_t)tt0 * (D / 2);
-        const uint16_t* st = vsp + (int64_t)tt0 * NG;
-        const uint16_t* zt = vzp + (int64_t)tt0 * NG;
-        if (tt0 + kTile <= Tq) {
-            r.k[0] = *reinterpret_cast<const u32x4*>(kt + koff);
-            r.k[1] = *reinterpret_cast<const u32x4*>(kt + koff + 16 * (D / 2));
-            r.v[0] = *reinterpret_cast<const u32x4*>(vt + voff);
-            r.v[1] = *reinterpret_cast<const u32x4*>(vt + voff + 1024);
-            if (lane < 16 * NG) {
-                if constexpr (NG == 1) {   // one bf16 per token: the (b, h) row may be only 2-byte aligned
-                    r.vs = (uint32_t)st[2 * lane] | ((uint32_t)st[2 * lane + 1] << 16);
-                    r.vz = (uint32_t)zt[2 * lane] | ((uint32_t)zt[2 * lane + 1] << 16);
-                } else {
-                    r.vs = reinterpret_cast<const uint32_t*>(st)[lane];
-                    r.vz = reinterpret_cast<const uint32_t*>(zt)[lane];
-                }
-            }
-        } else {
-            const int nmem = Tq - tt0;
-            const u32x4 z4 = u32x4{0u, 0u, 0u, 0u};
-            r.k[0] = n < nmem ? *reinterpret_cast<const u32x4*>(kt + koff) : z4;
-            r.k[1] = 16 + n < nmem ? *reinterpret_cast<const u32x4*>(kt + koff + 16 * (D / 2)) : z4;
-            r.v[0] = lane / 4 < nmem ? *reinterpret_cast<const u32x4*>(vt + voff) : z4;
-            r.v[1] = 16 + lane / 4 < nmem ? *reinterpret_cast<const u32x4*>(vt + voff + 1024) : z4;
-            r.vs = 0u;
-            r.vz = 0u;
-            if (lane < 16 * NG) {
-                const int e0 = 2 * lane;
-                if (e0 / NG < nmem) { r.vs = st[e0]; r.vz = zt[e0]; }
-                if ((e0 + 1) / NG < nmem) { r.vs |= (uint32_t)st[e0 + 1] << 16; r.vz |= (uint32_t)zt[e0 + 1] << 16; }
-            }
+        r.k[0] = *reinterpret_cast<const u32x4*>(kt + (uint32_t)(min(n, lim) * (D / 2) + 16 * G));
+        r.k[1] = *reinterpret_cast<const u32x4*>(kt + (uint32_t)(min(16 + n, lim) * (D / 2) + 16 * G));
+        r.v[0] = *reinterpret_cast<const u32x4*>(vt + (uint32_t)(min(lane / 4, lim) * (D / 2) + 16 * (lane % 4)));
+        r.v[1] = *reinterpret_cast<const u32x4*>(vt + (uint32_t)(min(16 + lane / 4, lim) * (D / 2) + 16 * (lane % 4)));
+        const uint8_t* st = reinterpret_cast<const uint8_t*>(vsp + (int64_t)tt0 * NG);
+        const uint8_t* zt = reinterpret_cast<const uint8_t*>(vzp + (int64_t)tt0 * NG);
+        if constexpr (NG == 1) {   // one bf16 per token: the (b, h) row may be only 2-byte aligned
+            const uint32_t s0 = (uint32_t)min(2 * sl, lim) * 2, s1 = (uint32_t)min(2 * sl + 1, lim) * 2;
+            r.vs = (uint32_t)*reinterpret_cast<const uint16_t*>(st + s0) |
+                   ((uint32_t)*reinterpret_cast<const uint16_t*>(st + s1) << 16);
+            r.vz = (uint32_t)*reinterpret_cast<const uint16_t*>(zt + s0) |
+                   ((uint32_t)*reinterpret_cast<const uint16_t*>(zt + s1) << 16);
+        } else {                   // NG even: both elements belong to one token, dword aligned
+            const uint32_t e = (uint32_t)(min(2 * sl / NG, lim) * NG + (2 * sl) % NG) * 2;
+            r.vs = *reinterpret_cast<const uint32_t*>(st + e);
+            r.vz = *reinterpret_cast<const uint32_t*>(zt + e);
         }
-        if ((tt0 % GS == 0 || tt0 == t_lo) && lane < 32) {
-            const uint16_t* src = (lane < 16 ? kscale : kzero) + (int64_t)(tt0 / GS) * D + 8 * (lane % 16);
-            r.kp = *reinterpret_cast<const u32x4*>(src);
-        }
+        r.kp = *reinterpret_cast<const u32x4*>(kpsrc + (int64_t)(tt0 / GS) * D);
     };
     // stage a tile in this wave's LDS: K and V codes, V (scale, zero) as fp32, K group params;
     // returns whether this lane holds a V scale at or above the current bound 2^e_s
@@ -493,34 +569,41 @@ attn_mfma_kernel(const MfmaArgs a) {
         }
     };
 
-    // one tile: stage it, refill its register set kBuf tiles ahead, compute it
-    auto step = [&](TileRegs& r, int tt) {
-        const bool new_grp = (tt % GS == 0) || (tt == t_lo);
-        const bool big_s = stage(r, new_grp);
-        if (tt + kBuf * kTile < t_hi) fetch(r, tt + kBuf * kTile);
-        __builtin_amdgcn_wave_barrier();
-        compute(tt, new_grp, big_s);
-        __builtin_amdgcn_wave_barrier();     // LDS reads done before the next tile overwrites
-    };
-    // register sets as separate objects (not an array) so nothing is ever indexed dynamically
-    static_assert(kBuf >= 2 && kBuf <= 4, "two to four register sets");
-    TileRegs r0, r1, r2, r3;
-    if (t_lo < t_hi) fetch(r0, t_lo);
-    if (t_lo + kTile < t_hi) fetch(r1, t_lo + kTile);
-    if constexpr (kBuf >= 3) {
-        if (t_lo + 2 * kTile < t_hi) fetch(r2, t_lo + 2 * kTile);
-    }
-    if constexpr (kBuf >= 4) {
-        if (t_lo + 3 * kTile < t_hi) fetch(r3, t_lo + 3 * kTile);
-    }
-    for (int t0 = t_lo; t0 < t_hi; t0 += kBuf * kTile) {
-        step(r0, t0);
-        if (t0 + kTile < t_hi) step(r1, t0 + kTile);
-        if constexpr (kBuf >= 3) {
-            if (t0 + 2 * kTile < t_hi) step(r2, t0 + 2 * kTile);
-        }
-        if constexpr (kBuf >= 4) {
-            if (t0 + 3 * kTile < t_hi) step(r3, t0 + 3 * kTile);
+    // one tile: stage it, refill its register set kBuf tiles ahead, compute it.  Tile i of the
+    // wave starts at t_lo + 32 i; the loop runs whole rounds of kBuf tiles, and a tile at or past
+    // t_hi (at most kBuf - 1 at the end of a range) is fully masked.  Loads past the wave's last
+    // tile re-read that tile, which is still in cache.
+    if (t_lo < t_hi) {
+        const int ntile = (t_hi - t_lo + kTile - 1) / kTile;
+        const int t_last = t_lo + (ntile - 1) * kTile;
+        auto tile_at = [&](int i) { return min(t_lo + i * kTile, t_last); };
+        auto step = [&](TileRegs& r, int i) {
+            const int tt = t_lo + i * kTile;
+            const bool new_grp = (tt % GS == 0) || (i == 0);
+            const bool big_s = stage(r, new_grp);
+            fetch(r, tile_at(i + kBuf));
+            __builtin_amdgcn_wave_barrier();
+            compute(tt, new_grp, big_s);
+            __builtin_amdgcn_wave_barrier();     // LDS reads done before the next tile overwrites
+            __builtin_amdgcn_sched_barrier(0);   // keep tiles apart in the schedule (register pressure)
+        };
+        // register sets as separate objects (not an array) so nothing is ever indexed dynamically
+        static_assert(kBuf >= 2 && kBuf <= 4, "two to four register sets");
+        TileRegs r0, r1, r2, r3;
+        // issue order r0, r1, ... (the schedule must not reorder them: the first wait counts on it)
+        fetch(r0, tile_at(0));
+        __builtin_amdgcn_sched_barrier(0);
+        fetch(r1, tile_at(1));
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (kBuf >= 3) fetch(r2, tile_at(2));
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (kBuf >= 4) fetch(r3, tile_at(3));
+        __builtin_amdgcn_sched_barrier(0);
+        for (int i = 0; i < ntile; i += kBuf) {
+            step(r0, i);
+            step(r1, i + 1);
+            if constexpr (kBuf >= 3) step(r2, i + 2);
+            if constexpr (kBuf >= 4) step(r3, i + 3);
         }
     }
 
@@ -568,14 +651,13 @@ attn_mfma_kernel(const MfmaArgs a) {
     }
 }
 
-// tiles in flight per wave for each variant: as many as fit two waves per SIMD without spilling
-constexpr int buf_for(int gs, int nq) {
-    return KVQ_ATTN_BUF_OVERRIDE > 0 ? KVQ_ATTN_BUF_OVERRIDE : (nq == 16 || (gs == 32 && nq == 8)) ? 3 : 4;
-}
+// tiles in flight per wave: two (measured faster than three or four at two waves per SIMD,
+// and the only depth at which every variant fits the register file)
+constexpr int buf_for(int, int) { return KVQ_ATTN_BUF_OVERRIDE > 0 ? KVQ_ATTN_BUF_OVERRIDE : 2; }
 
 template <int GS>
 void launch_nq(const MfmaArgs& a, int nq, hipStream_t st) {
-    const dim3 grid((unsigned)(a.B * a.H * a.nsplit)), blk(kThreads);
+    const dim3 grid((unsigned)(a.B * a.H * (a.nsplit + a.nres))), blk(kThreads);
     switch (nq) {
         case 1: hipLaunchKernelGGL((attn_mfma_kernel<GS, 1, buf_for(GS, 1)>), grid, blk, 0, st, a); break;
         case 2: hipLaunchKernelGGL((attn_mfma_kernel<GS, 2, buf_for(GS, 2)>), grid, blk, 0, st, a); break;
@@ -587,13 +669,19 @@ void launch_nq(const MfmaArgs& a, int nq, hipStream_t st) {
 
 }  // namespace
 
-// Launch the INT4 token range [0, Tq) on the matrix cores (d = 128).  Partials go to ws
-// slots 0 .. nsplit-1 of each (b, hq); the caller owns slot counts and the combine.
+int res_splits(int64_t R) { return (int)cdiv(R, kResTile); }
+
+// Launch the INT4 token range [0, Tq) on the matrix cores (d = 128) and the bf16 residual
+// [Tq, T) in blocks of the same grid.  Partials go to ws slots 0 .. nsplit-1 (INT4) and
+// nsplit .. nsplit + res_splits(R) - 1 (residual) of each (b, hq); nslot is their sum.
 void launch_attn_mfma(const kvq_int4_cache* c, const void* q, int64_t Hq, float qscale, float* ws, int nsplit,
                       int64_t split_len, int nslot, hipStream_t st) {
     MfmaArgs a;
     a.k_codes = c->k_codes; a.k_scale = c->k_scale; a.k_zero = c->k_zero;
     a.v_codes = c->v_codes; a.v_scale = c->v_scale; a.v_zero = c->v_zero;
+    a.k_res = c->k_res; a.v_res = c->v_res;
+    a.R = (int)c->R;
+    a.nres = res_splits(c->R);
     a.q = static_cast<const uint16_t*>(q);
     a.ws = ws;
     a.B = c->B; a.H = c->H; a.Hq = Hq;
