@@ -268,7 +268,23 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(const float* __restri
             L = __builtin_fmaf(sp[1], f, L);
         }
         const int ns = min(64, nslot - s0);
-        for (int k = 0; k < ns; ++k) {
+        int k = 0;
+        for (; k + 4 <= ns; k += 4) {   // four slots' loads in flight
+            float x[4][CPL];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float* sp = base + (int64_t)(s0 + k + u) * (D + 2) + 2;
+#pragma unroll
+                for (int j = 0; j < CPL; ++j) x[u][j] = sp[lane + 64 * j];
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float fk = __shfl(f, k + u);
+#pragma unroll
+                for (int j = 0; j < CPL; ++j) A[j] = __builtin_fmaf(x[u][j], fk, A[j]);
+            }
+        }
+        for (; k < ns; ++k) {
             const float fk = __shfl(f, k);
             const float* sp = base + (int64_t)(s0 + k) * (D + 2) + 2;
 #pragma unroll

@@ -51,9 +51,6 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
 constexpr int kTile = 32;           // tokens per wave iteration
-#ifndef KVQ_ATTN_BUF_OVERRIDE
-#define KVQ_ATTN_BUF_OVERRIDE 0
-#endif
 constexpr int D = 128;
 constexpr float kNegBig = -3.0e38f;
 constexpr float kMargin = 2.0f;     // head-room put above the largest logit when the reference moves
@@ -129,7 +126,7 @@ struct ResLds {
     uint16_t k[kResTile][kResPad];
     uint16_t v[kResTile][kResPad];
     float q[16][D];
-    float p[kResTile][17];
+    float p[16][kResTile];      // logits, then probabilities, per query
     float m[16], l[16];
 };
 
@@ -152,24 +149,35 @@ __device__ void residual_block(const MfmaArgs& a, ResLds& sr, int rb) {
     for (int e = tid; e < NQ * D; e += kThreads) sr.q[e / D][e % D] = bf_to_f(qp[e]) * a.qscale;
     __syncthreads();
     // logits: token fastest across lanes, so a wave reads one query row (broadcast)
+#pragma unroll 1
     for (int e = tid; e < nt * NQ; e += kThreads) {
         const int t = e % nt, n = e / nt;
         float acc = 0.0f;
-#pragma unroll 4
-        for (int c8 = 0; c8 < D; c8 += 8) {
-            const u32x4 kw = *reinterpret_cast<const u32x4*>(&sr.k[t][c8]);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                acc = __builtin_fmaf(sr.q[n][c8 + 2 * j], bf_lo(kw[j]), acc);
-                acc = __builtin_fmaf(sr.q[n][c8 + 2 * j + 1], bf_hi(kw[j]), acc);
-            }
+        for (int j0 = 0; j0 < D / 8; j0 += 4) {   // a quarter of the row's loads in flight at once
+          u32x4 kw[D / 8];
+#pragma unroll
+          for (int j = j0; j < j0 + 4; ++j) kw[j] = *reinterpret_cast<const u32x4*>(&sr.k[t][8 * j]);
+#pragma unroll
+          for (int j = j0; j < j0 + 4; ++j) {
+            const float4 q0 = *reinterpret_cast<const float4*>(&sr.q[n][8 * j]);
+            const float4 q1 = *reinterpret_cast<const float4*>(&sr.q[n][8 * j + 4]);
+            acc = __builtin_fmaf(q0.x, bf_lo(kw[j][0]), acc);
+            acc = __builtin_fmaf(q0.y, bf_hi(kw[j][0]), acc);
+            acc = __builtin_fmaf(q0.z, bf_lo(kw[j][1]), acc);
+            acc = __builtin_fmaf(q0.w, bf_hi(kw[j][1]), acc);
+            acc = __builtin_fmaf(q1.x, bf_lo(kw[j][2]), acc);
+            acc = __builtin_fmaf(q1.y, bf_hi(kw[j][2]), acc);
+            acc = __builtin_fmaf(q1.z, bf_lo(kw[j][3]), acc);
+            acc = __builtin_fmaf(q1.w, bf_hi(kw[j][3]), acc);
+          }
         }
-        sr.p[t][n] = acc;
+        sr.p[n][t] = acc;
     }
     __syncthreads();
     // softmax over the split: one wave per query, lanes over tokens
     for (int n = wv; n < NQ; n += kWaves) {
-        const float x = lane < nt ? sr.p[lane][n] : kNegBig;
+        const float x = lane < nt ? sr.p[n][lane] : kNegBig;
         float m = x;
 #pragma unroll
         for (int off = 32; off >= 1; off /= 2) m = vmax2(m, __shfl_xor(m, off));
@@ -177,30 +185,45 @@ __device__ void residual_block(const MfmaArgs& a, ResLds& sr, int rb) {
         float l = pv;
 #pragma unroll
         for (int off = 32; off >= 1; off /= 2) l += __shfl_xor(l, off);
-        if (lane < nt) sr.p[lane][n] = pv;
+        sr.p[n][lane] = pv;
         if (lane == 0) { sr.m[n] = m; sr.l[n] = l; }
     }
     __syncthreads();
-    // partial output: channel fastest across lanes
-    for (int e = tid; e < NQ * D; e += kThreads) {
-        const int n = e / D, c = e % D;
-        float acc = 0.0f;
-        for (int t = 0; t < nt; ++t) acc = __builtin_fmaf(sr.p[t][n], bf_to_f(sr.v[t][c]), acc);
+    // partial output: channel pairs fastest across lanes, tokens in groups of 4
+#pragma unroll 1
+    for (int e = tid; e < NQ * (D / 2); e += kThreads) {
+        const int n = e / (D / 2), c = 2 * (e % (D / 2));
+        float a0 = 0.0f, a1 = 0.0f;
+        int t = 0;
+        for (; t + 4 <= nt; t += 4) {
+            const float4 pw = *reinterpret_cast<const float4*>(&sr.p[n][t]);
+            const uint32_t v0 = *reinterpret_cast<const uint32_t*>(&sr.v[t][c]);
+            const uint32_t v1 = *reinterpret_cast<const uint32_t*>(&sr.v[t + 1][c]);
+            const uint32_t v2 = *reinterpret_cast<const uint32_t*>(&sr.v[t + 2][c]);
+            const uint32_t v3 = *reinterpret_cast<const uint32_t*>(&sr.v[t + 3][c]);
+            a0 = __builtin_fmaf(pw.x, bf_lo(v0), a0); a1 = __builtin_fmaf(pw.x, bf_hi(v0), a1);
+            a0 = __builtin_fmaf(pw.y, bf_lo(v1), a0); a1 = __builtin_fmaf(pw.y, bf_hi(v1), a1);
+            a0 = __builtin_fmaf(pw.z, bf_lo(v2), a0); a1 = __builtin_fmaf(pw.z, bf_hi(v2), a1);
+            a0 = __builtin_fmaf(pw.w, bf_lo(v3), a0); a1 = __builtin_fmaf(pw.w, bf_hi(v3), a1);
+        }
+        for (; t < nt; ++t) {
+            const uint32_t v0 = *reinterpret_cast<const uint32_t*>(&sr.v[t][c]);
+            a0 = __builtin_fmaf(sr.p[n][t], bf_lo(v0), a0);
+            a1 = __builtin_fmaf(sr.p[n][t], bf_hi(v0), a1);
+        }
         float* dst = a.ws + ((b * a.Hq + h * NQ + n) * a.nslot + (a.nslot - a.nres) + split) * (D + 2);
         if (c == 0) { dst[0] = sr.m[n]; dst[1] = sr.l[n]; }
-        dst[2 + c] = acc;
+        *reinterpret_cast<float2*>(dst + 2 + c) = make_float2(a0, a1);
     }
 }
 
-template <int GS, int NQ, int KBUF>
+template <int GS, int NQ>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 attn_mfma_kernel(const MfmaArgs a) {
     constexpr int NG = D / GS;          // V groups per token
     constexpr int BPG = GS / 16;        // MFMA channel blocks per V group
     constexpr int PB = GS / 32;         // bytes of one V group piece per lane per token
     constexpr int PASS = NQ >= 16 ? 4 : (NQ == 8 ? 2 : 1);   // Q' chunks each lane computes
-    // KBUF: tiles whose loads are in flight per wave
-    constexpr int kBuf = KBUF;
     static_assert(NQ <= 16, "at most 16 query heads per KV head");
 
     // per-wave V code tile (32 tokens x 64 bytes), V (scale, zero) pairs in fp32, K group
@@ -208,8 +231,8 @@ attn_mfma_kernel(const MfmaArgs a) {
     struct Loop {
         uint8_t k[kWaves][kTile * D / 2];
         uint8_t v[kWaves][kTile * D / 2];
-        float sz[kWaves][kTile * NG * 2];
-        uint16_t kp[kWaves][2 * D];
+        float sz[kWaves][2 * kTile * NG * 2];     // (scale, zero) of a tile pair
+        uint16_t kp[kWaves][(GS == 32 ? 4 : 2) * D];   // K group scale and zero rows of a tile pair
         uint32_t qx[kWaves][64][PASS * 8];
     };
     struct Merge {
@@ -294,25 +317,30 @@ attn_mfma_kernel(const MfmaArgs a) {
     uint16_t* skp = sm.lp.kp[wv];
     uint32_t* sqx = sm.lp.qx[wv][0];   // Q'^T chunks of the current K group (fp16 hi, lo) per lane
 
-    // ---- tile loads: kBuf tiles in flight per wave, in registers until staged ----
-    // K codes: token 16*hf + n, bytes 16G..16G+15.  V codes: 16-byte unit lane + 64j of the
-    // 2 KB tile.  V scale/zero: elements 2l, 2l+1 of the tile's [token][group] arrays for
-    // l = lane % (16 NG).  K group scale/zero: the scale row (lanes with G even) or the zero
-    // row (G odd) of the group holding the tile's first token.
+    // ---- tile loads: two tiles in flight per wave, in registers until staged ----
+    // Tiles go in pairs (the wave's range starts on a 128-token boundary, so a pair never
+    // straddles a K group of 64 or 128 tokens).  Every tile: K codes, token 16*hf + n, bytes
+    // 16G..16G+15; V codes, 16-byte unit lane + 64j of the 2 KB tile.  The even tile of a pair
+    // also brings the pair's side data in one access per array: the V (scale, zero) elements of
+    // token lane of the pair, and the K group scale and zero rows (both groups of the pair when
+    // g = 32: lane group G holds row G % 2 of the pair's group G / 2).
     // Every lane issues the same loads for every tile, whatever the position: rows past the
     // end of the cache are clamped to its last row (their logits are masked, so their values
     // never count).  With no load behind a branch, the wait before staging a tile leaves the
-    // loads of the kBuf - 1 tiles behind it in flight.
-    struct TileRegs {
-        u32x4 k[2], v[2], kp;
-        uint32_t vs, vz;
+    // loads of the tile behind it in flight.
+    constexpr int SW = NG >= 2 ? NG / 2 : 1;   // dwords of V scale (and of zero) per lane per pair
+    struct CodeRegs {
+        u32x4 k[2], v[2];
+    };
+    struct SideRegs {
+        u32x4 kp;
+        uint32_t vs[SW], vz[SW];
     };
     const int last_row = Tq - 1;
-    const int sl = lane % (16 * NG);
     const uint16_t* kpsrc = (G % 2 ? kzero : kscale) + 8 * n;
     // tt0 is at most the last row; rows of the tile past the last row are clamped to it.  Lane
     // offsets are unsigned 32-bit so the loads take the scalar-base + vector-offset form.
-    auto fetch = [&](TileRegs& r, int tt0) {
+    auto fetch_codes = [&](CodeRegs& r, int tt0) {
         const int lim = last_row - tt0;
         const uint8_t* kt = kc + (int64_t)tt0 * (D / 2);
         const uint8_t* vt = vc + (int64_t)tt0 * (D / 2);
@@ -320,46 +348,63 @@ attn_mfma_kernel(const MfmaArgs a) {
         r.k[1] = *reinterpret_cast<const u32x4*>(kt + (uint32_t)(min(16 + n, lim) * (D / 2) + 16 * G));
         r.v[0] = *reinterpret_cast<const u32x4*>(vt + (uint32_t)(min(lane / 4, lim) * (D / 2) + 16 * (lane % 4)));
         r.v[1] = *reinterpret_cast<const u32x4*>(vt + (uint32_t)(min(16 + lane / 4, lim) * (D / 2) + 16 * (lane % 4)));
+    };
+    auto fetch_side = [&](SideRegs& r, int tt0) {
+        const int lim = last_row - tt0;
         const uint8_t* st = reinterpret_cast<const uint8_t*>(vsp + (int64_t)tt0 * NG);
         const uint8_t* zt = reinterpret_cast<const uint8_t*>(vzp + (int64_t)tt0 * NG);
+        const uint32_t e = (uint32_t)min(lane, lim) * (NG * 2);   // byte offset of token lane's elements
         if constexpr (NG == 1) {   // one bf16 per token: the (b, h) row may be only 2-byte aligned
-            const uint32_t s0 = (uint32_t)min(2 * sl, lim) * 2, s1 = (uint32_t)min(2 * sl + 1, lim) * 2;
-            r.vs = (uint32_t)*reinterpret_cast<const uint16_t*>(st + s0) |
-                   ((uint32_t)*reinterpret_cast<const uint16_t*>(st + s1) << 16);
-            r.vz = (uint32_t)*reinterpret_cast<const uint16_t*>(zt + s0) |
-                   ((uint32_t)*reinterpret_cast<const uint16_t*>(zt + s1) << 16);
-        } else {                   // NG even: both elements belong to one token, dword aligned
-            const uint32_t e = (uint32_t)(min(2 * sl / NG, lim) * NG + (2 * sl) % NG) * 2;
-            r.vs = *reinterpret_cast<const uint32_t*>(st + e);
-            r.vz = *reinterpret_cast<const uint32_t*>(zt + e);
+            r.vs[0] = *reinterpret_cast<const uint16_t*>(st + e);
+            r.vz[0] = *reinterpret_cast<const uint16_t*>(zt + e);
+        } else if constexpr (NG == 2) {
+            r.vs[0] = *reinterpret_cast<const uint32_t*>(st + e);
+            r.vz[0] = *reinterpret_cast<const uint32_t*>(zt + e);
+        } else {
+            const uint2 a2 = *reinterpret_cast<const uint2*>(st + e);
+            const uint2 b2 = *reinterpret_cast<const uint2*>(zt + e);
+            r.vs[0] = a2.x; r.vs[1] = a2.y;
+            r.vz[0] = b2.x; r.vz[1] = b2.y;
         }
-        r.kp = *reinterpret_cast<const u32x4*>(kpsrc + (int64_t)(tt0 / GS) * D);
+        const int gt = GS == 32 ? min(tt0 + kTile * (G / 2), last_row) : tt0;
+        r.kp = *reinterpret_cast<const u32x4*>(kpsrc + (int64_t)(gt / GS) * D);
     };
-    // stage a tile in this wave's LDS: K and V codes, V (scale, zero) as fp32, K group params;
-    // returns whether this lane holds a V scale at or above the current bound 2^e_s
-    auto stage = [&](const TileRegs& r, bool new_grp) -> bool {
+    // stage a tile in this wave's LDS (the even tile of a pair also stages the side data: V
+    // (scale, zero) as fp32 pairs, K group rows); returns whether this lane holds a V scale at or
+    // above the current bound 2^e_s
+    auto stage_codes = [&](const CodeRegs& r) {
         *reinterpret_cast<u32x4*>(sk + 16 * lane) = r.k[0];
         *reinterpret_cast<u32x4*>(sk + 16 * lane + 1024) = r.k[1];
         *reinterpret_cast<u32x4*>(sv + 16 * lane) = r.v[0];
         *reinterpret_cast<u32x4*>(sv + 16 * lane + 1024) = r.v[1];
-        bool big = false;
-        if (lane < 16 * NG) {
-            const float s0 = bf_lo(r.vs), s1 = bf_hi(r.vs);
-            *reinterpret_cast<float4*>(ssz + 4 * lane) = make_float4(s0, bf_lo(r.vz), s1, bf_hi(r.vz));
-            big = vmax2(s0, s1) >= s_lim;
+    };
+    auto stage_side = [&](const SideRegs& r, bool new_grp) -> bool {
+        float smax;
+        if constexpr (NG == 1) {
+            smax = bf_lo(r.vs[0]);
+            reinterpret_cast<float2*>(ssz)[lane] = make_float2(smax, bf_lo(r.vz[0]));
+        } else {
+#pragma unroll
+            for (int w = 0; w < SW; ++w) {
+                const float s0 = bf_lo(r.vs[w]), s1 = bf_hi(r.vs[w]);
+                reinterpret_cast<float4*>(ssz)[lane * SW + w] = make_float4(s0, bf_lo(r.vz[w]), s1, bf_hi(r.vz[w]));
+                smax = w == 0 ? vmax2(s0, s1) : vmax3(smax, s0, s1);
+            }
         }
-        if (new_grp && lane < 32) reinterpret_cast<u32x4*>(skp)[lane] = r.kp;
-        return big;
+        if (GS == 32 || (new_grp && lane < 32)) reinterpret_cast<u32x4*>(skp)[lane] = r.kp;
+        return smax >= s_lim;
     };
 
     // ---- one 32-token tile from the staged LDS copy ----
-    auto compute = [&](int t0, bool new_grp, bool big_s) {
+    auto compute = [&](int t0, bool new_grp, bool big_s, int par) {
+        const float* tsz = ssz + par * (kTile * NG * 2);            // this tile's (scale, zero) pairs
+        const uint16_t* tkp = skp + (GS == 32 ? par * 2 * D : 0);   // this tile's K group rows
         const int nvalid = min(kTile, t_hi - t0);
         // ---- K group parameters -> Q'^T operand (fp16 hi + lo) and bias ----
         if (new_grp) {
             // pass 1: largest |q * s_K| of this lane's chunks (the fp16 range check)
             auto chunk_scaled = [&](int p, float (&qs)[8]) {
-                const u32x4 sw = *reinterpret_cast<const u32x4*>(skp + 32 * G + 8 * chunk_of(p));
+                const u32x4 sw = *reinterpret_cast<const u32x4*>(tkp + 32 * G + 8 * chunk_of(p));
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     qs[2 * e] = qv[p][2 * e] * bf_lo(sw[e]);
@@ -397,7 +442,7 @@ attn_mfma_kernel(const MfmaArgs a) {
 #pragma unroll
                     for (int j = 0; j < 8; ++j) qs[j] = __builtin_ldexpf(qs[j], -tau);
                 }
-                const u32x4 zw = *reinterpret_cast<const u32x4*>(skp + D + 32 * G + 8 * chunk_of(p));
+                const u32x4 zw = *reinterpret_cast<const u32x4*>(tkp + D + 32 * G + 8 * chunk_of(p));
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     bz = __builtin_fmaf(qs[2 * e], bf_lo(zw[e]), bz);
@@ -462,8 +507,10 @@ attn_mfma_kernel(const MfmaArgs a) {
             // move the reference: largest logit of the tile (+ margin) and largest V scale
             float tmax = vmax2(lmax, xor_lane<16>(lmax));
             tmax = vmax2(tmax, xor_lane<32>(tmax));
-            float sm2 = 0.0f;
-            if (lane < 16 * NG) sm2 = vmax2(ssz[4 * lane], ssz[4 * lane + 2]);
+            // largest V scale of the tile pair: lane holds token lane's NG scales
+            float sm2 = ssz[2 * NG * lane];
+#pragma unroll
+            for (int gI = 1; gI < NG; ++gI) sm2 = vmax2(sm2, ssz[2 * (NG * lane + gI)]);
             sm2 = vmax2(sm2, xor_lane<1>(sm2));
             sm2 = vmax2(sm2, xor_lane<2>(sm2));
             sm2 = vmax2(sm2, xor_lane<4>(sm2));
@@ -503,7 +550,7 @@ attn_mfma_kernel(const MfmaArgs a) {
         {
             // (scale, zero) of token 16*hf + 4G + i, group gI: float2 at (16*hf + 4G + i) * NG + gI
             auto sz2 = [&](int hf, int x) -> float2 {
-                return reinterpret_cast<const float2*>(ssz)[(16 * hf + 4 * G) * NG + x];
+                return reinterpret_cast<const float2*>(tsz)[(16 * hf + 4 * G) * NG + x];
             };
 #pragma unroll
             for (int gI = 0; gI < NG; ++gI) {
@@ -569,41 +616,45 @@ attn_mfma_kernel(const MfmaArgs a) {
         }
     };
 
-    // one tile: stage it, refill its register set kBuf tiles ahead, compute it.  Tile i of the
-    // wave starts at t_lo + 32 i; the loop runs whole rounds of kBuf tiles, and a tile at or past
-    // t_hi (at most kBuf - 1 at the end of a range) is fully masked.  Loads past the wave's last
-    // tile re-read that tile, which is still in cache.
+    // Tile i of the wave starts at t_lo + 32 i.  Each step stages a tile, refills its registers
+    // two tiles ahead and computes it; the loop runs whole pairs, and a tile at or past t_hi (the
+    // odd one of the last pair, at most) is fully masked.  Loads past the wave's last tile
+    // re-read that tile, which is still in cache.
     if (t_lo < t_hi) {
         const int ntile = (t_hi - t_lo + kTile - 1) / kTile;
         const int t_last = t_lo + (ntile - 1) * kTile;
         auto tile_at = [&](int i) { return min(t_lo + i * kTile, t_last); };
-        auto step = [&](TileRegs& r, int i) {
-            const int tt = t_lo + i * kTile;
-            const bool new_grp = (tt % GS == 0) || (i == 0);
-            const bool big_s = stage(r, new_grp);
-            fetch(r, tile_at(i + kBuf));
-            __builtin_amdgcn_wave_barrier();
-            compute(tt, new_grp, big_s);
-            __builtin_amdgcn_wave_barrier();     // LDS reads done before the next tile overwrites
-            __builtin_amdgcn_sched_barrier(0);   // keep tiles apart in the schedule (register pressure)
-        };
-        // register sets as separate objects (not an array) so nothing is ever indexed dynamically
-        static_assert(kBuf >= 2 && kBuf <= 4, "two to four register sets");
-        TileRegs r0, r1, r2, r3;
-        // issue order r0, r1, ... (the schedule must not reorder them: the first wait counts on it)
-        fetch(r0, tile_at(0));
+        CodeRegs ce, co;
+        SideRegs sd;
+        // issue order: even tile, its side data, odd tile (the schedule must keep it: the first
+        // wait counts on it)
+        fetch_codes(ce, tile_at(0));
+        fetch_side(sd, tile_at(0));
         __builtin_amdgcn_sched_barrier(0);
-        fetch(r1, tile_at(1));
+        fetch_codes(co, tile_at(1));
         __builtin_amdgcn_sched_barrier(0);
-        if constexpr (kBuf >= 3) fetch(r2, tile_at(2));
-        __builtin_amdgcn_sched_barrier(0);
-        if constexpr (kBuf >= 4) fetch(r3, tile_at(3));
-        __builtin_amdgcn_sched_barrier(0);
-        for (int i = 0; i < ntile; i += kBuf) {
-            step(r0, i);
-            step(r1, i + 1);
-            if constexpr (kBuf >= 3) step(r2, i + 2);
-            if constexpr (kBuf >= 4) step(r3, i + 3);
+        for (int i = 0; i < ntile; i += 2) {
+            {   // even tile: codes and the pair's side data
+                const int tt = t_lo + i * kTile;
+                const bool new_grp = (tt % GS == 0) || (i == 0);
+                stage_codes(ce);
+                const bool big_s = stage_side(sd, new_grp);
+                fetch_codes(ce, tile_at(i + 2));
+                fetch_side(sd, tile_at(i + 2));
+                __builtin_amdgcn_wave_barrier();
+                compute(tt, new_grp, big_s, 0);
+                __builtin_amdgcn_wave_barrier();     // LDS reads done before the next tile overwrites
+                __builtin_amdgcn_sched_barrier(0);   // keep tiles apart in the schedule (register pressure)
+            }
+            {   // odd tile: its side data came with the even one
+                const int tt = t_lo + (i + 1) * kTile;
+                stage_codes(co);
+                fetch_codes(co, tile_at(i + 3));
+                __builtin_amdgcn_wave_barrier();
+                compute(tt, GS == 32, false, 1);
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
     }
 
@@ -651,19 +702,15 @@ attn_mfma_kernel(const MfmaArgs a) {
     }
 }
 
-// tiles in flight per wave: two (measured faster than three or four at two waves per SIMD,
-// and the only depth at which every variant fits the register file)
-constexpr int buf_for(int, int) { return KVQ_ATTN_BUF_OVERRIDE > 0 ? KVQ_ATTN_BUF_OVERRIDE : 2; }
-
 template <int GS>
 void launch_nq(const MfmaArgs& a, int nq, hipStream_t st) {
     const dim3 grid((unsigned)(a.B * a.H * (a.nsplit + a.nres))), blk(kThreads);
     switch (nq) {
-        case 1: hipLaunchKernelGGL((attn_mfma_kernel<GS, 1, buf_for(GS, 1)>), grid, blk, 0, st, a); break;
-        case 2: hipLaunchKernelGGL((attn_mfma_kernel<GS, 2, buf_for(GS, 2)>), grid, blk, 0, st, a); break;
-        case 4: hipLaunchKernelGGL((attn_mfma_kernel<GS, 4, buf_for(GS, 4)>), grid, blk, 0, st, a); break;
-        case 8: hipLaunchKernelGGL((attn_mfma_kernel<GS, 8, buf_for(GS, 8)>), grid, blk, 0, st, a); break;
-        default: hipLaunchKernelGGL((attn_mfma_kernel<GS, 16, buf_for(GS, 16)>), grid, blk, 0, st, a); break;
+        case 1: hipLaunchKernelGGL((attn_mfma_kernel<GS, 1>), grid, blk, 0, st, a); break;
+        case 2: hipLaunchKernelGGL((attn_mfma_kernel<GS, 2>), grid, blk, 0, st, a); break;
+        case 4: hipLaunchKernelGGL((attn_mfma_kernel<GS, 4>), grid, blk, 0, st, a); break;
+        case 8: hipLaunchKernelGGL((attn_mfma_kernel<GS, 8>), grid, blk, 0, st, a); break;
+        default: hipLaunchKernelGGL((attn_mfma_kernel<GS, 16>), grid, blk, 0, st, a); break;
     }
 }
 
