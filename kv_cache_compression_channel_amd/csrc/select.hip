@@ -8,6 +8,9 @@
 // Column sums: each thread owns 4 consecutive tokens and adds the T_obs rows in step
 // order (float4 loads, coalesced along tokens), so every score is the same sequence of
 // fp32 additions as the definition.
+// H2O fused (T <= 32768, T % 4 == 0): one 1024-thread block per row sums the row's history
+// straight into registers (8 float4 of scores per thread) and selects from there, so the
+// scores never go to memory and back; each block streams its own 4*T_obs*T bytes.
 // Selection: one 1024-thread block per row.  Scores become order-preserving 32-bit keys
 // (NaN lowest, -0 == +0, recent tokens = key(-inf)); an MSB-first radix select (8-bit digits over
 // the bits where the row's keys differ) finds the k-th largest key t and how many keys
@@ -214,6 +217,194 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(const float* __rest
     }
 }
 
+// Block-wide exclusive prefix of per-thread counts; returns the prefix, *total gets the sum.
+__device__ __forceinline__ uint32_t block_prefix_n(uint32_t cnt, uint32_t* sh, uint32_t* total) {
+    const int lane = threadIdx.x % 64, w = threadIdx.x / 64;
+    uint32_t run = cnt;
+#pragma unroll
+    for (int off = 1; off < 64; off *= 2) {
+        const uint32_t o = __shfl_up(run, off);
+        if (lane >= off) run += o;
+    }
+    if (lane == 63) sh[w] = run;
+    __syncthreads();
+    uint32_t before = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < kSelWaves; ++i) {
+        const uint32_t c = sh[i];
+        before += (i < w) ? c : 0u;
+        tot += c;
+    }
+    __syncthreads();
+    *total = tot;
+    return before + run - cnt;
+}
+
+constexpr int kFusedChunks = 8;   // float4 token groups per thread: 8 x 4 x 1024 = 32768 tokens
+
+// Column sums and selection of one row (Walkthrough §3.1, §3.2).  Thread tid owns tokens
+// 4 (i * 1024 + tid) + e, i < 8, e < 4: token order is (i, tid, e) order, which the in-order
+// emit follows.  Each score is the same sequence of fp32 additions over the steps as the
+// definition.
+__global__ void __launch_bounds__(kSelThreads) h2o_fused_kernel(const float* __restrict__ histo, int64_t T_obs,
+                                                                int64_t T, int64_t budget, int64_t window, int64_t K,
+                                                                float* __restrict__ scores_out,
+                                                                int32_t* __restrict__ keep) {
+    __shared__ uint32_t hist[kSelWaves][256];
+    __shared__ uint32_t scan[256];
+    __shared__ uint32_t sh[kSelWaves];
+    __shared__ uint32_t s_min, s_max, s_digit, s_kk;
+    const int64_t row = blockIdx.x;
+    const int tid = threadIdx.x, w = tid / 64;
+    const float* hr = histo + row * T_obs * T;
+    // T <= 32768 on this path: token indices fit 32 bits
+    const int Ti = (int)T;
+    const int rs = T - window > 0 ? (int)(T - window) : 0;
+    int64_t heavy = budget - (T - rs);
+    heavy = heavy < 0 ? 0 : (heavy > T ? T : heavy);
+
+    // ---- column sums: one step's eight float4 loads in flight per thread ----
+    float4 acc[kFusedChunks];
+#pragma unroll
+    for (int i = 0; i < kFusedChunks; ++i) acc[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    auto tok = [&](int i) -> int { return 4 * (i * kSelThreads + tid); };
+    for (int64_t t = 0; t < T_obs; ++t) {
+        float4 a[kFusedChunks];
+#pragma unroll
+        for (int i = 0; i < kFusedChunks; ++i)
+            if (tok(i) < Ti) a[i] = *reinterpret_cast<const float4*>(hr + t * T + tok(i));
+#pragma unroll
+        for (int i = 0; i < kFusedChunks; ++i) {
+            if (tok(i) < Ti) { acc[i].x += a[i].x; acc[i].y += a[i].y; acc[i].z += a[i].z; acc[i].w += a[i].w; }
+        }
+    }
+    if (scores_out) {
+#pragma unroll
+        for (int i = 0; i < kFusedChunks; ++i)
+            if (tok(i) < Ti) *reinterpret_cast<float4*>(scores_out + row * T + tok(i)) = acc[i];
+    }
+    if (K == 0) return;
+
+    // ---- keys: order-preserving, recent tokens = key(-inf), past the end 0 (never counted) ----
+    uint32_t kreg[kFusedChunks][4];
+#pragma unroll
+    for (int i = 0; i < kFusedChunks; ++i) {
+        const float v[4] = {acc[i].x, acc[i].y, acc[i].z, acc[i].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int j = tok(i) + e;
+            kreg[i][e] = j >= Ti ? 0u : (j >= rs ? kKeyNegInf : order_key(v[e]));
+        }
+    }
+
+    // ---- threshold t: the heavy-th largest key; m: how many keys equal to t are taken ----
+    uint32_t thr = 0xffffffffu, take_eq = 0;
+    const bool none = heavy == 0, all = heavy >= T;
+    if (!none && !all) {
+        uint32_t lo = 0xffffffffu, hi = 0u;
+#pragma unroll
+        for (int i = 0; i < kFusedChunks; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (tok(i) + e < Ti) { lo = min(lo, kreg[i][e]); hi = max(hi, kreg[i][e]); }
+        for (int off = 32; off >= 1; off /= 2) { lo = min(lo, __shfl_xor(lo, off)); hi = max(hi, __shfl_xor(hi, off)); }
+        if (tid == 0) { s_min = 0xffffffffu; s_max = 0u; }
+        __syncthreads();
+        if (tid % 64 == 0) { atomicMin(&s_min, lo); atomicMax(&s_max, hi); }
+        __syncthreads();
+        const uint32_t diff = s_min ^ s_max;
+        int top = diff ? 31 - __clz((int)diff) : -1;   // highest differing bit
+        uint32_t prefix = s_max & (top >= 31 ? 0u : (0xffffffffu << (top + 1)));
+        uint32_t pmask = top >= 31 ? 0u : (0xffffffffu << (top + 1));
+        uint32_t kk = (uint32_t)heavy;
+        while (top >= 0) {
+            const int nb = top + 1 >= 8 ? 8 : top + 1;
+            const int shift = top + 1 - nb;
+            const uint32_t dmask = (1u << nb) - 1u;
+            for (int q = tid; q < kSelWaves * 256; q += kSelThreads) (&hist[0][0])[q] = 0u;
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < kFusedChunks; ++i)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t k = kreg[i][e];
+                    if (tok(i) + e < Ti && (k & pmask) == prefix) atomicAdd(&hist[w][(k >> shift) & dmask], 1u);
+                }
+            __syncthreads();
+            // digits from the largest down: inclusive running count
+            if (tid < 256) {
+                uint32_t c = 0;
+                const int dgt = 255 - tid;
+#pragma unroll
+                for (int q = 0; q < kSelWaves; ++q) c += hist[q][dgt];
+                scan[tid] = c;
+            }
+            __syncthreads();
+            if (tid < 64) {
+                uint32_t a0 = scan[4 * tid], a1 = scan[4 * tid + 1], a2 = scan[4 * tid + 2], a3 = scan[4 * tid + 3];
+                a1 += a0; a2 += a1; a3 += a2;
+                uint32_t run = a3;
+                for (int off = 1; off < 64; off *= 2) {
+                    const uint32_t o = __shfl_up(run, off);
+                    if (tid >= off) run += o;
+                }
+                const uint32_t base = run - a3;
+                const uint32_t inc[4] = {base + a0, base + a1, base + a2, base + a3};
+                const uint32_t exc[4] = {base, base + a0, base + a1, base + a2};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    if (exc[e] < kk && kk <= inc[e]) { s_digit = 255u - (uint32_t)(4 * tid + e); s_kk = kk - exc[e]; }
+                }
+            }
+            __syncthreads();
+            prefix |= (s_digit & dmask) << shift;
+            pmask |= dmask << shift;
+            kk = s_kk;
+            top -= nb;
+            __syncthreads();
+        }
+        thr = prefix;
+        take_eq = kk;
+    }
+
+    // ---- in-order emit: chunk i, then thread, then e ----
+    uint32_t base = 0, eq_seen = 0;
+#pragma unroll
+    for (int i = 0; i < kFusedChunks; ++i) {
+        if (i * kSelThreads * 4 >= Ti) break;
+        bool eq[4];
+        uint32_t neq = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            eq[e] = tok(i) + e < Ti && !none && !all && kreg[i][e] == thr;
+            neq += eq[e] ? 1u : 0u;
+        }
+        uint32_t eq_tot;
+        uint32_t eq_rank = eq_seen + block_prefix_n(neq, sh, &eq_tot);
+        bool take[4];
+        uint32_t ntake = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int j = tok(i) + e;
+            const uint32_t k = kreg[i][e];
+            take[e] = j < Ti && (all || j >= rs || (!none && (k > thr || (eq[e] && eq_rank < take_eq))));
+            if (eq[e]) ++eq_rank;
+            ntake += take[e] ? 1u : 0u;
+        }
+        uint32_t take_tot;
+        uint32_t pos = base + block_prefix_n(ntake, sh, &take_tot);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if (take[e]) {
+                if (pos < (uint64_t)K) keep[row * K + pos] = (int32_t)(tok(i) + e);
+                ++pos;
+            }
+        }
+        base += take_tot;
+        eq_seen += eq_tot;
+    }
+}
+
 int select_launch(const float* scores, int64_t rows, int64_t T, int64_t budget, int64_t window, int32_t* keep,
                   hipStream_t st) {
     const int64_t K = kvq_keep_count(T, budget, window);
@@ -254,6 +445,11 @@ int kvq_h2o_select(const float* hist, int64_t rows, int64_t T_obs, int64_t T, in
     KVQ_REQUIRE_ALIGNED(scores, "scores");
     KVQ_REQUIRE_ALIGNED(keep, "keep");
     hipStream_t st = static_cast<hipStream_t>(stream);
+    if (K > 0 && T % 4 == 0 && T <= (int64_t)kvq::kFusedChunks * 4 * kvq::kSelThreads) {
+        hipLaunchKernelGGL(kvq::h2o_fused_kernel, dim3((unsigned)rows), dim3(kvq::kSelThreads), 0, st, hist, T_obs, T,
+                           budget, window, K, scores_or_null, keep);
+        return kvq::launch_status("H2O selection");
+    }
     const dim3 grid((unsigned)kvq::cdiv(kvq::cdiv(T, 4), kvq::kSumThreads), (unsigned)rows);
     hipLaunchKernelGGL(kvq::colsum_kernel, grid, dim3(kvq::kSumThreads), 0, st, hist, T_obs, T, scores);
     const int rc = kvq::launch_status("H2O column sums");
