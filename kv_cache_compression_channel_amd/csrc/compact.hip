@@ -16,12 +16,15 @@ __global__ void __launch_bounds__(kThreads) compact_kernel(const uint16_t* __res
                                                            int64_t d, const int32_t* __restrict__ keep, int64_t K,
                                                            int64_t nrows, uint16_t* __restrict__ kd,
                                                            uint16_t* __restrict__ vd) {
-    const int64_t cpr = d / 8;   // 16-byte chunks per row
-    const int64_t total = nrows * cpr;
-    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < total; i += (int64_t)gridDim.x * kThreads) {
-        const int64_t row = i / cpr, c = i % cpr;
+    // chunk and row counts fit 31 bits (the host checks): index arithmetic in 32 bits
+    const uint32_t cpr = (uint32_t)(d / 8);   // 16-byte chunks per row
+    const uint32_t total = (uint32_t)(nrows * cpr);
+    const uint32_t Hu = (uint32_t)H, Ku = (uint32_t)K;
+    for (uint32_t i = blockIdx.x * kThreads + threadIdx.x; i < total; i += gridDim.x * kThreads) {
+        const uint32_t row = i / cpr, c = i - row * cpr;
         // destination row order [b][k][h]
-        const int64_t h = row % H, k = (row / H) % K, b = row / (H * K);
+        const uint32_t q = row / Hu;
+        const int64_t h = row - q * Hu, k = q % Ku, b = q / Ku;
         const int64_t t = keep[(b * H + h) * K + k];
         const int64_t so = ((b * T + t) * H + h) * d + 8 * c;
         const int64_t dof = row * d + 8 * c;
@@ -49,6 +52,7 @@ extern "C" int kvq_compact(const void* k_src, const void* v_src_or_null, int64_t
     KVQ_REQUIRE_ALIGNED(keep, "keep");
     const int64_t nrows = B * K * H;
     const int64_t total = nrows * (d / 8);
+    KVQ_REQUIRE(total < ((int64_t)1 << 31), "kvq_compact: more than 2^31 16-byte chunks to move");
     const unsigned blocks = (unsigned)std::min<int64_t>(kvq::cdiv(total, kvq::kThreads), 1 << 16);
     hipLaunchKernelGGL(kvq::compact_kernel, dim3(blocks), dim3(kvq::kThreads), 0, static_cast<hipStream_t>(stream),
                        static_cast<const uint16_t*>(k_src), static_cast<const uint16_t*>(v_src_or_null), T, H, d, keep,

@@ -42,6 +42,16 @@ struct I4Ptrs {
     uint16_t* v_res;
 };
 
+// (b, j, h) of block index u in a [B][n][H] ordering with h fastest, in 32-bit arithmetic
+// (block counts fit 31 bits; 64-bit division costs several times more instructions)
+struct Bjh {
+    int64_t b, j, h;
+};
+__device__ __forceinline__ Bjh split_bjh(uint32_t u, uint32_t H, uint32_t n) {
+    const uint32_t q = u / H;
+    return Bjh{(int64_t)(q / n), (int64_t)(q % n), (int64_t)(u - q * H)};
+}
+
 __device__ __forceinline__ void unpack8(const uint4 a, float (&v)[8]) {
     v[0] = bf_lo(a.x); v[1] = bf_hi(a.x); v[2] = bf_lo(a.y); v[3] = bf_hi(a.y);
     v[4] = bf_lo(a.z); v[5] = bf_hi(a.z); v[6] = bf_lo(a.w); v[7] = bf_hi(a.w);
@@ -138,7 +148,8 @@ __global__ void __launch_bounds__(kThreads) int4_quant_kernel(const uint16_t* __
     if (bid < nK) {
         // ---------------- K: one group of G tokens, every channel ----------------
         constexpr int NR = G / RPP;
-        const int64_t h = bid % H, j = (bid / H) % geo.nKg, b = bid / (H * geo.nKg);
+        const Bjh ix = split_bjh((uint32_t)bid, (uint32_t)H, (uint32_t)geo.nKg);
+        const int64_t h = ix.h, j = ix.j, b = ix.b;
         const int64_t t0 = j * G;
         const int n = (int)min<int64_t>(G, Tq - t0);
         uint4 raw[NR];
@@ -215,7 +226,8 @@ __global__ void __launch_bounds__(kThreads) int4_quant_kernel(const uint16_t* __
         // ---------------- V: 64 tokens, groups of G channels per token ----------------
         constexpr int NR = kVTile / RPP;
         constexpr int LPG = G / 8;   // lanes per group
-        const int64_t h = bid % H, jt = (bid / H) % geo.nVt, b = bid / (H * geo.nVt);
+        const Bjh ix = split_bjh((uint32_t)bid, (uint32_t)H, (uint32_t)geo.nVt);
+        const int64_t h = ix.h, jt = ix.j, b = ix.b;
         const int64_t t0 = jt * kVTile;
         const int n = (int)min<int64_t>(kVTile, Tq - t0);
         const int grp = (8 * lane) / G;
@@ -266,7 +278,8 @@ __global__ void __launch_bounds__(kThreads) int4_quant_kernel(const uint16_t* __
     bid -= nV;
     {
         // ---------------- residual: the last R tokens, verbatim ----------------
-        const int64_t h = bid % H, jr = (bid / H) % geo.nRt, b = bid / (H * geo.nRt);
+        const Bjh ix = split_bjh((uint32_t)bid, (uint32_t)H, (uint32_t)geo.nRt);
+        const int64_t h = ix.h, jr = ix.j, b = ix.b;
         const int64_t r0 = jr * kResTile;
         const int n = (int)min<int64_t>(kResTile, geo.R - r0);
         for (int r = rg; r < n; r += RPP) {
@@ -311,7 +324,8 @@ __global__ void __launch_bounds__(kThreads) int4_dequant_kernel(const uint8_t* _
     };
 
     if (bid < nQ) {
-        const int64_t h = bid % H, j = (bid / H) % ntile, b = bid / (H * ntile);
+        const Bjh ix = split_bjh((uint32_t)bid, (uint32_t)H, (uint32_t)ntile);
+        const int64_t h = ix.h, j = ix.j, b = ix.b;
         const int64_t t0 = j * TILE;
         const int n = (int)min<int64_t>(TILE, Tq - t0);
         float s8[8], zs8[8];
@@ -328,23 +342,33 @@ __global__ void __launch_bounds__(kThreads) int4_dequant_kernel(const uint8_t* _
         for (int r = rg; r < n; r += RPP) {
             const int64_t t = t0 + r;
             const uint32_t w = *reinterpret_cast<const uint32_t*>(codes + ((b * H + h) * Tq + t) * (D / 2) + 4 * lane);
+            // nibbles 2e and 2e+1 sit in byte e of w & 0x0f0f0f0f and of (w >> 4) & 0x0f0f0f0f;
+            // each byte converts with one v_cvt_f32_ubyte<e>
+            const uint32_t lo = w & 0x0f0f0f0fu, hi = (w >> 4) & 0x0f0f0f0fu;
+            float c[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                c[2 * e] = (float)((lo >> (8 * e)) & 0xffu);
+                c[2 * e + 1] = (float)((hi >> (8 * e)) & 0xffu);
+            }
             float v[8];
             if constexpr (IS_K) {
 #pragma unroll
-                for (int k = 0; k < 8; ++k) v[k] = __builtin_fmaf((float)((w >> (4 * k)) & 15u), s8[k], zs8[k]);
+                for (int k = 0; k < 8; ++k) v[k] = __builtin_fmaf(c[k], s8[k], zs8[k]);
             } else {
                 const int64_t mi = ((b * H + h) * Tq + t) * NGD + (8 * lane) / G;
                 const float s = bf_to_f(scale[mi]);
                 const float zs = -bf_to_f(zero[mi]) * s;
 #pragma unroll
-                for (int k = 0; k < 8; ++k) v[k] = __builtin_fmaf((float)((w >> (4 * k)) & 15u), s, zs);
+                for (int k = 0; k < 8; ++k) v[k] = __builtin_fmaf(c[k], s, zs);
             }
             store8(t, b, h, v);
         }
         return;
     }
     bid -= nQ;
-    const int64_t h = bid % H, jr = (bid / H) % geo.nRt, b = bid / (H * geo.nRt);
+    const Bjh ix = split_bjh((uint32_t)bid, (uint32_t)H, (uint32_t)geo.nRt);
+    const int64_t h = ix.h, jr = ix.j, b = ix.b;
     const int64_t r0 = jr * kResTile;
     const int n = (int)min<int64_t>(kResTile, geo.R - r0);
     for (int r = rg; r < n; r += RPP) {
@@ -437,6 +461,7 @@ int dequant_int4(const kvq_int4_cache* c, bool is_k, void* out, int ot, hipStrea
     KVQ_REQUIRE(ot == KVQ_FP32 || ot == KVQ_BF16, "kvq_dequant: ot must be KVQ_FP32 or KVQ_BF16");
     KVQ_REQUIRE_ALIGNED(out, "out");
     const I4Geom g = geom_of(c);
+    KVQ_REQUIRE(g.B * g.H * ((is_k ? g.nKg : g.nVt) + g.nRt) < ((int64_t)1 << 31), "kvq_dequant: grid too large");
     KVQ_DISPATCH_DG(c->d, c->g, launch_dequant, is_k, ot, c, g, out, st);
     return launch_status("INT4 dequantization");
 }

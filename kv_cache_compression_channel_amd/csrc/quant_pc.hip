@@ -63,10 +63,11 @@ __global__ void __launch_bounds__(kThreads) pc_minmax_kernel(const void* __restr
                                                              float2* __restrict__ part) {
     __shared__ float smn[kThreads * VEC];
     __shared__ float smx[kThreads * VEC];
-    int64_t bid = blockIdx.x;
-    const int64_t cb = bid % g.ncb; bid /= g.ncb;
-    const int64_t rc = bid % g.nrc;
-    const int64_t s = bid / g.nrc;
+    // block counts fit 31 bits (the host checks): 32-bit division
+    const uint32_t bid = blockIdx.x, q1 = bid / (uint32_t)g.ncb;
+    const int64_t cb = bid - q1 * (uint32_t)g.ncb;
+    const int64_t rc = q1 % (uint32_t)g.nrc;
+    const int64_t s = q1 / (uint32_t)g.nrc;
     const int lane = threadIdx.x % g.lpr, rl = threadIdx.x / g.lpr;
     const int64_t c0 = (cb * g.lpr + lane) * VEC;
     float mn[VEC], mx[VEC];
@@ -151,10 +152,11 @@ template <int XT, int VEC>
 __global__ void __launch_bounds__(kThreads) pc_code_kernel(const void* __restrict__ x, PcGeom g,
                                                            const PcParams* __restrict__ prm, int qmin, int qmax,
                                                            int8_t* __restrict__ q) {
-    int64_t bid = blockIdx.x;
-    const int64_t cb = bid % g.ncb; bid /= g.ncb;
-    const int64_t rc = bid % g.nrc;
-    const int64_t s = bid / g.nrc;
+    // block counts fit 31 bits (the host checks): 32-bit division
+    const uint32_t bid = blockIdx.x, q1 = bid / (uint32_t)g.ncb;
+    const int64_t cb = bid - q1 * (uint32_t)g.ncb;
+    const int64_t rc = q1 % (uint32_t)g.nrc;
+    const int64_t s = q1 / (uint32_t)g.nrc;
     const int lane = threadIdx.x % g.lpr, rl = threadIdx.x / g.lpr;
     const int64_t c0 = (cb * g.lpr + lane) * VEC;
     if (c0 >= g.C) return;
@@ -206,10 +208,11 @@ __global__ void __launch_bounds__(kThreads) pc_dequant_kernel(const int8_t* __re
                                                               const float* __restrict__ scale,
                                                               const int8_t* __restrict__ zp, PcGeom g,
                                                               void* __restrict__ out) {
-    int64_t bid = blockIdx.x;
-    const int64_t cb = bid % g.ncb; bid /= g.ncb;
-    const int64_t rc = bid % g.nrc;
-    const int64_t s = bid / g.nrc;
+    // block counts fit 31 bits (the host checks): 32-bit division
+    const uint32_t bid = blockIdx.x, q1 = bid / (uint32_t)g.ncb;
+    const int64_t cb = bid - q1 * (uint32_t)g.ncb;
+    const int64_t rc = q1 % (uint32_t)g.nrc;
+    const int64_t s = q1 / (uint32_t)g.nrc;
     const int lane = threadIdx.x % g.lpr, rl = threadIdx.x / g.lpr;
     const int64_t c0 = (cb * g.lpr + lane) * VEC;
     if (c0 >= g.C) return;
