@@ -93,19 +93,23 @@ int kvq_quant_asym(const void* x, int xt, int64_t nb, int64_t R, int64_t C, int6
  *     z = round(0 - min / s), stored as bf16 (exact while |z| <= 256)
  *     q = clip(round(x / s) + z, 0, 15), using the stored s and z.
  *   Dequantization: x_hat = (q - z) * s, rounded once (exact in fp32 for |z| < 2^15).
- * Sections (device, caller-allocated, sizes from kvq_int4_cache_sizes):
- *   [0] k_codes u8   [B][H][Tq][d/2]  byte j = code(2j) | code(2j+1) << 4
- *   [1] k_scale bf16 [B][H][ceil(Tq/g)][d]
- *   [2] k_zero  bf16 [B][H][ceil(Tq/g)][d]
- *   [3] v_codes u8   [B][H][Tq][d/2]
- *   [4] v_scale bf16 [B][H][Tq][d/g]
- *   [5] v_zero  bf16 [B][H][Tq][d/g]
- *   [6] k_res   bf16 [B][H][R][d]
- *   [7] v_res   bf16 [B][H][R][d]
- * Total bytes of the quantized region follow ceil(N/2) + ceil(N/g)*4 per group
- * axis [Explainer, group-size table].
+ * Sections (device, caller-allocated, sizes from kvq_int4_cache_sizes), with
+ * Q = cap (or Tq when cap is 0) and P = rcap (or R when rcap is 0) rows per (b, h):
+ *   [0] k_codes u8   [B][H][Q][d/2]  byte j = code(2j) | code(2j+1) << 4
+ *   [1] k_scale bf16 [B][H][ceil(Q/g)][d]
+ *   [2] k_zero  bf16 [B][H][ceil(Q/g)][d]
+ *   [3] v_codes u8   [B][H][Q][d/2]
+ *   [4] v_scale bf16 [B][H][Q][d/g]
+ *   [5] v_zero  bf16 [B][H][Q][d/g]
+ *   [6] k_res   bf16 [B][H][P][d]
+ *   [7] v_res   bf16 [B][H][P][d]
+ * Only the first Tq (resp. R) rows of each (b, h) are in use; cap and rcap let a
+ * cache grow in place (kvq_int4_append).  With cap = rcap = 0 the sections are
+ * dense.  Total bytes of the quantized region follow ceil(N/2) + ceil(N/g)*4 per
+ * group axis [Explainer, group-size table].
  * EINVAL: any of B, T, H < 1; d not in {64, 128, 256}; g not in {32, 64, 128} or
- *         g > d; R < 0 or R > T; a NULL section pointer of nonzero size.
+ *         g > d; R < 0 or R > T; cap (when nonzero) < Tq or not a multiple of g;
+ *         rcap (when nonzero) < R; a NULL section pointer of nonzero size.
  * ====================================================================== */
 typedef struct {
     int64_t B, T, H, d, g, R;
@@ -117,11 +121,35 @@ typedef struct {
     uint16_t* v_zero;
     uint16_t* k_res;
     uint16_t* v_res;
+    int64_t cap;  /* quantized-token rows per (b, h) in the sections; 0: Tq (dense)  */
+    int64_t rcap; /* residual rows per (b, h) in the sections; 0: R (dense)          */
 } kvq_int4_cache;
 
 int kvq_int4_cache_sizes(int64_t B, int64_t T, int64_t H, int64_t d, int64_t g, int64_t R,
                          size_t sect_bytes[8], size_t* total);
 int kvq_group_quant_int4(const void* K, const void* V, const kvq_int4_cache* c, kvq_stream stream);
+
+/* ======================================================================
+ * Streaming append (decode time)  [Explainer: residual-budget section -- the
+ * newest tokens stay bf16; grouping-axis section -- a K group spans g tokens of a
+ * channel, so it can only be quantized once g tokens have arrived]
+ *
+ * c: a growable cache (cap > 0, rcap > 0, both section layouts as above), with
+ *    T - R a multiple of g (a batch-quantized prefix, or empty: T = R = 0).
+ * k_new, v_new: bf16 [B][n][H][d] (device), 1 <= n <= g, the next n tokens.
+ * The n tokens go after the residual.  When the residual then holds at least
+ * r_keep + g tokens, its oldest g tokens are quantized -- K group (T - R) / g
+ * and V rows T - R .. T - R + g - 1, exactly as kvq_group_quant_int4 would --
+ * and the residual drops them (its rows move down by g).  Updates c->T and
+ * c->R on the host.  Afterwards the cache equals kvq_group_quant_int4 of all T
+ * tokens with the new R.  Needs rcap >= R + n and, on a flush, cap >= T - R + g;
+ * rcap >= r_keep + 2g - 1 always suffices.  Asynchronous on the stream; the
+ * sections must not be read by other work until it completes.
+ * EINVAL: NULL pointers; cap or rcap 0; T - R or cap not a multiple of g;
+ *         n outside [1, g]; R >= r_keep + g; capacity exceeded; shapes as above.
+ * ====================================================================== */
+int kvq_int4_append(kvq_int4_cache* c, const void* k_new, const void* v_new, int64_t n, int64_t r_keep,
+                    kvq_stream stream);
 
 /* ======================================================================
  * Dequantization  [Walkthrough §1.3: x_hat = (q - zero_point) * scale]

@@ -47,6 +47,7 @@ struct AttnArgs {
     int ot;
     float* ws;
     int64_t B, T, H, R, Tq, nKg, Hq;
+    int64_t ldq, ldk, ldr;        // rows per (b, h) of the code / V-scale, K-group and residual sections
     int64_t range_lo, range_hi;   // token range this launch covers
     int64_t split_len;
     int nsplit;                   // splits of this launch per (b, h)
@@ -94,8 +95,8 @@ __global__ void __launch_bounds__(kThreads) attn_split_kernel(const AttnArgs a) 
     }
     float qk[NQ][8], zb[NQ];
     int64_t cur_grp = -1;
-    const uint8_t* kc = a.k_codes + (b * a.H + h) * Tq * (D / 2) + 4 * li;
-    const uint8_t* vc = a.v_codes + (b * a.H + h) * Tq * (D / 2) + 4 * li;
+    const uint8_t* kc = a.k_codes + (b * a.H + h) * a.ldq * (D / 2) + 4 * li;
+    const uint8_t* vc = a.v_codes + (b * a.H + h) * a.ldq * (D / 2) + 4 * li;
     const int vgrp = (8 * li) / GS;
 
     for (int64_t t0 = t_begin; t0 < t_end; t0 += TPS) {
@@ -105,7 +106,7 @@ __global__ void __launch_bounds__(kThreads) attn_split_kernel(const AttnArgs a) 
         if (valid && t < Tq) {
             const int64_t grp = t / GS;
             if (grp != cur_grp) {
-                const int64_t mi = ((b * a.H + h) * a.nKg + grp) * D + 8 * li;
+                const int64_t mi = ((b * a.H + h) * a.ldk + grp) * D + 8 * li;
                 float s[8], z[8];
                 unpack8(*reinterpret_cast<const uint4*>(a.k_scale + mi), s);
                 unpack8(*reinterpret_cast<const uint4*>(a.k_zero + mi), z);
@@ -134,7 +135,7 @@ __global__ void __launch_bounds__(kThreads) attn_split_kernel(const AttnArgs a) 
             }
         } else if (valid) {
             float kv[8];
-            unpack8(*reinterpret_cast<const uint4*>(a.k_res + ((b * a.H + h) * a.R + (t - Tq)) * D + 8 * li), kv);
+            unpack8(*reinterpret_cast<const uint4*>(a.k_res + ((b * a.H + h) * a.ldr + (t - Tq)) * D + 8 * li), kv);
 #pragma unroll
             for (int qi = 0; qi < NQ; ++qi) {
                 float p = 0.0f;
@@ -168,7 +169,7 @@ __global__ void __launch_bounds__(kThreads) attn_split_kernel(const AttnArgs a) 
         }
         if (valid && t < Tq) {
             const uint32_t w = *reinterpret_cast<const uint32_t*>(vc + t * (D / 2));
-            const int64_t mi = ((b * a.H + h) * Tq + t) * NGD + vgrp;
+            const int64_t mi = ((b * a.H + h) * a.ldq + t) * NGD + vgrp;
             const float vs = bf_to_f(a.v_scale[mi]), vz = bf_to_f(a.v_zero[mi]);
             float code[8];
 #pragma unroll
@@ -182,7 +183,7 @@ __global__ void __launch_bounds__(kThreads) attn_split_kernel(const AttnArgs a) 
             }
         } else if (valid) {
             float vv[8];
-            unpack8(*reinterpret_cast<const uint4*>(a.v_res + ((b * a.H + h) * a.R + (t - Tq)) * D + 8 * li), vv);
+            unpack8(*reinterpret_cast<const uint4*>(a.v_res + ((b * a.H + h) * a.ldr + (t - Tq)) * D + 8 * li), vv);
 #pragma unroll
             for (int qi = 0; qi < NQ; ++qi)
 #pragma unroll
@@ -431,6 +432,9 @@ int kvq_decode_attn_int4(const kvq_int4_cache* c, const void* q, int64_t Hq, flo
     a.ws = static_cast<float*>(ws);
     a.B = c->B; a.T = c->T; a.H = c->H; a.R = c->R; a.Tq = c->T - c->R;
     a.nKg = kvq::cdiv(a.Tq, c->g);
+    a.ldq = c->cap ? c->cap : a.Tq;
+    a.ldk = kvq::cdiv(a.ldq, c->g);
+    a.ldr = c->rcap ? c->rcap : c->R;
     a.Hq = Hq;
     a.nslot = p.nslot;
     a.qscale = sm_scale * 1.4426950408889634f;

@@ -74,6 +74,7 @@ struct MfmaArgs {
     float* ws;
     int64_t B, H, Hq;
     int Tq, nKg;
+    int64_t ldq, ldk, ldr;   // rows per (b, h) of the code / V-scale, K-group and residual sections
     int R;               // residual (bf16) tokens per (b, h)
     int nres;            // residual splits per (b, h), kResTile tokens each; their blocks come first
     int split_len;       // tokens per split (multiple of 4 * kTile)
@@ -138,8 +139,8 @@ __device__ void residual_block(const MfmaArgs& a, ResLds& sr, int rb) {
     const int64_t b = bh / a.H, h = bh % a.H;
     const int r_lo = split * kResTile;
     const int nt = min(kResTile, a.R - r_lo);
-    const uint16_t* kr = a.k_res + (bh * a.R + r_lo) * D;
-    const uint16_t* vr = a.v_res + (bh * a.R + r_lo) * D;
+    const uint16_t* kr = a.k_res + (bh * a.ldr + r_lo) * D;
+    const uint16_t* vr = a.v_res + (bh * a.ldr + r_lo) * D;
     for (int i = tid; i < nt * (D / 8); i += kThreads) {
         const int t = i / (D / 8), c8 = 8 * (i % (D / 8));
         *reinterpret_cast<u32x4*>(&sr.k[t][c8]) = *reinterpret_cast<const u32x4*>(kr + t * D + c8);
@@ -305,12 +306,12 @@ attn_mfma_kernel(const MfmaArgs a) {
 
     float lscale = a.qscale, c0 = 0.0f;   // logit - ref = S' * lscale - c0
 
-    const uint8_t* kc = a.k_codes + bh * (int64_t)Tq * (D / 2);
-    const uint8_t* vc = a.v_codes + bh * (int64_t)Tq * (D / 2);
-    const uint16_t* vsp = a.v_scale + bh * (int64_t)Tq * NG;
-    const uint16_t* vzp = a.v_zero + bh * (int64_t)Tq * NG;
-    const uint16_t* kscale = a.k_scale + bh * (int64_t)a.nKg * D;
-    const uint16_t* kzero = a.k_zero + bh * (int64_t)a.nKg * D;
+    const uint8_t* kc = a.k_codes + bh * a.ldq * (D / 2);
+    const uint8_t* vc = a.v_codes + bh * a.ldq * (D / 2);
+    const uint16_t* vsp = a.v_scale + bh * a.ldq * NG;
+    const uint16_t* vzp = a.v_zero + bh * a.ldq * NG;
+    const uint16_t* kscale = a.k_scale + bh * a.ldk * D;
+    const uint16_t* kzero = a.k_zero + bh * a.ldk * D;
     uint8_t* sk = sm.lp.k[wv];
     uint8_t* sv = sm.lp.v[wv];
     float* ssz = sm.lp.sz[wv];
@@ -733,6 +734,9 @@ void launch_attn_mfma(const kvq_int4_cache* c, const void* q, int64_t Hq, float 
     a.ws = ws;
     a.B = c->B; a.H = c->H; a.Hq = Hq;
     a.Tq = (int)(c->T - c->R); a.nKg = (int)cdiv(a.Tq, c->g);
+    a.ldq = c->cap ? c->cap : a.Tq;
+    a.ldk = cdiv(a.ldq, c->g);
+    a.ldr = c->rcap ? c->rcap : c->R;
     a.split_len = (int)split_len;
     a.nsplit = nsplit;
     a.nslot = nslot;

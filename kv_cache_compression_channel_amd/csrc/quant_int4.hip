@@ -29,6 +29,10 @@ struct I4Geom {
     int64_t nKg;   // K groups per (b, h) = ceil(Tq / g)
     int64_t nVt;   // V tiles per (b, h) = ceil(Tq / 64)
     int64_t nRt;   // residual tiles per (b, h) = ceil(R / 64)
+    int64_t ldq;   // quantized-token rows per (b, h) in the sections (cap, or Tq)
+    int64_t ldk;   // K group rows per (b, h) in the sections = ceil(ldq / g)
+    int64_t ldr;   // residual rows per (b, h) in the sections (rcap, or R)
+    int64_t sb, st, sh;   // element strides of the quantizer's input over b, token, h ([B][T][H][d]: T*H*d, H*d, d)
 };
 
 struct I4Ptrs {
@@ -141,7 +145,7 @@ __global__ void __launch_bounds__(kThreads) int4_quant_kernel(const uint16_t* __
 
     const int tid = threadIdx.x, lane = tid % LPR, rg = tid / LPR;
     const int wave = tid / 64;
-    const int64_t H = geo.H, T = geo.T, Tq = geo.Tq;
+    const int64_t H = geo.H, Tq = geo.Tq;
     int64_t bid = blockIdx.x;
     const int64_t nK = geo.B * geo.nKg * H, nV = geo.B * geo.nVt * H;
 
@@ -159,13 +163,13 @@ __global__ void __launch_bounds__(kThreads) int4_quant_kernel(const uint16_t* __
         if (n == G) {
 #pragma unroll
             for (int i = 0; i < NR; ++i)
-                raw[i] = *reinterpret_cast<const uint4*>(K + ((b * T + t0 + rg + RPP * i) * H + h) * D + 8 * lane);
+                raw[i] = *reinterpret_cast<const uint4*>(K + b * geo.sb + (t0 + rg + RPP * i) * geo.st + h * geo.sh + 8 * lane);
         } else {
 #pragma unroll
             for (int i = 0; i < NR; ++i) {
                 const int r = rg + RPP * i;
                 // rows past the group repeat row 0 of this lane, which leaves min and max unchanged
-                raw[i] = *reinterpret_cast<const uint4*>(K + ((b * T + t0 + (r < n ? r : 0)) * H + h) * D + 8 * lane);
+                raw[i] = *reinterpret_cast<const uint4*>(K + b * geo.sb + (t0 + (r < n ? r : 0)) * geo.st + h * geo.sh + 8 * lane);
             }
         }
 #pragma unroll
@@ -195,7 +199,7 @@ __global__ void __launch_bounds__(kThreads) int4_quant_kernel(const uint16_t* __
 #pragma unroll
             for (int w = 1; w < NW; ++w) { a = vmin2(a, s_mn[w * D + c]); z = vmax2(z, s_mx[w * D + c]); }
             const GroupParams p = group_params(a, z);
-            const int64_t mi = ((b * H + h) * geo.nKg + j) * D + c;
+            const int64_t mi = ((b * H + h) * geo.ldk + j) * D + c;
             out.k_scale[mi] = p.sb;
             out.k_zero[mi] = p.zb;
             s_ps[c] = p.s; s_pr[c] = p.r; s_pz[c] = p.z;
@@ -215,7 +219,7 @@ __global__ void __launch_bounds__(kThreads) int4_quant_kernel(const uint16_t* __
                 float v[8], q[8];
                 unpack8(raw[i], v);
                 codes8<false>(v, ps, pr, pz, fast, q);
-                *reinterpret_cast<uint32_t*>(out.k_codes + ((b * H + h) * Tq + t0 + r) * (D / 2) + 4 * lane) =
+                *reinterpret_cast<uint32_t*>(out.k_codes + ((b * H + h) * geo.ldq + t0 + r) * (D / 2) + 4 * lane) =
                     pack_codes(q);
             }
         }
@@ -237,7 +241,7 @@ __global__ void __launch_bounds__(kThreads) int4_quant_kernel(const uint16_t* __
             const int r = rg + RPP * i;
             float mn = FLT_MAX, mx = -FLT_MAX;
             if (r < n) {
-                raw[i] = *reinterpret_cast<const uint4*>(V + ((b * T + t0 + r) * H + h) * D + 8 * lane);
+                raw[i] = *reinterpret_cast<const uint4*>(V + b * geo.sb + (t0 + r) * geo.st + h * geo.sh + 8 * lane);
                 float v[8];
                 unpack8(raw[i], v);
                 minmax8(v, mn, mx);
@@ -252,7 +256,7 @@ __global__ void __launch_bounds__(kThreads) int4_quant_kernel(const uint16_t* __
         __syncthreads();
         for (int p = tid; p < n * NGD; p += kThreads) {
             const GroupParams gp = group_params(s_mn[p], s_mx[p]);
-            const int64_t mi = ((b * H + h) * Tq + t0) * NGD + p;
+            const int64_t mi = ((b * H + h) * geo.ldq + t0) * NGD + p;
             out.v_scale[mi] = gp.sb;
             out.v_zero[mi] = gp.zb;
             s_ps[p] = gp.s; s_pr[p] = gp.r; s_pz[p] = gp.z;
@@ -269,7 +273,7 @@ __global__ void __launch_bounds__(kThreads) int4_quant_kernel(const uint16_t* __
                 float v[8], q[8];
                 unpack8(raw[i], v);
                 codes8<true>(v, ps8, pr8, pz8, fast, q);
-                *reinterpret_cast<uint32_t*>(out.v_codes + ((b * H + h) * Tq + t0 + r) * (D / 2) + 4 * lane) =
+                *reinterpret_cast<uint32_t*>(out.v_codes + ((b * H + h) * geo.ldq + t0 + r) * (D / 2) + 4 * lane) =
                     pack_codes(q);
             }
         }
@@ -283,8 +287,8 @@ __global__ void __launch_bounds__(kThreads) int4_quant_kernel(const uint16_t* __
         const int64_t r0 = jr * kResTile;
         const int n = (int)min<int64_t>(kResTile, geo.R - r0);
         for (int r = rg; r < n; r += RPP) {
-            const int64_t src = ((b * T + Tq + r0 + r) * H + h) * D + 8 * lane;
-            const int64_t dst = ((b * H + h) * geo.R + r0 + r) * D + 8 * lane;
+            const int64_t src = b * geo.sb + (Tq + r0 + r) * geo.st + h * geo.sh + 8 * lane;
+            const int64_t dst = ((b * H + h) * geo.ldr + r0 + r) * D + 8 * lane;
             *reinterpret_cast<uint4*>(out.k_res + dst) = *reinterpret_cast<const uint4*>(K + src);
             *reinterpret_cast<uint4*>(out.v_res + dst) = *reinterpret_cast<const uint4*>(V + src);
         }
@@ -330,7 +334,7 @@ __global__ void __launch_bounds__(kThreads) int4_dequant_kernel(const uint8_t* _
         const int n = (int)min<int64_t>(TILE, Tq - t0);
         float s8[8], zs8[8];
         if constexpr (IS_K) {
-            const int64_t mi = ((b * H + h) * geo.nKg + j) * D + 8 * lane;
+            const int64_t mi = ((b * H + h) * geo.ldk + j) * D + 8 * lane;
             const uint4 sv = *reinterpret_cast<const uint4*>(scale + mi);
             const uint4 zv = *reinterpret_cast<const uint4*>(zero + mi);
             float zf[8];
@@ -341,7 +345,7 @@ __global__ void __launch_bounds__(kThreads) int4_dequant_kernel(const uint8_t* _
         }
         for (int r = rg; r < n; r += RPP) {
             const int64_t t = t0 + r;
-            const uint32_t w = *reinterpret_cast<const uint32_t*>(codes + ((b * H + h) * Tq + t) * (D / 2) + 4 * lane);
+            const uint32_t w = *reinterpret_cast<const uint32_t*>(codes + ((b * H + h) * geo.ldq + t) * (D / 2) + 4 * lane);
             // nibbles 2e and 2e+1 sit in byte e of w & 0x0f0f0f0f and of (w >> 4) & 0x0f0f0f0f;
             // each byte converts with one v_cvt_f32_ubyte<e>
             const uint32_t lo = w & 0x0f0f0f0fu, hi = (w >> 4) & 0x0f0f0f0fu;
@@ -356,7 +360,7 @@ __global__ void __launch_bounds__(kThreads) int4_dequant_kernel(const uint8_t* _
 #pragma unroll
                 for (int k = 0; k < 8; ++k) v[k] = __builtin_fmaf(c[k], s8[k], zs8[k]);
             } else {
-                const int64_t mi = ((b * H + h) * Tq + t) * NGD + (8 * lane) / G;
+                const int64_t mi = ((b * H + h) * geo.ldq + t) * NGD + (8 * lane) / G;
                 const float s = bf_to_f(scale[mi]);
                 const float zs = -bf_to_f(zero[mi]) * s;
 #pragma unroll
@@ -372,7 +376,7 @@ __global__ void __launch_bounds__(kThreads) int4_dequant_kernel(const uint8_t* _
     const int64_t r0 = jr * kResTile;
     const int n = (int)min<int64_t>(kResTile, geo.R - r0);
     for (int r = rg; r < n; r += RPP) {
-        const uint4 a = *reinterpret_cast<const uint4*>(res + ((b * H + h) * geo.R + r0 + r) * D + 8 * lane);
+        const uint4 a = *reinterpret_cast<const uint4*>(res + ((b * H + h) * geo.ldr + r0 + r) * D + 8 * lane);
         if constexpr (OT == KVQ_BF16) {
             *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + ((b * T + Tq + r0 + r) * H + h) * D + 8 * lane) = a;
         } else {
@@ -383,12 +387,60 @@ __global__ void __launch_bounds__(kThreads) int4_dequant_kernel(const uint8_t* _
     }
 }
 
+// Streaming append, residual side.  mode 0: rows R .. R+n-1 of each (b, h) residual receive the
+// n new tokens (new is [B][n][H][d]).  mode 1: rows g .. m-1 move down to 0 .. m-g-1, in
+// ascending chunks of at most g rows, each read completely (barrier) before it is written, so
+// no row is overwritten before it has been read.  One workgroup per (b, h); K and V together.
+template <int D>
+__global__ void __launch_bounds__(kThreads) int4_residual_kernel(uint16_t* __restrict__ k_res,
+                                                                 uint16_t* __restrict__ v_res,
+                                                                 const uint16_t* __restrict__ k_new,
+                                                                 const uint16_t* __restrict__ v_new, int64_t H,
+                                                                 int64_t ldr, int64_t R, int64_t n, int64_t g,
+                                                                 int64_t m, int mode) {
+    constexpr int LPR = D / 8;
+    constexpr int RPP = kThreads / LPR;
+    const int tid = threadIdx.x, lane = tid % LPR, rg = tid / LPR;
+    const int64_t bh = blockIdx.x, b = bh / H, h = bh % H;
+    uint16_t* kr = k_res + bh * ldr * D + 8 * lane;
+    uint16_t* vr = v_res + bh * ldr * D + 8 * lane;
+    if (mode == 0) {
+        for (int64_t i = rg; i < n; i += RPP) {
+            const int64_t src = ((b * n + i) * H + h) * D + 8 * lane;
+            *reinterpret_cast<uint4*>(kr + (R + i) * D) = *reinterpret_cast<const uint4*>(k_new + src);
+            *reinterpret_cast<uint4*>(vr + (R + i) * D) = *reinterpret_cast<const uint4*>(v_new + src);
+        }
+        return;
+    }
+    // chunk of RPP rows (RPP <= 32 <= g): read rows c0 + g + rg, barrier, write rows c0 + rg
+    for (int64_t c0 = 0; c0 < m - g; c0 += RPP) {
+        const int64_t i = c0 + rg;
+        uint4 ka = {0u, 0u, 0u, 0u}, va = {0u, 0u, 0u, 0u};
+        if (i < m - g) {
+            ka = *reinterpret_cast<const uint4*>(kr + (i + g) * D);
+            va = *reinterpret_cast<const uint4*>(vr + (i + g) * D);
+        }
+        __syncthreads();
+        if (i < m - g) {
+            *reinterpret_cast<uint4*>(kr + i * D) = ka;
+            *reinterpret_cast<uint4*>(vr + i * D) = va;
+        }
+        __syncthreads();
+    }
+}
+
 I4Geom geom_of(const kvq_int4_cache* c) {
     I4Geom g;
     g.B = c->B; g.T = c->T; g.H = c->H; g.d = c->d; g.g = c->g; g.R = c->R;
     g.Tq = c->T - c->R;
     g.nKg = cdiv(g.Tq, g.g);
     g.nVt = cdiv(g.Tq, kVTile);
+    g.ldq = c->cap ? c->cap : g.Tq;
+    g.ldk = cdiv(g.ldq, g.g);
+    g.ldr = c->rcap ? c->rcap : g.R;
+    g.st = g.H * g.d;
+    g.sh = g.d;
+    g.sb = g.T * g.st;
     g.nRt = cdiv(g.R, kResTile);
     return g;
 }
@@ -444,6 +496,11 @@ int check_cache_shape(const kvq_int4_cache* c, const char* name) {
     KVQ_REQUIRE(c->R >= 0 && c->R <= c->T, "%s: need 0 <= R <= T", name);
     KVQ_REQUIRE(c->B * c->T * c->H * c->d < ((int64_t)1 << 40), "%s: cache too large", name);
     const int64_t Tq = c->T - c->R;
+    KVQ_REQUIRE(c->cap == 0 || (c->cap >= Tq && c->cap % c->g == 0),
+                "%s: cap (%lld) must be 0 or a multiple of g that is >= T - R (%lld)", name, (long long)c->cap,
+                (long long)Tq);
+    KVQ_REQUIRE(c->rcap == 0 || c->rcap >= c->R, "%s: rcap (%lld) must be 0 or >= R (%lld)", name,
+                (long long)c->rcap, (long long)c->R);
     const void* ptrs[8] = {c->k_codes, c->k_scale, c->k_zero, c->v_codes, c->v_scale, c->v_zero, c->k_res, c->v_res};
     const char* names[8] = {"k_codes", "k_scale", "k_zero", "v_codes", "v_scale", "v_zero", "k_res", "v_res"};
     for (int i = 0; i < 8; ++i) {
@@ -504,6 +561,82 @@ int kvq_group_quant_int4(const void* K, const void* V, const kvq_int4_cache* c, 
     KVQ_DISPATCH_DG(c->d, c->g, kvq::launch_quant, static_cast<const uint16_t*>(K), static_cast<const uint16_t*>(V),
                     g, p, nblk, st);
     return kvq::launch_status("INT4 group quantization");
+}
+
+int kvq_int4_append(kvq_int4_cache* c, const void* k_new, const void* v_new, int64_t n, int64_t r_keep,
+                    kvq_stream stream) {
+    KVQ_REQUIRE(c, "kvq_int4_append: NULL cache descriptor");
+    KVQ_REQUIRE(k_new && v_new, "kvq_int4_append: NULL k_new or v_new");
+    KVQ_REQUIRE(c->B >= 1 && c->H >= 1 && c->T >= 0 && c->R >= 0 && c->R <= c->T,
+                "kvq_int4_append: need B, H >= 1 and 0 <= R <= T");
+    KVQ_REQUIRE(c->d == 64 || c->d == 128 || c->d == 256, "kvq_int4_append: d must be 64, 128 or 256");
+    KVQ_REQUIRE((c->g == 32 || c->g == 64 || c->g == 128) && c->g <= c->d,
+                "kvq_int4_append: g must be 32, 64 or 128 and <= d");
+    KVQ_REQUIRE(c->cap > 0 && c->rcap > 0, "kvq_int4_append: the cache needs cap and rcap (a growable layout)");
+    const int64_t g = c->g, Tq = c->T - c->R;
+    KVQ_REQUIRE(Tq % g == 0 && c->cap % g == 0 && Tq <= c->cap,
+                "kvq_int4_append: T - R (%lld) and cap (%lld) must be multiples of g with T - R <= cap",
+                (long long)Tq, (long long)c->cap);
+    KVQ_REQUIRE(n >= 1 && n <= g, "kvq_int4_append: 1 <= n <= g (got n = %lld)", (long long)n);
+    KVQ_REQUIRE(r_keep >= 0 && c->R < r_keep + g,
+                "kvq_int4_append: need r_keep >= 0 and R (%lld) < r_keep + g", (long long)c->R);
+    const bool flush = c->R + n >= r_keep + g;
+    KVQ_REQUIRE(c->R + n <= c->rcap, "kvq_int4_append: rcap (%lld) < R + n (%lld)", (long long)c->rcap,
+                (long long)(c->R + n));
+    KVQ_REQUIRE(!flush || Tq + g <= c->cap, "kvq_int4_append: cap (%lld) full", (long long)c->cap);
+    KVQ_REQUIRE(c->B * c->T * c->H * c->d < ((int64_t)1 << 40), "kvq_int4_append: cache too large");
+    const void* ptrs[8] = {c->k_codes, c->k_scale, c->k_zero, c->v_codes, c->v_scale, c->v_zero, c->k_res, c->v_res};
+    for (int i = 0; i < 8; ++i) {
+        KVQ_REQUIRE(ptrs[i], "kvq_int4_append: NULL section pointer");
+        KVQ_REQUIRE_ALIGNED(ptrs[i], "section");
+    }
+    KVQ_REQUIRE_ALIGNED(k_new, "k_new");
+    KVQ_REQUIRE_ALIGNED(v_new, "v_new");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int64_t H = c->H, R = c->R, m = R + n;
+    const dim3 rgrid((unsigned)(c->B * H)), blk(kvq::kThreads);
+    const uint16_t* kn = static_cast<const uint16_t*>(k_new);
+    const uint16_t* vn = static_cast<const uint16_t*>(v_new);
+#define KVQ_RES_LAUNCH(DD, MODE)                                                                              \
+    hipLaunchKernelGGL((kvq::int4_residual_kernel<DD>), rgrid, blk, 0, st, c->k_res, c->v_res, kn, vn, H, c->rcap, \
+                       R, n, g, m, MODE)
+    // 1) the new tokens go after the residual
+    if (c->d == 64) KVQ_RES_LAUNCH(64, 0);
+    else if (c->d == 128) KVQ_RES_LAUNCH(128, 0);
+    else KVQ_RES_LAUNCH(256, 0);
+    if (flush) {
+        // 2) the oldest g residual rows become K group Tq / g and V rows Tq .. Tq + g - 1: the batch
+        //    quantizer over a g-token input read from the residual section ([B][H][rcap][d])
+        kvq_int4_cache f = *c;
+        f.T = g;
+        f.R = 0;
+        f.k_codes = c->k_codes + Tq * (c->d / 2);
+        f.v_codes = c->v_codes + Tq * (c->d / 2);
+        f.k_scale = c->k_scale + (Tq / g) * c->d;
+        f.k_zero = c->k_zero + (Tq / g) * c->d;
+        f.v_scale = c->v_scale + Tq * (c->d / g);
+        f.v_zero = c->v_zero + Tq * (c->d / g);
+        kvq::I4Geom geo = kvq::geom_of(&f);
+        geo.ldq = c->cap;
+        geo.ldk = c->cap / g;
+        geo.ldr = c->rcap;
+        geo.sb = H * c->rcap * c->d;
+        geo.st = c->d;
+        geo.sh = c->rcap * c->d;
+        const kvq::I4Ptrs p{f.k_codes, f.k_scale, f.k_zero, f.v_codes, f.v_scale, f.v_zero, f.k_res, f.v_res};
+        const int64_t nblk = geo.B * geo.H * (geo.nKg + geo.nVt + geo.nRt);
+        KVQ_DISPATCH_DG(c->d, g, kvq::launch_quant, c->k_res, c->v_res, geo, p, nblk, st);
+        // 3) the rest of the residual moves down by g rows
+        if (c->d == 64) KVQ_RES_LAUNCH(64, 1);
+        else if (c->d == 128) KVQ_RES_LAUNCH(128, 1);
+        else KVQ_RES_LAUNCH(256, 1);
+    }
+#undef KVQ_RES_LAUNCH
+    const int rc = kvq::launch_status("kvq_int4_append");
+    if (rc) return rc;
+    c->T += n;
+    c->R = flush ? m - g : m;
+    return KVQ_OK;
 }
 
 }  // extern "C"

@@ -23,7 +23,7 @@ KVQ_FMT_PER_CHANNEL, KVQ_FMT_INT4_K, KVQ_FMT_INT4_V = 1, 2, 3
 EXPORTED = [
     "kvq_last_error", "kvq_abi_version",
     "kvq_quant_pc_ws", "kvq_quant_sym", "kvq_quant_asym",
-    "kvq_int4_cache_sizes", "kvq_group_quant_int4", "kvq_dequant",
+    "kvq_int4_cache_sizes", "kvq_group_quant_int4", "kvq_int4_append", "kvq_dequant",
     "kvq_err_stats_ws", "kvq_err_stats", "kvq_stats_finalize",
     "kvq_compression_ratio", "kvq_int4_bytes", "kvq_token_ratio", "kvq_total_gain", "kvq_kv_bytes",
     "kvq_keep_count",
@@ -45,7 +45,7 @@ class Int4Desc(C.Structure):
                 ("R", C.c_int64),
                 ("k_codes", C.c_void_p), ("k_scale", C.c_void_p), ("k_zero", C.c_void_p),
                 ("v_codes", C.c_void_p), ("v_scale", C.c_void_p), ("v_zero", C.c_void_p),
-                ("k_res", C.c_void_p), ("v_res", C.c_void_p)]
+                ("k_res", C.c_void_p), ("v_res", C.c_void_p), ("cap", C.c_int64), ("rcap", C.c_int64)]
 
 
 class PcDesc(C.Structure):
@@ -77,6 +77,7 @@ def lib():
     L.kvq_quant_asym.argtypes = [P, I, I64, I64, I64, I64, I64, I, I, P, P, P, P, SZ, P]
     L.kvq_int4_cache_sizes.argtypes = [I64] * 6 + [P, P]
     L.kvq_group_quant_int4.argtypes = [P, P, P, P]
+    L.kvq_int4_append.argtypes = [P, P, P, I64, I64, P]
     L.kvq_dequant.argtypes = [P, P, I, P]
     L.kvq_err_stats_ws.argtypes = [I64]
     L.kvq_err_stats_ws.restype = SZ
@@ -222,6 +223,8 @@ class Int4Cache:
     v_zero: torch.Tensor
     k_res: torch.Tensor
     v_res: torch.Tensor
+    cap: int = 0     # quantized-token rows per (b, h) in the sections (0: dense, T - R)
+    rcap: int = 0    # residual rows per (b, h) in the sections (0: dense, R)
 
     SECTIONS = ("k_codes", "k_scale", "k_zero", "v_codes", "v_scale", "v_zero", "k_res", "v_res")
 
@@ -238,12 +241,35 @@ class Int4Cache:
                          e((B, H, Tq, d // 2), u8), e((B, H, Tq, d // g), bf), e((B, H, Tq, d // g), bf),
                          e((B, H, R, d), bf), e((B, H, R, d), bf))
 
+    @staticmethod
+    def empty_stream(B, H, d, g, cap, rcap, device):
+        """An empty growable cache: sections sized for cap quantized and rcap residual tokens."""
+        u8, bf = torch.uint8, torch.bfloat16
+
+        def e(shape, dt):
+            return torch.empty(shape, dtype=dt, device=device)
+        nKg = -(-cap // g)
+        return Int4Cache(B, 0, H, d, g, 0,
+                         e((B, H, cap, d // 2), u8), e((B, H, nKg, d), bf), e((B, H, nKg, d), bf),
+                         e((B, H, cap, d // 2), u8), e((B, H, cap, d // g), bf), e((B, H, cap, d // g), bf),
+                         e((B, H, rcap, d), bf), e((B, H, rcap, d), bf), cap, rcap)
+
+    def valid(self, section: str) -> torch.Tensor:
+        """The rows of a section in use (all of it for a dense cache)."""
+        t = getattr(self, section)
+        Tq = self.T - self.R
+        if section in ("k_scale", "k_zero"):
+            return t[:, :, :-(-Tq // self.g) if Tq > 0 else 0]
+        if section in ("k_res", "v_res"):
+            return t[:, :, :self.R]
+        return t[:, :, :Tq]
+
     def desc(self) -> Int4Desc:
         def p(t):
             return t.data_ptr() if t.numel() else None
         return Int4Desc(self.B, self.T, self.H, self.d, self.g, self.R,
                         p(self.k_codes), p(self.k_scale), p(self.k_zero), p(self.v_codes), p(self.v_scale),
-                        p(self.v_zero), p(self.k_res), p(self.v_res))
+                        p(self.v_zero), p(self.k_res), p(self.v_res), self.cap, self.rcap)
 
     def nbytes(self) -> int:
         return sum(getattr(self, s).numel() * getattr(self, s).element_size() for s in self.SECTIONS)
@@ -261,6 +287,22 @@ def group_quant_int4(K: torch.Tensor, V: torch.Tensor, g: int = 64, R: int = 128
         cache = Int4Cache.empty(B, T, H, d, g, R, K.device)
     desc = cache.desc()
     _check(lib().kvq_group_quant_int4(_p(K), _p(V), C.byref(desc), _stream(K)))
+    return cache
+
+
+def int4_append(cache: Int4Cache, k_new: torch.Tensor, v_new: torch.Tensor, r_keep: int) -> Int4Cache:
+    """Append n <= g tokens (bf16 [B][n][H][d]) to a growable cache in place; flushes the oldest g
+    residual tokens to INT4 when the residual reaches r_keep + g.  Updates cache.T and cache.R."""
+    _need_cuda(k_new, v_new)
+    if k_new.dtype != torch.bfloat16 or v_new.dtype != torch.bfloat16:
+        raise TypeError("k_new and v_new must be bfloat16")
+    if k_new.shape != v_new.shape or k_new.dim() != 4 or not k_new.is_contiguous() or not v_new.is_contiguous():
+        raise ValueError("k_new and v_new must be contiguous [B][n][H][d] of the same shape")
+    if (k_new.shape[0], k_new.shape[2], k_new.shape[3]) != (cache.B, cache.H, cache.d):
+        raise ValueError("k_new does not match the cache's B, H, d")
+    desc = cache.desc()
+    _check(lib().kvq_int4_append(C.byref(desc), _p(k_new), _p(v_new), k_new.shape[1], r_keep, _stream(k_new)))
+    cache.T, cache.R = int(desc.T), int(desc.R)
     return cache
 
 

@@ -102,12 +102,46 @@ def test_quant_pc_validation(L):
 
 
 def _desc(**kw):
-    base = dict(B=1, T=128, H=2, d=128, g=64, R=0)
+    base = dict(B=1, T=128, H=2, d=128, g=64, R=0, cap=0, rcap=0)
     base.update(kw)
     d = kvq.Int4Desc(base["B"], base["T"], base["H"], base["d"], base["g"], base["R"])
     for f in kvq.Int4Cache.SECTIONS:
         setattr(d, f, kw.get(f, 0x200000))
+    d.cap, d.rcap = base["cap"], base["rcap"]
     return d
+
+
+def test_int4_growable_layout_validation(L):
+    # cap must cover T - R and be a multiple of g; rcap must cover R
+    for kw in (dict(cap=64), dict(cap=130), dict(R=100, rcap=50)):
+        d = _desc(**kw)
+        assert L.kvq_group_quant_int4(FAKE, FAKE, C.byref(d), None) == kvq.KVQ_EINVAL, kw
+        assert L.kvq_decode_attn_int4(C.byref(d), FAKE, 2, 1.0, FAKE, 1, FAKE, 1 << 30, None) == kvq.KVQ_EINVAL
+    ok = dict(T=192, R=64, cap=256, rcap=256)          # T - R = 128, two groups of 64
+    app = L.kvq_int4_append
+    cases = [
+        (dict(ok, cap=0), 1, 64),                       # dense layout cannot grow
+        (dict(ok, rcap=0), 1, 64),
+        (dict(ok, T=200), 1, 64),                       # T - R not a multiple of g
+        (dict(ok, cap=200), 1, 64),                     # cap not a multiple of g
+        (ok, 0, 64),                                    # n = 0
+        (ok, 65, 64),                                   # n > g
+        (dict(ok, R=128, T=256), 1, 64),                # R >= r_keep + g
+        (dict(ok, rcap=64), 1, 64),                     # rcap < R + n
+        (dict(ok, cap=128), 64, 64),                    # a flush with the quantized rows full
+        (dict(ok, d=96), 1, 64),
+        (dict(ok, k_res=None), 1, 64),
+    ]
+    for kw, n, r_keep in cases:
+        d = _desc(**kw)
+        T0, R0 = d.T, d.R
+        assert app(C.byref(d), FAKE, FAKE, n, r_keep, None) == kvq.KVQ_EINVAL, (kw, n, r_keep)
+        assert (d.T, d.R) == (T0, R0), "a rejected append left the descriptor changed"
+        assert L.kvq_last_error()
+    d = _desc(**ok)
+    assert app(C.byref(d), None, FAKE, 1, 64, None) == kvq.KVQ_EINVAL
+    assert app(None, FAKE, FAKE, 1, 64, None) == kvq.KVQ_EINVAL
+    assert app(C.byref(d), MISALIGNED, FAKE, 1, 64, None) == kvq.KVQ_EALIGN
 
 
 def test_int4_validation(L):
