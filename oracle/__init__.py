@@ -57,7 +57,8 @@ def _declare(L):
     L.orc_int4_dequant.argtypes = [C.c_int, P, P, P, P, I64, I64, I64, I64, I64, I64, P]
     L.orc_int4_dequant.restype = None
     L.orc_decode_attn.argtypes = [P] * 8 + [I64] * 6 + [P, I64, C.c_double, P]
-    L.orc_decode_attn_rows.argtypes = [P] * 8 + [I64] * 6 + [P, I64, C.c_double, P, P, I64, P]
+    L.orc_decode_attn_rows.argtypes = [P] * 8 + [I64] * 6 + [P, I64, C.c_double, P, P, I64, P, P]
+    L.orc_int4_evict.argtypes = [P] * 8 + [I64] * 6 + [P, I64, I64] + [P] * 8
     L.orc_colsum.argtypes = [P, I64, I64, I64, P]
     L.orc_colsum.restype = None
     L.orc_keep_count.argtypes = [I64, I64, I64]
@@ -225,8 +226,62 @@ def decode_attn(c: dict, q: np.ndarray, sm_scale: float = 1.0, rows=None):
     rb = np.ascontiguousarray([r[0] for r in rows], np.int64)
     rh = np.ascontiguousarray([r[1] for r in rows], np.int64)
     out = np.empty((len(rows), d), np.float64)
-    _check(lib().orc_decode_attn_rows(*args, _p(rb), _p(rh), len(rows), _p(out)), "decode_attn_rows")
+    _check(lib().orc_decode_attn_rows(*args, _p(rb), _p(rh), len(rows), _p(out), None), "decode_attn_rows")
     return out
+
+
+def decode_attn_probs(c: dict, q: np.ndarray, sm_scale: float = 1.0):
+    """Attention output fp64 [B][Hq][d] and the attention weights fp64 [B][Hq][T]."""
+    q = np.ascontiguousarray(q, np.uint16)
+    B, Hq, d = q.shape
+    T = c["T"]
+    rb = np.repeat(np.arange(B, dtype=np.int64), Hq)
+    rh = np.tile(np.arange(Hq, dtype=np.int64), B)
+    out = np.empty((B, Hq, d), np.float64)
+    probs = np.empty((B, Hq, T), np.float64)
+    args = _cache_ptrs(c) + [c["B"], T, c["H"], c["d"], c["g"], c["R"], _p(q), Hq, float(sm_scale)]
+    _check(lib().orc_decode_attn_rows(*args, _p(rb), _p(rh), B * Hq, _p(out), _p(probs)), "decode_attn_probs")
+    return out, probs
+
+
+def h2o_decode_scores(acc: np.ndarray, probs: np.ndarray) -> np.ndarray:
+    """[Walkthrough §3.1] cumulative attention, one decode step at a time: the score of
+    token i grows by the weight this step's query puts on it.  READING (GQA): the query
+    heads that share a KV head are that head's observations in the step, so their weights
+    add up.  acc [B][H][T], probs [B][Hq][T] (consecutive query heads share a KV head);
+    fp64."""
+    B, H, T = acc.shape
+    G = probs.shape[1] // H
+    grouped = np.asarray(probs, np.float64).reshape(B, H, G, T)
+    step = np.zeros((B, H, T), np.float64)
+    for j in range(G):
+        step += grouped[:, :, j]
+    return np.asarray(acc, np.float64) + step
+
+
+def int4_evict(c: dict, keep: np.ndarray, R2: int) -> dict:
+    """Eviction on a dense oracle cache dict; keep int32 [B][H][K] -> new cache dict (K tokens, R2 bf16)."""
+    keep = np.ascontiguousarray(keep, np.int32)
+    B, T, H, d, g, R = (c[k] for k in ("B", "T", "H", "d", "g", "R"))
+    K = keep.shape[-1]
+    Tq2 = K - R2
+    nKg2 = -(-Tq2 // g) if Tq2 > 0 else 0
+    o = dict(
+        k_codes=np.zeros((B, H, Tq2, d // 2), np.uint8),
+        k_scale=np.zeros((B, H, nKg2, d), np.uint16),
+        k_zero=np.zeros((B, H, nKg2, d), np.uint16),
+        v_codes=np.zeros((B, H, Tq2, d // 2), np.uint8),
+        v_scale=np.zeros((B, H, Tq2, d // g), np.uint16),
+        v_zero=np.zeros((B, H, Tq2, d // g), np.uint16),
+        k_res=np.zeros((B, H, R2, d), np.uint16),
+        v_res=np.zeros((B, H, R2, d), np.uint16),
+    )
+    rc = lib().orc_int4_evict(*_cache_ptrs(c), B, T, H, d, g, R, _p(keep), K, R2,
+                              *[_p(o[k]) for k in ("k_codes", "k_scale", "k_zero", "v_codes", "v_scale",
+                                                   "v_zero", "k_res", "v_res")])
+    _check(rc, "int4_evict")
+    o.update(B=B, T=K, H=H, d=d, g=g, R=R2)
+    return o
 
 
 # -------------------------------------------------------------- selection ---

@@ -318,7 +318,7 @@ static void slice_fp64(int is_k, const uint8_t* codes, const uint16_t* scale, co
  * reads the low-bit cache and dequantizes it; GQA: query head hq reads KV head
  * hq / (Hq / Hkv), consecutive query heads sharing one KV head). */
 static void attend_row(const double* kh, const double* vh, int64_t T, int64_t d,
-                       const uint16_t* qrow, double sm_scale, double* logit, double* o) {
+                       const uint16_t* qrow, double sm_scale, double* logit, double* o, double* probs) {
     double m = -INFINITY;
     for (int64_t t = 0; t < T; ++t) {
         double acc = 0.0;
@@ -334,6 +334,9 @@ static void attend_row(const double* kh, const double* vh, int64_t T, int64_t d,
         for (int64_t c = 0; c < d; ++c) o[c] += p * vh[t * d + c];
     }
     for (int64_t c = 0; c < d; ++c) o[c] /= Z;
+    /* the attention weights themselves, softmax(sm_scale * q . k_t) over t */
+    if (probs)
+        for (int64_t t = 0; t < T; ++t) probs[t] = exp(logit[t] - m) / Z;
 }
 
 int orc_decode_attn_rows(const uint8_t* k_codes, const uint16_t* k_scale, const uint16_t* k_zero,
@@ -341,7 +344,8 @@ int orc_decode_attn_rows(const uint8_t* k_codes, const uint16_t* k_scale, const 
                          const uint16_t* k_res, const uint16_t* v_res,
                          int64_t B, int64_t T, int64_t Hkv, int64_t d, int64_t g, int64_t R,
                          const uint16_t* q, int64_t Hq, double sm_scale,
-                         const int64_t* rows_b, const int64_t* rows_hq, int64_t n_rows, double* out) {
+                         const int64_t* rows_b, const int64_t* rows_hq, int64_t n_rows, double* out,
+                         double* probs) {
     if (B <= 0 || T <= 0 || Hkv <= 0 || Hq <= 0 || Hq % Hkv || d <= 0 || d % g || R < 0 || R > T) return -1;
     double* kh = (double*)malloc(sizeof(double) * (size_t)(T * d));
     double* vh = (double*)malloc(sizeof(double) * (size_t)(T * d));
@@ -356,7 +360,7 @@ int orc_decode_attn_rows(const uint8_t* k_codes, const uint16_t* k_scale, const 
             cur_b = b;
             cur_h = h;
         }
-        attend_row(kh, vh, T, d, &q[(b * Hq + hq) * d], sm_scale, lg, &out[i * d]);
+        attend_row(kh, vh, T, d, &q[(b * Hq + hq) * d], sm_scale, lg, &out[i * d], probs ? &probs[i * T] : NULL);
     }
     free(kh); free(vh); free(lg);
     return 0;
@@ -377,7 +381,7 @@ int orc_decode_attn(const uint8_t* k_codes, const uint16_t* k_scale, const uint1
             rh[b * Hq + hq] = hq;
         }
     const int rc = orc_decode_attn_rows(k_codes, k_scale, k_zero, v_codes, v_scale, v_zero, k_res, v_res,
-                                        B, T, Hkv, d, g, R, q, Hq, sm_scale, rb, rh, B * Hq, out);
+                                        B, T, Hkv, d, g, R, q, Hq, sm_scale, rb, rh, B * Hq, out, NULL);
     free(rb); free(rh);
     return rc;
 }
@@ -469,6 +473,128 @@ void orc_compact(const uint16_t* src, int64_t B, int64_t T, int64_t H, int64_t d
                 const int64_t t = keep[(b * H + h) * K + k];
                 memcpy(&dst[((b * K + k) * H + h) * d], &src[((b * T + t) * H + h) * d], (size_t)d * 2);
             }
+}
+
+/* ------------------------------------------- eviction on the 4-bit cache --- */
+
+/* Current value of token t of head (b, h) in channel c: the dequantized 4-bit level for a
+ * quantized token (t < Tq), the stored bf16 value for a residual token. */
+static float int4_value(int is_k, const uint8_t* codes, const uint16_t* scale, const uint16_t* zero,
+                        const uint16_t* res, int64_t b, int64_t h, int64_t t, int64_t c,
+                        int64_t H, int64_t d, int64_t g, int64_t Tq, int64_t R) {
+    if (t >= Tq) return orc_bf16_to_f32(res[((b * H + h) * R + (t - Tq)) * d + c]);
+    const int64_t nKg = ceil_div(Tq, g);
+    const uint8_t byte = codes[((b * H + h) * Tq + t) * (d / 2) + c / 2];
+    const unsigned code = (c & 1) ? (byte >> 4) : (byte & 15u);
+    const int64_t mi = is_k ? ((b * H + h) * nKg + t / g) * d + c : ((b * H + h) * Tq + t) * (d / g) + c / g;
+    return int4_level(code, scale[mi], zero[mi]);
+}
+
+/* [Explainer, eviction section: only the selected KV is kept; Walkthrough §4: the token
+ * saving multiplies the byte saving] applied to a KIVI cache (Explainer, grouping-axis and
+ * residual-budget sections).  The K = keep-count kept tokens of every (b, h), in keep
+ * order, form a new cache of T2 = K tokens whose last R2 stay bf16.  READING (the pages
+ * do not spell out eviction on a grouped 4-bit cache):
+ *   - a kept quantized V row keeps its codes, scale and zero (V groups lie inside a token);
+ *   - a new K group (g consecutive kept tokens, the last one partial) whose tokens are
+ *     exactly all tokens of one old quantized K group, in order, keeps that group's codes,
+ *     scale and zero; every other new K group is quantized afresh, per channel, from the
+ *     current values of its tokens (the dequantized levels, exact in fp32, or the bf16
+ *     residual values) with the steps of int4_group;
+ *   - a kept residual token that lands in the quantized part is quantized like a new token
+ *     (its V row from its bf16 values, its K channels inside its new group);
+ *   - a new residual row holds the current value rounded to the nearest bf16 (the bf16
+ *     value itself for a residual token).
+ * Output layouts as orc_int4_quant with T2 = K, R2. */
+int orc_int4_evict(const uint8_t* k_codes, const uint16_t* k_scale, const uint16_t* k_zero,
+                   const uint8_t* v_codes, const uint16_t* v_scale, const uint16_t* v_zero,
+                   const uint16_t* k_res, const uint16_t* v_res,
+                   int64_t B, int64_t T, int64_t H, int64_t d, int64_t g, int64_t R,
+                   const int32_t* keep, int64_t K, int64_t R2,
+                   uint8_t* dk_codes, uint16_t* dk_scale, uint16_t* dk_zero,
+                   uint8_t* dv_codes, uint16_t* dv_scale, uint16_t* dv_zero,
+                   uint16_t* dk_res, uint16_t* dv_res) {
+    if (B <= 0 || T <= 0 || H <= 0 || d <= 0 || d % 2 || g <= 0 || d % g || R < 0 || R > T) return -1;
+    if (K < 1 || K > T || R2 < 0 || R2 > K) return -1;
+    const int64_t Tq = T - R, nKg = ceil_div(Tq, g);
+    const int64_t Tq2 = K - R2, nKg2 = ceil_div(Tq2, g);
+    float* xk = (float*)malloc(sizeof(float) * (size_t)(K * d));
+    float* xv = (float*)malloc(sizeof(float) * (size_t)(K * d));
+    float* vals = (float*)malloc(sizeof(float) * (size_t)(g > d ? g : d));
+    uint8_t* cg = (uint8_t*)malloc((size_t)(g > d ? g : d));
+    uint8_t* row = (uint8_t*)malloc((size_t)d);
+    uint8_t* kq = (uint8_t*)malloc((size_t)(Tq2 > 0 ? Tq2 : 1) * (size_t)d);
+    if (!xk || !xv || !vals || !cg || !row || !kq) {
+        free(xk); free(xv); free(vals); free(cg); free(row); free(kq);
+        return -2;
+    }
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t h = 0; h < H; ++h) {
+            const int32_t* kp = &keep[(b * H + h) * K];
+            for (int64_t i = 0; i < K; ++i) {
+                if (kp[i] < 0 || kp[i] >= T) {
+                    free(xk); free(xv); free(vals); free(cg); free(row); free(kq);
+                    return -1;
+                }
+                for (int64_t c = 0; c < d; ++c) {
+                    xk[i * d + c] = int4_value(1, k_codes, k_scale, k_zero, k_res, b, h, kp[i], c, H, d, g, Tq, R);
+                    xv[i * d + c] = int4_value(0, v_codes, v_scale, v_zero, v_res, b, h, kp[i], c, H, d, g, Tq, R);
+                }
+            }
+            /* K groups of the new quantized part */
+            for (int64_t j = 0; j < nKg2; ++j) {
+                const int64_t i0 = j * g, n = (i0 + g <= Tq2) ? g : Tq2 - i0;
+                const int64_t t0 = kp[i0];
+                int whole = t0 < Tq && t0 % g == 0 && n == ((t0 + g <= Tq) ? g : Tq - t0);
+                for (int64_t i = 0; whole && i < n; ++i) whole = kp[i0 + i] == t0 + i;
+                for (int64_t c = 0; c < d; ++c) {
+                    const int64_t mi = ((b * H + h) * nKg2 + j) * d + c;
+                    if (whole) {
+                        const int64_t si = ((b * H + h) * nKg + t0 / g) * d + c;
+                        dk_scale[mi] = k_scale[si];
+                        dk_zero[mi] = k_zero[si];
+                        for (int64_t i = 0; i < n; ++i) {
+                            const uint8_t byte = k_codes[((b * H + h) * Tq + t0 + i) * (d / 2) + c / 2];
+                            kq[(i0 + i) * d + c] = (uint8_t)((c & 1) ? (byte >> 4) : (byte & 15u));
+                        }
+                    } else {
+                        for (int64_t i = 0; i < n; ++i) vals[i] = xk[(i0 + i) * d + c];
+                        int4_group(vals, n, &dk_scale[mi], &dk_zero[mi], cg);
+                        for (int64_t i = 0; i < n; ++i) kq[(i0 + i) * d + c] = cg[i];
+                    }
+                }
+            }
+            for (int64_t i = 0; i < Tq2; ++i) pack_row(&kq[i * d], d, &dk_codes[((b * H + h) * Tq2 + i) * (d / 2)]);
+            /* V rows of the new quantized part */
+            for (int64_t i = 0; i < Tq2; ++i) {
+                const int64_t t = kp[i];
+                uint8_t* out = &dv_codes[((b * H + h) * Tq2 + i) * (d / 2)];
+                for (int64_t k = 0; k < d / g; ++k) {
+                    const int64_t mi = ((b * H + h) * Tq2 + i) * (d / g) + k;
+                    if (t < Tq) {
+                        const int64_t si = ((b * H + h) * Tq + t) * (d / g) + k;
+                        dv_scale[mi] = v_scale[si];
+                        dv_zero[mi] = v_zero[si];
+                        for (int64_t c = k * g; c < k * g + g; ++c) {
+                            const uint8_t byte = v_codes[((b * H + h) * Tq + t) * (d / 2) + c / 2];
+                            row[c] = (uint8_t)((c & 1) ? (byte >> 4) : (byte & 15u));
+                        }
+                    } else {
+                        for (int64_t c = 0; c < g; ++c) vals[c] = xv[i * d + k * g + c];
+                        int4_group(vals, g, &dv_scale[mi], &dv_zero[mi], &row[k * g]);
+                    }
+                }
+                pack_row(row, d, out);
+            }
+            /* new residual rows */
+            for (int64_t r = 0; r < R2; ++r)
+                for (int64_t c = 0; c < d; ++c) {
+                    dk_res[((b * H + h) * R2 + r) * d + c] = orc_f32_to_bf16(xk[(Tq2 + r) * d + c]);
+                    dv_res[((b * H + h) * R2 + r) * d + c] = orc_f32_to_bf16(xv[(Tq2 + r) * d + c]);
+                }
+        }
+    free(xk); free(xv); free(vals); free(cg); free(row); free(kq);
+    return 0;
 }
 
 /* ------------------------------------------------------------ accounting --- */

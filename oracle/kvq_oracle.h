@@ -53,13 +53,15 @@ int orc_decode_attn(const uint8_t* k_codes, const uint16_t* k_scale, const uint1
                     const uint16_t* k_res, const uint16_t* v_res,
                     int64_t B, int64_t T, int64_t Hkv, int64_t d, int64_t g, int64_t R,
                     const uint16_t* q, int64_t Hq, double sm_scale, double* out);
-/* Same, only for the listed (b, hq) rows: out [n_rows][d]. */
+/* Same, only for the listed (b, hq) rows: out [n_rows][d]; when probs is not NULL it also
+ * receives each row's attention weights, fp64 [n_rows][T]. */
 int orc_decode_attn_rows(const uint8_t* k_codes, const uint16_t* k_scale, const uint16_t* k_zero,
                          const uint8_t* v_codes, const uint16_t* v_scale, const uint16_t* v_zero,
                          const uint16_t* k_res, const uint16_t* v_res,
                          int64_t B, int64_t T, int64_t Hkv, int64_t d, int64_t g, int64_t R,
                          const uint16_t* q, int64_t Hq, double sm_scale,
-                         const int64_t* rows_b, const int64_t* rows_hq, int64_t n_rows, double* out);
+                         const int64_t* rows_b, const int64_t* rows_hq, int64_t n_rows, double* out,
+                         double* probs);
 
 /* H2O / SnapKV token selection. */
 void orc_colsum(const float* hist, int64_t rows, int64_t T_obs, int64_t T, float* scores);
@@ -69,6 +71,17 @@ int orc_h2o_select(const float* hist, int64_t rows, int64_t T_obs, int64_t T, in
                    int64_t window, float* scores, int32_t* keep);
 void orc_compact(const uint16_t* src, int64_t B, int64_t T, int64_t H, int64_t d,
                  const int32_t* keep, int64_t K, uint16_t* dst);
+
+/* Eviction on the 4-bit cache: keep int32 [B][H][K] (indices into the T tokens); the new
+ * cache has K tokens, the last R2 of them bf16.  Destination layouts as orc_int4_quant. */
+int orc_int4_evict(const uint8_t* k_codes, const uint16_t* k_scale, const uint16_t* k_zero,
+                   const uint8_t* v_codes, const uint16_t* v_scale, const uint16_t* v_zero,
+                   const uint16_t* k_res, const uint16_t* v_res,
+                   int64_t B, int64_t T, int64_t H, int64_t d, int64_t g, int64_t R,
+                   const int32_t* keep, int64_t K, int64_t R2,
+                   uint8_t* dk_codes, uint16_t* dk_scale, uint16_t* dk_zero,
+                   uint8_t* dv_codes, uint16_t* dv_scale, uint16_t* dv_zero,
+                   uint16_t* dk_res, uint16_t* dv_res);
 
 /* Accounting. */
 uint64_t orc_int4_bytes(uint64_t N, uint64_t g);

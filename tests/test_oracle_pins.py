@@ -600,3 +600,215 @@ def test_bf16_helpers():
     assert oracle.f32_to_bf16(np.float32(1 + 3 * 2.0**-8)).item() == 0x3F82
     assert oracle.f32_to_bf16(np.float32(-1.5)).item() == 0xBFC0
     assert float(oracle.bf16_to_f32(np.array([0x4049], np.uint16))[0]) == 3.140625
+
+
+# ------------------------------------------------ eviction on the 4-bit cache --
+
+def _gather_tokens(X, keep):
+    """X [B][T][H][d], keep [B][H][K] -> [B][K][H][d] (plain fancy indexing)."""
+    B, T, H, d = X.shape
+    out = np.empty((B, keep.shape[-1], H, d), X.dtype)
+    for b in range(B):
+        for h in range(H):
+            out[b, :, h] = X[b, keep[b, h], h]
+    return out
+
+
+def _assert_same_cache(a, b):
+    for k in ("k_codes", "k_scale", "k_zero", "v_codes", "v_scale", "v_zero", "k_res", "v_res"):
+        assert a[k].shape == b[k].shape, k
+        assert np.array_equal(a[k], b[k]), k
+
+
+@pytest.mark.parametrize("T,R,g", [(300, 44, 64), (256, 0, 32), (128 * 3 + 5, 5, 128)])
+def test_evict_keep_all_is_identity(T, R, g):
+    B, H, d = 2, 2, 128
+    Kb, Vb = _c2_like(B, T, H, d, seed=T)
+    c = oracle.int4_quant(Kb, Vb, g, R)
+    keep = np.broadcast_to(np.arange(T, dtype=np.int32), (B, H, T)).copy()
+    _assert_same_cache(oracle.int4_evict(c, keep, R), c)
+
+
+@pytest.mark.parametrize("g", [32, 64, 128])
+def test_evict_whole_groups_equals_quantizing_the_kept_tokens(g):
+    # Eviction that keeps whole K groups (any of them, a different set per head) and the
+    # residual: every group is a function of its own values only, so the result must be
+    # the quantization of the gathered input.
+    B, H, d = 2, 3, 128
+    ng, R = 6, 40
+    T = ng * g + 17 + R            # a partial last K group of 17 tokens
+    Kb, Vb = _c2_like(B, T, H, d, seed=g + 1)
+    c = oracle.int4_quant(Kb, Vb, g, R)
+    rng = np.random.default_rng(g)
+    keep = np.empty((B, H, 3 * g + 17 + R), np.int32)
+    for b in range(B):
+        for h in range(H):
+            groups = np.sort(rng.choice(ng, 3, replace=False))
+            toks = [np.arange(j * g, (j + 1) * g) for j in groups]
+            toks.append(np.arange(ng * g, T))          # the partial group and the residual
+            keep[b, h] = np.concatenate(toks)
+    got = oracle.int4_evict(c, keep, R)
+    want = oracle.int4_quant(_gather_tokens(Kb, keep), _gather_tokens(Vb, keep), g, R)
+    _assert_same_cache(got, want)
+
+
+@pytest.mark.parametrize("g,R2", [(64, 0), (64, 37), (32, 5), (128, 0)])
+def test_evict_from_the_bf16_window_equals_the_quantizer(g, R2):
+    # A cache held entirely in the bf16 residual: the kept tokens' values are their bf16
+    # inputs, so every new group (K across tokens, V across channels) and the new residual
+    # must be exactly what the quantizer makes of the gathered tokens.
+    B, H, d, T = 1, 2, 128, 400
+    Kb, Vb = _c2_like(B, T, H, d, seed=g + R2)
+    c = oracle.int4_quant(Kb, Vb, g, T)
+    rng = np.random.default_rng(R2)
+    K = 3 * g + 11 + R2
+    keep = np.sort(np.stack([[rng.choice(T, K, replace=False) for _ in range(H)] for _ in range(B)]), -1)
+    keep = keep.astype(np.int32)
+    got = oracle.int4_evict(c, keep, R2)
+    want = oracle.int4_quant(_gather_tokens(Kb, keep), _gather_tokens(Vb, keep), g, R2)
+    _assert_same_cache(got, want)
+
+
+def _check_evicted(c, keep, R2, e):
+    """Properties every eviction result has, whatever the kept set."""
+    B, T, H, d, g, R = (c[k] for k in ("B", "T", "H", "d", "g", "R"))
+    K = keep.shape[-1]
+    Tq, Tq2 = T - R, K - R2
+    gk = _gather_tokens(oracle.int4_dequant(c, "k"), keep)
+    gv = _gather_tokens(oracle.int4_dequant(c, "v"), keep)
+    # V: kept quantized rows come back exactly
+    ev = oracle.int4_dequant(e, "v")
+    from_q = (keep < Tq).transpose(0, 2, 1)[:, :Tq2]               # [B][Tq2][H]
+    assert np.array_equal(ev[:, :Tq2][from_q], gv[:, :Tq2][from_q])
+    # K: every new group keeps each value within half of its (new) step, on the nearest level
+    ek = oracle.int4_dequant(e, "k")[:, :Tq2].astype(np.float64)
+    x = gk[:, :Tq2].astype(np.float64)
+    q, s, z = _levels_and_ids(e, "k")
+    assert np.all(np.abs(x - ek) <= s / 2)
+    levels = (np.arange(16)[None, None, None, None, :] - z[..., None]) * s[..., None]
+    dist = np.abs(x[..., None] - levels)
+    assert np.all(np.take_along_axis(dist, q[..., None], -1)[..., 0] == dist.min(-1))
+    # a requantized group's scale is the smallest bf16 at or above (max - min) / 15 of its
+    # values; a group copied whole is one whose tokens are exactly an old aligned group
+    n_copied = 0
+    for b in range(B):
+        for h in range(H):
+            for j in range(-(-Tq2 // g)):
+                toks = keep[b, h, j * g:min((j + 1) * g, Tq2)]
+                t0 = int(toks[0])
+                old_n = min(g, Tq - t0) if t0 < Tq else -1
+                whole = t0 % g == 0 and len(toks) == old_n and np.array_equal(toks, np.arange(t0, t0 + old_n))
+                if whole:
+                    n_copied += 1
+                    assert np.array_equal(e["k_scale"][b, h, j], c["k_scale"][b, h, t0 // g])
+                    assert np.array_equal(e["k_zero"][b, h, j], c["k_zero"][b, h, t0 // g])
+                    continue
+                vals = x[b, j * g:(j + 1) * g, h]
+                floor = np.maximum(vals.max(0) - vals.min(0), np.float32(1e-8)).astype(np.float32) / np.float32(15)
+                assert np.all(f32(e["k_scale"][b, h, j]) >= floor)
+                assert np.all(f32(e["k_scale"][b, h, j] - np.uint16(1)) < floor)
+    # residual rows: the kept values rounded to the nearest bf16; torch's fp32 -> bf16
+    # conversion (round to nearest, ties to even) is the independent rounding
+    import torch
+    for side, gx in (("k", gk), ("v", gv)):
+        want = torch.from_numpy(np.ascontiguousarray(gx[:, Tq2:])).to(torch.bfloat16).view(torch.int16).numpy()
+        assert np.array_equal(e[side + "_res"], want.view(np.uint16).transpose(0, 2, 1, 3))
+    return n_copied
+
+
+@pytest.mark.parametrize("g", [32, 64, 128])
+def test_evict_requantized_groups_bound_nearest_level_and_residual_rounding(g):
+    B, H, d, R = 1, 2, 128, 30
+    T = 5 * g + 9 + R
+    Kb, Vb = _c2_like(B, T, H, d, seed=3 * g)
+    c = oracle.int4_quant(Kb, Vb, g, R)
+    rng = np.random.default_rng(g + 7)
+    K = 3 * g + 20
+    keep = np.sort(np.stack([[rng.choice(T, K, replace=False) for _ in range(H)] for _ in range(B)]), -1)
+    keep = keep.astype(np.int32)
+    _check_evicted(c, keep, 13, oracle.int4_evict(c, keep, 13))
+
+
+@pytest.mark.parametrize("g", [32, 64])
+def test_evict_shifted_and_aligned_runs(g):
+    # head 0 keeps a contiguous run that starts mid-group (every group must be requantized);
+    # head 1 keeps two whole aligned groups and then the same kind of shifted run
+    B, H, d, R = 1, 2, 128, 16
+    T = 6 * g + R
+    Kb, Vb = _c2_like(B, T, H, d, seed=g + 11)
+    c = oracle.int4_quant(Kb, Vb, g, R)
+    K = 4 * g
+    keep = np.stack([np.arange(g // 2, g // 2 + K),
+                     np.concatenate([np.arange(g, 3 * g), np.arange(3 * g + 5, 5 * g + 5)])])[None].astype(np.int32)
+    e = oracle.int4_evict(c, keep, 0)
+    assert _check_evicted(c, keep, 0, e) == 2
+
+
+@pytest.mark.parametrize("g", [32, 128])
+def test_evict_prefix_of_a_group_and_quantized_tokens_into_the_window(g):
+    # keep the first 2g + 5 + 20 tokens with 20 bf16 rows: the new quantized part ends 5
+    # tokens into old group 2 (a prefix of a group is not that group: requantized), and the
+    # window receives 20 dequantized 4-bit tokens, rounded to bf16
+    B, H, d, R = 1, 1, 128, 8
+    T = 4 * g + R
+    Kb, Vb = _c2_like(B, T, H, d, seed=g + 21)
+    c = oracle.int4_quant(Kb, Vb, g, R)
+    keep = np.arange(2 * g + 25, dtype=np.int32)[None, None]
+    e = oracle.int4_evict(c, keep, 20)
+    assert _check_evicted(c, keep, 20, e) == 2
+    assert not np.array_equal(e["k_scale"][0, 0, 2], c["k_scale"][0, 0, 2])
+
+
+def test_evict_rejects_bad_arguments():
+    Kb, Vb = _c2_like(1, 100, 1, 64, seed=0)
+    c = oracle.int4_quant(Kb, Vb, 64, 10)
+    keep = np.arange(50, dtype=np.int32)[None, None]
+    with pytest.raises(Exception):
+        oracle.int4_evict(c, keep, 51)
+    with pytest.raises(Exception):
+        oracle.int4_evict(c, np.full((1, 1, 5), 100, np.int32), 0)
+
+
+# ------------------------------------------------------ decode-time H2O scores --
+
+def test_h2o_decode_two_tokens_closed_form_per_query_head():
+    # two tokens, k_0 = 0, k_1 = a e_0; query head hq has q = (hq + 1) e_0, so its weight on
+    # token 1 is e^{(hq+1) a} / (1 + e^{(hq+1) a}); the KV head's score adds those of its
+    # query heads (4 query heads over 2 KV heads).
+    d = 64
+    K = np.zeros((1, 2, 2, d), np.float32)
+    K[0, 1, :, 0] = 0.375
+    V = np.ones((1, 2, 2, d), np.float32)
+    Kb, Vb = bf16(K), bf16(V)
+    a = float(f32(Kb)[0, 1, 0, 0])
+    q = np.zeros((1, 4, d), np.float32)
+    q[0, :, 0] = np.arange(1, 5)
+    c = _all_residual_cache(Kb, Vb)
+    _, probs = oracle.decode_attn_probs(c, bf16(q))
+    acc0 = np.array([[[0.5, 0.25], [1.0, 2.0]]])
+    acc = oracle.h2o_decode_scores(acc0, probs)
+    w = lambda m: math.exp(m * a) / (1 + math.exp(m * a))
+    for h in range(2):
+        want1 = acc0[0, h, 1] + w(2 * h + 1) + w(2 * h + 2)
+        want0 = acc0[0, h, 0] + (1 - w(2 * h + 1)) + (1 - w(2 * h + 2))
+        assert abs(acc[0, h, 1] - want1) < 1e-14 and abs(acc[0, h, 0] - want0) < 1e-14
+
+
+def test_h2o_decode_scores_sum_and_match_offline_colsum():
+    # each decode step hands out exactly G = Hq / H units of weight per KV head; summed over
+    # steps, the running score equals the offline H2O column sum of the same weights
+    B, T, H, Hq, d, g = 1, 150, 2, 4, 64, 32
+    Kb, Vb = _c2_like(B, T, H, d, seed=9)
+    c = oracle.int4_quant(Kb, Vb, g, 22)
+    rng = np.random.default_rng(9)
+    acc = np.zeros((B, H, T))
+    hist = []
+    for step in range(5):
+        q = bf16(rng.standard_normal((B, Hq, d)) / 8)
+        _, probs = oracle.decode_attn_probs(c, q)
+        new = oracle.h2o_decode_scores(acc, probs)
+        assert np.allclose((new - acc).sum(-1), Hq // H, rtol=0, atol=1e-12)
+        acc = new
+        hist.append(probs.reshape(B, H, Hq // H, T))
+    hist = np.concatenate(hist, axis=2).reshape(B * H, -1, T).astype(np.float32)
+    assert np.allclose(oracle.colsum(hist), acc.reshape(B * H, T), rtol=1e-5, atol=1e-7)
