@@ -152,6 +152,31 @@ int kvq_int4_append(kvq_int4_cache* c, const void* k_new, const void* v_new, int
                     kvq_stream stream);
 
 /* ======================================================================
+ * Eviction on a 4-bit cache  [Explainer: eviction section (only the selected KV
+ * is kept) on the layout of its grouping-axis and residual-budget sections;
+ * Walkthrough §4: the token saving multiplies the byte saving]
+ *
+ * keep: int32 [B][H][K] (device), for every (b, h) the tokens to keep, as indices
+ * into the T tokens of src (the selectors' output with rows = B*H is one such
+ * list).  dst (B, H, d, g of src; dst->T = K with 1 <= K <= src->T; dst->R = R2
+ * with 0 <= R2 <= K; dense or growable) receives, per (b, h), the kept tokens in
+ * keep order: the first K - R2 quantized, the last R2 as bf16.  With x the current
+ * value of a kept token (its dequantized level, or its bf16 value):
+ *   - a V row from the quantized part keeps its codes, scale and zero;
+ *   - a new K group (g consecutive kept tokens; the last may be partial) whose
+ *     tokens are exactly all tokens of one old K group, in order, keeps that
+ *     group's codes, scales and zeros; every other new K group, and every V row
+ *     of a kept bf16 token, is quantized from x as in kvq_group_quant_int4;
+ *   - a new bf16 row is x rounded to nearest even.
+ * Keeping every token with R2 = src->R reproduces src.  Indices outside [0, T)
+ * are clamped into it (unspecified result, no out-of-bounds access).  No dst
+ * section may overlap a src section (checked).  Asynchronous on the stream.
+ * EINVAL: shapes as in kvq_group_quant_int4 for src and dst; mismatched B, H, d,
+ *         g; dst->T > src->T; NULL keep; overlapping sections.
+ * ====================================================================== */
+int kvq_int4_evict(const kvq_int4_cache* src, const int32_t* keep, const kvq_int4_cache* dst, kvq_stream stream);
+
+/* ======================================================================
  * Dequantization  [Walkthrough §1.3: x_hat = (q - zero_point) * scale]
  *
  * kind KVQ_FMT_PER_CHANNEL: desc -> kvq_pc_tensor; out [nb][R][C] dense.

@@ -1,0 +1,338 @@
+// evict.hip -- eviction on a KIVI-style 4-bit cache: the kept tokens of every (b, h) form a
+// new cache of K tokens whose last R2 stay bf16.
+//
+// Explainer (KV cache 压缩：把历史装得更小), eviction section (only the selected KV stays)
+// applied to the 4-bit layout of its grouping-axis and residual-budget sections; the
+// Walkthrough (KV Compression 公式到源码对照) §4 multiplies the token saving with the byte
+// saving.  What happens to a group:
+//   - V groups lie inside one token, so a kept quantized V row keeps its codes, scale, zero;
+//   - a K group spans g tokens of one channel.  A new K group whose tokens are exactly one
+//     whole old group, in order, keeps that group's codes, scale and zero; any other new K
+//     group is quantized afresh, per channel, from the current values of its tokens (the
+//     dequantized levels, exact in fp32, or the bf16 window values);
+//   - a window token that lands in the quantized part is quantized like a new token;
+//   - a new window row holds the current value rounded to the nearest bf16.
+//
+// One launch, three kinds of block, each over one (b, h) (block order (b, tile, h), h fastest):
+//   K blocks: one new K group (g tokens x d channels).  The keep indices go to LDS; one
+//     block-wide vote decides "whole old group" (copy 16-byte rows) or requantize: every lane
+//     owns 8 channels of RPP-strided rows, dequantizes them into registers, and the group's
+//     min/max, parameters and codes follow the quantizer's steps.
+//   V blocks: 64 new quantized rows; per row, copy codes + scale/zero or quantize the bf16 row
+//     (the g-channel groups reduce across g/8 lanes with shuffles; no LDS).
+//   window blocks: 64 new bf16 rows; copy, or dequantize and round to bf16.
+// Keep indices outside [0, T) are clamped into it: the result is then unspecified, but no
+// access leaves the source sections.
+#include "int4_common.h"
+
+namespace kvq {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kTile = 64;   // rows per V / window block
+
+struct EvGeom {
+    int64_t T, H, Tq;                 // source tokens, heads, quantized tokens
+    int64_t ldq, ldk, ldr;            // source rows per (b, h): codes / V params, K params, window
+    int64_t K, Tq2, R2;               // kept tokens, of which quantized / window
+    int64_t dldq, dldk, dldr;         // destination rows per (b, h)
+    int64_t nKb, nVb, nRb;            // blocks per (b, h) of each kind
+};
+
+__device__ __forceinline__ int64_t clamp_tok(int32_t t, int64_t T) {
+    return t < 0 ? 0 : (t >= T ? T - 1 : (int64_t)t);
+}
+
+// 8 codes of one packed dword (low nibble = even channel) as floats.
+__device__ __forceinline__ void unpack_codes8(uint32_t w, float (&c)[8]) {
+    const uint32_t lo = w & 0x0f0f0f0fu, hi = (w >> 4) & 0x0f0f0f0fu;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        c[2 * e] = (float)((lo >> (8 * e)) & 0xffu);
+        c[2 * e + 1] = (float)((hi >> (8 * e)) & 0xffu);
+    }
+}
+
+// Current K values of channels 8*lane .. 8*lane+7 of source token t: (q - z) * s rounded once
+// (q*s and z*s are exact in fp32, so the fma rounds the exact value once), or the bf16 window.
+template <int D, int G>
+__device__ __forceinline__ void k_values(const kvq_int4_cache& s, const EvGeom& geo, int64_t bh, int64_t t,
+                                         int lane, float (&v)[8]) {
+    if (t < geo.Tq) {
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(s.k_codes + (bh * geo.ldq + t) * (D / 2) + 4 * lane);
+        const int64_t mi = (bh * geo.ldk + t / G) * D + 8 * lane;
+        float sc[8], zf[8], c[8];
+        unpack8(*reinterpret_cast<const uint4*>(s.k_scale + mi), sc);
+        unpack8(*reinterpret_cast<const uint4*>(s.k_zero + mi), zf);
+        unpack_codes8(w, c);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = __builtin_fmaf(c[k], sc[k], -zf[k] * sc[k]);
+    } else {
+        unpack8(*reinterpret_cast<const uint4*>(s.k_res + (bh * geo.ldr + (t - geo.Tq)) * D + 8 * lane), v);
+    }
+}
+
+// Same for V (one scale and zero per g channels of the token).
+template <int D, int G>
+__device__ __forceinline__ void v_values(const kvq_int4_cache& s, const EvGeom& geo, int64_t bh, int64_t t,
+                                         int lane, float (&v)[8]) {
+    if (t < geo.Tq) {
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(s.v_codes + (bh * geo.ldq + t) * (D / 2) + 4 * lane);
+        const int64_t mi = (bh * geo.ldq + t) * (D / G) + (8 * lane) / G;
+        const float sc = bf_to_f(s.v_scale[mi]);
+        const float zs = -bf_to_f(s.v_zero[mi]) * sc;
+        float c[8];
+        unpack_codes8(w, c);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = __builtin_fmaf(c[k], sc, zs);
+    } else {
+        unpack8(*reinterpret_cast<const uint4*>(s.v_res + (bh * geo.ldr + (t - geo.Tq)) * D + 8 * lane), v);
+    }
+}
+
+template <int D, int G>
+__global__ void __launch_bounds__(kThreads) int4_evict_kernel(const kvq_int4_cache src, const int32_t* __restrict__ keep,
+                                                              kvq_int4_cache dst, EvGeom geo) {
+    constexpr int LPR = D / 8;            // lanes per token row (8 channels each)
+    constexpr int RPP = kThreads / LPR;   // rows per pass
+    constexpr int NW = kThreads / 64;
+    constexpr int NGD = D / G;
+    constexpr int LPG = G / 8;            // lanes per V group
+    const int tid = threadIdx.x, lane = tid % LPR, rg = tid / LPR, wave = tid / 64;
+    const uint32_t H = (uint32_t)geo.H;
+    uint32_t bid = blockIdx.x;
+    const uint32_t nK = (uint32_t)(src.B * geo.nKb * geo.H), nV = (uint32_t)(src.B * geo.nVb * geo.H);
+
+    if (bid < nK) {
+        // ------------------------------ one new K group ------------------------------
+        static_assert(G % RPP == 0, "tile shape");
+        constexpr int NR = G / RPP;
+        __shared__ int32_t s_keep[G];
+        __shared__ float s_mn[NW * D], s_mx[NW * D];
+        __shared__ float s_ps[D], s_pr[D], s_pz[D];
+        const Bjh ix = split_bjh(bid, H, (uint32_t)geo.nKb);
+        const int64_t bh = ix.b * geo.H + ix.h, j = ix.j, i0 = j * G;
+        const int n = (int)min<int64_t>(G, geo.Tq2 - i0);
+        const int32_t* kp = keep + bh * geo.K + i0;
+        const int64_t first = clamp_tok(kp[0], geo.T);
+        int run = 1;
+        for (int i = tid; i < n; i += kThreads) {
+            const int64_t t = clamp_tok(kp[i], geo.T);
+            s_keep[i] = (int32_t)t;
+            run &= (t == first + i);
+        }
+        const bool whole = __syncthreads_and(run) && first < geo.Tq && first % G == 0 &&
+                           n == (int)min<int64_t>(G, geo.Tq - first);
+        if (whole) {
+            // codes rows first .. first+n-1 -> rows i0 .. i0+n-1 (contiguous in both), 16 B per lane
+            const uint4* cs = reinterpret_cast<const uint4*>(src.k_codes + (bh * geo.ldq + first) * (D / 2));
+            uint4* cd = reinterpret_cast<uint4*>(dst.k_codes + (bh * geo.dldq + i0) * (D / 2));
+            for (int e = tid; e < n * (D / 32); e += kThreads) cd[e] = cs[e];
+            const int64_t si = (bh * geo.ldk + first / G) * D, di = (bh * geo.dldk + j) * D;
+            for (int e = tid; e < D / 8; e += kThreads) {
+                reinterpret_cast<uint4*>(dst.k_scale + di)[e] = reinterpret_cast<const uint4*>(src.k_scale + si)[e];
+                reinterpret_cast<uint4*>(dst.k_zero + di)[e] = reinterpret_cast<const uint4*>(src.k_zero + si)[e];
+            }
+            return;
+        }
+        float v[NR][8];
+        float mn[8], mx[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) { mn[k] = FLT_MAX; mx[k] = -FLT_MAX; }
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+            const int r = rg + RPP * i;
+            // rows past the group repeat row 0 of this lane, which leaves min and max unchanged
+            k_values<D, G>(src, geo, bh, s_keep[r < n ? r : 0], lane, v[i]);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) { mn[k] = vmin2(mn[k], v[i][k]); mx[k] = vmax2(mx[k], v[i][k]); }
+        }
+#pragma unroll
+        for (int off = LPR; off < 64; off *= 2) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                mn[k] = vmin2(mn[k], __shfl_xor(mn[k], off));
+                mx[k] = vmax2(mx[k], __shfl_xor(mx[k], off));
+            }
+        }
+        if ((tid % 64) < LPR) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) { s_mn[wave * D + 8 * lane + k] = mn[k]; s_mx[wave * D + 8 * lane + k] = mx[k]; }
+        }
+        __syncthreads();
+        for (int c = tid; c < D; c += kThreads) {
+            float a = s_mn[c], z = s_mx[c];
+#pragma unroll
+            for (int w = 1; w < NW; ++w) { a = vmin2(a, s_mn[w * D + c]); z = vmax2(z, s_mx[w * D + c]); }
+            const GroupParams p = group_params(a, z);
+            const int64_t mi = (bh * geo.dldk + j) * D + c;
+            dst.k_scale[mi] = p.sb;
+            dst.k_zero[mi] = p.zb;
+            s_ps[c] = p.s; s_pr[c] = p.r; s_pz[c] = p.z;
+        }
+        __syncthreads();
+        float ps[8], pr[8], pz[8];
+        bool fast = true;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            ps[k] = s_ps[8 * lane + k]; pr[k] = s_pr[8 * lane + k]; pz[k] = s_pz[8 * lane + k];
+            fast = fast && pz[k] >= 0.0f && pz[k] <= 15.0f;
+        }
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+            const int r = rg + RPP * i;
+            if (r < n) {
+                float q[8];
+                codes8<false>(v[i], ps, pr, pz, fast, q);
+                *reinterpret_cast<uint32_t*>(dst.k_codes + (bh * geo.dldq + i0 + r) * (D / 2) + 4 * lane) =
+                    pack_codes(q);
+            }
+        }
+        return;
+    }
+    bid -= nK;
+    if (bid < nV) {
+        // ------------------------------ 64 new V rows ------------------------------
+        const Bjh ix = split_bjh(bid, H, (uint32_t)geo.nVb);
+        const int64_t bh = ix.b * geo.H + ix.h, i0 = ix.j * kTile;
+        const int n = (int)min<int64_t>(kTile, geo.Tq2 - i0);
+        const int32_t* kp = keep + bh * geo.K + i0;
+        const int grp = (8 * lane) / G;
+        for (int r = rg; r < n; r += RPP) {
+            const int64_t t = clamp_tok(kp[r], geo.T), i = i0 + r;
+            uint8_t* crow = dst.v_codes + (bh * geo.dldq + i) * (D / 2);
+            const int64_t dmi = (bh * geo.dldq + i) * NGD;
+            if (t < geo.Tq) {
+                *reinterpret_cast<uint32_t*>(crow + 4 * lane) =
+                    *reinterpret_cast<const uint32_t*>(src.v_codes + (bh * geo.ldq + t) * (D / 2) + 4 * lane);
+                if (lane < NGD) {
+                    const int64_t smi = (bh * geo.ldq + t) * NGD + lane;
+                    dst.v_scale[dmi + lane] = src.v_scale[smi];
+                    dst.v_zero[dmi + lane] = src.v_zero[smi];
+                }
+            } else {
+                float x[8];
+                unpack8(*reinterpret_cast<const uint4*>(src.v_res + (bh * geo.ldr + (t - geo.Tq)) * D + 8 * lane), x);
+                float mn = FLT_MAX, mx = -FLT_MAX;
+                minmax8(x, mn, mx);
+                // the LPG lanes of a group are consecutive and take this branch together (same row)
+#pragma unroll
+                for (int off = 1; off < LPG; off *= 2) {
+                    mn = vmin2(mn, __shfl_xor(mn, off));
+                    mx = vmax2(mx, __shfl_xor(mx, off));
+                }
+                const GroupParams gp = group_params(mn, mx);
+                if (lane % LPG == 0) {
+                    dst.v_scale[dmi + grp] = gp.sb;
+                    dst.v_zero[dmi + grp] = gp.zb;
+                }
+                const bool fast = gp.z >= 0.0f && gp.z <= 15.0f;
+                const float ps8[8] = {gp.s, gp.s, gp.s, gp.s, gp.s, gp.s, gp.s, gp.s};
+                const float pr8[8] = {gp.r, gp.r, gp.r, gp.r, gp.r, gp.r, gp.r, gp.r};
+                const float pz8[8] = {gp.z, gp.z, gp.z, gp.z, gp.z, gp.z, gp.z, gp.z};
+                float q[8];
+                codes8<true>(x, ps8, pr8, pz8, fast, q);
+                *reinterpret_cast<uint32_t*>(crow + 4 * lane) = pack_codes(q);
+            }
+        }
+        return;
+    }
+    bid -= nV;
+    {
+        // ------------------------------ 64 new window rows ------------------------------
+        const Bjh ix = split_bjh(bid, H, (uint32_t)geo.nRb);
+        const int64_t bh = ix.b * geo.H + ix.h, r0 = ix.j * kTile;
+        const int n = (int)min<int64_t>(kTile, geo.R2 - r0);
+        const int32_t* kp = keep + bh * geo.K + geo.Tq2 + r0;
+        for (int r = rg; r < n; r += RPP) {
+            const int64_t t = clamp_tok(kp[r], geo.T);
+            const int64_t o = (bh * geo.dldr + r0 + r) * D + 8 * lane;
+            if (t >= geo.Tq) {
+                const int64_t si = (bh * geo.ldr + (t - geo.Tq)) * D + 8 * lane;
+                *reinterpret_cast<uint4*>(dst.k_res + o) = *reinterpret_cast<const uint4*>(src.k_res + si);
+                *reinterpret_cast<uint4*>(dst.v_res + o) = *reinterpret_cast<const uint4*>(src.v_res + si);
+            } else {
+                float a[8], b[8];
+                k_values<D, G>(src, geo, bh, t, lane, a);
+                v_values<D, G>(src, geo, bh, t, lane, b);
+                *reinterpret_cast<uint4*>(dst.k_res + o) =
+                    make_uint4(pack_bf2(a[0], a[1]), pack_bf2(a[2], a[3]), pack_bf2(a[4], a[5]), pack_bf2(a[6], a[7]));
+                *reinterpret_cast<uint4*>(dst.v_res + o) =
+                    make_uint4(pack_bf2(b[0], b[1]), pack_bf2(b[2], b[3]), pack_bf2(b[4], b[5]), pack_bf2(b[6], b[7]));
+            }
+        }
+    }
+}
+
+template <int D, int G>
+void launch_evict(const kvq_int4_cache& s, const int32_t* keep, const kvq_int4_cache& d, const EvGeom& geo,
+                  int64_t nblk, hipStream_t st) {
+    hipLaunchKernelGGL((int4_evict_kernel<D, G>), dim3((unsigned)nblk), dim3(kThreads), 0, st, s, keep, d, geo);
+}
+
+// Byte extent of section i of a cache (rows per (b, h) from cap / rcap).
+size_t section_bytes(const kvq_int4_cache* c, int i) {
+    const int64_t Tq = c->T - c->R, ldq = c->cap ? c->cap : Tq, ldr = c->rcap ? c->rcap : c->R;
+    const size_t bh = (size_t)(c->B * c->H), d = (size_t)c->d;
+    switch (i) {
+    case 0: case 3: return bh * (size_t)ldq * d / 2;
+    case 1: case 2: return bh * (size_t)cdiv(ldq, c->g) * d * 2;
+    case 4: case 5: return bh * (size_t)ldq * (d / (size_t)c->g) * 2;
+    default: return bh * (size_t)ldr * d * 2;
+    }
+}
+
+const void* section_ptr(const kvq_int4_cache* c, int i) {
+    const void* p[8] = {c->k_codes, c->k_scale, c->k_zero, c->v_codes, c->v_scale, c->v_zero, c->k_res, c->v_res};
+    return p[i];
+}
+
+}  // namespace
+}  // namespace kvq
+
+extern "C" int kvq_int4_evict(const kvq_int4_cache* src, const int32_t* keep, const kvq_int4_cache* dst,
+                              kvq_stream stream) {
+    int rc = kvq::check_cache_shape(src, "kvq_int4_evict (src)");
+    if (rc) return rc;
+    rc = kvq::check_cache_shape(dst, "kvq_int4_evict (dst)");
+    if (rc) return rc;
+    KVQ_REQUIRE(keep, "kvq_int4_evict: NULL keep");
+    KVQ_REQUIRE(dst->B == src->B && dst->H == src->H && dst->d == src->d && dst->g == src->g,
+                "kvq_int4_evict: dst must have the B, H, d, g of src");
+    KVQ_REQUIRE(dst->T <= src->T, "kvq_int4_evict: dst->T (kept tokens, %lld) must be <= src->T (%lld)",
+                (long long)dst->T, (long long)src->T);
+    // the destination is written while the source is read: no section may overlap
+    for (int i = 0; i < 8; ++i) {
+        const size_t nd = kvq::section_bytes(dst, i);
+        const uintptr_t d0 = reinterpret_cast<uintptr_t>(kvq::section_ptr(dst, i));
+        if (!nd || !d0) continue;
+        for (int k = 0; k < 8; ++k) {
+            const size_t ns = kvq::section_bytes(src, k);
+            const uintptr_t s0 = reinterpret_cast<uintptr_t>(kvq::section_ptr(src, k));
+            if (!ns || !s0) continue;
+            KVQ_REQUIRE(d0 + nd <= s0 || s0 + ns <= d0, "kvq_int4_evict: dst section %d overlaps src section %d", i,
+                        k);
+        }
+    }
+    kvq::EvGeom geo;
+    geo.T = src->T;
+    geo.H = src->H;
+    geo.Tq = src->T - src->R;
+    geo.ldq = src->cap ? src->cap : geo.Tq;
+    geo.ldk = kvq::cdiv(geo.ldq, src->g);
+    geo.ldr = src->rcap ? src->rcap : src->R;
+    geo.K = dst->T;
+    geo.R2 = dst->R;
+    geo.Tq2 = dst->T - dst->R;
+    geo.dldq = dst->cap ? dst->cap : geo.Tq2;
+    geo.dldk = kvq::cdiv(geo.dldq, dst->g);
+    geo.dldr = dst->rcap ? dst->rcap : dst->R;
+    geo.nKb = kvq::cdiv(geo.Tq2, src->g);
+    geo.nVb = kvq::cdiv(geo.Tq2, kvq::kTile);
+    geo.nRb = kvq::cdiv(geo.R2, kvq::kTile);
+    const int64_t nblk = src->B * src->H * (geo.nKb + geo.nVb + geo.nRb);
+    KVQ_REQUIRE(nblk < ((int64_t)1 << 31), "kvq_int4_evict: grid too large");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    KVQ_DISPATCH_DG(src->d, src->g, kvq::launch_evict, *src, keep, *dst, geo, nblk, st);
+    return kvq::launch_status("kvq_int4_evict");
+}

@@ -13,9 +13,7 @@
 // of bf16, one 4-byte store of packed codes); the 256 threads cover 2048/d rows per pass.
 // Block order is (b, token block, h) with h fastest, so concurrently running blocks
 // read neighbouring token rows of the [B][T][H][d] input.
-#include <cfloat>
-
-#include "kvq_internal.h"
+#include "int4_common.h"
 
 namespace kvq {
 namespace {
@@ -23,112 +21,6 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kVTile = 64;   // tokens per V tile
 constexpr int kResTile = 64; // tokens per residual tile
-
-struct I4Geom {
-    int64_t B, T, H, d, g, R, Tq;
-    int64_t nKg;   // K groups per (b, h) = ceil(Tq / g)
-    int64_t nVt;   // V tiles per (b, h) = ceil(Tq / 64)
-    int64_t nRt;   // residual tiles per (b, h) = ceil(R / 64)
-    int64_t ldq;   // quantized-token rows per (b, h) in the sections (cap, or Tq)
-    int64_t ldk;   // K group rows per (b, h) in the sections = ceil(ldq / g)
-    int64_t ldr;   // residual rows per (b, h) in the sections (rcap, or R)
-    int64_t sb, st, sh;   // element strides of the quantizer's input over b, token, h ([B][T][H][d]: T*H*d, H*d, d)
-};
-
-struct I4Ptrs {
-    uint8_t* k_codes;
-    uint16_t* k_scale;
-    uint16_t* k_zero;
-    uint8_t* v_codes;
-    uint16_t* v_scale;
-    uint16_t* v_zero;
-    uint16_t* k_res;
-    uint16_t* v_res;
-};
-
-// (b, j, h) of block index u in a [B][n][H] ordering with h fastest, in 32-bit arithmetic
-// (block counts fit 31 bits; 64-bit division costs several times more instructions)
-struct Bjh {
-    int64_t b, j, h;
-};
-__device__ __forceinline__ Bjh split_bjh(uint32_t u, uint32_t H, uint32_t n) {
-    const uint32_t q = u / H;
-    return Bjh{(int64_t)(q / n), (int64_t)(q % n), (int64_t)(u - q * H)};
-}
-
-__device__ __forceinline__ void unpack8(const uint4 a, float (&v)[8]) {
-    v[0] = bf_lo(a.x); v[1] = bf_hi(a.x); v[2] = bf_lo(a.y); v[3] = bf_hi(a.y);
-    v[4] = bf_lo(a.z); v[5] = bf_hi(a.z); v[6] = bf_lo(a.w); v[7] = bf_hi(a.w);
-}
-
-// Per-group parameters from the group's min and max:
-//   s = smallest bf16 >= max(max - min, 1e-8) / 15, z = bf16(round(0 - min / s)).
-struct GroupParams {
-    float s, r, z;
-    uint16_t sb, zb;
-};
-
-__device__ __forceinline__ GroupParams group_params(float mn, float mx) {
-    GroupParams p;
-    float range = mx - mn;
-    range = vmax2(range, 1e-8f);
-    p.sb = bf_ceil_pos(range / 15.0f);
-    p.s = bf_to_f(p.sb);
-    // 0 - m: the backend lowers a subtraction from +0 to a negation, which turns m = +0 into
-    // -0; IEEE gives 0 - (+-0) = +0, so the zero quotient is handled explicitly
-    const float m = mn / p.s;
-    const float zr = (m == 0.0f) ? 0.0f : __builtin_rintf(-m);
-    p.zb = f_to_bf(zr);
-    p.z = bf_to_f(p.zb);
-    p.r = 1.0f / p.s;
-    return p;
-}
-
-// q = clip(round(x / s) + z, 0, 15) with IEEE-division semantics, for 8 elements.
-// Fast path (z in [0, 15], so |x / s| <= 31 for every x of the group):
-// w = fma(x, 1/s, z) lies within 4e-6 of x/s + z and fl(x/s) within 2e-6 of x/s, so
-// unless x/s + z is within 1e-5 of a half-integer, rint(w) = rint(fl(x/s)) + z;
-// otherwise |w - rint(w)| > 0.4999 and the true division decides (this also settles
-// exact ties, which round half to even on x/s before z is added).  The fallback sits
-// behind one branch per 8 elements; groups with z outside [0, 15] always take it:
-// rint(x/s) + z is then an fp32 sum of two integers, exact whenever the result can
-// fall in [0, 15] (Sterbenz) and far outside otherwise.
-template <bool UNIFORM>
-__device__ __forceinline__ void codes8(const float (&x)[8], const float (&s)[8], const float (&r)[8],
-                                       const float (&z)[8], bool fast, float (&q)[8]) {
-    float n[8];
-    bool slow = !fast;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        const float w = __builtin_fmaf(x[k], r[k], z[k]);
-        n[k] = __builtin_rintf(w);
-        slow |= __builtin_fabsf(w - n[k]) > 0.4999f;
-    }
-    if (slow) {
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const float w = __builtin_fmaf(x[k], r[k], z[k]);
-            if (!fast || __builtin_fabsf(w - __builtin_rintf(w)) > 0.4999f)
-                n[k] = __builtin_rintf(x[k] / s[k]) + z[k];
-        }
-    }
-#pragma unroll
-    for (int k = 0; k < 8; ++k) q[k] = vclamp(n[k], 0.0f, 15.0f);
-}
-
-// 8 codes (as floats in [0, 15]) -> one dword, byte j = code(2j) | code(2j+1) << 4.
-__device__ __forceinline__ uint32_t pack_codes(const float (&q)[8]) {
-    uint32_t even = 0, odd = 0;
-    even = __builtin_amdgcn_cvt_pk_u8_f32(q[0], 0, even);
-    even = __builtin_amdgcn_cvt_pk_u8_f32(q[2], 1, even);
-    even = __builtin_amdgcn_cvt_pk_u8_f32(q[4], 2, even);
-    even = __builtin_amdgcn_cvt_pk_u8_f32(q[6], 3, even);
-    odd = __builtin_amdgcn_cvt_pk_u8_f32(q[1], 0, odd);
-    odd = __builtin_amdgcn_cvt_pk_u8_f32(q[3], 1, odd);
-    odd = __builtin_amdgcn_cvt_pk_u8_f32(q[5], 2, odd);
-    odd = __builtin_amdgcn_cvt_pk_u8_f32(q[7], 3, odd);
-    return even | (odd << 4);
-}
 
 template <int D, int G>
 __global__ void __launch_bounds__(kThreads) int4_quant_kernel(const uint16_t* __restrict__ K,
@@ -472,17 +364,6 @@ void launch_dequant(bool is_k, int ot, const kvq_int4_cache* c, const I4Geom& g,
     }
 }
 
-#define KVQ_DISPATCH_DG(d, g, FN, ...)                                        \
-    do {                                                                      \
-        if (d == 64 && g == 32) FN<64, 32>(__VA_ARGS__);                      \
-        else if (d == 64 && g == 64) FN<64, 64>(__VA_ARGS__);                 \
-        else if (d == 128 && g == 32) FN<128, 32>(__VA_ARGS__);               \
-        else if (d == 128 && g == 64) FN<128, 64>(__VA_ARGS__);               \
-        else if (d == 128 && g == 128) FN<128, 128>(__VA_ARGS__);             \
-        else if (d == 256 && g == 32) FN<256, 32>(__VA_ARGS__);               \
-        else if (d == 256 && g == 64) FN<256, 64>(__VA_ARGS__);               \
-        else FN<256, 128>(__VA_ARGS__);                                       \
-    } while (0)
 
 }  // namespace
 

@@ -23,7 +23,7 @@ KVQ_FMT_PER_CHANNEL, KVQ_FMT_INT4_K, KVQ_FMT_INT4_V = 1, 2, 3
 EXPORTED = [
     "kvq_last_error", "kvq_abi_version",
     "kvq_quant_pc_ws", "kvq_quant_sym", "kvq_quant_asym",
-    "kvq_int4_cache_sizes", "kvq_group_quant_int4", "kvq_int4_append", "kvq_dequant",
+    "kvq_int4_cache_sizes", "kvq_group_quant_int4", "kvq_int4_append", "kvq_int4_evict", "kvq_dequant",
     "kvq_err_stats_ws", "kvq_err_stats", "kvq_stats_finalize",
     "kvq_compression_ratio", "kvq_int4_bytes", "kvq_token_ratio", "kvq_total_gain", "kvq_kv_bytes",
     "kvq_keep_count",
@@ -78,6 +78,7 @@ def lib():
     L.kvq_int4_cache_sizes.argtypes = [I64] * 6 + [P, P]
     L.kvq_group_quant_int4.argtypes = [P, P, P, P]
     L.kvq_int4_append.argtypes = [P, P, P, I64, I64, P]
+    L.kvq_int4_evict.argtypes = [P, P, P, P]
     L.kvq_dequant.argtypes = [P, P, I, P]
     L.kvq_err_stats_ws.argtypes = [I64]
     L.kvq_err_stats_ws.restype = SZ
@@ -304,6 +305,30 @@ def int4_append(cache: Int4Cache, k_new: torch.Tensor, v_new: torch.Tensor, r_ke
     _check(lib().kvq_int4_append(C.byref(desc), _p(k_new), _p(v_new), k_new.shape[1], r_keep, _stream(k_new)))
     cache.T, cache.R = int(desc.T), int(desc.R)
     return cache
+
+
+def int4_evict(cache: Int4Cache, keep: torch.Tensor, r2: int, out: Int4Cache | None = None) -> Int4Cache:
+    """Keep the tokens keep[b][h][:] (int32 [B][H][K], indices into the cache's T tokens) of every
+    (b, h): a new cache of K tokens whose last r2 are bf16.  Kept V rows and whole kept K groups
+    are copied; other K groups are requantized from their current values.  ``out`` (dense or
+    growable, not overlapping ``cache``) receives the result; its T and R become K and r2."""
+    _need_cuda(keep)
+    if keep.dtype != torch.int32 or keep.dim() != 3 or not keep.is_contiguous():
+        raise ValueError("keep must be contiguous int32 [B][H][K]")
+    if (keep.shape[0], keep.shape[1]) != (cache.B, cache.H):
+        raise ValueError("keep does not match the cache's B, H")
+    K = keep.shape[2]
+    if out is None:
+        out = Int4Cache.empty(cache.B, K, cache.H, cache.d, cache.g, r2, keep.device)
+        sd, dd = cache.desc(), out.desc()
+    else:
+        before = (out.T, out.R)
+        out.T, out.R = K, r2
+        sd, dd = cache.desc(), out.desc()
+        out.T, out.R = before
+    _check(lib().kvq_int4_evict(C.byref(sd), _p(keep), C.byref(dd), _stream(keep)))
+    out.T, out.R = K, r2
+    return out
 
 
 def dequant_int4(cache: Int4Cache, side: str, out_dtype=torch.bfloat16, out=None):

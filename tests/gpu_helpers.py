@@ -59,3 +59,28 @@ def assert_rel(got, want, rtol, what):
     den = np.maximum(np.abs(want), 1e-300)
     rel = np.abs(got - want) / den
     assert np.all(rel <= rtol), f"{what}: max rel err {rel.max():.3e} > {rtol} (got {got}, want {want})"
+
+
+def gpu_cache(c: dict, cap: int = 0, rcap: int = 0):
+    """An oracle cache dict uploaded as a kvq.Int4Cache (dense, or growable with cap / rcap rows)."""
+    from kv_cache_compression_channel_amd import kvq
+    B, T, H, d, g, R = (c[k] for k in ("B", "T", "H", "d", "g", "R"))
+    Tq = T - R
+    if cap or rcap:
+        cache = kvq.Int4Cache.empty_stream(B, H, d, g, cap, rcap, DEV)
+        cache.T, cache.R = T, R
+        for s in cache.SECTIONS:
+            cache.valid(s).copy_(_to_dev(c[s]))
+        return cache
+    cache = kvq.Int4Cache.empty(B, T, H, d, g, R, DEV)
+    for s in cache.SECTIONS:
+        getattr(cache, s).copy_(_to_dev(c[s]))
+    assert cache.k_codes.shape[2] == Tq
+    return cache
+
+
+def _to_dev(a: np.ndarray) -> torch.Tensor:
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(DEV)
+    return torch.from_numpy(a).to(DEV)

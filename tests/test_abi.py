@@ -144,6 +144,32 @@ def test_int4_growable_layout_validation(L):
     assert app(C.byref(d), MISALIGNED, FAKE, 1, 64, None) == kvq.KVQ_EALIGN
 
 
+def test_int4_evict_validation(L):
+    src = dict(T=512, R=64)
+    far = {f: 0x40000000 + 0x1000000 * i for i, f in enumerate(kvq.Int4Cache.SECTIONS)}
+    ev = L.kvq_int4_evict
+    cases = [
+        (src, dict(far, T=600, R=0)),                 # more kept tokens than src holds
+        (src, dict(far, T=128, R=129)),               # R2 > K
+        (src, dict(far, T=128, R=0, d=64)),           # d differs
+        (src, dict(far, T=128, R=0, g=32)),           # g differs
+        (src, dict(far, T=128, R=0, H=3)),            # H differs
+        (src, dict(T=128, R=0)),                      # dst sections overlap the src sections
+        (src, dict(far, T=128, R=0, cap=64)),         # dst cap below its quantized rows
+        (dict(src, cap=100), dict(far, T=128, R=0)),  # src cap not a multiple of g
+    ]
+    for skw, dkw in cases:
+        s_, d_ = _desc(**skw), _desc(**dkw)
+        assert ev(C.byref(s_), FAKE, C.byref(d_), None) == kvq.KVQ_EINVAL, (skw, dkw)
+        assert L.kvq_last_error()
+    s_, d_ = _desc(**src), _desc(**dict(far, T=128, R=0))
+    assert ev(C.byref(s_), None, C.byref(d_), None) == kvq.KVQ_EINVAL
+    assert ev(None, FAKE, C.byref(d_), None) == kvq.KVQ_EINVAL
+    assert ev(C.byref(s_), FAKE, None, None) == kvq.KVQ_EINVAL
+    d_ = _desc(**dict(far, T=128, R=0, k_codes=0x40000008))
+    assert ev(C.byref(s_), FAKE, C.byref(d_), None) == kvq.KVQ_EALIGN
+
+
 def test_int4_validation(L):
     bad = [dict(d=96), dict(d=32), dict(g=16), dict(g=256), dict(d=64, g=128), dict(R=129), dict(R=-1),
            dict(B=0), dict(T=0), dict(H=0), dict(k_codes=None), dict(v_zero=None)]

@@ -17,7 +17,7 @@ import torch
 
 import oracle
 from kv_cache_compression_channel_amd import kvq, synth
-from tests.gpu_helpers import ATTN_ROW_RTOL, DEV, cache_np, need_gpu, np_, say, u16
+from tests.gpu_helpers import ATTN_ROW_RTOL, DEV, assert_bits_equal, gpu_cache, need_gpu, np_, say, u16
 
 pytestmark = pytest.mark.gpu
 
@@ -48,14 +48,16 @@ def run_attn(B, T, H, Hq, d, g, R, seed, sm_scale=None, q_scale=1.0, k_gain=1.0)
 
 
 def check_attn(K, V, q, g, R, sm):
-    """Quantize bf16 K, V [B][T][H][d], attend with q [B][Hq][d] on the GPU, compare with the oracle."""
+    """The oracle's INT4 cache of bf16 K, V [B][T][H][d], uploaded; attend with q [B][Hq][d] on the
+    GPU and compare with the oracle's attention over the same cache."""
     B, T, H, d = K.shape
     Hq = q.shape[1]
-    cache = kvq.group_quant_int4(K.to(DEV), V.to(DEV), g=g, R=R)
+    want = oracle.int4_quant(u16(K), u16(V), g, R)
+    cache = gpu_cache(want)
     out32 = kvq.decode_attn_int4(cache, q.to(DEV), sm, out_dtype=torch.float32)
     out16 = kvq.decode_attn_int4(cache, q.to(DEV), sm, out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
-    ref = oracle.decode_attn(cache_np(cache), u16(q), sm)
+    ref = oracle.decode_attn(want, u16(q), sm)
     got = np_(out32).astype(np.float64)
     err = row_rel_err(got.reshape(B * Hq, d), ref.reshape(B * Hq, d))
     assert err.max() <= ATTN_ROW_RTOL, f"max row rel err {err.max():.3e}"
@@ -118,7 +120,6 @@ def test_config4_full_size_sampled_rows():
     K, V, _ = synth.kv_layer(B, T, H, d, seed=0, device=DEV, n_outlier=0)
     q = synth.decode_query(B, Hq, d, seed=1, device=DEV)
     cache = kvq.group_quant_int4(K, V, g=g, R=R)
-    del K, V
     out = kvq.decode_attn_int4(cache, q, 1.0, out_dtype=torch.float32)
     out16 = kvq.decode_attn_int4(cache, q, 1.0)
     torch.cuda.synchronize()
@@ -129,10 +130,12 @@ def test_config4_full_size_sampled_rows():
                   {(0, 0), (B - 1, Hq - 1)})
     for (b, hq) in rows:
         h = hq // (Hq // H)
-        # copy the (b, h) slice of every section and ask the oracle for this row
-        sl = {s: getattr(cache, s)[b:b + 1, h:h + 1] for s in kvq.Int4Cache.SECTIONS}
-        sub = {s: (u16(t) if t.dtype == torch.bfloat16 else np_(t)) for s, t in sl.items()}
-        sub.update(B=1, T=T, H=1, d=d, g=g, R=R)
+        # the oracle quantizes the (b, h) input slice; the GPU cache must hold exactly that
+        # slice, and the oracle attends over its own copy
+        sub = oracle.int4_quant(u16(K[b:b + 1, :, h:h + 1]), u16(V[b:b + 1, :, h:h + 1]), g, R)
+        for s in kvq.Int4Cache.SECTIONS:
+            t = getattr(cache, s)[b:b + 1, h:h + 1]
+            assert_bits_equal(u16(t) if t.dtype == torch.bfloat16 else np_(t), sub[s], f"cache slice ({b},{h}) {s}")
         qrow = u16(q[b:b + 1, hq:hq + 1])
         ref = oracle.decode_attn(sub, qrow, 1.0)[0, 0]
         err = row_rel_err(got[b, hq][None], ref[None])[0]
