@@ -254,6 +254,26 @@ int kvq_decode_attn_int4(const kvq_int4_cache* c, const void* q, int64_t Hq, flo
                          int ot, void* ws, size_t ws_bytes, kvq_stream stream);
 
 /* ======================================================================
+ * Decode attention with running H2O scores  [Walkthrough §3.1: a token's score
+ * is the attention it has received, summed over the observed steps; applied one
+ * decode step at a time; the attention itself as kvq_decode_attn_int4]
+ *
+ * out as kvq_decode_attn_int4 (bit for bit).  In addition, for every b, KV head h
+ * and token t < T:
+ *   acc[b][h][t] += sum over the Hq/H query heads hq of h (in hq order, fp32) of
+ *                   p[b][hq][t] = softmax weight of token t in row (b, hq),
+ * one fp32 addition per element.  acc: fp32 (device), row (b, h) at acc +
+ * (b*H + h) * ld_acc; elements t >= T are not touched, so a caller can keep one
+ * array for a growing cache (ld_acc = capacity) and evict with its rows.
+ * Workspace (device): kvq_decode_attn_int4_h2o_ws(c, Hq) bytes (the attention's,
+ * plus the per-token logits of every query head and each row's softmax max and sum).
+ * EINVAL: as kvq_decode_attn_int4; NULL acc; ld_acc < T.  EALIGN: acc not 16-byte aligned.
+ * ====================================================================== */
+size_t kvq_decode_attn_int4_h2o_ws(const kvq_int4_cache* c, int64_t Hq);
+int kvq_decode_attn_int4_h2o(const kvq_int4_cache* c, const void* q, int64_t Hq, float sm_scale, void* out, int ot,
+                             float* acc, int64_t ld_acc, void* ws, size_t ws_bytes, kvq_stream stream);
+
+/* ======================================================================
  * H2O / SnapKV token selection  [Walkthrough §3.1-§3.3]
  *
  * kvq_h2o_select: hist fp32 [rows][T_obs][T] (device).  score[j] = sum over t of

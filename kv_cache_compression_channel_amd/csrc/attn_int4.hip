@@ -24,7 +24,7 @@
 namespace kvq {
 int check_cache_shape(const kvq_int4_cache* c, const char* name);
 void launch_attn_mfma(const kvq_int4_cache* c, const void* q, int64_t Hq, float qscale, float* ws, int nsplit,
-                      int64_t split_len, int nslot, hipStream_t st);
+                      int64_t split_len, int nslot, float* lgw, int64_t ldl, hipStream_t st);
 int res_splits(int64_t R);
 
 namespace {
@@ -46,6 +46,9 @@ struct AttnArgs {
     void* out;
     int ot;
     float* ws;
+    float* lgw;                   // base-2 logits [B][Hq][ldl], or NULL
+    float* ml;                    // per (b, hq): final max logit and sum of 2^(logit - max), or NULL
+    int64_t ldl;
     int64_t B, T, H, R, Tq, nKg, Hq;
     int64_t ldq, ldk, ldr;        // rows per (b, h) of the code / V-scale, K-group and residual sections
     int64_t range_lo, range_hi;   // token range this launch covers
@@ -152,6 +155,10 @@ __global__ void __launch_bounds__(kThreads) attn_split_kernel(const AttnArgs a) 
         for (int off = 1; off < LPT; off *= 2)
 #pragma unroll
             for (int qi = 0; qi < NQ; ++qi) logit[qi] += __shfl_xor(logit[qi], off);
+        if (a.lgw && valid && li == 0) {
+#pragma unroll
+            for (int qi = 0; qi < NQ; ++qi) a.lgw[(b * a.Hq + h * NQ + qi) * a.ldl + t] = logit[qi];
+        }
 
         float p[NQ];
 #pragma unroll
@@ -247,7 +254,7 @@ __global__ void __launch_bounds__(kThreads) attn_split_kernel(const AttnArgs a) 
 // slots with every slot's weight taken from the lane that holds it.
 template <int D, int OT>
 __global__ void __launch_bounds__(256) attn_combine_kernel(const float* __restrict__ ws, int nslot, int64_t rows,
-                                                          void* __restrict__ out) {
+                                                          void* __restrict__ out, float* __restrict__ ml) {
     constexpr int CPL = D / 64;     // channels per lane
     const int lane = threadIdx.x % 64;
     const int64_t row = (int64_t)blockIdx.x * 4 + threadIdx.x / 64;   // b * Hq + hq
@@ -294,6 +301,7 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(const float* __restri
     }
 #pragma unroll
     for (int off = 32; off >= 1; off /= 2) L += __shfl_xor(L, off);
+    if (ml && lane == 0) *reinterpret_cast<float2*>(ml + 2 * row) = make_float2(M, L);
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
         const int c = lane + 64 * j;
@@ -303,6 +311,56 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(const float* __restri
         else
             static_cast<uint16_t*>(out)[row * D + c] = f_to_bf(o);
     }
+}
+
+// Decode-time H2O scores: acc[b][h][t] += sum over the NQ query heads n of KV head h of
+// 2^(lgw[b][h*NQ+n][t] - M_n) / L_n, the attention weight of token t in this step (summed over n in
+// order, in fp32, then added to acc once).  Four consecutive tokens per thread; the logit rows
+// are 16-byte aligned (ldl % 4 == 0).
+template <int NQ>
+__global__ void __launch_bounds__(256) h2o_accum_kernel(const float* __restrict__ lgw, const float* __restrict__ ml,
+                                                       float* __restrict__ acc, int64_t ldl, int64_t ld_acc, int64_t H,
+                                                       int64_t Hq, int64_t T, int nchunk) {
+    const int64_t bh = blockIdx.x / nchunk;
+    const int64_t b = bh / H, h = bh % H;
+    const int64_t t = ((int64_t)(blockIdx.x % nchunk) * 256 + threadIdx.x) * 4;
+    if (t >= T) return;
+    float M[NQ], L[NQ];
+#pragma unroll
+    for (int n = 0; n < NQ; ++n) {
+        const float2 v = *reinterpret_cast<const float2*>(ml + 2 * (b * Hq + h * NQ + n));
+        M[n] = v.x;
+        L[n] = v.y;
+    }
+    float s[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int n = 0; n < NQ; ++n) {
+        const float4 x = *reinterpret_cast<const float4*>(lgw + (b * Hq + h * NQ + n) * ldl + t);
+        s[0] += exp2f(x.x - M[n]) / L[n];
+        s[1] += exp2f(x.y - M[n]) / L[n];
+        s[2] += exp2f(x.z - M[n]) / L[n];
+        s[3] += exp2f(x.w - M[n]) / L[n];
+    }
+    float* ar = acc + bh * ld_acc + t;
+    const int nt = (int)min<int64_t>(4, T - t);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        if (i < nt) ar[i] += s[i];
+}
+
+void launch_h2o_accum(const AttnArgs& a, float* acc, int64_t ld_acc, int nq, hipStream_t st) {
+    const int nchunk = (int)cdiv(a.T, 1024);
+    const dim3 grid((unsigned)(a.B * a.H * nchunk)), blk(256);
+#define KVQ_ACC(NQ_) hipLaunchKernelGGL((h2o_accum_kernel<NQ_>), grid, blk, 0, st, a.lgw, a.ml, acc, a.ldl, ld_acc, \
+                                        a.H, a.Hq, a.T, nchunk)
+    switch (nq) {
+        case 1: KVQ_ACC(1); break;
+        case 2: KVQ_ACC(2); break;
+        case 4: KVQ_ACC(4); break;
+        case 8: KVQ_ACC(8); break;
+        default: KVQ_ACC(16); break;
+    }
+#undef KVQ_ACC
 }
 
 // How the token axis is cut.  d = 128: the INT4 tokens [0, Tq) go to the matrix-core kernel
@@ -358,9 +416,9 @@ void launch_combine(const AttnArgs& a, hipStream_t st) {
     const int64_t rows = a.B * a.Hq;
     const dim3 grid((unsigned)cdiv(rows, 4)), blk(256);
     if (a.ot == KVQ_FP32)
-        hipLaunchKernelGGL((attn_combine_kernel<D, KVQ_FP32>), grid, blk, 0, st, a.ws, a.nslot, rows, a.out);
+        hipLaunchKernelGGL((attn_combine_kernel<D, KVQ_FP32>), grid, blk, 0, st, a.ws, a.nslot, rows, a.out, a.ml);
     else
-        hipLaunchKernelGGL((attn_combine_kernel<D, KVQ_BF16>), grid, blk, 0, st, a.ws, a.nslot, rows, a.out);
+        hipLaunchKernelGGL((attn_combine_kernel<D, KVQ_BF16>), grid, blk, 0, st, a.ws, a.nslot, rows, a.out, a.ml);
 }
 
 template <int D, int GS>
@@ -402,27 +460,38 @@ size_t kvq_decode_attn_int4_ws(const kvq_int4_cache* c, int64_t Hq) {
     return (size_t)(c->B * Hq * p.nslot * (c->d + 2)) * sizeof(float);
 }
 
-int kvq_decode_attn_int4(const kvq_int4_cache* c, const void* q, int64_t Hq, float sm_scale, void* out, int ot,
-                         void* ws, size_t ws_bytes, kvq_stream stream) {
-    const int rc = kvq::check_cache_shape(c, "kvq_decode_attn_int4");
+}  // extern "C"
+
+namespace kvq {
+namespace {
+
+// Logit rows of the H2O variant: 16-byte aligned, after the split partials in the workspace.
+int64_t logit_ld(int64_t T) { return cdiv(T, 4) * 4; }
+size_t h2o_ws_offset(const kvq_int4_cache* c, int64_t Hq) {
+    return (size_t)cdiv((int64_t)kvq_decode_attn_int4_ws(c, Hq), 256) * 256;
+}
+
+// Shared body of the two decode-attention entry points; acc == NULL: plain attention.
+int decode_attn(const char* name, const kvq_int4_cache* c, const void* q, int64_t Hq, float sm_scale, void* out,
+                int ot, float* acc, int64_t ld_acc, void* ws, size_t ws_bytes, size_t ws_need, hipStream_t st) {
+    const int rc = check_cache_shape(c, name);
     if (rc) return rc;
-    KVQ_REQUIRE(q && out, "kvq_decode_attn_int4: NULL q or out");
-    KVQ_REQUIRE(ot == KVQ_FP32 || ot == KVQ_BF16, "kvq_decode_attn_int4: ot must be KVQ_FP32 or KVQ_BF16");
-    KVQ_REQUIRE(Hq >= 1 && Hq % c->H == 0, "kvq_decode_attn_int4: Hq (%lld) must be a multiple of H (%lld)",
-                (long long)Hq, (long long)c->H);
+    KVQ_REQUIRE(q && out, "%s: NULL q or out", name);
+    KVQ_REQUIRE(ot == KVQ_FP32 || ot == KVQ_BF16, "%s: ot must be KVQ_FP32 or KVQ_BF16", name);
+    KVQ_REQUIRE(Hq >= 1 && Hq % c->H == 0, "%s: Hq (%lld) must be a multiple of H (%lld)", name, (long long)Hq,
+                (long long)c->H);
     const int64_t nq = Hq / c->H;
     KVQ_REQUIRE(nq == 1 || nq == 2 || nq == 4 || nq == 8 || nq == 16,
-                "kvq_decode_attn_int4: Hq / H must be 1, 2, 4, 8 or 16 (got %lld)", (long long)nq);
-    KVQ_REQUIRE(ws && ws_bytes >= kvq_decode_attn_int4_ws(c, Hq), "kvq_decode_attn_int4: workspace of %zu bytes needed",
-                kvq_decode_attn_int4_ws(c, Hq));
-    KVQ_REQUIRE(c->T <= ((int64_t)1 << 30), "kvq_decode_attn_int4: T must be at most 2^30 tokens");
+                "%s: Hq / H must be 1, 2, 4, 8 or 16 (got %lld)", name, (long long)nq);
+    KVQ_REQUIRE(ws && ws_bytes >= ws_need, "%s: workspace of %zu bytes needed", name, ws_need);
+    KVQ_REQUIRE(c->T <= ((int64_t)1 << 30), "%s: T must be at most 2^30 tokens", name);
     KVQ_REQUIRE_ALIGNED(q, "q");
     KVQ_REQUIRE_ALIGNED(out, "out");
     KVQ_REQUIRE_ALIGNED(ws, "ws");
-    const kvq::SplitPlan p = kvq::plan_splits(c->B, c->H, c->T, c->R, c->d, c->g);
+    const SplitPlan p = plan_splits(c->B, c->H, c->T, c->R, c->d, c->g);
     KVQ_REQUIRE(c->B * c->H * p.nslot < ((int64_t)1 << 31) && c->B * Hq * p.nslot < ((int64_t)1 << 31),
-                "kvq_decode_attn_int4: grid too large");
-    kvq::AttnArgs a;
+                "%s: grid too large", name);
+    AttnArgs a;
     a.k_codes = c->k_codes; a.k_scale = c->k_scale; a.k_zero = c->k_zero;
     a.v_codes = c->v_codes; a.v_scale = c->v_scale; a.v_zero = c->v_zero;
     a.k_res = c->k_res; a.v_res = c->v_res;
@@ -430,27 +499,60 @@ int kvq_decode_attn_int4(const kvq_int4_cache* c, const void* q, int64_t Hq, flo
     a.out = out;
     a.ot = ot;
     a.ws = static_cast<float*>(ws);
+    a.lgw = nullptr;
+    a.ml = nullptr;
+    a.ldl = logit_ld(c->T);
+    if (acc) {
+        a.lgw = reinterpret_cast<float*>(static_cast<char*>(ws) + h2o_ws_offset(c, Hq));
+        a.ml = a.lgw + c->B * Hq * a.ldl;
+    }
     a.B = c->B; a.T = c->T; a.H = c->H; a.R = c->R; a.Tq = c->T - c->R;
-    a.nKg = kvq::cdiv(a.Tq, c->g);
+    a.nKg = cdiv(a.Tq, c->g);
     a.ldq = c->cap ? c->cap : a.Tq;
-    a.ldk = kvq::cdiv(a.ldq, c->g);
+    a.ldk = cdiv(a.ldq, c->g);
     a.ldr = c->rcap ? c->rcap : c->R;
     a.Hq = Hq;
     a.nslot = p.nslot;
     a.qscale = sm_scale * 1.4426950408889634f;
-    hipStream_t st = static_cast<hipStream_t>(stream);
     if (p.mfma) {
-        kvq::launch_attn_mfma(c, q, Hq, a.qscale, a.ws, p.nsplit_q, p.len_q, p.nslot, st);
+        launch_attn_mfma(c, q, Hq, a.qscale, a.ws, p.nsplit_q, p.len_q, p.nslot, a.lgw, a.ldl, st);
     } else {
         a.range_lo = 0;
         a.range_hi = c->T;
         a.split_len = p.len_v;
         a.nsplit = p.nsplit_v;
         a.slot_off = 0;
-        kvq::dispatch(a, c->d, c->g, (int)nq, st);
+        dispatch(a, c->d, c->g, (int)nq, st);
     }
-    kvq::dispatch_combine(a, c->d, st);
-    return kvq::launch_status("kvq_decode_attn_int4");
+    dispatch_combine(a, c->d, st);
+    if (acc) launch_h2o_accum(a, acc, ld_acc, (int)nq, st);
+    return launch_status(name);
+}
+
+}  // namespace
+}  // namespace kvq
+
+extern "C" {
+
+int kvq_decode_attn_int4(const kvq_int4_cache* c, const void* q, int64_t Hq, float sm_scale, void* out, int ot,
+                         void* ws, size_t ws_bytes, kvq_stream stream) {
+    return kvq::decode_attn("kvq_decode_attn_int4", c, q, Hq, sm_scale, out, ot, nullptr, 0, ws, ws_bytes,
+                            kvq_decode_attn_int4_ws(c, Hq), static_cast<hipStream_t>(stream));
+}
+
+size_t kvq_decode_attn_int4_h2o_ws(const kvq_int4_cache* c, int64_t Hq) {
+    const size_t base = kvq_decode_attn_int4_ws(c, Hq);
+    if (!base) return 0;
+    return kvq::h2o_ws_offset(c, Hq) + (size_t)(c->B * Hq * (kvq::logit_ld(c->T) + 2)) * sizeof(float);
+}
+
+int kvq_decode_attn_int4_h2o(const kvq_int4_cache* c, const void* q, int64_t Hq, float sm_scale, void* out, int ot,
+                             float* acc, int64_t ld_acc, void* ws, size_t ws_bytes, kvq_stream stream) {
+    KVQ_REQUIRE(acc, "kvq_decode_attn_int4_h2o: NULL acc");
+    KVQ_REQUIRE(c && ld_acc >= c->T, "kvq_decode_attn_int4_h2o: ld_acc must be >= T");
+    KVQ_REQUIRE_ALIGNED(acc, "acc");
+    return kvq::decode_attn("kvq_decode_attn_int4_h2o", c, q, Hq, sm_scale, out, ot, acc, ld_acc, ws, ws_bytes,
+                            kvq_decode_attn_int4_h2o_ws(c, Hq), static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -72,6 +72,8 @@ struct MfmaArgs {
     const uint16_t* v_res;
     const uint16_t* q;
     float* ws;
+    float* lgw;              // base-2 logits [B][Hq][ldl] (token t of head (b, hq) at row * ldl + t), or NULL
+    int64_t ldl;
     int64_t B, H, Hq;
     int Tq, nKg;
     int64_t ldq, ldk, ldr;   // rows per (b, h) of the code / V-scale, K-group and residual sections
@@ -131,7 +133,7 @@ struct ResLds {
     float m[16], l[16];
 };
 
-template <int NQ>
+template <int NQ, bool LG>
 __device__ void residual_block(const MfmaArgs& a, ResLds& sr, int rb) {
     const int tid = threadIdx.x, lane = tid % 64, wv = tid / 64;
     const int64_t bh = rb / a.nres;
@@ -174,6 +176,7 @@ __device__ void residual_block(const MfmaArgs& a, ResLds& sr, int rb) {
           }
         }
         sr.p[n][t] = acc;
+        if constexpr (LG) a.lgw[(b * a.Hq + h * NQ + n) * a.ldl + a.Tq + r_lo + t] = acc;
     }
     __syncthreads();
     // softmax over the split: one wave per query, lanes over tokens
@@ -218,7 +221,7 @@ __device__ void residual_block(const MfmaArgs& a, ResLds& sr, int rb) {
     }
 }
 
-template <int GS, int NQ>
+template <int GS, int NQ, bool LG>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 attn_mfma_kernel(const MfmaArgs a) {
     constexpr int NG = D / GS;          // V groups per token
@@ -248,7 +251,7 @@ attn_mfma_kernel(const MfmaArgs a) {
 
     const int nres_blocks = (int)(a.B * a.H) * a.nres;
     if ((int)blockIdx.x < nres_blocks) {      // uniform per block
-        residual_block<NQ>(a, sm.rs, (int)blockIdx.x);
+        residual_block<NQ, LG>(a, sm.rs, (int)blockIdx.x);
         return;
     }
     const int blk = (int)blockIdx.x - nres_blocks;
@@ -496,6 +499,25 @@ attn_mfma_kernel(const MfmaArgs a) {
             lg[i] = __builtin_fmaf(sc[0][i], lscale, -c0);
             lg[4 + i] = __builtin_fmaf(sc[1][i], lscale, -c0);
         }
+        if constexpr (LG) {
+            // the base-2 logits themselves (lg + ref), for the valid tokens of the real queries
+            if (n < NQ) {
+                float* lrow = a.lgw + (b * a.Hq + h * NQ + n) * a.ldl + t0;
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf) {
+                    const int tb = 16 * hf + 4 * G;
+                    const float x0 = lg[4 * hf] + ref, x1 = lg[4 * hf + 1] + ref;
+                    const float x2 = lg[4 * hf + 2] + ref, x3 = lg[4 * hf + 3] + ref;
+                    if (tb + 3 < nvalid) {
+                        *reinterpret_cast<float4*>(lrow + tb) = make_float4(x0, x1, x2, x3);
+                    } else {
+                        if (tb < nvalid) lrow[tb] = x0;
+                        if (tb + 1 < nvalid) lrow[tb + 1] = x1;
+                        if (tb + 2 < nvalid) lrow[tb + 2] = x2;
+                    }
+                }
+            }
+        }
         if (nvalid < kTile) {   // only the last tile of a range is partial
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -703,16 +725,23 @@ attn_mfma_kernel(const MfmaArgs a) {
     }
 }
 
-template <int GS>
+template <int GS, bool LG>
 void launch_nq(const MfmaArgs& a, int nq, hipStream_t st) {
     const dim3 grid((unsigned)(a.B * a.H * (a.nsplit + a.nres))), blk(kThreads);
     switch (nq) {
-        case 1: hipLaunchKernelGGL((attn_mfma_kernel<GS, 1>), grid, blk, 0, st, a); break;
-        case 2: hipLaunchKernelGGL((attn_mfma_kernel<GS, 2>), grid, blk, 0, st, a); break;
-        case 4: hipLaunchKernelGGL((attn_mfma_kernel<GS, 4>), grid, blk, 0, st, a); break;
-        case 8: hipLaunchKernelGGL((attn_mfma_kernel<GS, 8>), grid, blk, 0, st, a); break;
-        default: hipLaunchKernelGGL((attn_mfma_kernel<GS, 16>), grid, blk, 0, st, a); break;
+        case 1: hipLaunchKernelGGL((attn_mfma_kernel<GS, 1, LG>), grid, blk, 0, st, a); break;
+        case 2: hipLaunchKernelGGL((attn_mfma_kernel<GS, 2, LG>), grid, blk, 0, st, a); break;
+        case 4: hipLaunchKernelGGL((attn_mfma_kernel<GS, 4, LG>), grid, blk, 0, st, a); break;
+        case 8: hipLaunchKernelGGL((attn_mfma_kernel<GS, 8, LG>), grid, blk, 0, st, a); break;
+        default: hipLaunchKernelGGL((attn_mfma_kernel<GS, 16, LG>), grid, blk, 0, st, a); break;
     }
+}
+
+template <bool LG>
+void launch_g(const MfmaArgs& a, int64_t g, int nq, hipStream_t st) {
+    if (g == 32) launch_nq<32, LG>(a, nq, st);
+    else if (g == 64) launch_nq<64, LG>(a, nq, st);
+    else launch_nq<128, LG>(a, nq, st);
 }
 
 }  // namespace
@@ -721,9 +750,10 @@ int res_splits(int64_t R) { return (int)cdiv(R, kResTile); }
 
 // Launch the INT4 token range [0, Tq) on the matrix cores (d = 128) and the bf16 residual
 // [Tq, T) in blocks of the same grid.  Partials go to ws slots 0 .. nsplit-1 (INT4) and
-// nsplit .. nsplit + res_splits(R) - 1 (residual) of each (b, hq); nslot is their sum.
+// nsplit .. nsplit + res_splits(R) - 1 (residual) of each (b, hq); nslot is their sum.  With lgw,
+// every token's base-2 logit also goes to lgw[(b * Hq + hq) * ldl + t].
 void launch_attn_mfma(const kvq_int4_cache* c, const void* q, int64_t Hq, float qscale, float* ws, int nsplit,
-                      int64_t split_len, int nslot, hipStream_t st) {
+                      int64_t split_len, int nslot, float* lgw, int64_t ldl, hipStream_t st) {
     MfmaArgs a;
     a.k_codes = c->k_codes; a.k_scale = c->k_scale; a.k_zero = c->k_zero;
     a.v_codes = c->v_codes; a.v_scale = c->v_scale; a.v_zero = c->v_zero;
@@ -732,6 +762,8 @@ void launch_attn_mfma(const kvq_int4_cache* c, const void* q, int64_t Hq, float 
     a.nres = res_splits(c->R);
     a.q = static_cast<const uint16_t*>(q);
     a.ws = ws;
+    a.lgw = lgw;
+    a.ldl = ldl;
     a.B = c->B; a.H = c->H; a.Hq = Hq;
     a.Tq = (int)(c->T - c->R); a.nKg = (int)cdiv(a.Tq, c->g);
     a.ldq = c->cap ? c->cap : a.Tq;
@@ -742,9 +774,8 @@ void launch_attn_mfma(const kvq_int4_cache* c, const void* q, int64_t Hq, float 
     a.nslot = nslot;
     a.qscale = qscale;
     const int nq = (int)(Hq / c->H);
-    if (c->g == 32) launch_nq<32>(a, nq, st);
-    else if (c->g == 64) launch_nq<64>(a, nq, st);
-    else launch_nq<128>(a, nq, st);
+    if (lgw) launch_g<true>(a, c->g, nq, st);
+    else launch_g<false>(a, c->g, nq, st);
 }
 
 }  // namespace kvq

@@ -27,7 +27,7 @@ EXPORTED = [
     "kvq_err_stats_ws", "kvq_err_stats", "kvq_stats_finalize",
     "kvq_compression_ratio", "kvq_int4_bytes", "kvq_token_ratio", "kvq_total_gain", "kvq_kv_bytes",
     "kvq_keep_count",
-    "kvq_decode_attn_int4_ws", "kvq_decode_attn_int4",
+    "kvq_decode_attn_int4_ws", "kvq_decode_attn_int4", "kvq_decode_attn_int4_h2o_ws", "kvq_decode_attn_int4_h2o",
     "kvq_select_ws", "kvq_h2o_select", "kvq_snapkv_select", "kvq_compact",
 ]
 
@@ -97,6 +97,9 @@ def lib():
     L.kvq_decode_attn_int4_ws.argtypes = [P, I64]
     L.kvq_decode_attn_int4_ws.restype = SZ
     L.kvq_decode_attn_int4.argtypes = [P, P, I64, C.c_float, P, I, P, SZ, P]
+    L.kvq_decode_attn_int4_h2o_ws.argtypes = [P, I64]
+    L.kvq_decode_attn_int4_h2o_ws.restype = SZ
+    L.kvq_decode_attn_int4_h2o.argtypes = [P, P, I64, C.c_float, P, I, P, I64, P, SZ, P]
     L.kvq_select_ws.argtypes = [I64, I64]
     L.kvq_select_ws.restype = SZ
     L.kvq_h2o_select.argtypes = [P, I64, I64, I64, I64, I64, P, P, P, SZ, P]
@@ -414,6 +417,27 @@ def decode_attn_int4(cache: Int4Cache, q: torch.Tensor, sm_scale: float = 1.0, o
     w, wb = _ws(int(lib().kvq_decode_attn_int4_ws(C.byref(desc), Hq)), q.device, ws)
     _check(lib().kvq_decode_attn_int4(C.byref(desc), _p(q), Hq, float(sm_scale), _p(out), _dt(out), _p(w), wb,
                                       _stream(q)))
+    return out
+
+
+def decode_attn_int4_h2o(cache: Int4Cache, q: torch.Tensor, acc: torch.Tensor, sm_scale: float = 1.0, out=None,
+                         ws=None, out_dtype=torch.bfloat16):
+    """Decode attention (as decode_attn_int4) that also adds this step's attention weights to the
+    running H2O scores: acc fp32 [B][H][L] with L >= cache.T, updated in place for t < cache.T
+    (the weights of the Hq/H query heads of a KV head summed)."""
+    _need_cuda(q, acc)
+    if q.dtype != torch.bfloat16 or not q.is_contiguous():
+        raise TypeError("q must be a contiguous bfloat16 [B][Hq][d] tensor")
+    if acc.dtype != torch.float32 or acc.dim() != 3 or not acc.is_contiguous() or \
+            acc.shape[0] != cache.B or acc.shape[1] != cache.H:
+        raise ValueError("acc must be contiguous float32 [B][H][L]")
+    B, Hq, d = q.shape
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=out_dtype, device=q.device)
+    desc = cache.desc()
+    w, wb = _ws(int(lib().kvq_decode_attn_int4_h2o_ws(C.byref(desc), Hq)), q.device, ws)
+    _check(lib().kvq_decode_attn_int4_h2o(C.byref(desc), _p(q), Hq, float(sm_scale), _p(out), _dt(out), _p(acc),
+                                          acc.shape[2], _p(w), wb, _stream(q)))
     return out
 
 

@@ -217,6 +217,22 @@ def test_attn_validation(L):
     assert L.kvq_decode_attn_int4_ws(None, 4) == 0
 
 
+def test_attn_h2o_validation(L):
+    d = _desc(H=8)                                   # T = 128
+    f = L.kvq_decode_attn_int4_h2o
+    big = 1 << 30
+    assert f(C.byref(d), FAKE, 32, 1.0, FAKE, 1, None, 128, FAKE, big, None) == kvq.KVQ_EINVAL      # NULL acc
+    assert f(C.byref(d), FAKE, 32, 1.0, FAKE, 1, FAKE, 127, FAKE, big, None) == kvq.KVQ_EINVAL      # ld_acc < T
+    assert f(C.byref(d), FAKE, 32, 1.0, FAKE, 1, MISALIGNED, 128, FAKE, big, None) == kvq.KVQ_EALIGN
+    assert f(C.byref(d), FAKE, 12, 1.0, FAKE, 1, FAKE, 128, FAKE, big, None) == kvq.KVQ_EINVAL      # Hq % H
+    assert f(None, FAKE, 32, 1.0, FAKE, 1, FAKE, 128, FAKE, big, None) == kvq.KVQ_EINVAL
+    # the workspace covers the attention's and the logits of every query head
+    need = L.kvq_decode_attn_int4_h2o_ws(C.byref(d), 32)
+    assert need >= L.kvq_decode_attn_int4_ws(C.byref(d), 32) + 32 * 128 * 4
+    assert f(C.byref(d), FAKE, 32, 1.0, FAKE, 1, FAKE, 128, FAKE, need - 1, None) == kvq.KVQ_EINVAL
+    assert L.kvq_decode_attn_int4_h2o_ws(None, 4) == 0
+
+
 def test_select_and_compact_validation(L):
     big = 1 << 30
     h2o = L.kvq_h2o_select
