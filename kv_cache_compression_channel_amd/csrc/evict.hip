@@ -13,13 +13,14 @@
 //   - a window token that lands in the quantized part is quantized like a new token;
 //   - a new window row holds the current value rounded to the nearest bf16.
 //
-// One launch, three kinds of block, each over one (b, h) (block order (b, tile, h), h fastest):
-//   K blocks: one new K group (g tokens x d channels).  The keep indices go to LDS; one
-//     block-wide vote decides "whole old group" (copy 16-byte rows) or requantize: every lane
-//     owns 8 channels of RPP-strided rows, dequantizes them into registers, and the group's
-//     min/max, parameters and codes follow the quantizer's steps.
-//   V blocks: 64 new quantized rows; per row, copy codes + scale/zero or quantize the bf16 row
-//     (the g-channel groups reduce across g/8 lanes with shuffles; no LDS).
+// One launch, two kinds of block, each over one (b, h) (block order (b, tile, h), h fastest):
+//   group blocks: the g new quantized tokens of one new K group, K and V.  The keep indices go
+//     to LDS; one block-wide vote decides "whole old group".  Every lane owns 8 channels of
+//     RPP-strided rows and issues the loads of all its rows before using any (the 4-bit rows
+//     unconditionally, from the clamped row, so no load waits behind a branch).  V rows are
+//     copied or, for window tokens, quantized (the g-channel groups reduce across g/8 lanes
+//     with shuffles).  K is copied when whole, else the rows are dequantized in registers and
+//     the group's min/max, parameters and codes follow the quantizer's steps.
 //   window blocks: 64 new bf16 rows; copy, or dequantize and round to bf16.
 // Keep indices outside [0, T) are clamped into it: the result is then unspecified, but no
 // access leaves the source sections.
@@ -36,7 +37,7 @@ struct EvGeom {
     int64_t ldq, ldk, ldr;            // source rows per (b, h): codes / V params, K params, window
     int64_t K, Tq2, R2;               // kept tokens, of which quantized / window
     int64_t dldq, dldk, dldr;         // destination rows per (b, h)
-    int64_t nKb, nVb, nRb;            // blocks per (b, h) of each kind
+    int64_t nKb, nRb;                 // blocks per (b, h) of each kind
 };
 
 __device__ __forceinline__ int64_t clamp_tok(int32_t t, int64_t T) {
@@ -53,40 +54,62 @@ __device__ __forceinline__ void unpack_codes8(uint32_t w, float (&c)[8]) {
     }
 }
 
-// Current K values of channels 8*lane .. 8*lane+7 of source token t: (q - z) * s rounded once
-// (q*s and z*s are exact in fp32, so the fma rounds the exact value once), or the bf16 window.
+// Raw source data of one kept token for one lane (8 channels): the 4-bit path (codes, K group
+// scale/zero, V scale/zero of the lane's V group) read from the quantized row min(t, Tq - 1), and
+// the bf16 rows when t is a window token.  The quantized loads carry no condition, so a thread
+// issues those of all its rows before it uses any.
+struct RowRaw {
+    uint32_t kc, vc;
+    uint4 ks, kz, kr, vr;
+    uint16_t vs, vz;
+};
+
 template <int D, int G>
-__device__ __forceinline__ void k_values(const kvq_int4_cache& s, const EvGeom& geo, int64_t bh, int64_t t,
-                                         int lane, float (&v)[8]) {
-    if (t < geo.Tq) {
-        const uint32_t w = *reinterpret_cast<const uint32_t*>(s.k_codes + (bh * geo.ldq + t) * (D / 2) + 4 * lane);
-        const int64_t mi = (bh * geo.ldk + t / G) * D + 8 * lane;
+__device__ __forceinline__ void load_quantized(const kvq_int4_cache& s, const EvGeom& geo, int64_t bh, int64_t t,
+                                               int lane, RowRaw& r) {
+    const int64_t tq = t < geo.Tq ? t : geo.Tq - 1;
+    r.kc = *reinterpret_cast<const uint32_t*>(s.k_codes + (bh * geo.ldq + tq) * (D / 2) + 4 * lane);
+    r.vc = *reinterpret_cast<const uint32_t*>(s.v_codes + (bh * geo.ldq + tq) * (D / 2) + 4 * lane);
+    const int64_t mk = (bh * geo.ldk + tq / G) * D + 8 * lane;
+    r.ks = *reinterpret_cast<const uint4*>(s.k_scale + mk);
+    r.kz = *reinterpret_cast<const uint4*>(s.k_zero + mk);
+    const int64_t mv = (bh * geo.ldq + tq) * (D / G) + (8 * lane) / G;
+    r.vs = s.v_scale[mv];
+    r.vz = s.v_zero[mv];
+}
+
+template <int D>
+__device__ __forceinline__ void load_window(const kvq_int4_cache& s, const EvGeom& geo, int64_t bh, int64_t t,
+                                            int lane, RowRaw& r) {
+    const int64_t o = (bh * geo.ldr + (t - geo.Tq)) * D + 8 * lane;
+    r.kr = *reinterpret_cast<const uint4*>(s.k_res + o);
+    r.vr = *reinterpret_cast<const uint4*>(s.v_res + o);
+}
+
+// Current values (fp32) of the lane's 8 channels: (q - z) * s rounded once (q*s and z*s are
+// exact in fp32, so the fma rounds the exact value once), or the bf16 window values.
+__device__ __forceinline__ void k_values(const RowRaw& r, bool quantized, float (&v)[8]) {
+    if (quantized) {
         float sc[8], zf[8], c[8];
-        unpack8(*reinterpret_cast<const uint4*>(s.k_scale + mi), sc);
-        unpack8(*reinterpret_cast<const uint4*>(s.k_zero + mi), zf);
-        unpack_codes8(w, c);
+        unpack8(r.ks, sc);
+        unpack8(r.kz, zf);
+        unpack_codes8(r.kc, c);
 #pragma unroll
         for (int k = 0; k < 8; ++k) v[k] = __builtin_fmaf(c[k], sc[k], -zf[k] * sc[k]);
     } else {
-        unpack8(*reinterpret_cast<const uint4*>(s.k_res + (bh * geo.ldr + (t - geo.Tq)) * D + 8 * lane), v);
+        unpack8(r.kr, v);
     }
 }
 
-// Same for V (one scale and zero per g channels of the token).
-template <int D, int G>
-__device__ __forceinline__ void v_values(const kvq_int4_cache& s, const EvGeom& geo, int64_t bh, int64_t t,
-                                         int lane, float (&v)[8]) {
-    if (t < geo.Tq) {
-        const uint32_t w = *reinterpret_cast<const uint32_t*>(s.v_codes + (bh * geo.ldq + t) * (D / 2) + 4 * lane);
-        const int64_t mi = (bh * geo.ldq + t) * (D / G) + (8 * lane) / G;
-        const float sc = bf_to_f(s.v_scale[mi]);
-        const float zs = -bf_to_f(s.v_zero[mi]) * sc;
+__device__ __forceinline__ void v_values(const RowRaw& r, bool quantized, float (&v)[8]) {
+    if (quantized) {
+        const float sc = bf_to_f(r.vs), zs = -bf_to_f(r.vz) * sc;
         float c[8];
-        unpack_codes8(w, c);
+        unpack_codes8(r.vc, c);
 #pragma unroll
         for (int k = 0; k < 8; ++k) v[k] = __builtin_fmaf(c[k], sc, zs);
     } else {
-        unpack8(*reinterpret_cast<const uint4*>(s.v_res + (bh * geo.ldr + (t - geo.Tq)) * D + 8 * lane), v);
+        unpack8(r.vr, v);
     }
 }
 
@@ -101,10 +124,10 @@ __global__ void __launch_bounds__(kThreads) int4_evict_kernel(const kvq_int4_cac
     const int tid = threadIdx.x, lane = tid % LPR, rg = tid / LPR, wave = tid / 64;
     const uint32_t H = (uint32_t)geo.H;
     uint32_t bid = blockIdx.x;
-    const uint32_t nK = (uint32_t)(src.B * geo.nKb * geo.H), nV = (uint32_t)(src.B * geo.nVb * geo.H);
+    const uint32_t nK = (uint32_t)(src.B * geo.nKb * geo.H);
 
     if (bid < nK) {
-        // ------------------------------ one new K group ------------------------------
+        // ------------- one new K group and the V rows of the same G tokens -------------
         static_assert(G % RPP == 0, "tile shape");
         constexpr int NR = G / RPP;
         __shared__ int32_t s_keep[G];
@@ -123,11 +146,76 @@ __global__ void __launch_bounds__(kThreads) int4_evict_kernel(const kvq_int4_cac
         }
         const bool whole = __syncthreads_and(run) && first < geo.Tq && first % G == 0 &&
                            n == (int)min<int64_t>(G, geo.Tq - first);
+
+        // loads of every row this thread handles (rows past the group repeat row 0)
+        RowRaw raw[NR];
+        int64_t tok[NR];
+        bool anyw = false;
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+            const int r = rg + RPP * i;
+            tok[i] = s_keep[r < n ? r : 0];
+            anyw |= tok[i] >= geo.Tq;
+        }
+        if (geo.Tq > 0) {
+#pragma unroll
+            for (int i = 0; i < NR; ++i) load_quantized<D, G>(src, geo, bh, tok[i], lane, raw[i]);
+        }
+        if (anyw) {
+#pragma unroll
+            for (int i = 0; i < NR; ++i)
+                if (tok[i] >= geo.Tq) load_window<D>(src, geo, bh, tok[i], lane, raw[i]);
+        }
+
+        // V rows: a quantized row keeps codes, scale and zero; a window row is quantized.  The
+        // group reduction runs for every row (the G/8 lanes of a group share the row, so the
+        // shuffles never cross rows), the result is used for window rows only.
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+            const int r = rg + RPP * i;
+            const bool q = tok[i] < geo.Tq;
+            float x[8];
+            v_values(raw[i], q, x);
+            float mn = FLT_MAX, mx = -FLT_MAX;
+            minmax8(x, mn, mx);
+#pragma unroll
+            for (int off = 1; off < LPG; off *= 2) {
+                mn = vmin2(mn, __shfl_xor(mn, off));
+                mx = vmax2(mx, __shfl_xor(mx, off));
+            }
+            if (r < n) {
+                uint8_t* crow = dst.v_codes + (bh * geo.dldq + i0 + r) * (D / 2);
+                const int64_t dmi = (bh * geo.dldq + i0 + r) * NGD + (8 * lane) / G;
+                if (q) {
+                    *reinterpret_cast<uint32_t*>(crow + 4 * lane) = raw[i].vc;
+                    if (lane % LPG == 0) {
+                        dst.v_scale[dmi] = raw[i].vs;
+                        dst.v_zero[dmi] = raw[i].vz;
+                    }
+                } else {
+                    const GroupParams gp = group_params(mn, mx);
+                    if (lane % LPG == 0) {
+                        dst.v_scale[dmi] = gp.sb;
+                        dst.v_zero[dmi] = gp.zb;
+                    }
+                    const bool fast = gp.z >= 0.0f && gp.z <= 15.0f;
+                    const float ps8[8] = {gp.s, gp.s, gp.s, gp.s, gp.s, gp.s, gp.s, gp.s};
+                    const float pr8[8] = {gp.r, gp.r, gp.r, gp.r, gp.r, gp.r, gp.r, gp.r};
+                    const float pz8[8] = {gp.z, gp.z, gp.z, gp.z, gp.z, gp.z, gp.z, gp.z};
+                    float qv[8];
+                    codes8<true>(x, ps8, pr8, pz8, fast, qv);
+                    *reinterpret_cast<uint32_t*>(crow + 4 * lane) = pack_codes(qv);
+                }
+            }
+        }
+
         if (whole) {
-            // codes rows first .. first+n-1 -> rows i0 .. i0+n-1 (contiguous in both), 16 B per lane
-            const uint4* cs = reinterpret_cast<const uint4*>(src.k_codes + (bh * geo.ldq + first) * (D / 2));
-            uint4* cd = reinterpret_cast<uint4*>(dst.k_codes + (bh * geo.dldq + i0) * (D / 2));
-            for (int e = tid; e < n * (D / 32); e += kThreads) cd[e] = cs[e];
+            // the K group is one old group: its codes (in the loaded rows) and its scale/zero row
+#pragma unroll
+            for (int i = 0; i < NR; ++i) {
+                const int r = rg + RPP * i;
+                if (r < n) *reinterpret_cast<uint32_t*>(dst.k_codes + (bh * geo.dldq + i0 + r) * (D / 2) + 4 * lane) = raw[i].kc;
+            }
             const int64_t si = (bh * geo.ldk + first / G) * D, di = (bh * geo.dldk + j) * D;
             for (int e = tid; e < D / 8; e += kThreads) {
                 reinterpret_cast<uint4*>(dst.k_scale + di)[e] = reinterpret_cast<const uint4*>(src.k_scale + si)[e];
@@ -141,9 +229,7 @@ __global__ void __launch_bounds__(kThreads) int4_evict_kernel(const kvq_int4_cac
         for (int k = 0; k < 8; ++k) { mn[k] = FLT_MAX; mx[k] = -FLT_MAX; }
 #pragma unroll
         for (int i = 0; i < NR; ++i) {
-            const int r = rg + RPP * i;
-            // rows past the group repeat row 0 of this lane, which leaves min and max unchanged
-            k_values<D, G>(src, geo, bh, s_keep[r < n ? r : 0], lane, v[i]);
+            k_values(raw[i], tok[i] < geo.Tq, v[i]);
 #pragma unroll
             for (int k = 0; k < 8; ++k) { mn[k] = vmin2(mn[k], v[i][k]); mx[k] = vmax2(mx[k], v[i][k]); }
         }
@@ -191,53 +277,6 @@ __global__ void __launch_bounds__(kThreads) int4_evict_kernel(const kvq_int4_cac
         return;
     }
     bid -= nK;
-    if (bid < nV) {
-        // ------------------------------ 64 new V rows ------------------------------
-        const Bjh ix = split_bjh(bid, H, (uint32_t)geo.nVb);
-        const int64_t bh = ix.b * geo.H + ix.h, i0 = ix.j * kTile;
-        const int n = (int)min<int64_t>(kTile, geo.Tq2 - i0);
-        const int32_t* kp = keep + bh * geo.K + i0;
-        const int grp = (8 * lane) / G;
-        for (int r = rg; r < n; r += RPP) {
-            const int64_t t = clamp_tok(kp[r], geo.T), i = i0 + r;
-            uint8_t* crow = dst.v_codes + (bh * geo.dldq + i) * (D / 2);
-            const int64_t dmi = (bh * geo.dldq + i) * NGD;
-            if (t < geo.Tq) {
-                *reinterpret_cast<uint32_t*>(crow + 4 * lane) =
-                    *reinterpret_cast<const uint32_t*>(src.v_codes + (bh * geo.ldq + t) * (D / 2) + 4 * lane);
-                if (lane < NGD) {
-                    const int64_t smi = (bh * geo.ldq + t) * NGD + lane;
-                    dst.v_scale[dmi + lane] = src.v_scale[smi];
-                    dst.v_zero[dmi + lane] = src.v_zero[smi];
-                }
-            } else {
-                float x[8];
-                unpack8(*reinterpret_cast<const uint4*>(src.v_res + (bh * geo.ldr + (t - geo.Tq)) * D + 8 * lane), x);
-                float mn = FLT_MAX, mx = -FLT_MAX;
-                minmax8(x, mn, mx);
-                // the LPG lanes of a group are consecutive and take this branch together (same row)
-#pragma unroll
-                for (int off = 1; off < LPG; off *= 2) {
-                    mn = vmin2(mn, __shfl_xor(mn, off));
-                    mx = vmax2(mx, __shfl_xor(mx, off));
-                }
-                const GroupParams gp = group_params(mn, mx);
-                if (lane % LPG == 0) {
-                    dst.v_scale[dmi + grp] = gp.sb;
-                    dst.v_zero[dmi + grp] = gp.zb;
-                }
-                const bool fast = gp.z >= 0.0f && gp.z <= 15.0f;
-                const float ps8[8] = {gp.s, gp.s, gp.s, gp.s, gp.s, gp.s, gp.s, gp.s};
-                const float pr8[8] = {gp.r, gp.r, gp.r, gp.r, gp.r, gp.r, gp.r, gp.r};
-                const float pz8[8] = {gp.z, gp.z, gp.z, gp.z, gp.z, gp.z, gp.z, gp.z};
-                float q[8];
-                codes8<true>(x, ps8, pr8, pz8, fast, q);
-                *reinterpret_cast<uint32_t*>(crow + 4 * lane) = pack_codes(q);
-            }
-        }
-        return;
-    }
-    bid -= nV;
     {
         // ------------------------------ 64 new window rows ------------------------------
         const Bjh ix = split_bjh(bid, H, (uint32_t)geo.nRb);
@@ -252,9 +291,11 @@ __global__ void __launch_bounds__(kThreads) int4_evict_kernel(const kvq_int4_cac
                 *reinterpret_cast<uint4*>(dst.k_res + o) = *reinterpret_cast<const uint4*>(src.k_res + si);
                 *reinterpret_cast<uint4*>(dst.v_res + o) = *reinterpret_cast<const uint4*>(src.v_res + si);
             } else {
+                RowRaw rr;
+                load_quantized<D, G>(src, geo, bh, t, lane, rr);
                 float a[8], b[8];
-                k_values<D, G>(src, geo, bh, t, lane, a);
-                v_values<D, G>(src, geo, bh, t, lane, b);
+                k_values(rr, true, a);
+                v_values(rr, true, b);
                 *reinterpret_cast<uint4*>(dst.k_res + o) =
                     make_uint4(pack_bf2(a[0], a[1]), pack_bf2(a[2], a[3]), pack_bf2(a[4], a[5]), pack_bf2(a[6], a[7]));
                 *reinterpret_cast<uint4*>(dst.v_res + o) =
@@ -328,9 +369,8 @@ extern "C" int kvq_int4_evict(const kvq_int4_cache* src, const int32_t* keep, co
     geo.dldk = kvq::cdiv(geo.dldq, dst->g);
     geo.dldr = dst->rcap ? dst->rcap : dst->R;
     geo.nKb = kvq::cdiv(geo.Tq2, src->g);
-    geo.nVb = kvq::cdiv(geo.Tq2, kvq::kTile);
     geo.nRb = kvq::cdiv(geo.R2, kvq::kTile);
-    const int64_t nblk = src->B * src->H * (geo.nKb + geo.nVb + geo.nRb);
+    const int64_t nblk = src->B * src->H * (geo.nKb + geo.nRb);
     KVQ_REQUIRE(nblk < ((int64_t)1 << 31), "kvq_int4_evict: grid too large");
     hipStream_t st = static_cast<hipStream_t>(stream);
     KVQ_DISPATCH_DG(src->d, src->g, kvq::launch_evict, *src, keep, *dst, geo, nblk, st);

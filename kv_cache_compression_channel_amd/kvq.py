@@ -404,6 +404,11 @@ def decode_attn_ws_bytes(cache: Int4Cache, Hq: int) -> int:
     return int(lib().kvq_decode_attn_int4_ws(C.byref(desc), Hq))
 
 
+def decode_attn_h2o_ws_bytes(cache: Int4Cache, Hq: int) -> int:
+    desc = cache.desc()
+    return int(lib().kvq_decode_attn_int4_h2o_ws(C.byref(desc), Hq))
+
+
 def decode_attn_int4(cache: Int4Cache, q: torch.Tensor, sm_scale: float = 1.0, out=None, ws=None,
                      out_dtype=torch.bfloat16):
     """q bf16 [B][Hq][d] -> out [B][Hq][d] (bf16 = the fp32 result rounded to nearest even, or fp32)."""
