@@ -54,36 +54,34 @@ __device__ __forceinline__ void unpack_codes8(uint32_t w, float (&c)[8]) {
     }
 }
 
-// Raw source data of one kept token for one lane (8 channels): the 4-bit path (codes, K group
-// scale/zero, V scale/zero of the lane's V group) read from the quantized row min(t, Tq - 1), and
-// the bf16 rows when t is a window token.  The quantized loads carry no condition, so a thread
-// issues those of all its rows before it uses any.
+// Raw source data of one kept token for one lane (8 channels), loaded without a branch: the
+// codes and the V scale/zero from the quantized row min(t, Tq - 1) (unused for a window
+// token), and two 16-byte words whose address depends on the token: the K group scale and
+// zero rows for a quantized token, its bf16 K and V rows for a window token.
 struct RowRaw {
     uint32_t kc, vc;
-    uint4 ks, kz, kr, vr;
+    uint4 a, b;        // quantized: K scale, K zero;  window: K row, V row
     uint16_t vs, vz;
 };
 
 template <int D, int G>
-__device__ __forceinline__ void load_quantized(const kvq_int4_cache& s, const EvGeom& geo, int64_t bh, int64_t t,
-                                               int lane, RowRaw& r) {
-    const int64_t tq = t < geo.Tq ? t : geo.Tq - 1;
-    r.kc = *reinterpret_cast<const uint32_t*>(s.k_codes + (bh * geo.ldq + tq) * (D / 2) + 4 * lane);
-    r.vc = *reinterpret_cast<const uint32_t*>(s.v_codes + (bh * geo.ldq + tq) * (D / 2) + 4 * lane);
-    const int64_t mk = (bh * geo.ldk + tq / G) * D + 8 * lane;
-    r.ks = *reinterpret_cast<const uint4*>(s.k_scale + mk);
-    r.kz = *reinterpret_cast<const uint4*>(s.k_zero + mk);
-    const int64_t mv = (bh * geo.ldq + tq) * (D / G) + (8 * lane) / G;
-    r.vs = s.v_scale[mv];
-    r.vz = s.v_zero[mv];
-}
-
-template <int D>
-__device__ __forceinline__ void load_window(const kvq_int4_cache& s, const EvGeom& geo, int64_t bh, int64_t t,
-                                            int lane, RowRaw& r) {
-    const int64_t o = (bh * geo.ldr + (t - geo.Tq)) * D + 8 * lane;
-    r.kr = *reinterpret_cast<const uint4*>(s.k_res + o);
-    r.vr = *reinterpret_cast<const uint4*>(s.v_res + o);
+__device__ __forceinline__ void load_row(const kvq_int4_cache& s, const EvGeom& geo, int64_t bh, int64_t t, int lane,
+                                         RowRaw& r) {
+    const bool q = t < geo.Tq;
+    if (geo.Tq > 0) {   // uniform: with no quantized tokens the 4-bit sections may be empty
+        const int64_t tq = q ? t : geo.Tq - 1;
+        r.kc = *reinterpret_cast<const uint32_t*>(s.k_codes + (bh * geo.ldq + tq) * (D / 2) + 4 * lane);
+        r.vc = *reinterpret_cast<const uint32_t*>(s.v_codes + (bh * geo.ldq + tq) * (D / 2) + 4 * lane);
+        const int64_t mv = (bh * geo.ldq + tq) * (D / G) + (8 * lane) / G;
+        r.vs = s.v_scale[mv];
+        r.vz = s.v_zero[mv];
+    }
+    const int64_t mk = (bh * geo.ldk + (q ? t / G : 0)) * D + 8 * lane;         // quantized token
+    const int64_t mr = (bh * geo.ldr + (q ? 0 : t - geo.Tq)) * D + 8 * lane;    // window token
+    const uint16_t* pa = q ? s.k_scale + mk : s.k_res + mr;
+    const uint16_t* pb = q ? s.k_zero + mk : s.v_res + mr;
+    r.a = *reinterpret_cast<const uint4*>(pa);
+    r.b = *reinterpret_cast<const uint4*>(pb);
 }
 
 // Current values (fp32) of the lane's 8 channels: (q - z) * s rounded once (q*s and z*s are
@@ -91,13 +89,13 @@ __device__ __forceinline__ void load_window(const kvq_int4_cache& s, const EvGeo
 __device__ __forceinline__ void k_values(const RowRaw& r, bool quantized, float (&v)[8]) {
     if (quantized) {
         float sc[8], zf[8], c[8];
-        unpack8(r.ks, sc);
-        unpack8(r.kz, zf);
+        unpack8(r.a, sc);
+        unpack8(r.b, zf);
         unpack_codes8(r.kc, c);
 #pragma unroll
         for (int k = 0; k < 8; ++k) v[k] = __builtin_fmaf(c[k], sc[k], -zf[k] * sc[k]);
     } else {
-        unpack8(r.kr, v);
+        unpack8(r.a, v);
     }
 }
 
@@ -109,7 +107,7 @@ __device__ __forceinline__ void v_values(const RowRaw& r, bool quantized, float 
 #pragma unroll
         for (int k = 0; k < 8; ++k) v[k] = __builtin_fmaf(c[k], sc, zs);
     } else {
-        unpack8(r.vr, v);
+        unpack8(r.b, v);
     }
 }
 
@@ -130,7 +128,6 @@ __global__ void __launch_bounds__(kThreads) int4_evict_kernel(const kvq_int4_cac
         // ------------- one new K group and the V rows of the same G tokens -------------
         static_assert(G % RPP == 0, "tile shape");
         constexpr int NR = G / RPP;
-        __shared__ int32_t s_keep[G];
         __shared__ float s_mn[NW * D], s_mx[NW * D];
         __shared__ float s_ps[D], s_pr[D], s_pz[D];
         const Bjh ix = split_bjh(bid, H, (uint32_t)geo.nKb);
@@ -138,34 +135,21 @@ __global__ void __launch_bounds__(kThreads) int4_evict_kernel(const kvq_int4_cac
         const int n = (int)min<int64_t>(G, geo.Tq2 - i0);
         const int32_t* kp = keep + bh * geo.K + i0;
         const int64_t first = clamp_tok(kp[0], geo.T);
-        int run = 1;
-        for (int i = tid; i < n; i += kThreads) {
-            const int64_t t = clamp_tok(kp[i], geo.T);
-            s_keep[i] = (int32_t)t;
-            run &= (t == first + i);
-        }
-        const bool whole = __syncthreads_and(run) && first < geo.Tq && first % G == 0 &&
-                           n == (int)min<int64_t>(G, geo.Tq - first);
-
-        // loads of every row this thread handles (rows past the group repeat row 0)
+        // this thread's rows (rows past the group repeat row 0), then all of their loads; the
+        // block-wide "whole old group" vote waits until the loads are in flight
         RowRaw raw[NR];
         int64_t tok[NR];
-        bool anyw = false;
+        int run = 1;
 #pragma unroll
         for (int i = 0; i < NR; ++i) {
             const int r = rg + RPP * i;
-            tok[i] = s_keep[r < n ? r : 0];
-            anyw |= tok[i] >= geo.Tq;
+            tok[i] = clamp_tok(kp[r < n ? r : 0], geo.T);
+            run &= (r >= n) || (tok[i] == first + r);
         }
-        if (geo.Tq > 0) {
 #pragma unroll
-            for (int i = 0; i < NR; ++i) load_quantized<D, G>(src, geo, bh, tok[i], lane, raw[i]);
-        }
-        if (anyw) {
-#pragma unroll
-            for (int i = 0; i < NR; ++i)
-                if (tok[i] >= geo.Tq) load_window<D>(src, geo, bh, tok[i], lane, raw[i]);
-        }
+        for (int i = 0; i < NR; ++i) load_row<D, G>(src, geo, bh, tok[i], lane, raw[i]);
+        const bool whole = __syncthreads_and(run) && first < geo.Tq && first % G == 0 &&
+                           n == (int)min<int64_t>(G, geo.Tq - first);
 
         // V rows: a quantized row keeps codes, scale and zero; a window row is quantized.  The
         // group reduction runs for every row (the G/8 lanes of a group share the row, so the
@@ -292,7 +276,7 @@ __global__ void __launch_bounds__(kThreads) int4_evict_kernel(const kvq_int4_cac
                 *reinterpret_cast<uint4*>(dst.v_res + o) = *reinterpret_cast<const uint4*>(src.v_res + si);
             } else {
                 RowRaw rr;
-                load_quantized<D, G>(src, geo, bh, t, lane, rr);
+                load_row<D, G>(src, geo, bh, t, lane, rr);
                 float a[8], b[8];
                 k_values(rr, true, a);
                 v_values(rr, true, b);
