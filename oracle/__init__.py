@@ -59,6 +59,14 @@ def _declare(L):
     L.orc_decode_attn.argtypes = [P] * 8 + [I64] * 6 + [P, I64, C.c_double, P]
     L.orc_decode_attn_rows.argtypes = [P] * 8 + [I64] * 6 + [P, I64, C.c_double, P, P, I64, P, P]
     L.orc_int4_evict.argtypes = [P] * 8 + [I64] * 6 + [P, I64, I64] + [P] * 8
+    L.orc_rotate_f32.argtypes = [P, P, I64, I64, P]
+    L.orc_rotate_f32.restype = None
+    L.orc_unrotate_f32.argtypes = [P, P, I64, I64, P]
+    L.orc_unrotate_f32.restype = None
+    L.orc_rot_quant.argtypes = [P, P] + [I64] * 5 + [P, P] + [P] * 6
+    L.orc_rot_dequant.argtypes = [P, P, P, P] + [I64] * 5 + [P]
+    L.orc_rot_dequant.restype = None
+    L.orc_rot_decode_attn.argtypes = [P] * 8 + [I64] * 5 + [P, I64, C.c_double, P]
     L.orc_colsum.argtypes = [P, I64, I64, I64, P]
     L.orc_colsum.restype = None
     L.orc_keep_count.argtypes = [I64, I64, I64]
@@ -328,6 +336,71 @@ def compact(src: np.ndarray, keep: np.ndarray):
     dst = np.empty((B, K, H, d), np.uint16)
     lib().orc_compact(_p(src), B, T, H, d, _p(keep), K, _p(dst))
     return dst
+
+
+# ----------------------------------------------- Hadamard-rotated cache ---
+
+def _signs(s, d):
+    s = np.ascontiguousarray(s, np.int8)
+    if s.shape != (d,) or not np.all(np.abs(s.astype(np.int64)) == 1):
+        raise ValueError("signs must be d entries in {+1, -1}")
+    return s
+
+
+def rotate(x: np.ndarray, signs: np.ndarray) -> np.ndarray:
+    """fp32 rows [..., d] -> (1/sqrt(d)) H (signs * x), fp32 butterflies in the fixed order."""
+    x = np.ascontiguousarray(x, np.float32)
+    d = x.shape[-1]
+    s = _signs(signs, d)
+    y = np.empty_like(x)
+    lib().orc_rotate_f32(_p(x), _p(s), x.size // d, d, _p(y))
+    return y
+
+
+def unrotate(y: np.ndarray, signs: np.ndarray) -> np.ndarray:
+    y = np.ascontiguousarray(y, np.float32)
+    d = y.shape[-1]
+    s = _signs(signs, d)
+    x = np.empty_like(y)
+    lib().orc_unrotate_f32(_p(y), _p(s), y.size // d, d, _p(x))
+    return x
+
+
+def rot_quant(K: np.ndarray, V: np.ndarray, g: int, k_signs, v_signs) -> dict:
+    """K, V bf16-as-uint16 [B][T][H][d] -> rotated per-token 4-bit cache dict."""
+    K = np.ascontiguousarray(K, np.uint16)
+    V = np.ascontiguousarray(V, np.uint16)
+    B, T, H, d = K.shape
+    ks, vs = _signs(k_signs, d), _signs(v_signs, d)
+    c = dict(k_codes=np.zeros((B, H, T, d // 2), np.uint8), k_scale=np.zeros((B, H, T, d // g), np.uint16),
+             k_zero=np.zeros((B, H, T, d // g), np.uint16), v_codes=np.zeros((B, H, T, d // 2), np.uint8),
+             v_scale=np.zeros((B, H, T, d // g), np.uint16), v_zero=np.zeros((B, H, T, d // g), np.uint16))
+    rc = lib().orc_rot_quant(_p(K), _p(V), B, T, H, d, g, _p(ks), _p(vs),
+                             *[_p(c[k]) for k in ("k_codes", "k_scale", "k_zero", "v_codes", "v_scale", "v_zero")])
+    _check(rc, "rot_quant")
+    c.update(B=B, T=T, H=H, d=d, g=g, k_signs=ks.copy(), v_signs=vs.copy())
+    return c
+
+
+def rot_dequant(c: dict, side: str) -> np.ndarray:
+    """One side back in the original coordinates, fp32 [B][T][H][d]."""
+    B, T, H, d, g = (c[k] for k in ("B", "T", "H", "d", "g"))
+    s = side.lower()
+    out = np.empty((B, T, H, d), np.float32)
+    lib().orc_rot_dequant(_p(c[s + "_codes"]), _p(c[s + "_scale"]), _p(c[s + "_zero"]), _p(c[s + "_signs"]),
+                          B, T, H, d, g, _p(out))
+    return out
+
+
+def rot_decode_attn(c: dict, q: np.ndarray, sm_scale: float = 1.0) -> np.ndarray:
+    q = np.ascontiguousarray(q, np.uint16)
+    B, Hq, d = q.shape
+    out = np.empty((B, Hq, d), np.float64)
+    rc = lib().orc_rot_decode_attn(*[_p(c[k]) for k in ("k_codes", "k_scale", "k_zero", "v_codes", "v_scale",
+                                                         "v_zero", "k_signs", "v_signs")],
+                                   c["B"], c["T"], c["H"], c["d"], c["g"], _p(q), Hq, float(sm_scale), _p(out))
+    _check(rc, "rot_decode_attn")
+    return out
 
 
 # ------------------------------------------------------------- accounting ---

@@ -597,6 +597,177 @@ int orc_int4_evict(const uint8_t* k_codes, const uint16_t* k_scale, const uint16
     return 0;
 }
 
+/* ------------------------------------------- Hadamard-rotated 4-bit cache --- */
+
+/* [KV-COBRA notes, item 4 (Walsh-Hadamard rotation with fixed random sign flips): an
+ * orthogonal Walsh-Hadamard matrix with a fixed random sign flip mixes the coordinates so
+ * that every coordinate gets the mean variance before scalar quantization; the vs-QuaRot /
+ * TurboQuant remark: rotation removes outliers.]  Calibration-free reading (no low-rank
+ * projection): y = (1/sqrt(d)) * H_d * (s (.) x) with H_d the Sylvester Hadamard matrix
+ * (H_1 = [1], H_2n = [[H_n, H_n], [H_n, -H_n]]) and s in {+1, -1}^d given.
+ * READING (precision): the transform is evaluated in fp32 as butterflies in a fixed order,
+ * stage h = 1, 2, 4, ..., d/2, each pair (j, j + h) with j & h == 0 becoming (a + b, a - b),
+ * then one multiply by fp32(1/sqrt(d)); the quantizer's decisions are taken on these values. */
+static void fwht_f32(float* y, int64_t d) {
+    for (int64_t h = 1; h < d; h *= 2)
+        for (int64_t i = 0; i < d; i += 2 * h)
+            for (int64_t j = i; j < i + h; ++j) {
+                const float a = y[j], b = y[j + h];
+                y[j] = a + b;
+                y[j + h] = a - b;
+            }
+}
+
+void orc_rotate_f32(const float* x, const int8_t* signs, int64_t n, int64_t d, float* y) {
+    const float c = (float)(1.0 / sqrt((double)d));
+    for (int64_t r = 0; r < n; ++r) {
+        float* yr = &y[r * d];
+        for (int64_t k = 0; k < d; ++k) yr[k] = signs[k] < 0 ? -x[r * d + k] : x[r * d + k];
+        fwht_f32(yr, d);
+        for (int64_t k = 0; k < d; ++k) yr[k] = yr[k] * c;
+    }
+}
+
+/* The inverse (H_d is symmetric and H_d H_d = d I): x = s (.) ((1/sqrt(d)) * H_d * y), same order. */
+void orc_unrotate_f32(const float* y, const int8_t* signs, int64_t n, int64_t d, float* x) {
+    const float c = (float)(1.0 / sqrt((double)d));
+    for (int64_t r = 0; r < n; ++r) {
+        float* xr = &x[r * d];
+        for (int64_t k = 0; k < d; ++k) xr[k] = y[r * d + k];
+        fwht_f32(xr, d);
+        for (int64_t k = 0; k < d; ++k) {
+            const float v = xr[k] * c;
+            xr[k] = signs[k] < 0 ? -v : v;
+        }
+    }
+}
+
+/* fp64 versions for the attention reference (no rounding to speak of). */
+static void rotate_f64(double* y, const int8_t* signs, int64_t d, int inverse) {
+    if (!inverse)
+        for (int64_t k = 0; k < d; ++k) y[k] = signs[k] < 0 ? -y[k] : y[k];
+    for (int64_t h = 1; h < d; h *= 2)
+        for (int64_t i = 0; i < d; i += 2 * h)
+            for (int64_t j = i; j < i + h; ++j) {
+                const double a = y[j], b = y[j + h];
+                y[j] = a + b;
+                y[j + h] = a - b;
+            }
+    const double c = 1.0 / sqrt((double)d);
+    for (int64_t k = 0; k < d; ++k) y[k] *= c;
+    if (inverse)
+        for (int64_t k = 0; k < d; ++k) y[k] = signs[k] < 0 ? -y[k] : y[k];
+}
+
+/* Every token of K and V rotated (its own sign vector per side) and quantized per token in
+ * groups of g consecutive rotated coordinates with the steps of int4_group (READING: the
+ * calibration-free variant keeps a bf16 scale and zero per group instead of the notes'
+ * calibrated fixed step; a per-token layout needs no bf16 window).  Layouts:
+ *   codes u8 [B][H][T][d/2] (low nibble = even coordinate), scale / zero bf16 [B][H][T][d/g]. */
+int orc_rot_quant(const uint16_t* K, const uint16_t* V, int64_t B, int64_t T, int64_t H, int64_t d, int64_t g,
+                  const int8_t* k_signs, const int8_t* v_signs,
+                  uint8_t* k_codes, uint16_t* k_scale, uint16_t* k_zero,
+                  uint8_t* v_codes, uint16_t* v_scale, uint16_t* v_zero) {
+    if (B <= 0 || T <= 0 || H <= 0 || d <= 1 || (d & (d - 1)) || g <= 0 || d % g) return -1;
+    float* x = (float*)malloc(sizeof(float) * (size_t)d);
+    float* y = (float*)malloc(sizeof(float) * (size_t)d);
+    uint8_t* row = (uint8_t*)malloc((size_t)d);
+    if (!x || !y || !row) { free(x); free(y); free(row); return -2; }
+    for (int side = 0; side < 2; ++side) {
+        const uint16_t* X = side ? V : K;
+        const int8_t* sg = side ? v_signs : k_signs;
+        uint8_t* codes = side ? v_codes : k_codes;
+        uint16_t* sc = side ? v_scale : k_scale;
+        uint16_t* zr = side ? v_zero : k_zero;
+        for (int64_t b = 0; b < B; ++b)
+            for (int64_t t = 0; t < T; ++t)
+                for (int64_t h = 0; h < H; ++h) {
+                    for (int64_t c = 0; c < d; ++c) x[c] = orc_bf16_to_f32(X[((b * T + t) * H + h) * d + c]);
+                    orc_rotate_f32(x, sg, 1, d, y);
+                    const int64_t o = ((b * H + h) * T + t);
+                    for (int64_t k = 0; k < d / g; ++k)
+                        int4_group(&y[k * g], g, &sc[o * (d / g) + k], &zr[o * (d / g) + k], &row[k * g]);
+                    pack_row(row, d, &codes[o * (d / 2)]);
+                }
+    }
+    free(x); free(y); free(row);
+    return 0;
+}
+
+/* Dequantize one side back to the original coordinates: the levels (q - z) * s (fp32, rounded
+ * once), then the inverse rotation in fp32.  out fp32 [B][T][H][d]. */
+void orc_rot_dequant(const uint8_t* codes, const uint16_t* scale, const uint16_t* zero, const int8_t* signs,
+                     int64_t B, int64_t T, int64_t H, int64_t d, int64_t g, float* out) {
+    float* y = (float*)malloc(sizeof(float) * (size_t)d);
+    if (!y) return;
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t t = 0; t < T; ++t)
+            for (int64_t h = 0; h < H; ++h) {
+                const int64_t o = ((b * H + h) * T + t);
+                for (int64_t c = 0; c < d; ++c) {
+                    const uint8_t byte = codes[o * (d / 2) + c / 2];
+                    const unsigned code = (c & 1) ? (byte >> 4) : (byte & 15u);
+                    y[c] = int4_level(code, scale[o * (d / g) + c / g], zero[o * (d / g) + c / g]);
+                }
+                orc_unrotate_f32(y, signs, 1, d, &out[((b * T + t) * H + h) * d]);
+            }
+    free(y);
+}
+
+/* Decode attention over the rotated cache, fp64: q' = R_K q, softmax over t of
+ * sm_scale * q' . k'_t with k'_t the rotated levels, o' = sum_t p_t v'_t, out = R_V^-1 o'.
+ * Since R_K is orthogonal, q' . k'_t = q . (R_K^-1 k'_t): this is attention over the
+ * dequantized, un-rotated cache.  GQA as orc_decode_attn.  out fp64 [B][Hq][d]. */
+int orc_rot_decode_attn(const uint8_t* k_codes, const uint16_t* k_scale, const uint16_t* k_zero,
+                        const uint8_t* v_codes, const uint16_t* v_scale, const uint16_t* v_zero,
+                        const int8_t* k_signs, const int8_t* v_signs,
+                        int64_t B, int64_t T, int64_t Hkv, int64_t d, int64_t g,
+                        const uint16_t* q, int64_t Hq, double sm_scale, double* out) {
+    if (B <= 0 || T <= 0 || Hkv <= 0 || Hq <= 0 || Hq % Hkv || d <= 1 || (d & (d - 1)) || d % g) return -1;
+    double* kh = (double*)malloc(sizeof(double) * (size_t)(T * d));
+    double* vh = (double*)malloc(sizeof(double) * (size_t)(T * d));
+    double* lg = (double*)malloc(sizeof(double) * (size_t)T);
+    double* qr = (double*)malloc(sizeof(double) * (size_t)d);
+    double* o = (double*)malloc(sizeof(double) * (size_t)d);
+    if (!kh || !vh || !lg || !qr || !o) { free(kh); free(vh); free(lg); free(qr); free(o); return -2; }
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t h = 0; h < Hkv; ++h) {
+            for (int64_t t = 0; t < T; ++t) {
+                const int64_t r = (b * Hkv + h) * T + t;
+                for (int64_t c = 0; c < d; ++c) {
+                    const uint8_t kb = k_codes[r * (d / 2) + c / 2], vb = v_codes[r * (d / 2) + c / 2];
+                    kh[t * d + c] = (double)int4_level((c & 1) ? (kb >> 4) : (kb & 15u), k_scale[r * (d / g) + c / g],
+                                                       k_zero[r * (d / g) + c / g]);
+                    vh[t * d + c] = (double)int4_level((c & 1) ? (vb >> 4) : (vb & 15u), v_scale[r * (d / g) + c / g],
+                                                       v_zero[r * (d / g) + c / g]);
+                }
+            }
+            for (int64_t hq = h * (Hq / Hkv); hq < (h + 1) * (Hq / Hkv); ++hq) {
+                for (int64_t c = 0; c < d; ++c) qr[c] = (double)orc_bf16_to_f32(q[(b * Hq + hq) * d + c]);
+                rotate_f64(qr, k_signs, d, 0);
+                double m = -INFINITY;
+                for (int64_t t = 0; t < T; ++t) {
+                    double acc = 0.0;
+                    for (int64_t c = 0; c < d; ++c) acc += qr[c] * kh[t * d + c];
+                    lg[t] = sm_scale * acc;
+                    if (lg[t] > m) m = lg[t];
+                }
+                double Z = 0.0;
+                for (int64_t c = 0; c < d; ++c) o[c] = 0.0;
+                for (int64_t t = 0; t < T; ++t) {
+                    const double p = exp(lg[t] - m);
+                    Z += p;
+                    for (int64_t c = 0; c < d; ++c) o[c] += p * vh[t * d + c];
+                }
+                for (int64_t c = 0; c < d; ++c) o[c] /= Z;
+                rotate_f64(o, v_signs, d, 1);
+                for (int64_t c = 0; c < d; ++c) out[(b * Hq + hq) * d + c] = o[c];
+            }
+        }
+    free(kh); free(vh); free(lg); free(qr); free(o);
+    return 0;
+}
+
 /* ------------------------------------------------------------ accounting --- */
 
 /* [Explainer, group-size table] bytes = ceil(N/2) + ceil(N/g) * 4. */

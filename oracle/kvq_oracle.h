@@ -83,6 +83,21 @@ int orc_int4_evict(const uint8_t* k_codes, const uint16_t* k_scale, const uint16
                    uint8_t* dv_codes, uint16_t* dv_scale, uint16_t* dv_zero,
                    uint16_t* dk_res, uint16_t* dv_res);
 
+/* Hadamard-rotated per-token 4-bit cache.  signs: d entries in {+1, -1}. */
+void orc_rotate_f32(const float* x, const int8_t* signs, int64_t n, int64_t d, float* y);
+void orc_unrotate_f32(const float* y, const int8_t* signs, int64_t n, int64_t d, float* x);
+int orc_rot_quant(const uint16_t* K, const uint16_t* V, int64_t B, int64_t T, int64_t H, int64_t d, int64_t g,
+                  const int8_t* k_signs, const int8_t* v_signs,
+                  uint8_t* k_codes, uint16_t* k_scale, uint16_t* k_zero,
+                  uint8_t* v_codes, uint16_t* v_scale, uint16_t* v_zero);
+void orc_rot_dequant(const uint8_t* codes, const uint16_t* scale, const uint16_t* zero, const int8_t* signs,
+                     int64_t B, int64_t T, int64_t H, int64_t d, int64_t g, float* out);
+int orc_rot_decode_attn(const uint8_t* k_codes, const uint16_t* k_scale, const uint16_t* k_zero,
+                        const uint8_t* v_codes, const uint16_t* v_scale, const uint16_t* v_zero,
+                        const int8_t* k_signs, const int8_t* v_signs,
+                        int64_t B, int64_t T, int64_t Hkv, int64_t d, int64_t g,
+                        const uint16_t* q, int64_t Hq, double sm_scale, double* out);
+
 /* Accounting. */
 uint64_t orc_int4_bytes(uint64_t N, uint64_t g);
 int orc_int4_cache_sizes(int64_t B, int64_t T, int64_t H, int64_t d, int64_t g, int64_t R,

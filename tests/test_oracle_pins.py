@@ -812,3 +812,135 @@ def test_h2o_decode_scores_sum_and_match_offline_colsum():
         hist.append(probs.reshape(B, H, Hq // H, T))
     hist = np.concatenate(hist, axis=2).reshape(B * H, -1, T).astype(np.float32)
     assert np.allclose(oracle.colsum(hist), acc.reshape(B * H, T), rtol=1e-5, atol=1e-7)
+
+
+# -------------------------------------------------- Hadamard-rotated 4-bit cache --
+
+def _signs(d, seed):
+    return np.where(np.random.default_rng(seed).random(d) < 0.5, -1, 1).astype(np.int8)
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_rotation_is_the_sylvester_hadamard_matrix(d):
+    from scipy.linalg import hadamard
+    Hm = hadamard(d).astype(np.float64)
+    s = _signs(d, d)
+    rng = np.random.default_rng(d)
+    x = rng.standard_normal((50, d)).astype(np.float32)
+    ref = (x.astype(np.float64) * s) @ Hm.T / math.sqrt(d)
+    y = oracle.rotate(x, s).astype(np.float64)
+    assert np.allclose(y, ref, rtol=0, atol=2e-6 * np.abs(x).sum(-1, keepdims=True).max())
+    # small integers: every butterfly sum is exact, so only the final scale rounds
+    xi = rng.integers(-8, 9, (20, d)).astype(np.float32)
+    exact = ((xi.astype(np.float64) * s) @ Hm.T).astype(np.float32)
+    want = exact * np.float32(1.0 / math.sqrt(d))
+    assert np.array_equal(oracle.rotate(xi, s), want)
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_rotation_orthogonal_inverse_and_outlier_spreading(d):
+    s = _signs(d, d + 1)
+    # the basis vectors map to rows of +-1/sqrt(d), mutually orthogonal
+    E = np.eye(d, dtype=np.float32)
+    R = oracle.rotate(E, s).astype(np.float64)
+    assert np.allclose(np.abs(R), 1 / math.sqrt(d), rtol=1e-6, atol=0)
+    assert np.allclose(R @ R.T, np.eye(d), atol=1e-6)
+    # one outlier channel of size a spreads into d coordinates of size a / sqrt(d)
+    x = np.zeros((1, d), np.float32)
+    x[0, 5] = 100.0
+    assert np.allclose(np.abs(oracle.rotate(x, s)), 100.0 / math.sqrt(d), rtol=1e-6)
+    # the inverse recovers the input and the norm is kept
+    rng = np.random.default_rng(d)
+    x = rng.standard_normal((40, d)).astype(np.float32) * (1 + 30 * (rng.random(d) < 0.05))
+    y = oracle.rotate(x, s)
+    assert np.allclose(np.linalg.norm(y, axis=-1), np.linalg.norm(x, axis=-1), rtol=1e-5)
+    assert np.allclose(oracle.unrotate(y, s), x, rtol=0, atol=1e-5 * np.abs(x).max())
+
+
+def test_rotation_equalizes_coordinate_variance():
+    # independent coordinates with variances lambda_i -> every rotated coordinate has variance mean(lambda)
+    d, n = 128, 20000
+    rng = np.random.default_rng(7)
+    lam = np.exp(rng.uniform(-3, 4, d))
+    x = (rng.standard_normal((n, d)) * np.sqrt(lam)).astype(np.float32)
+    y = oracle.rotate(x, _signs(d, 7)).astype(np.float64)
+    var = y.var(0)
+    assert lam.max() / lam.min() > 500
+    assert np.all(np.abs(var / lam.mean() - 1) < 0.06)
+
+
+@pytest.mark.parametrize("g", [32, 64, 128])
+def test_rot_quant_round_trip_nearest_level_and_norm_bound(g):
+    from scipy.linalg import hadamard
+    B, T, H, d = 1, 40, 2, 128
+    Kb, Vb = _c2_like(B, T, H, d, seed=g + 3)
+    ks, vs = _signs(d, 1), _signs(d, 2)
+    c = oracle.rot_quant(Kb, Vb, g, ks, vs)
+    Hm = hadamard(d).astype(np.float64) / math.sqrt(d)
+    for side, X, s in (("k", Kb, ks), ("v", Vb, vs)):
+        x = f32(X).astype(np.float64)                          # [B][T][H][d]
+        y = (x * s) @ Hm.T                                      # rotated, fp64
+        codes = c[side + "_codes"]
+        q = np.stack([codes & 15, codes >> 4], -1).reshape(B, H, T, d).transpose(0, 2, 1, 3).astype(np.int64)
+        sc = np.repeat(f32(c[side + "_scale"]).astype(np.float64), g, -1).transpose(0, 2, 1, 3)
+        z = np.repeat(f32(c[side + "_zero"]).astype(np.float64), g, -1).transpose(0, 2, 1, 3)
+        yh = (q - z) * sc
+        # each rotated value within half a step of its level, on the nearest level (away from ties)
+        assert np.all(np.abs(y - yh) <= sc / 2 * (1 + 1e-5) + 1e-6)
+        levels = (np.arange(16)[None, None, None, None, :] - z[..., None]) * sc[..., None]
+        dist = np.abs(y[..., None] - levels)
+        srt = np.sort(dist, -1)
+        clear = srt[..., 1] - srt[..., 0] > 1e-5 * sc
+        assert np.array_equal(np.argmin(dist, -1)[clear], q[clear])
+        # back in the original coordinates the error norm equals the rotated one (orthogonality)
+        xh = oracle.rot_dequant(c, side).astype(np.float64)
+        e_orig = np.linalg.norm(x - xh, axis=-1)
+        e_rot = np.linalg.norm(y - yh, axis=-1)
+        assert np.allclose(e_orig, e_rot, rtol=1e-4, atol=1e-6)
+
+
+def test_rotation_beats_plain_per_token_quantization_on_outlier_channels():
+    # K with 4 outlier channels (x10): per-token 4-bit groups waste their range on the outliers
+    # unless the rotation spreads them first
+    B, T, H, d, g = 1, 256, 2, 128, 64
+    Kb, Vb = _c2_like(B, T, H, d, seed=5)
+    ident = np.ones(d, np.int8)
+    c = oracle.rot_quant(Kb, Vb, g, _signs(d, 5), ident)
+    x = f32(Kb).astype(np.float64)
+    err_rot = np.sqrt(((x - oracle.rot_dequant(c, "k")) ** 2).mean())
+    # plain per-token groups = the 4-bit V format of the KIVI quantizer applied to K
+    plain = oracle.int4_quant(Vb, Kb, g, 0)
+    err_plain = np.sqrt(((x - oracle.int4_dequant(plain, "v")) ** 2).mean())
+    assert err_rot < 0.6 * err_plain
+
+
+def test_rot_attention_is_attention_over_the_unrotated_cache():
+    # softmax attention (numpy, fp64) over the dequantized cache taken back to the original
+    # coordinates must equal the rotated-space attention with its output rotated back
+    from scipy.linalg import hadamard
+    B, T, H, Hq, d, g = 2, 70, 2, 8, 64, 32
+    Kb, Vb = _c2_like(B, T, H, d, seed=8)
+    ks, vs = _signs(d, 3), _signs(d, 4)
+    c = oracle.rot_quant(Kb, Vb, g, ks, vs)
+    rng = np.random.default_rng(8)
+    q = bf16(rng.standard_normal((B, Hq, d)) / 8)
+    out = oracle.rot_decode_attn(c, q, 0.5)
+    Hm = hadamard(d).astype(np.float64) / math.sqrt(d)
+
+    def levels(side):
+        codes = c[side + "_codes"]
+        qq = np.stack([codes & 15, codes >> 4], -1).reshape(B, H, T, d).astype(np.float64)
+        sc = np.repeat(f32(c[side + "_scale"]).astype(np.float64), g, -1)
+        z = np.repeat(f32(c[side + "_zero"]).astype(np.float64), g, -1)
+        return (qq - z) * sc                                   # [B][H][T][d], rotated coordinates
+
+    Kx = (levels("k") @ Hm) * ks                               # back to the original coordinates
+    Vx = (levels("v") @ Hm) * vs
+    qf = f32(q).astype(np.float64)
+    for b in range(B):
+        for hq in range(Hq):
+            h = hq // (Hq // H)
+            lg = 0.5 * Kx[b, h] @ qf[b, hq]
+            p = np.exp(lg - lg.max())
+            want = p @ Vx[b, h] / p.sum()
+            assert np.allclose(out[b, hq], want, rtol=0, atol=1e-10)
