@@ -177,6 +177,56 @@ int kvq_int4_append(kvq_int4_cache* c, const void* k_new, const void* v_new, int
 int kvq_int4_evict(const kvq_int4_cache* src, const int32_t* keep, const kvq_int4_cache* dst, kvq_stream stream);
 
 /* ======================================================================
+ * Hadamard-rotated per-token 4-bit cache  [KV-COBRA notes (papernotes.org),
+ * item 4: an orthogonal Walsh-Hadamard matrix with a fixed random sign flip
+ * spreads every coordinate to the mean variance before scalar quantization;
+ * the QuaRot / TurboQuant comparison: rotation removes outliers.  Group steps
+ * as kvq_group_quant_int4 (Explainer, quantization section).]
+ *
+ * For every token and head, K and V rows are rotated,
+ *   y = (1/sqrt(d)) * H_d * (s (.) x),   H_d the Sylvester Hadamard matrix,
+ * with the caller's signs s (k_signs for K, v_signs for V: HOST arrays of d
+ * int8 entries, each +1 or -1; the method's random draw).  The transform is
+ * fp32 butterflies in a fixed order: stage h = 1, 2, 4, ..., d/2, pair
+ * (j, j + h) with j & h == 0 -> (a + b, a - b); then one multiply by
+ * fp32(1/sqrt(d)).  Every token is then quantized per token in groups of g
+ * consecutive rotated coordinates (s, z, q as in kvq_group_quant_int4).  There
+ * is no bf16 window: a per-token group does not wait for later tokens.
+ * Sections (device, caller-allocated, sizes from kvq_rot_cache_sizes):
+ *   [0] k_codes u8 [B][H][T][d/2] (low nibble = even coordinate)
+ *   [1] k_scale, [2] k_zero bf16 [B][H][T][d/g]
+ *   [3] v_codes, [4] v_scale, [5] v_zero likewise.
+ * kvq_rot_dequant: one side (0 = K, 1 = V) back to the original coordinates,
+ *   the levels (q - z) * s, then the inverse rotation s (.) ((1/sqrt(d)) H_d y)
+ *   in the same fp32 order; out [B][T][H][d] of type ot.
+ * kvq_rot_decode_attn: GQA decode attention in the rotated space: q' = R_K q
+ *   (fp32), softmax over all T tokens of sm_scale * q' . k'_t (k' the rotated
+ *   levels), o' = sum_t p_t v'_t, out = R_V^-1 o' (fp32, then ot).  Since R_K
+ *   is orthogonal this is attention over the dequantized cache.  Head map and
+ *   output types as kvq_decode_attn_int4; workspace kvq_rot_decode_attn_ws().
+ * EINVAL: B, T, H < 1; d not in {64, 128, 256}; g not in {32, 64, 128} or
+ *   g > d; B*T*H >= 2^31; NULL pointers; signs other than +-1; side / ot / Hq
+ *   as above; short workspace.  EALIGN: device pointers not 16-byte aligned.
+ * ====================================================================== */
+typedef struct {
+    int64_t B, T, H, d, g;
+    uint8_t* k_codes;
+    uint16_t* k_scale;
+    uint16_t* k_zero;
+    uint8_t* v_codes;
+    uint16_t* v_scale;
+    uint16_t* v_zero;
+} kvq_rot_cache;
+
+int kvq_rot_cache_sizes(int64_t B, int64_t T, int64_t H, int64_t d, int64_t g, size_t sect_bytes[6], size_t* total);
+int kvq_rot_quant_int4(const void* K, const void* V, const int8_t* k_signs, const int8_t* v_signs,
+                       const kvq_rot_cache* c, kvq_stream stream);
+int kvq_rot_dequant(const kvq_rot_cache* c, int side, const int8_t* signs, void* out, int ot, kvq_stream stream);
+size_t kvq_rot_decode_attn_ws(const kvq_rot_cache* c, int64_t Hq);
+int kvq_rot_decode_attn(const kvq_rot_cache* c, const int8_t* k_signs, const int8_t* v_signs, const void* q,
+                        int64_t Hq, float sm_scale, void* out, int ot, void* ws, size_t ws_bytes, kvq_stream stream);
+
+/* ======================================================================
  * Dequantization  [Walkthrough §1.3: x_hat = (q - zero_point) * scale]
  *
  * kind KVQ_FMT_PER_CHANNEL: desc -> kvq_pc_tensor; out [nb][R][C] dense.

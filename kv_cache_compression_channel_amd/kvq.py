@@ -29,6 +29,7 @@ EXPORTED = [
     "kvq_keep_count",
     "kvq_decode_attn_int4_ws", "kvq_decode_attn_int4", "kvq_decode_attn_int4_h2o_ws", "kvq_decode_attn_int4_h2o",
     "kvq_select_ws", "kvq_h2o_select", "kvq_snapkv_select", "kvq_compact",
+    "kvq_rot_cache_sizes", "kvq_rot_quant_int4", "kvq_rot_dequant", "kvq_rot_decode_attn_ws", "kvq_rot_decode_attn",
 ]
 
 
@@ -46,6 +47,12 @@ class Int4Desc(C.Structure):
                 ("k_codes", C.c_void_p), ("k_scale", C.c_void_p), ("k_zero", C.c_void_p),
                 ("v_codes", C.c_void_p), ("v_scale", C.c_void_p), ("v_zero", C.c_void_p),
                 ("k_res", C.c_void_p), ("v_res", C.c_void_p), ("cap", C.c_int64), ("rcap", C.c_int64)]
+
+
+class RotDesc(C.Structure):
+    _fields_ = [("B", C.c_int64), ("T", C.c_int64), ("H", C.c_int64), ("d", C.c_int64), ("g", C.c_int64),
+                ("k_codes", C.c_void_p), ("k_scale", C.c_void_p), ("k_zero", C.c_void_p),
+                ("v_codes", C.c_void_p), ("v_scale", C.c_void_p), ("v_zero", C.c_void_p)]
 
 
 class PcDesc(C.Structure):
@@ -79,6 +86,12 @@ def lib():
     L.kvq_group_quant_int4.argtypes = [P, P, P, P]
     L.kvq_int4_append.argtypes = [P, P, P, I64, I64, P]
     L.kvq_int4_evict.argtypes = [P, P, P, P]
+    L.kvq_rot_cache_sizes.argtypes = [I64] * 5 + [P, P]
+    L.kvq_rot_quant_int4.argtypes = [P, P, P, P, P, P]
+    L.kvq_rot_dequant.argtypes = [P, I, P, P, I, P]
+    L.kvq_rot_decode_attn_ws.argtypes = [P, I64]
+    L.kvq_rot_decode_attn_ws.restype = SZ
+    L.kvq_rot_decode_attn.argtypes = [P, P, P, P, I64, C.c_float, P, I, P, SZ, P]
     L.kvq_dequant.argtypes = [P, P, I, P]
     L.kvq_err_stats_ws.argtypes = [I64]
     L.kvq_err_stats_ws.restype = SZ
@@ -343,6 +356,96 @@ def dequant_int4(cache: Int4Cache, side: str, out_dtype=torch.bfloat16, out=None
     qd = QDesc(kind, C.cast(C.pointer(desc), C.c_void_p))
     _check(lib().kvq_dequant(C.byref(qd), _p(out), _dt(out), _stream(out)))
     return out
+
+
+# ----------------------------------------------- Hadamard-rotated cache --
+
+@dataclass
+class RotCache:
+    """Per-token 4-bit codes of Hadamard-rotated K and V (device tensors) and their shape."""
+    B: int
+    T: int
+    H: int
+    d: int
+    g: int
+    k_codes: torch.Tensor
+    k_scale: torch.Tensor
+    k_zero: torch.Tensor
+    v_codes: torch.Tensor
+    v_scale: torch.Tensor
+    v_zero: torch.Tensor
+
+    SECTIONS = ("k_codes", "k_scale", "k_zero", "v_codes", "v_scale", "v_zero")
+
+    @staticmethod
+    def empty(B, T, H, d, g, device):
+        def e(shape, dt):
+            return torch.empty(shape, dtype=dt, device=device)
+        u8, bf = torch.uint8, torch.bfloat16
+        return RotCache(B, T, H, d, g, e((B, H, T, d // 2), u8), e((B, H, T, d // g), bf), e((B, H, T, d // g), bf),
+                        e((B, H, T, d // 2), u8), e((B, H, T, d // g), bf), e((B, H, T, d // g), bf))
+
+    def desc(self) -> RotDesc:
+        return RotDesc(self.B, self.T, self.H, self.d, self.g, *[getattr(self, s).data_ptr() for s in self.SECTIONS])
+
+    def nbytes(self) -> int:
+        return sum(getattr(self, s).numel() * getattr(self, s).element_size() for s in self.SECTIONS)
+
+
+def _signs_host(s, d) -> torch.Tensor:
+    t = torch.as_tensor(s, dtype=torch.int8).contiguous().cpu()
+    if t.shape != (d,):
+        raise ValueError(f"signs must have d = {d} entries")
+    return t
+
+
+def rot_quant_int4(K: torch.Tensor, V: torch.Tensor, g: int, k_signs, v_signs, cache: RotCache | None = None):
+    """K, V bf16 [B][T][H][d] -> RotCache (each row rotated by (1/sqrt(d)) H diag(signs), then
+    per-token 4-bit groups of g).  Signs: d host values in {+1, -1} per side."""
+    _need_cuda(K, V)
+    if K.dtype != torch.bfloat16 or V.dtype != torch.bfloat16 or K.shape != V.shape or K.dim() != 4 \
+            or not K.is_contiguous() or not V.is_contiguous():
+        raise ValueError("K and V must be contiguous bfloat16 [B][T][H][d] of the same shape")
+    B, T, H, d = K.shape
+    ks, vs = _signs_host(k_signs, d), _signs_host(v_signs, d)
+    if cache is None:
+        cache = RotCache.empty(B, T, H, d, g, K.device)
+    desc = cache.desc()
+    _check(lib().kvq_rot_quant_int4(_p(K), _p(V), ks.data_ptr(), vs.data_ptr(), C.byref(desc), _stream(K)))
+    return cache
+
+
+def rot_dequant(cache: RotCache, side: str, signs, out_dtype=torch.bfloat16, out=None):
+    """One side back in the original coordinates, [B][T][H][d]."""
+    if out is None:
+        out = torch.empty((cache.B, cache.T, cache.H, cache.d), dtype=out_dtype, device=cache.k_codes.device)
+    sg = _signs_host(signs, cache.d)
+    desc = cache.desc()
+    _check(lib().kvq_rot_dequant(C.byref(desc), 0 if side.lower() == "k" else 1, sg.data_ptr(), _p(out), _dt(out),
+                                 _stream(out)))
+    return out
+
+
+def rot_decode_attn(cache: RotCache, q: torch.Tensor, k_signs, v_signs, sm_scale: float = 1.0, out=None, ws=None,
+                    out_dtype=torch.bfloat16):
+    """GQA decode attention over the rotated cache; q bf16 [B][Hq][d] -> out [B][Hq][d]."""
+    _need_cuda(q)
+    if q.dtype != torch.bfloat16 or not q.is_contiguous():
+        raise TypeError("q must be a contiguous bfloat16 [B][Hq][d] tensor")
+    B, Hq, d = q.shape
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=out_dtype, device=q.device)
+    ks, vs = _signs_host(k_signs, d), _signs_host(v_signs, d)
+    desc = cache.desc()
+    w, wb = _ws(int(lib().kvq_rot_decode_attn_ws(C.byref(desc), Hq)), q.device, ws)
+    _check(lib().kvq_rot_decode_attn(C.byref(desc), ks.data_ptr(), vs.data_ptr(), _p(q), Hq, float(sm_scale), _p(out),
+                                     _dt(out), _p(w), wb, _stream(q)))
+    return out
+
+
+def rot_attn_ws_bytes(cache: RotCache, Hq: int) -> int:
+    desc = cache.desc()
+    return int(lib().kvq_rot_decode_attn_ws(C.byref(desc), Hq))
 
 
 # ------------------------------------------------------------------- stats --

@@ -233,6 +233,41 @@ def test_attn_h2o_validation(L):
     assert L.kvq_decode_attn_int4_h2o_ws(None, 4) == 0
 
 
+def test_rot_validation(L):
+    import numpy as np
+    def rd(**kw):
+        base = dict(B=1, T=16, H=2, d=128, g=64)
+        base.update(kw)
+        return kvq.RotDesc(base["B"], base["T"], base["H"], base["d"], base["g"],
+                           *[kw.get(f, 0x200000) for f in kvq.RotCache.SECTIONS])
+    good = np.ones(128, np.int8)
+    bad = good.copy()
+    bad[7] = 0
+    gp, bp = good.ctypes.data, bad.ctypes.data
+    q = L.kvq_rot_quant_int4
+    for kw in (dict(d=96), dict(g=16), dict(d=64, g=128), dict(T=0), dict(k_scale=None)):
+        assert q(FAKE, FAKE, gp, gp, C.byref(rd(**kw)), None) == kvq.KVQ_EINVAL, kw
+    assert q(FAKE, FAKE, bp, gp, C.byref(rd()), None) == kvq.KVQ_EINVAL          # a zero sign
+    assert q(FAKE, FAKE, gp, None, C.byref(rd()), None) == kvq.KVQ_EINVAL
+    assert q(None, FAKE, gp, gp, C.byref(rd()), None) == kvq.KVQ_EINVAL
+    assert q(MISALIGNED, FAKE, gp, gp, C.byref(rd()), None) == kvq.KVQ_EALIGN
+    dq = L.kvq_rot_dequant
+    assert dq(C.byref(rd()), 2, gp, FAKE, 0, None) == kvq.KVQ_EINVAL             # side
+    assert dq(C.byref(rd()), 0, gp, FAKE, 7, None) == kvq.KVQ_EINVAL             # ot
+    assert dq(C.byref(rd()), 0, bp, FAKE, 0, None) == kvq.KVQ_EINVAL
+    at = L.kvq_rot_decode_attn
+    need = L.kvq_rot_decode_attn_ws(C.byref(rd()), 8)
+    assert need > 0
+    assert at(C.byref(rd()), gp, gp, FAKE, 6, 1.0, FAKE, 1, FAKE, need, None) == kvq.KVQ_EINVAL     # Hq % H
+    assert at(C.byref(rd()), gp, gp, FAKE, 64, 1.0, FAKE, 1, FAKE, 1 << 30, None) == kvq.KVQ_EINVAL  # Hq / H = 32
+    assert at(C.byref(rd()), gp, gp, FAKE, 8, 1.0, FAKE, 1, FAKE, need - 1, None) == kvq.KVQ_EINVAL
+    assert at(C.byref(rd()), gp, bp, FAKE, 8, 1.0, FAKE, 1, FAKE, need, None) == kvq.KVQ_EINVAL
+    sect = (C.c_size_t * 6)()
+    tot = C.c_size_t()
+    assert L.kvq_rot_cache_sizes(2, 10, 3, 128, 64, sect, C.byref(tot)) == kvq.KVQ_OK
+    assert list(sect) == [2 * 3 * 10 * 64, 2 * 3 * 10 * 2 * 2, 2 * 3 * 10 * 2 * 2] * 2 and tot.value == sum(sect)
+
+
 def test_select_and_compact_validation(L):
     big = 1 << 30
     h2o = L.kvq_h2o_select
