@@ -35,6 +35,26 @@ __device__ __forceinline__ uint32_t sign8(const SignBits& s, int c0) {   // bits
     return (s.w[c0 / 32] >> (c0 % 32)) & 0xffu;
 }
 
+// x from the lane whose index differs in bit pattern M (M < 32): ds_swizzle's bit mode, which
+// needs no address computation.
+template <int M>
+__device__ __forceinline__ float swz_xor(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x1f | (M << 10)));
+}
+
+template <int M, int LPR>
+__device__ __forceinline__ void fwht_cross(float (&v)[8], int lane) {
+    if constexpr (M < LPR) {
+        const bool hi = (lane & M) != 0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const float p = swz_xor<M>(v[k]);
+            v[k] = hi ? (p - v[k]) : (v[k] + p);
+        }
+        fwht_cross<2 * M, LPR>(v, lane);
+    }
+}
+
 // Butterflies of one row held as 8 consecutive coordinates per lane, LPR lanes per row.
 template <int LPR>
 __device__ __forceinline__ void fwht_row(float (&v)[8], int lane) {
@@ -48,15 +68,7 @@ __device__ __forceinline__ void fwht_row(float (&v)[8], int lane) {
             v[j + h] = a - b;
         }
     }
-#pragma unroll
-    for (int m = 1; m < LPR; m *= 2) {
-        const bool hi = (lane & m) != 0;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const float p = __shfl_xor(v[k], m);
-            v[k] = hi ? (p - v[k]) : (v[k] + p);
-        }
-    }
+    fwht_cross<1, LPR>(v, lane);
 }
 
 struct RotGeom {
@@ -66,26 +78,36 @@ struct RotGeom {
 };
 
 // ---------------- quantization: K and V rows of the [B][T][H][d] input ----------------
+// Each thread loads the K and V pieces of all its rows first (rows past the end repeat the last
+// row and are not stored, so every lane takes part in every shuffle), then rotates and quantizes.
 template <int D, int G>
 __global__ void __launch_bounds__(kThreads) rot_quant_kernel(const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
                                                             RotGeom geo, SignBits ks, SignBits vs, kvq_rot_cache out) {
-    constexpr int LPR = D / 8, RPP = kThreads / LPR, LPG = G / 8, NGD = D / G;
+    constexpr int LPR = D / 8, RPP = kThreads / LPR, LPG = G / 8, NGD = D / G, NR = kRowsPerBlock / RPP;
     const int tid = threadIdx.x, lane = tid % LPR, rg = tid / LPR;
     const uint32_t r0 = blockIdx.x * kRowsPerBlock;
-    for (int rr = rg; rr < kRowsPerBlock; rr += RPP) {
-        const uint32_t r = r0 + rr;
-        if (r >= geo.rows) break;           // uniform per row: the row's lanes leave together
-        const uint32_t q1 = r / (uint32_t)geo.H;
-        const int64_t h = r - q1 * (uint32_t)geo.H, t = q1 % (uint32_t)geo.T, b = q1 / (uint32_t)geo.T;
+    uint4 raw[2][NR];
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+        const uint32_t r = min(r0 + rg + RPP * i, geo.rows - 1);
+        raw[0][i] = *reinterpret_cast<const uint4*>(K + (int64_t)r * D + 8 * lane);
+        raw[1][i] = *reinterpret_cast<const uint4*>(V + (int64_t)r * D + 8 * lane);
+    }
+    const uint32_t sgn[2] = {sign8(ks, 8 * lane), sign8(vs, 8 * lane)};
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+        const uint32_t r = r0 + rg + RPP * i;
+        const bool live = r < geo.rows;
+        const uint32_t rc = live ? r : geo.rows - 1;
+        const uint32_t q1 = rc / (uint32_t)geo.H;
+        const int64_t h = rc - q1 * (uint32_t)geo.H, t = q1 % (uint32_t)geo.T, b = q1 / (uint32_t)geo.T;
         const int64_t o = (b * geo.H + h) * geo.T + t;          // [B][H][T] output row
 #pragma unroll
         for (int side = 0; side < 2; ++side) {
-            const uint16_t* X = side ? V : K;
-            const uint32_t sb = sign8(side ? vs : ks, 8 * lane);
             float v[8];
-            unpack8(*reinterpret_cast<const uint4*>(X + (int64_t)r * D + 8 * lane), v);
+            unpack8(raw[side][i], v);
 #pragma unroll
-            for (int k = 0; k < 8; ++k) v[k] = ((sb >> k) & 1u) ? -v[k] : v[k];
+            for (int k = 0; k < 8; ++k) v[k] = ((sgn[side] >> k) & 1u) ? -v[k] : v[k];
             fwht_row<LPR>(v, lane);
             float mn = FLT_MAX, mx = -FLT_MAX;
 #pragma unroll
@@ -100,42 +122,54 @@ __global__ void __launch_bounds__(kThreads) rot_quant_kernel(const uint16_t* __r
                 mx = vmax2(mx, __shfl_xor(mx, off));
             }
             const GroupParams gp = group_params(mn, mx);
-            const int64_t mi = o * NGD + (8 * lane) / G;
-            if (lane % LPG == 0) {
-                (side ? out.v_scale : out.k_scale)[mi] = gp.sb;
-                (side ? out.v_zero : out.k_zero)[mi] = gp.zb;
-            }
             const bool fast = gp.z >= 0.0f && gp.z <= 15.0f;
             const float ps8[8] = {gp.s, gp.s, gp.s, gp.s, gp.s, gp.s, gp.s, gp.s};
             const float pr8[8] = {gp.r, gp.r, gp.r, gp.r, gp.r, gp.r, gp.r, gp.r};
             const float pz8[8] = {gp.z, gp.z, gp.z, gp.z, gp.z, gp.z, gp.z, gp.z};
             float q[8];
             codes8<true>(v, ps8, pr8, pz8, fast, q);
-            *reinterpret_cast<uint32_t*>((side ? out.v_codes : out.k_codes) + o * (D / 2) + 4 * lane) = pack_codes(q);
+            if (live) {
+                const int64_t mi = o * NGD + (8 * lane) / G;
+                if (lane % LPG == 0) {
+                    (side ? out.v_scale : out.k_scale)[mi] = gp.sb;
+                    (side ? out.v_zero : out.k_zero)[mi] = gp.zb;
+                }
+                *reinterpret_cast<uint32_t*>((side ? out.v_codes : out.k_codes) + o * (D / 2) + 4 * lane) =
+                    pack_codes(q);
+            }
         }
     }
 }
 
 // ---------------- dequantization of one side back to the original coordinates ----------------
+// Loads of all the thread's rows first (rows past the end repeat the last row, not stored).
 template <int D, int G, int OT>
 __global__ void __launch_bounds__(kThreads) rot_dequant_kernel(const uint8_t* __restrict__ codes,
                                                               const uint16_t* __restrict__ scale,
                                                               const uint16_t* __restrict__ zero, RotGeom geo,
                                                               SignBits sg, void* __restrict__ out) {
-    constexpr int LPR = D / 8, RPP = kThreads / LPR, NGD = D / G;
+    constexpr int LPR = D / 8, RPP = kThreads / LPR, NGD = D / G, NR = kRowsPerBlock / RPP;
     const int tid = threadIdx.x, lane = tid % LPR, rg = tid / LPR;
     const uint32_t r0 = blockIdx.x * kRowsPerBlock;
     const uint32_t sb = sign8(sg, 8 * lane);
-    for (int rr = rg; rr < kRowsPerBlock; rr += RPP) {
-        const uint32_t r = r0 + rr;        // [B][T][H] output row
-        if (r >= geo.rows) break;
-        const uint32_t q1 = r / (uint32_t)geo.H;
-        const int64_t h = r - q1 * (uint32_t)geo.H, t = q1 % (uint32_t)geo.T, b = q1 / (uint32_t)geo.T;
+    uint32_t w[NR];
+    uint16_t sc[NR], zr[NR];
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+        const uint32_t rc = min(r0 + rg + RPP * i, geo.rows - 1);   // [B][T][H] output row
+        const uint32_t q1 = rc / (uint32_t)geo.H;
+        const int64_t h = rc - q1 * (uint32_t)geo.H, t = q1 % (uint32_t)geo.T, b = q1 / (uint32_t)geo.T;
         const int64_t o = (b * geo.H + h) * geo.T + t;
-        const uint32_t w = *reinterpret_cast<const uint32_t*>(codes + o * (D / 2) + 4 * lane);
+        w[i] = *reinterpret_cast<const uint32_t*>(codes + o * (D / 2) + 4 * lane);
         const int64_t mi = o * NGD + (8 * lane) / G;
-        const float s = bf_to_f(scale[mi]), zs = -bf_to_f(zero[mi]) * s;
-        const uint32_t lo = w & 0x0f0f0f0fu, hi = (w >> 4) & 0x0f0f0f0fu;
+        sc[i] = scale[mi];
+        zr[i] = zero[mi];
+    }
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+        const uint32_t r = r0 + rg + RPP * i;
+        const float s = bf_to_f(sc[i]), zs = -bf_to_f(zr[i]) * s;
+        const uint32_t lo = w[i] & 0x0f0f0f0fu, hi = (w[i] >> 4) & 0x0f0f0f0fu;
         float v[8];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -148,6 +182,7 @@ __global__ void __launch_bounds__(kThreads) rot_dequant_kernel(const uint8_t* __
             const float x = v[k] * geo.c;
             v[k] = ((sb >> k) & 1u) ? -x : x;
         }
+        if (r >= geo.rows) continue;
         if constexpr (OT == KVQ_FP32) {
             float* p = static_cast<float*>(out) + (int64_t)r * D + 8 * lane;
             *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
