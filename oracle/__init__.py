@@ -67,6 +67,13 @@ def _declare(L):
     L.orc_rot_dequant.argtypes = [P, P, P, P] + [I64] * 5 + [P]
     L.orc_rot_dequant.restype = None
     L.orc_rot_decode_attn.argtypes = [P] * 8 + [I64] * 5 + [P, I64, C.c_double, P]
+    L.orc_mixed_plan.argtypes = [P, I64, P, P]
+    L.orc_mixed_plan.restype = None
+    L.orc_mixed_quant.argtypes = [P, I64, I64, P, P] + [P] * 8
+    L.orc_mixed_dequant.argtypes = [I64, I64, P, P] + [P] * 8 + [P]
+    L.orc_mixed_dequant.restype = None
+    L.orc_mixed_bytes.argtypes = [P, I64, I64, P]
+    L.orc_mixed_bytes.restype = None
     L.orc_colsum.argtypes = [P, I64, I64, I64, P]
     L.orc_colsum.restype = None
     L.orc_keep_count.argtypes = [I64, I64, I64]
@@ -401,6 +408,61 @@ def rot_decode_attn(c: dict, q: np.ndarray, sm_scale: float = 1.0) -> np.ndarray
                                    c["B"], c["T"], c["H"], c["d"], c["g"], _p(q), Hq, float(sm_scale), _p(out))
     _check(rc, "rot_decode_attn")
     return out
+
+
+# ---------------------------------------------- per-token mixed precision ---
+
+MIXED_BITS = (2, 4, 8, 16)   # tag 0, 1, 2, 3
+
+
+def pack_tags(tags: np.ndarray) -> np.ndarray:
+    """tag values 0..3 per row -> packed bytes (row r in bits 2(r%4) of byte r/4)."""
+    t = np.asarray(tags, np.uint8) & 3
+    n = len(t)
+    pad = np.zeros(-(-n // 4) * 4, np.uint8)
+    pad[:n] = t
+    q = pad.reshape(-1, 4)
+    return (q[:, 0] | (q[:, 1] << 2) | (q[:, 2] << 4) | (q[:, 3] << 6)).astype(np.uint8)
+
+
+def mixed_plan(tags_packed: np.ndarray, N: int):
+    tags_packed = np.ascontiguousarray(tags_packed, np.uint8)
+    slot = np.empty(N, np.int32)
+    counts = np.empty(4, np.int64)
+    lib().orc_mixed_plan(_p(tags_packed), N, _p(slot), _p(counts))
+    return slot, counts
+
+
+def mixed_quant(x: np.ndarray, tags_packed: np.ndarray) -> dict:
+    """x bf16-as-uint16 [N][C] -> dict with the slot plan, the counts and the four pools."""
+    x = np.ascontiguousarray(x, np.uint16)
+    N, Cc = x.shape
+    tags_packed = np.ascontiguousarray(tags_packed, np.uint8)
+    slot, counts = mixed_plan(tags_packed, N)
+    n2, n4, n8, n16 = (int(v) for v in counts)
+    m = dict(q2=np.zeros((n2, Cc // 4), np.uint8), s2=np.zeros(n2, np.float32),
+             q4=np.zeros((n4, Cc // 2), np.uint8), s4=np.zeros(n4, np.float32),
+             q8=np.zeros((n8, Cc), np.int8), s8=np.zeros(n8, np.float32), z8=np.zeros(n8, np.int8),
+             x16=np.zeros((n16, Cc), np.uint16))
+    rc = lib().orc_mixed_quant(_p(x), N, Cc, _p(tags_packed), _p(slot),
+                               *[_p(m[k]) for k in ("q2", "s2", "q4", "s4", "q8", "s8", "z8", "x16")])
+    _check(rc, "mixed_quant")
+    m.update(N=N, C=Cc, tags=tags_packed, slot=slot, counts=counts)
+    return m
+
+
+def mixed_dequant(m: dict) -> np.ndarray:
+    out = np.empty((m["N"], m["C"]), np.float32)
+    lib().orc_mixed_dequant(m["N"], m["C"], _p(m["tags"]), _p(m["slot"]),
+                            *[_p(m[k]) for k in ("q2", "s2", "q4", "s4", "q8", "s8", "z8", "x16")], _p(out))
+    return out
+
+
+def mixed_bytes(counts, N: int, Cc: int):
+    cnt = np.ascontiguousarray(counts, np.int64)
+    out = np.empty(3, np.uint64)
+    lib().orc_mixed_bytes(_p(cnt), N, Cc, _p(out))
+    return [int(v) for v in out]
 
 
 # ------------------------------------------------------------- accounting ---

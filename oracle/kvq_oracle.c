@@ -768,6 +768,121 @@ int orc_rot_decode_attn(const uint8_t* k_codes, const uint16_t* k_scale, const u
     return 0;
 }
 
+/* ------------------------------------------- per-token mixed precision --- */
+
+/* [Adaptive-bit blog: §2.1 four precision levels 2/4/8/16 bits, chosen per token by a
+ * controller; §3.1 per-token dynamic quantization, symmetric at 2 and 4 bits, asymmetric at 8
+ * bits and above; §3.2 a 2-bit precision tag per token (00/01/10/11 = 2/4/8/16 bits) and
+ * tokens of one precision stored contiguously.]  The controller is not part of this: the tags
+ * are given, packed four to a byte (row r in bits 2(r%4) .. 2(r%4)+1 of byte r/4).
+ * READINGS: a row is one token's C channels (the caller decides what a token row spans);
+ * 2 and 4 bits use the steps of Walkthrough §1.1 over the row, 8 bits those of §1.2 with
+ * qmin = -128, qmax = 127; a 16-bit row keeps its bf16 bits (the page's fp16 is its model's own
+ * 16-bit type); the rows of one width go to that width's pool in row order, at
+ * slot = number of earlier rows with the same tag; 2-bit codes are 2-bit two's complement, four
+ * to a byte (channel 4j+i in bits 2i, 2i+1 of byte j), 4-bit codes 4-bit two's complement, two to
+ * a byte (even channel in the low nibble); scales are fp32, the 8-bit zero point int8. */
+static int tag_of(const uint8_t* tags, int64_t r) { return (tags[r / 4] >> (2 * (r % 4))) & 3; }
+
+void orc_mixed_plan(const uint8_t* tags, int64_t N, int32_t* slot, int64_t counts[4]) {
+    int64_t n[4] = {0, 0, 0, 0};
+    for (int64_t r = 0; r < N; ++r) {
+        const int t = tag_of(tags, r);
+        slot[r] = (int32_t)n[t];
+        n[t] += 1;
+    }
+    for (int k = 0; k < 4; ++k) counts[k] = n[k];
+}
+
+int orc_mixed_quant(const uint16_t* x, int64_t N, int64_t C, const uint8_t* tags, const int32_t* slot,
+                    uint8_t* q2, float* s2, uint8_t* q4, float* s4, int8_t* q8, float* s8, int8_t* z8,
+                    uint16_t* x16) {
+    if (N <= 0 || C <= 0 || C % 8) return -1;
+    for (int64_t r = 0; r < N; ++r) {
+        const int t = tag_of(tags, r);
+        const int64_t k = slot[r];
+        const uint16_t* row = &x[r * C];
+        if (t == 3) {
+            memcpy(&x16[k * C], row, (size_t)C * 2);
+            continue;
+        }
+        if (t == 2) {
+            float mn = orc_bf16_to_f32(row[0]), mx = mn;
+            for (int64_t c = 1; c < C; ++c) {
+                const float v = orc_bf16_to_f32(row[c]);
+                if (v < mn) mn = v;
+                if (v > mx) mx = v;
+            }
+            float range = mx - mn;
+            if (range < RANGE_FLOOR) range = RANGE_FLOOR;
+            const float sc = range / 255.0f;
+            const int z = (int)clampd((double)rintf(-128.0f - mn / sc), -128.0, 127.0);
+            s8[k] = sc;
+            z8[k] = (int8_t)z;
+            for (int64_t c = 0; c < C; ++c)
+                q8[k * C + c] = (int8_t)clampd((double)rintf(orc_bf16_to_f32(row[c]) / sc) + (double)z, -128.0, 127.0);
+            continue;
+        }
+        const int qmax = t == 0 ? 1 : 7;
+        float absmax = 0.0f;
+        for (int64_t c = 0; c < C; ++c) {
+            const float a = fabsf(orc_bf16_to_f32(row[c]));
+            if (a > absmax) absmax = a;
+        }
+        if (absmax < RANGE_FLOOR) absmax = RANGE_FLOOR;
+        const float sc = absmax / (float)qmax;
+        if (t == 0) {
+            s2[k] = sc;
+            memset(&q2[k * (C / 4)], 0, (size_t)(C / 4));
+        } else {
+            s4[k] = sc;
+            memset(&q4[k * (C / 2)], 0, (size_t)(C / 2));
+        }
+        for (int64_t c = 0; c < C; ++c) {
+            const int q = (int)clampd((double)rintf(orc_bf16_to_f32(row[c]) / sc), -qmax, qmax);
+            if (t == 0) q2[k * (C / 4) + c / 4] |= (uint8_t)((q & 3) << (2 * (c % 4)));
+            else q4[k * (C / 2) + c / 2] |= (uint8_t)((q & 15) << (4 * (c % 2)));
+        }
+    }
+    return 0;
+}
+
+/* x_hat = q * scale (2, 4 bits), (q - zero_point) * scale (8 bits), the bf16 value (16 bits);
+ * fp32 out [N][C]. */
+void orc_mixed_dequant(int64_t N, int64_t C, const uint8_t* tags, const int32_t* slot,
+                       const uint8_t* q2, const float* s2, const uint8_t* q4, const float* s4,
+                       const int8_t* q8, const float* s8, const int8_t* z8, const uint16_t* x16, float* out) {
+    for (int64_t r = 0; r < N; ++r) {
+        const int t = tag_of(tags, r);
+        const int64_t k = slot[r];
+        for (int64_t c = 0; c < C; ++c) {
+            float v;
+            if (t == 3) {
+                v = orc_bf16_to_f32(x16[k * C + c]);
+            } else if (t == 2) {
+                v = ((float)q8[k * C + c] - (float)z8[k]) * s8[k];
+            } else if (t == 1) {
+                int q = (q4[k * (C / 2) + c / 2] >> (4 * (c % 2))) & 15;
+                if (q >= 8) q -= 16;
+                v = (float)q * s4[k];
+            } else {
+                int q = (q2[k * (C / 4) + c / 4] >> (2 * (c % 4))) & 3;
+                if (q >= 2) q -= 4;
+                v = (float)q * s2[k];
+            }
+            out[r * C + c] = v;
+        }
+    }
+}
+
+/* Bytes of a mixed-precision store: codes + scales (+ zero points) per pool, 16-bit rows, and
+ * the 2-bit tags; out[0] = data, out[1] = scales and zero points, out[2] = tags. */
+void orc_mixed_bytes(const int64_t counts[4], int64_t N, int64_t C, uint64_t out[3]) {
+    out[0] = (uint64_t)(counts[0] * (C / 4) + counts[1] * (C / 2) + counts[2] * C + counts[3] * C * 2);
+    out[1] = (uint64_t)(counts[0] * 4 + counts[1] * 4 + counts[2] * 5);
+    out[2] = (uint64_t)((N + 3) / 4);
+}
+
 /* ------------------------------------------------------------ accounting --- */
 
 /* [Explainer, group-size table] bytes = ceil(N/2) + ceil(N/g) * 4. */

@@ -98,6 +98,16 @@ int orc_rot_decode_attn(const uint8_t* k_codes, const uint16_t* k_scale, const u
                         int64_t B, int64_t T, int64_t Hkv, int64_t d, int64_t g,
                         const uint16_t* q, int64_t Hq, double sm_scale, double* out);
 
+/* Per-token mixed precision (tags packed four to a byte). */
+void orc_mixed_plan(const uint8_t* tags, int64_t N, int32_t* slot, int64_t counts[4]);
+int orc_mixed_quant(const uint16_t* x, int64_t N, int64_t C, const uint8_t* tags, const int32_t* slot,
+                    uint8_t* q2, float* s2, uint8_t* q4, float* s4, int8_t* q8, float* s8, int8_t* z8,
+                    uint16_t* x16);
+void orc_mixed_dequant(int64_t N, int64_t C, const uint8_t* tags, const int32_t* slot,
+                       const uint8_t* q2, const float* s2, const uint8_t* q4, const float* s4,
+                       const int8_t* q8, const float* s8, const int8_t* z8, const uint16_t* x16, float* out);
+void orc_mixed_bytes(const int64_t counts[4], int64_t N, int64_t C, uint64_t out[3]);
+
 /* Accounting. */
 uint64_t orc_int4_bytes(uint64_t N, uint64_t g);
 int orc_int4_cache_sizes(int64_t B, int64_t T, int64_t H, int64_t d, int64_t g, int64_t R,

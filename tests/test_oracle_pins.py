@@ -944,3 +944,110 @@ def test_rot_attention_is_attention_over_the_unrotated_cache():
             p = np.exp(lg - lg.max())
             want = p @ Vx[b, h] / p.sum()
             assert np.allclose(out[b, hq], want, rtol=0, atol=1e-10)
+
+
+# ------------------------------------------------------ per-token mixed precision --
+
+def _mixed_case(N, Cc, seed):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((N, Cc)).astype(np.float32) * np.exp(rng.uniform(-2, 2, (N, 1))).astype(np.float32)
+    x[rng.random(N) < 0.1, :] += 3.0          # some rows offset from zero
+    tags = rng.integers(0, 4, N).astype(np.uint8)
+    return bf16(x), tags
+
+
+def _unpack(codes, bits, Cc):
+    per = 8 // bits
+    out = np.zeros((codes.shape[0], Cc), np.int64)
+    for i in range(per):
+        v = (codes.astype(np.int64) >> (bits * i)) & ((1 << bits) - 1)
+        v = np.where(v >= (1 << (bits - 1)), v - (1 << bits), v)
+        out[:, i::per] = v
+    return out
+
+
+def test_mixed_tag_packing_and_slots_bruteforce():
+    rng = np.random.default_rng(1)
+    tags = rng.integers(0, 4, 1001).astype(np.uint8)
+    packed = oracle.pack_tags(tags)
+    assert len(packed) == 251
+    for r in (0, 1, 2, 3, 4, 999, 1000):
+        assert (packed[r // 4] >> (2 * (r % 4))) & 3 == tags[r]
+    slot, counts = oracle.mixed_plan(packed, len(tags))
+    seen = [0, 0, 0, 0]
+    for r, t in enumerate(tags):
+        assert slot[r] == seen[t]
+        seen[t] += 1
+    assert list(counts) == seen == list(np.bincount(tags, minlength=4))
+
+
+@pytest.mark.parametrize("Cc", [64, 128, 4096])
+def test_mixed_rows_equal_the_per_channel_quantizers_on_one_row(Cc):
+    # a row quantized at 2 / 4 bits is the symmetric quantizer of Walkthrough §1.1 applied to that
+    # row as one channel; at 8 bits the asymmetric one of §1.2 with [-128, 127]; 16 bits keeps the bits
+    N = 60
+    xb, tags = _mixed_case(N, Cc, seed=Cc)
+    m = oracle.mixed_quant(xb, oracle.pack_tags(tags))
+    codes = {0: _unpack(m["q2"], 2, Cc), 1: _unpack(m["q4"], 4, Cc)}
+    for r in range(N):
+        t, k = int(tags[r]), int(m["slot"][r])
+        col = xb[r][:, None]                          # the row as one channel of Cc "rows"
+        if t in (0, 1):
+            q = np.zeros((Cc, 1), np.int8)
+            s = np.zeros(1, np.float32)
+            oracle.lib().orc_quant_sym(oracle._p(np.ascontiguousarray(col)), 1, 1, Cc, 1, 2 if t == 0 else 4,
+                                       oracle._p(q), oracle._p(s), None)
+            assert np.array_equal(codes[t][k], q[:, 0].astype(np.int64)), (r, t)
+            assert m["s2" if t == 0 else "s4"][k] == s[0]
+        elif t == 2:
+            q = np.zeros((Cc, 1), np.int8)
+            s = np.zeros(1, np.float32)
+            z = np.zeros(1, np.int8)
+            oracle.lib().orc_quant_asym(oracle._p(np.ascontiguousarray(col)), 1, 1, Cc, 1, -128, 127,
+                                        oracle._p(q), oracle._p(s), oracle._p(z))
+            assert np.array_equal(m["q8"][k], q[:, 0]) and m["s8"][k] == s[0] and m["z8"][k] == z[0]
+        else:
+            assert np.array_equal(m["x16"][k], xb[r])
+
+
+def test_mixed_round_trip_bounds_and_levels():
+    N, Cc = 200, 128
+    xb, tags = _mixed_case(N, Cc, seed=2)
+    m = oracle.mixed_quant(xb, oracle.pack_tags(tags))
+    x = f32(xb).astype(np.float64)
+    xh = oracle.mixed_dequant(m).astype(np.float64)
+    for r in range(N):
+        t, k = int(tags[r]), int(m["slot"][r])
+        if t == 3:
+            assert np.array_equal(xh[r], x[r])
+            continue
+        s = float({0: m["s2"], 1: m["s4"], 2: m["s8"]}[t][k])
+        qmax = {0: 1, 1: 7, 2: None}[t]
+        if qmax is not None:
+            # symmetric: s = absmax / qmax exactly as fp32 quotient; every value within s/2 of its level
+            assert np.float32(max(np.abs(x[r]).max(), np.float32(1e-8))) / np.float32(qmax) == np.float32(s)
+        # half a level, plus the fp32 rounding of the quotient x / s that the codes are taken from
+        # (a quotient that rounds onto a half-integer then rounds to even)
+        e = np.abs(x[r] - xh[r]) - 2.0**-22 * np.abs(x[r])
+        if t == 2:
+            # the rounded zero point can push the row's extremes one level past the code range:
+            # codes away from the bounds are within s/2, clipped ones within 3s/2
+            q = m["q8"][k].astype(np.int64)
+            inner = (q > -128) & (q < 127)
+            assert np.all(e[inner] <= s / 2) and np.all(e <= 1.5 * s), r
+        else:
+            assert np.all(e <= s / 2), (r, t)
+    # worst-case error shrinks with the width: mean |error| / row scale orders 2 > 4 > 8 bits
+    err = {t: np.mean([np.abs(x[r] - xh[r]).mean() / np.abs(x[r]).max() for r in range(N) if tags[r] == t])
+           for t in (0, 1, 2)}
+    assert err[0] > err[1] > err[2]
+
+
+def test_mixed_bytes_closed_form():
+    # counts (10, 20, 30, 40) of 2/4/8/16-bit rows of 128 channels, 100 rows
+    data, meta, tagb = oracle.mixed_bytes([10, 20, 30, 40], 100, 128)
+    assert data == 10 * 32 + 20 * 64 + 30 * 128 + 40 * 256
+    assert meta == 10 * 4 + 20 * 4 + 30 * 5
+    assert tagb == 25                                    # 2 bits per token
+    # tags are 2 bits of 2*128*8 = 2048 bits of a bf16 token row: 1/1024 of the unquantized store
+    assert oracle.mixed_bytes([0, 0, 0, 8192], 8192, 128)[2] / (8192 * 256) == 1 / 1024
