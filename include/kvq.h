@@ -227,6 +227,60 @@ int kvq_rot_decode_attn(const kvq_rot_cache* c, const int8_t* k_signs, const int
                         int64_t Hq, float sm_scale, void* out, int ot, void* ws, size_t ws_bytes, kvq_stream stream);
 
 /* ======================================================================
+ * Per-token mixed precision  [Adaptive-bit blog: §2.1 four precision levels,
+ * 2/4/8/16 bits, chosen per token by a controller; §3.1 per-token dynamic
+ * quantization, symmetric at 2 and 4 bits, asymmetric at 8 bits; §3.2 2-bit
+ * precision tags 00/01/10/11 = 2/4/8/16 bits, tokens of one precision stored
+ * contiguously.  Steps of Walkthrough §1.1 / §1.2 over a row.]
+ *
+ * The store holds N rows of C channels (a row is one token: the caller decides
+ * whether it spans one head, C = d, or all heads, C = H*d).  The controller that
+ * picks the widths is not part of this library: tags are given, packed four to a
+ * byte, row r in bits 2(r%4), 2(r%4)+1 of tags[r/4] (device).
+ *   tag 0, 2 bits, tag 1, 4 bits: qmax = 1 / 7; scale = max(max|x|, fp32(1e-8)) / qmax;
+ *     q = clip(round(x / scale), -qmax, qmax); x_hat = q * scale.
+ *   tag 2, 8 bits: scale = max(max x - min x, fp32(1e-8)) / 255;
+ *     zp = round(-128 - min x / scale) saturated to int8;
+ *     q = clip(round(x / scale) + zp, -128, 127); x_hat = (q - zp) * scale.
+ *   tag 3, 16 bits: the bf16 row itself.
+ * round() is round-half-to-even of the IEEE fp32 quotient; scales fp32.
+ * kvq_mixed_plan: slot[r] = number of rows before r with the same tag (int32, device)
+ *   and counts[4] = rows per tag (int64, device); workspace kvq_mixed_plan_ws(N).
+ * Pools (device, caller-allocated, cap[t] rows each, usually the counts):
+ *   q2 u8 [cap0][C/4] (2-bit two's complement, channel 4j+i in bits 2i..2i+1 of byte j),
+ *   s2 fp32 [cap0]; q4 u8 [cap1][C/2] (4-bit two's complement, even channel low), s4 fp32 [cap1];
+ *   q8 int8 [cap2][C], s8 fp32 [cap2], z8 int8 [cap2]; x16 bf16 [cap3][C].
+ * kvq_mixed_quant: x bf16 [N][C] (device) -> row r at slot[r] of its tag's pool.
+ * kvq_mixed_dequant: out [N][C] of type ot (fp32, or bf16 = RNE of the fp32 value).
+ * A row whose slot is outside [0, cap) of its pool is skipped (dequant writes 0).
+ * kvq_mixed_bytes (host): out[0] codes + 16-bit rows, out[1] scales + zero points,
+ *   out[2] tag bytes, for given counts.
+ * EINVAL: N < 1 or N >= 2^31; C not a power of two in [64, 8192]; NULL tags, slot,
+ *   counts or a needed pool; negative capacities; short workspace.
+ * ====================================================================== */
+typedef struct {
+    int64_t N, C;
+    const uint8_t* tags;
+    const int32_t* slot;
+    int64_t cap[4];
+    uint8_t* q2;
+    float* s2;
+    uint8_t* q4;
+    float* s4;
+    int8_t* q8;
+    float* s8;
+    int8_t* z8;
+    uint16_t* x16;
+} kvq_mixed_store;
+
+size_t kvq_mixed_plan_ws(int64_t N);
+int kvq_mixed_plan(const uint8_t* tags, int64_t N, int32_t* slot, int64_t* counts, void* ws, size_t ws_bytes,
+                   kvq_stream stream);
+int kvq_mixed_quant(const void* x, const kvq_mixed_store* m, kvq_stream stream);
+int kvq_mixed_dequant(const kvq_mixed_store* m, void* out, int ot, kvq_stream stream);
+int kvq_mixed_bytes(const int64_t counts[4], int64_t N, int64_t C, uint64_t out[3]);
+
+/* ======================================================================
  * Dequantization  [Walkthrough §1.3: x_hat = (q - zero_point) * scale]
  *
  * kind KVQ_FMT_PER_CHANNEL: desc -> kvq_pc_tensor; out [nb][R][C] dense.

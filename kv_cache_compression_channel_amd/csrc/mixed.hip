@@ -1,0 +1,399 @@
+// mixed.hip -- per-token mixed precision: every row (token) is stored at 2, 4, 8 or 16 bits as its
+// 2-bit tag says, rows of one width together in that width's pool.
+//
+// Adaptive-bit blog (自适应量化框架): §2.1 four precision levels 2/4/8/16 chosen per token by a
+// controller (the controller is not part of this library: tags are inputs); §3.1 per-token
+// dynamic quantization, symmetric at 2 and 4 bits, asymmetric at 8 bits; §3.2 2-bit precision
+// tags (00/01/10/11 = 2/4/8/16 bits) and tokens of one precision stored contiguously.  The
+// symmetric and asymmetric steps are those of the Walkthrough (KV Compression 公式到源码对照)
+// §1.1 and §1.2, taken over a row instead of over a channel.
+//
+// kvq_mixed_plan: slot[r] = number of earlier rows with the tag of row r (the row's place in its
+//   pool) and the four pool sizes.  Three launches: per-block tag counts (1024 rows per block,
+//   four rows = one tag byte per thread), a scan of the block counts, then per-row ranks inside the
+//   block.  The four counters travel packed in 16-bit fields of one 64-bit word, so a single block
+//   scan serves all four tags.
+// kvq_mixed_quant / kvq_mixed_dequant: C/8 lanes per row (at most 64), 8 channels per lane and
+//   chunk; the row's reduction (absmax, or min and max) finishes with xor shuffles inside the
+//   row's lanes.
+#include "int4_common.h"
+
+namespace kvq {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kPlanRows = 1024;   // rows per plan block (one tag byte per thread)
+
+__device__ __forceinline__ int tag_at(uint32_t byte, int i) { return (int)((byte >> (2 * i)) & 3u); }
+
+// Inclusive scan over the block of a 64-bit word of four 16-bit counters (sums stay below 2^16).
+__device__ __forceinline__ uint64_t block_scan_u64(uint64_t v, uint64_t* s_w) {
+    const int tid = threadIdx.x, lane = tid % 64, w = tid / 64;
+#pragma unroll
+    for (int off = 1; off < 64; off *= 2) {
+        const uint64_t o = __shfl_up(v, off);
+        if (lane >= off) v += o;
+    }
+    if (lane == 63) s_w[w] = v;
+    __syncthreads();
+    uint64_t base = 0;
+    for (int i = 0; i < w; ++i) base += s_w[i];
+    return v + base;
+}
+
+__global__ void __launch_bounds__(kThreads) mixed_count_kernel(const uint8_t* __restrict__ tags, int64_t N,
+                                                              uint64_t* __restrict__ blk) {
+    __shared__ uint64_t s_w[kThreads / 64];
+    const int64_t r0 = (int64_t)blockIdx.x * kPlanRows + 4 * threadIdx.x;
+    uint64_t c = 0;
+    if (r0 < N) {
+        const uint32_t byte = tags[r0 / 4];
+        for (int i = 0; i < 4 && r0 + i < N; ++i) c += (uint64_t)1 << (16 * tag_at(byte, i));
+    }
+    const uint64_t inc = block_scan_u64(c, s_w);
+    if (threadIdx.x == kThreads - 1) blk[blockIdx.x] = inc;
+}
+
+// One block: exclusive prefix of the block counts (in place, as 4 x 32-bit offsets per block) and
+// the totals.  Offsets can pass 2^16, so they are widened to 32-bit fields here.
+__global__ void __launch_bounds__(1024) mixed_scan_kernel(uint64_t* __restrict__ blk, uint4* __restrict__ off,
+                                                         int64_t nblk, int64_t* __restrict__ counts) {
+    __shared__ uint32_t s_part[1024 / 64][4];
+    const int tid = threadIdx.x, lane = tid % 64, w = tid / 64;
+    uint32_t carry[4] = {0u, 0u, 0u, 0u};
+    for (int64_t b0 = 0; b0 < nblk; b0 += 1024) {
+        const int64_t b = b0 + tid;
+        const uint64_t v = b < nblk ? blk[b] : 0;
+        uint32_t x[4], inc[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            x[k] = (uint32_t)((v >> (16 * k)) & 0xffffu);
+            inc[k] = x[k];
+        }
+#pragma unroll
+        for (int d = 1; d < 64; d *= 2) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const uint32_t o = __shfl_up(inc[k], d);
+                if (lane >= d) inc[k] += o;
+            }
+        }
+        if (lane == 63) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) s_part[w][k] = inc[k];
+        }
+        __syncthreads();
+        uint32_t base[4] = {carry[0], carry[1], carry[2], carry[3]};
+        for (int i = 0; i < w; ++i) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) base[k] += s_part[i][k];
+        }
+        if (b < nblk) off[b] = make_uint4(base[0] + inc[0] - x[0], base[1] + inc[1] - x[1], base[2] + inc[2] - x[2],
+                                          base[3] + inc[3] - x[3]);
+        uint32_t tot[4] = {0u, 0u, 0u, 0u};
+        for (int i = 0; i < 1024 / 64; ++i) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) tot[k] += s_part[i][k];
+        }
+        __syncthreads();   // s_part is rewritten by the next chunk
+#pragma unroll
+        for (int k = 0; k < 4; ++k) carry[k] += tot[k];
+    }
+    if (tid == 0) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) counts[k] = carry[k];
+    }
+}
+
+__global__ void __launch_bounds__(kThreads) mixed_slot_kernel(const uint8_t* __restrict__ tags, int64_t N,
+                                                             const uint4* __restrict__ off, int32_t* __restrict__ slot) {
+    __shared__ uint64_t s_w[kThreads / 64];
+    const int64_t r0 = (int64_t)blockIdx.x * kPlanRows + 4 * threadIdx.x;
+    uint32_t byte = 0;
+    uint64_t c = 0;
+    if (r0 < N) {
+        byte = tags[r0 / 4];
+        for (int i = 0; i < 4 && r0 + i < N; ++i) c += (uint64_t)1 << (16 * tag_at(byte, i));
+    }
+    uint64_t ex = block_scan_u64(c, s_w) - c;   // rows of each tag before this thread's rows
+    if (r0 >= N) return;
+    const uint4 o = off[blockIdx.x];
+    const uint32_t ob[4] = {o.x, o.y, o.z, o.w};
+    for (int i = 0; i < 4 && r0 + i < N; ++i) {
+        const int t = tag_at(byte, i);
+        slot[r0 + i] = (int32_t)(ob[t] + (uint32_t)((ex >> (16 * t)) & 0xffffu));
+        ex += (uint64_t)1 << (16 * t);
+    }
+}
+
+// round(x / s) with IEEE-division semantics: the reciprocal fast path of rint_div holds while
+// |x / s| < 256 (kvq_internal.h), larger quotients take the division.
+__device__ __forceinline__ float rint_q(float x, float s, float r) {
+    const float y = x * r;
+    float n = __builtin_rintf(y);
+    if (__builtin_fabsf(y - n) > 0.4999f || __builtin_fabsf(y) >= 255.0f) n = __builtin_rintf(x / s);
+    return n;
+}
+
+// xor-shuffle reductions over the LPR lanes of a row
+template <int LPR>
+__device__ __forceinline__ float row_max(float v) {
+#pragma unroll
+    for (int o = 1; o < LPR; o *= 2) v = vmax2(v, __shfl_xor(v, o));
+    return v;
+}
+template <int LPR>
+__device__ __forceinline__ float row_min(float v) {
+#pragma unroll
+    for (int o = 1; o < LPR; o *= 2) v = vmin2(v, __shfl_xor(v, o));
+    return v;
+}
+
+// One row per LPR lanes; NCH chunks of 8 channels per lane (C = 8 * LPR * NCH).  The row's chunks
+// are loaded before anything else; rows beyond N are skipped as a whole (uniform per row).
+template <int LPR, int NCH>
+__global__ void __launch_bounds__(kThreads) mixed_quant_kernel(const uint16_t* __restrict__ x, kvq_mixed_store m) {
+    constexpr int RPB = kThreads / LPR;
+    const int tid = threadIdx.x, lane = tid % LPR;
+    const int64_t r = (int64_t)blockIdx.x * RPB + tid / LPR;
+    if (r >= m.N) return;
+    const int64_t C = m.C;
+    uint4 raw[NCH];
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) raw[j] = *reinterpret_cast<const uint4*>(x + r * C + 8 * (lane + LPR * j));
+    const int t = tag_at(m.tags[r / 4], (int)(r % 4));
+    const int64_t k = m.slot[r];
+    const bool fits = k >= 0 && k < m.cap[t];
+    if (t == 3) {
+        if (!fits) return;
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) *reinterpret_cast<uint4*>(m.x16 + k * C + 8 * (lane + LPR * j)) = raw[j];
+        return;
+    }
+    float v[NCH][8];
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) unpack8(raw[j], v[j]);
+    if (t == 2) {
+        float mn = FLT_MAX, mx = -FLT_MAX;
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) minmax8(v[j], mn, mx);
+        mn = row_min<LPR>(mn);
+        mx = row_max<LPR>(mx);
+        const float range = vmax2(mx - mn, 1e-8f);
+        const float s = range / 255.0f;
+        const float zr = __builtin_rintf(-128.0f - mn / s);
+        const float z = vclamp(zr, -128.0f, 127.0f);
+        const float rs = 1.0f / s;
+        if (!fits) return;
+        if (lane == 0) {
+            m.s8[k] = s;
+            m.z8[k] = (int8_t)(int)z;
+        }
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) {
+            uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int q = (int)vclamp(rint_q(v[j][e], s, rs) + z, -128.0f, 127.0f);
+                if (e < 4) w0 |= ((uint32_t)q & 0xffu) << (8 * e);
+                else w1 |= ((uint32_t)q & 0xffu) << (8 * (e - 4));
+            }
+            *reinterpret_cast<uint2*>(m.q8 + k * C + 8 * (lane + LPR * j)) = make_uint2(w0, w1);
+        }
+        return;
+    }
+    // 2 or 4 bits, symmetric
+    float am = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NCH; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) am = vmax2(am, __builtin_fabsf(v[j][e]));
+    am = row_max<LPR>(am);
+    const float qmax = t == 0 ? 1.0f : 7.0f;
+    const float s = vmax2(am, 1e-8f) / qmax;
+    const float rs = 1.0f / s;
+    if (!fits) return;
+    if (lane == 0) (t == 0 ? m.s2 : m.s4)[k] = s;
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+        uint32_t w = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int q = (int)vclamp(rint_q(v[j][e], s, rs), -qmax, qmax);
+            w |= t == 0 ? ((uint32_t)q & 3u) << (2 * e) : ((uint32_t)q & 15u) << (4 * e);
+        }
+        const int c0 = 8 * (lane + LPR * j);
+        if (t == 0) *reinterpret_cast<uint16_t*>(m.q2 + k * (C / 4) + c0 / 4) = (uint16_t)w;
+        else *reinterpret_cast<uint32_t*>(m.q4 + k * (C / 2) + c0 / 2) = w;
+    }
+}
+
+template <int LPR, int NCH, int OT>
+__global__ void __launch_bounds__(kThreads) mixed_dequant_kernel(const kvq_mixed_store m, void* __restrict__ out) {
+    constexpr int RPB = kThreads / LPR;
+    const int tid = threadIdx.x, lane = tid % LPR;
+    const int64_t r = (int64_t)blockIdx.x * RPB + tid / LPR;
+    if (r >= m.N) return;
+    const int64_t C = m.C;
+    const int t = tag_at(m.tags[r / 4], (int)(r % 4));
+    const int64_t k = m.slot[r];
+    const bool fits = k >= 0 && k < m.cap[t];
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+        const int c0 = 8 * (lane + LPR * j);
+        float v[8];
+        if (!fits) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = 0.0f;
+        } else if (t == 3) {
+            unpack8(*reinterpret_cast<const uint4*>(m.x16 + k * C + c0), v);
+        } else if (t == 2) {
+            const uint2 w = *reinterpret_cast<const uint2*>(m.q8 + k * C + c0);
+            const float s = m.s8[k], z = (float)m.z8[k];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int q = (int)(int8_t)(((e < 4 ? w.x : w.y) >> (8 * (e % 4))) & 0xffu);
+                v[e] = ((float)q - z) * s;
+            }
+        } else if (t == 1) {
+            const uint32_t w = *reinterpret_cast<const uint32_t*>(m.q4 + k * (C / 2) + c0 / 2);
+            const float s = m.s4[k];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int q = ((int)((w >> (4 * e)) & 15u) ^ 8) - 8;   // 4-bit two's complement
+                v[e] = (float)q * s;
+            }
+        } else {
+            const uint32_t w = *reinterpret_cast<const uint16_t*>(m.q2 + k * (C / 4) + c0 / 4);
+            const float s = m.s2[k];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int q = ((int)((w >> (2 * e)) & 3u) ^ 2) - 2;    // 2-bit two's complement
+                v[e] = (float)q * s;
+            }
+        }
+        if constexpr (OT == KVQ_FP32) {
+            float* p = static_cast<float*>(out) + r * C + c0;
+            *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+            *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+        } else {
+            *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + r * C + c0) =
+                make_uint4(pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]), pack_bf2(v[4], v[5]), pack_bf2(v[6], v[7]));
+        }
+    }
+}
+
+// C = 8 * LPR * NCH with LPR = min(C / 8, 64)
+#define KVQ_MIXED_DISPATCH(C, LAUNCH)                      \
+    do {                                                   \
+        switch (C) {                                       \
+            case 64: LAUNCH(8, 1); break;                  \
+            case 128: LAUNCH(16, 1); break;                \
+            case 256: LAUNCH(32, 1); break;                \
+            case 512: LAUNCH(64, 1); break;                \
+            case 1024: LAUNCH(64, 2); break;               \
+            case 2048: LAUNCH(64, 4); break;               \
+            case 4096: LAUNCH(64, 8); break;               \
+            default: LAUNCH(64, 16); break;                \
+        }                                                  \
+    } while (0)
+
+int check_store(const kvq_mixed_store* m, const char* name, bool need_pools) {
+    KVQ_REQUIRE(m, "%s: NULL store descriptor", name);
+    KVQ_REQUIRE(m->N >= 1 && m->N < ((int64_t)1 << 31), "%s: need 1 <= N < 2^31", name);
+    KVQ_REQUIRE(m->C == 64 || m->C == 128 || m->C == 256 || m->C == 512 || m->C == 1024 || m->C == 2048 ||
+                    m->C == 4096 || m->C == 8192,
+                "%s: C must be a power of two in [64, 8192] (got %lld)", name, (long long)m->C);
+    KVQ_REQUIRE(m->tags && m->slot, "%s: NULL tags or slot", name);
+    for (int i = 0; i < 4; ++i) KVQ_REQUIRE(m->cap[i] >= 0, "%s: negative pool capacity", name);
+    if (need_pools) {
+        KVQ_REQUIRE(m->cap[0] == 0 || (m->q2 && m->s2), "%s: NULL 2-bit pool", name);
+        KVQ_REQUIRE(m->cap[1] == 0 || (m->q4 && m->s4), "%s: NULL 4-bit pool", name);
+        KVQ_REQUIRE(m->cap[2] == 0 || (m->q8 && m->s8 && m->z8), "%s: NULL 8-bit pool", name);
+        KVQ_REQUIRE(m->cap[3] == 0 || m->x16, "%s: NULL 16-bit pool", name);
+        KVQ_REQUIRE_ALIGNED(m->q2, "q2");
+        KVQ_REQUIRE_ALIGNED(m->q4, "q4");
+        KVQ_REQUIRE_ALIGNED(m->q8, "q8");
+        KVQ_REQUIRE_ALIGNED(m->x16, "x16");
+    }
+    return KVQ_OK;
+}
+
+}  // namespace
+}  // namespace kvq
+
+extern "C" {
+
+size_t kvq_mixed_plan_ws(int64_t N) {
+    if (N < 1) return 0;
+    const int64_t nblk = kvq::cdiv(N, kvq::kPlanRows);
+    return (size_t)(kvq::cdiv(nblk * 8, 16) * 16 + nblk * 16);
+}
+
+int kvq_mixed_plan(const uint8_t* tags, int64_t N, int32_t* slot, int64_t* counts, void* ws, size_t ws_bytes,
+                   kvq_stream stream) {
+    KVQ_REQUIRE(N >= 1 && N < ((int64_t)1 << 31), "kvq_mixed_plan: need 1 <= N < 2^31");
+    KVQ_REQUIRE(tags && slot && counts, "kvq_mixed_plan: NULL tags, slot or counts");
+    KVQ_REQUIRE(ws && ws_bytes >= kvq_mixed_plan_ws(N), "kvq_mixed_plan: workspace of %zu bytes needed",
+                kvq_mixed_plan_ws(N));
+    KVQ_REQUIRE_ALIGNED(ws, "ws");
+    const int64_t nblk = kvq::cdiv(N, kvq::kPlanRows);
+    uint64_t* blk = static_cast<uint64_t*>(ws);
+    uint4* off = reinterpret_cast<uint4*>(static_cast<char*>(ws) + kvq::cdiv(nblk * 8, 16) * 16);
+    KVQ_REQUIRE(kvq::cdiv(nblk * 8, 16) * 16 + nblk * 16 <= (int64_t)ws_bytes, "kvq_mixed_plan: workspace too small");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipLaunchKernelGGL(kvq::mixed_count_kernel, dim3((unsigned)nblk), dim3(kvq::kThreads), 0, st, tags, N, blk);
+    hipLaunchKernelGGL(kvq::mixed_scan_kernel, dim3(1), dim3(1024), 0, st, blk, off, nblk, counts);
+    hipLaunchKernelGGL(kvq::mixed_slot_kernel, dim3((unsigned)nblk), dim3(kvq::kThreads), 0, st, tags, N,
+                       static_cast<const uint4*>(off), slot);
+    return kvq::launch_status("kvq_mixed_plan");
+}
+
+int kvq_mixed_quant(const void* x, const kvq_mixed_store* m, kvq_stream stream) {
+    const int rc = kvq::check_store(m, "kvq_mixed_quant", true);
+    if (rc) return rc;
+    KVQ_REQUIRE(x, "kvq_mixed_quant: NULL x");
+    KVQ_REQUIRE_ALIGNED(x, "x");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const uint16_t* xp = static_cast<const uint16_t*>(x);
+#define KVQ_MQ(LPR, NCH)                                                                                    \
+    hipLaunchKernelGGL((kvq::mixed_quant_kernel<LPR, NCH>), dim3((unsigned)kvq::cdiv(m->N, kvq::kThreads / LPR)), \
+                       dim3(kvq::kThreads), 0, st, xp, *m)
+    KVQ_MIXED_DISPATCH(m->C, KVQ_MQ);
+#undef KVQ_MQ
+    return kvq::launch_status("kvq_mixed_quant");
+}
+
+int kvq_mixed_dequant(const kvq_mixed_store* m, void* out, int ot, kvq_stream stream) {
+    const int rc = kvq::check_store(m, "kvq_mixed_dequant", true);
+    if (rc) return rc;
+    KVQ_REQUIRE(out, "kvq_mixed_dequant: NULL out");
+    KVQ_REQUIRE(ot == KVQ_FP32 || ot == KVQ_BF16, "kvq_mixed_dequant: ot must be KVQ_FP32 or KVQ_BF16");
+    KVQ_REQUIRE_ALIGNED(out, "out");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+#define KVQ_MD(LPR, NCH)                                                                                       \
+    do {                                                                                                       \
+        const dim3 grid((unsigned)kvq::cdiv(m->N, kvq::kThreads / LPR));                                       \
+        if (ot == KVQ_FP32)                                                                                    \
+            hipLaunchKernelGGL((kvq::mixed_dequant_kernel<LPR, NCH, KVQ_FP32>), grid, dim3(kvq::kThreads), 0, st, \
+                               *m, out);                                                                       \
+        else                                                                                                   \
+            hipLaunchKernelGGL((kvq::mixed_dequant_kernel<LPR, NCH, KVQ_BF16>), grid, dim3(kvq::kThreads), 0, st, \
+                               *m, out);                                                                       \
+    } while (0)
+    KVQ_MIXED_DISPATCH(m->C, KVQ_MD);
+#undef KVQ_MD
+    return kvq::launch_status("kvq_mixed_dequant");
+}
+
+int kvq_mixed_bytes(const int64_t counts[4], int64_t N, int64_t C, uint64_t out[3]) {
+    KVQ_REQUIRE(counts && out, "kvq_mixed_bytes: NULL pointer");
+    KVQ_REQUIRE(N >= 0 && C >= 8 && C % 8 == 0, "kvq_mixed_bytes: invalid N or C");
+    for (int i = 0; i < 4; ++i) KVQ_REQUIRE(counts[i] >= 0, "kvq_mixed_bytes: negative count");
+    out[0] = (uint64_t)(counts[0] * (C / 4) + counts[1] * (C / 2) + counts[2] * C + counts[3] * C * 2);
+    out[1] = (uint64_t)(counts[0] * 4 + counts[1] * 4 + counts[2] * 5);
+    out[2] = (uint64_t)((N + 3) / 4);
+    return KVQ_OK;
+}
+
+}  // extern "C"

@@ -30,6 +30,7 @@ EXPORTED = [
     "kvq_decode_attn_int4_ws", "kvq_decode_attn_int4", "kvq_decode_attn_int4_h2o_ws", "kvq_decode_attn_int4_h2o",
     "kvq_select_ws", "kvq_h2o_select", "kvq_snapkv_select", "kvq_compact",
     "kvq_rot_cache_sizes", "kvq_rot_quant_int4", "kvq_rot_dequant", "kvq_rot_decode_attn_ws", "kvq_rot_decode_attn",
+    "kvq_mixed_plan_ws", "kvq_mixed_plan", "kvq_mixed_quant", "kvq_mixed_dequant", "kvq_mixed_bytes",
 ]
 
 
@@ -53,6 +54,13 @@ class RotDesc(C.Structure):
     _fields_ = [("B", C.c_int64), ("T", C.c_int64), ("H", C.c_int64), ("d", C.c_int64), ("g", C.c_int64),
                 ("k_codes", C.c_void_p), ("k_scale", C.c_void_p), ("k_zero", C.c_void_p),
                 ("v_codes", C.c_void_p), ("v_scale", C.c_void_p), ("v_zero", C.c_void_p)]
+
+
+class MixedDesc(C.Structure):
+    _fields_ = [("N", C.c_int64), ("C", C.c_int64), ("tags", C.c_void_p), ("slot", C.c_void_p),
+                ("cap", C.c_int64 * 4),
+                ("q2", C.c_void_p), ("s2", C.c_void_p), ("q4", C.c_void_p), ("s4", C.c_void_p),
+                ("q8", C.c_void_p), ("s8", C.c_void_p), ("z8", C.c_void_p), ("x16", C.c_void_p)]
 
 
 class PcDesc(C.Structure):
@@ -87,6 +95,12 @@ def lib():
     L.kvq_int4_append.argtypes = [P, P, P, I64, I64, P]
     L.kvq_int4_evict.argtypes = [P, P, P, P]
     L.kvq_rot_cache_sizes.argtypes = [I64] * 5 + [P, P]
+    L.kvq_mixed_plan_ws.argtypes = [I64]
+    L.kvq_mixed_plan_ws.restype = SZ
+    L.kvq_mixed_plan.argtypes = [P, I64, P, P, P, SZ, P]
+    L.kvq_mixed_quant.argtypes = [P, P, P]
+    L.kvq_mixed_dequant.argtypes = [P, P, I, P]
+    L.kvq_mixed_bytes.argtypes = [P, I64, I64, P]
     L.kvq_rot_quant_int4.argtypes = [P, P, P, P, P, P]
     L.kvq_rot_dequant.argtypes = [P, I, P, P, I, P]
     L.kvq_rot_decode_attn_ws.argtypes = [P, I64]
@@ -446,6 +460,89 @@ def rot_decode_attn(cache: RotCache, q: torch.Tensor, k_signs, v_signs, sm_scale
 def rot_attn_ws_bytes(cache: RotCache, Hq: int) -> int:
     desc = cache.desc()
     return int(lib().kvq_rot_decode_attn_ws(C.byref(desc), Hq))
+
+
+# ---------------------------------------------- per-token mixed precision --
+
+@dataclass
+class MixedStore:
+    """Rows of N x C at 2/4/8/16 bits per their tags: the plan (slot, counts) and the four pools."""
+    N: int
+    C: int
+    tags: torch.Tensor      # uint8 [ceil(N/4)], four 2-bit tags per byte
+    slot: torch.Tensor      # int32 [N]
+    cap: tuple
+    q2: torch.Tensor
+    s2: torch.Tensor
+    q4: torch.Tensor
+    s4: torch.Tensor
+    q8: torch.Tensor
+    s8: torch.Tensor
+    z8: torch.Tensor
+    x16: torch.Tensor
+
+    POOLS = ("q2", "s2", "q4", "s4", "q8", "s8", "z8", "x16")
+
+    def desc(self) -> MixedDesc:
+        def p(t):
+            return t.data_ptr() if t.numel() else None
+        d = MixedDesc(self.N, self.C, self.tags.data_ptr(), self.slot.data_ptr())
+        for i in range(4):
+            d.cap[i] = int(self.cap[i])
+        for f in self.POOLS:
+            setattr(d, f, p(getattr(self, f)))
+        return d
+
+    def nbytes(self) -> int:
+        return sum(getattr(self, f).numel() * getattr(self, f).element_size() for f in self.POOLS)
+
+
+def mixed_plan(tags: torch.Tensor, N: int, slot=None, counts=None, ws=None):
+    """Slots (int32 [N]) and rows per tag (int64 [4]) on the device."""
+    _need_cuda(tags)
+    if slot is None:
+        slot = torch.empty(N, dtype=torch.int32, device=tags.device)
+    if counts is None:
+        counts = torch.empty(4, dtype=torch.int64, device=tags.device)
+    w, wb = _ws(int(lib().kvq_mixed_plan_ws(N)), tags.device, ws)
+    _check(lib().kvq_mixed_plan(_p(tags), N, _p(slot), _p(counts), _p(w), wb, _stream(tags)))
+    return slot, counts
+
+
+def mixed_store_empty(N: int, Cc: int, tags: torch.Tensor, slot: torch.Tensor, cap, device) -> MixedStore:
+    n2, n4, n8, n16 = (int(v) for v in cap)
+
+    def e(shape, dt):
+        return torch.empty(shape, dtype=dt, device=device)
+    return MixedStore(N, Cc, tags, slot, (n2, n4, n8, n16), e((n2, Cc // 4), torch.uint8), e(n2, torch.float32),
+                      e((n4, Cc // 2), torch.uint8), e(n4, torch.float32), e((n8, Cc), torch.int8), e(n8, torch.float32),
+                      e(n8, torch.int8), e((n16, Cc), torch.bfloat16))
+
+
+def mixed_quant(x: torch.Tensor, store: MixedStore) -> MixedStore:
+    """x bf16 [N][C] -> the store's pools (slots and capacities as planned)."""
+    _need_cuda(x)
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_contiguous() or tuple(x.shape) != (store.N, store.C):
+        raise ValueError("x must be contiguous bfloat16 [N][C] matching the store")
+    d = store.desc()
+    _check(lib().kvq_mixed_quant(_p(x), C.byref(d), _stream(x)))
+    return store
+
+
+def mixed_quantize(x: torch.Tensor, tags: torch.Tensor) -> MixedStore:
+    """Plan, size the pools from the counts (one device-to-host copy), quantize."""
+    N, Cc = x.shape
+    slot, counts = mixed_plan(tags, N)
+    cap = [int(v) for v in counts.cpu()]
+    return mixed_quant(x, mixed_store_empty(N, Cc, tags, slot, cap, x.device))
+
+
+def mixed_dequant(store: MixedStore, out_dtype=torch.bfloat16, out=None):
+    if out is None:
+        out = torch.empty((store.N, store.C), dtype=out_dtype, device=store.slot.device)
+    d = store.desc()
+    _check(lib().kvq_mixed_dequant(C.byref(d), _p(out), _dt(out), _stream(out)))
+    return out
 
 
 # ------------------------------------------------------------------- stats --

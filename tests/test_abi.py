@@ -268,6 +268,33 @@ def test_rot_validation(L):
     assert list(sect) == [2 * 3 * 10 * 64, 2 * 3 * 10 * 2 * 2, 2 * 3 * 10 * 2 * 2] * 2 and tot.value == sum(sect)
 
 
+def test_mixed_validation(L):
+    def md(**kw):
+        d = kvq.MixedDesc(kw.get("N", 100), kw.get("C", 128), kw.get("tags", 0x200000), kw.get("slot", 0x200000))
+        for i, c in enumerate(kw.get("cap", (10, 20, 30, 40))):
+            d.cap[i] = c
+        for f in kvq.MixedStore.POOLS:
+            setattr(d, f, kw.get(f, 0x200000))
+        return d
+    for kw in (dict(N=0), dict(C=100), dict(C=32), dict(C=16384), dict(tags=None), dict(slot=None),
+               dict(cap=(10, -1, 0, 0)), dict(q4=None), dict(z8=None), dict(x16=None)):
+        assert L.kvq_mixed_quant(FAKE, C.byref(md(**kw)), None) == kvq.KVQ_EINVAL, kw
+        assert L.kvq_mixed_dequant(C.byref(md(**kw)), FAKE, 0, None) == kvq.KVQ_EINVAL, kw
+    # a pool that holds no rows may be NULL
+    assert L.kvq_mixed_quant(None, C.byref(md(cap=(0, 5, 0, 0), q2=None, s2=None)), None) == kvq.KVQ_EINVAL
+    assert L.kvq_mixed_dequant(C.byref(md()), FAKE, 9, None) == kvq.KVQ_EINVAL
+    assert L.kvq_mixed_quant(MISALIGNED, C.byref(md()), None) == kvq.KVQ_EALIGN
+    need = L.kvq_mixed_plan_ws(5000)
+    assert need >= 5 * 24
+    assert L.kvq_mixed_plan(FAKE, 5000, FAKE, FAKE, FAKE, need - 1, None) == kvq.KVQ_EINVAL
+    assert L.kvq_mixed_plan(FAKE, 0, FAKE, FAKE, FAKE, need, None) == kvq.KVQ_EINVAL
+    assert L.kvq_mixed_plan(None, 5000, FAKE, FAKE, FAKE, need, None) == kvq.KVQ_EINVAL
+    out = (C.c_uint64 * 3)()
+    cnt = (C.c_int64 * 4)(10, 20, 30, 40)
+    assert L.kvq_mixed_bytes(cnt, 100, 128, out) == kvq.KVQ_OK
+    assert list(out) == [10 * 32 + 20 * 64 + 30 * 128 + 40 * 256, 10 * 4 + 20 * 4 + 30 * 5, 25]
+
+
 def test_select_and_compact_validation(L):
     big = 1 << 30
     h2o = L.kvq_h2o_select

@@ -1,0 +1,108 @@
+"""GPU parity: per-token mixed precision (given 2-bit tags for 2/4/8/16 bits) against the oracle,
+bit for bit: the slot plan and the counts, every pool (codes, scales, zero points, 16-bit rows),
+and the dequantized rows in fp32 (bf16 output = their round-to-nearest-even).
+
+Cases: every supported row width C (64 .. 8192), row counts that are not multiples of 4 or of
+the plan's 1024-row blocks, one row, a single width for all rows, rows of zeros, constant rows
+and rows far from zero, and the full decode cache (batch 16 x 32768 tokens x 8 KV heads, rows of
+d = 128: 4.2 M rows) with a mixed tag distribution, checked on the whole plan and on sampled rows."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from kv_cache_compression_channel_amd import kvq, synth
+from tests.gpu_helpers import DEV, assert_bits_equal, need_gpu, np_, say, u16
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    need_gpu()
+
+
+def bf16_rows(x: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(torch.bfloat16)
+
+
+def check(x: torch.Tensor, tags: np.ndarray, what: str):
+    N, Cc = x.shape
+    say("mixed", dict(what=what, N=N, C=Cc, counts=np.bincount(tags, minlength=4).tolist()))
+    packed = oracle.pack_tags(tags)
+    st = kvq.mixed_quantize(x.to(DEV), torch.from_numpy(packed).to(DEV))
+    o32 = kvq.mixed_dequant(st, torch.float32)
+    o16 = kvq.mixed_dequant(st, torch.bfloat16)
+    torch.cuda.synchronize()
+    want = oracle.mixed_quant(u16(x), packed)
+    assert_bits_equal(np_(st.slot), want["slot"], f"{what}: slots")
+    assert list(st.cap) == [int(v) for v in want["counts"]], what
+    for f in ("q2", "s2", "q4", "s4", "q8", "s8", "z8"):
+        g = np_(getattr(st, f))
+        assert_bits_equal(g.view(np.uint32) if g.dtype == np.float32 else g,
+                          want[f].view(np.uint32) if want[f].dtype == np.float32 else want[f], f"{what}: {f}")
+    assert_bits_equal(u16(st.x16), want["x16"], f"{what}: x16")
+    ref = oracle.mixed_dequant(want)
+    assert_bits_equal(np_(o32).view(np.uint32), ref.view(np.uint32), f"{what}: dequant fp32")
+    assert_bits_equal(u16(o16), oracle.f32_to_bf16(ref), f"{what}: dequant bf16")
+
+
+@pytest.mark.parametrize("Cc", [64, 128, 256, 512, 1024, 4096, 8192])
+def test_row_widths(Cc):
+    N = 1037 if Cc <= 1024 else 131
+    rng = np.random.default_rng(Cc)
+    x = rng.standard_normal((N, Cc)).astype(np.float32) * np.exp(rng.uniform(-3, 3, (N, 1))).astype(np.float32)
+    check(bf16_rows(x), rng.integers(0, 4, N).astype(np.uint8), f"C={Cc}")
+
+
+@pytest.mark.parametrize("N", [1, 3, 1024, 1025, 5003])
+def test_row_counts_and_single_width(N):
+    rng = np.random.default_rng(N)
+    x = bf16_rows(rng.standard_normal((N, 128)))
+    check(x, rng.integers(0, 4, N).astype(np.uint8), f"N={N}")
+    for t in range(4):
+        check(x, np.full(N, t, np.uint8), f"N={N} all tag {t}")
+
+
+def test_special_rows():
+    rng = np.random.default_rng(7)
+    N, Cc = 400, 256
+    x = rng.standard_normal((N, Cc)).astype(np.float32)
+    x[0:40] = 0.0                              # zeros: the 1e-8 floor
+    x[40:80] = 2.5                             # constant rows
+    x[80:120] += 1000.0                        # far from zero: huge quotients, saturated zero point
+    x[120:160] *= 1e-30                        # tiny values
+    x[160:200, ::7] = -3.0e4                   # large negative entries
+    tags = np.tile(np.arange(4, dtype=np.uint8), N // 4)
+    check(bf16_rows(x), tags, "special rows")
+
+
+def test_full_decode_cache_rows():
+    B, T, H, d = 16, 32768, 8, 128
+    N = B * T * H
+    say("mixed full", dict(N=N, C=d))
+    K, _, _ = synth.kv_layer(B, T, H, d, seed=0, device=DEV)
+    x = K.view(N, d)
+    rng = np.random.default_rng(0)
+    tags = rng.choice(4, N, p=[0.3, 0.4, 0.2, 0.1]).astype(np.uint8)
+    packed = oracle.pack_tags(tags)
+    st = kvq.mixed_quantize(x, torch.from_numpy(packed).to(DEV))
+    out = kvq.mixed_dequant(st, torch.float32)
+    torch.cuda.synchronize()
+    slot, counts = oracle.mixed_plan(packed, N)
+    assert_bits_equal(np_(st.slot), slot, "full plan: slots")
+    assert list(st.cap) == [int(v) for v in counts]
+    rows = np.unique(np.concatenate([rng.integers(0, N, 300), [0, N - 1]]))
+    xs = u16(x[torch.from_numpy(rows).to(DEV)])
+    for i, r in enumerate(rows):
+        t, k = int(tags[r]), int(slot[r])
+        one = oracle.mixed_quant(xs[i:i + 1], oracle.pack_tags(np.array([t], np.uint8)))
+        pools = {0: ("q2", "s2"), 1: ("q4", "s4"), 2: ("q8", "s8", "z8"), 3: ("x16",)}[t]
+        for f in pools:
+            g = getattr(st, f)[k:k + 1]
+            g = u16(g) if g.dtype == torch.bfloat16 else np_(g)
+            w = one[f]
+            assert_bits_equal(g.view(np.uint32) if g.dtype == np.float32 else g,
+                              w.view(np.uint32) if w.dtype == np.float32 else w, f"row {r} tag {t}: {f}")
+        assert_bits_equal(np_(out[int(r)]).view(np.uint32), oracle.mixed_dequant(one)[0].view(np.uint32),
+                          f"row {r}: dequant")
