@@ -149,20 +149,11 @@ __device__ __forceinline__ float row_min(float v) {
     return v;
 }
 
-// One row per LPR lanes; NCH chunks of 8 channels per lane (C = 8 * LPR * NCH).  The row's chunks
-// are loaded before anything else; rows beyond N are skipped as a whole (uniform per row).
+// One row: LPR lanes, NCH chunks of 8 channels per lane (C = 8 * LPR * NCH), tag t, pool row k.
 template <int LPR, int NCH>
-__global__ void __launch_bounds__(kThreads) mixed_quant_kernel(const uint16_t* __restrict__ x, kvq_mixed_store m) {
-    constexpr int RPB = kThreads / LPR;
-    const int tid = threadIdx.x, lane = tid % LPR;
-    const int64_t r = (int64_t)blockIdx.x * RPB + tid / LPR;
-    if (r >= m.N) return;
+__device__ __forceinline__ void quant_row(const kvq_mixed_store& m, const uint4 (&raw)[NCH], int t, int64_t k,
+                                          int lane) {
     const int64_t C = m.C;
-    uint4 raw[NCH];
-#pragma unroll
-    for (int j = 0; j < NCH; ++j) raw[j] = *reinterpret_cast<const uint4*>(x + r * C + 8 * (lane + LPR * j));
-    const int t = tag_at(m.tags[r / 4], (int)(r % 4));
-    const int64_t k = m.slot[r];
     const bool fits = k >= 0 && k < m.cap[t];
     if (t == 3) {
         if (!fits) return;
@@ -228,16 +219,72 @@ __global__ void __launch_bounds__(kThreads) mixed_quant_kernel(const uint16_t* _
     }
 }
 
-template <int LPR, int NCH, int OT>
-__global__ void __launch_bounds__(kThreads) mixed_dequant_kernel(const kvq_mixed_store m, void* __restrict__ out) {
-    constexpr int RPB = kThreads / LPR;
+// Rows of a block: NR passes of RPB consecutive rows (NR = 4 for rows of at most 512 channels);
+// every row's chunks, tag and slot are loaded before any row is processed.  Rows beyond N are
+// skipped as a whole (uniform over the row's lanes).
+template <int LPR, int NCH>
+__global__ void __launch_bounds__(kThreads) mixed_quant_kernel(const uint16_t* __restrict__ x, kvq_mixed_store m) {
+    constexpr int RPB = kThreads / LPR, NR = NCH == 1 ? 4 : 1;
     const int tid = threadIdx.x, lane = tid % LPR;
-    const int64_t r = (int64_t)blockIdx.x * RPB + tid / LPR;
-    if (r >= m.N) return;
+    const int64_t rb = (int64_t)blockIdx.x * RPB * NR + tid / LPR;
+    uint4 raw[NR][NCH];
+    int tg[NR];
+    int64_t kk[NR];
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+        const int64_t r = min(rb + (int64_t)RPB * i, m.N - 1);
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) raw[i][j] = *reinterpret_cast<const uint4*>(x + r * m.C + 8 * (lane + LPR * j));
+        tg[i] = tag_at(m.tags[r / 4], (int)(r % 4));
+        kk[i] = m.slot[r];
+    }
+#pragma unroll
+    for (int i = 0; i < NR; ++i)
+        if (rb + (int64_t)RPB * i < m.N) quant_row<LPR, NCH>(m, raw[i], tg[i], kk[i], lane);
+}
+
+// Dequantization: NR passes of RPB consecutive rows per block as in the quantizer; every row's tag
+// and slot first, then every row's pool words, then the arithmetic and the stores.
+template <int NCH>
+struct RowWords {
+    uint4 w[NCH];   // 16-bit rows: 8 bf16; 8 bits: .x .y codes; 4 bits: .x; 2 bits: .x low half
+    float s, z;
+};
+
+template <int LPR, int NCH>
+__device__ __forceinline__ void load_row_words(const kvq_mixed_store& m, int t, int64_t k, int lane, RowWords<NCH>& rw) {
     const int64_t C = m.C;
-    const int t = tag_at(m.tags[r / 4], (int)(r % 4));
-    const int64_t k = m.slot[r];
     const bool fits = k >= 0 && k < m.cap[t];
+    const int64_t kc = fits ? k : 0;
+    rw.s = 0.0f;
+    rw.z = 0.0f;
+    if (!fits) return;
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+        const int c0 = 8 * (lane + LPR * j);
+        if (t == 3) {
+            rw.w[j] = *reinterpret_cast<const uint4*>(m.x16 + kc * C + c0);
+        } else if (t == 2) {
+            const uint2 q = *reinterpret_cast<const uint2*>(m.q8 + kc * C + c0);
+            rw.w[j] = make_uint4(q.x, q.y, 0u, 0u);
+        } else if (t == 1) {
+            rw.w[j] = make_uint4(*reinterpret_cast<const uint32_t*>(m.q4 + kc * (C / 2) + c0 / 2), 0u, 0u, 0u);
+        } else {
+            rw.w[j] = make_uint4(*reinterpret_cast<const uint16_t*>(m.q2 + kc * (C / 4) + c0 / 4), 0u, 0u, 0u);
+        }
+    }
+    if (t == 2) {
+        rw.s = m.s8[kc];
+        rw.z = (float)m.z8[kc];
+    } else if (t < 2) {
+        rw.s = (t == 0 ? m.s2 : m.s4)[kc];
+    }
+}
+
+template <int LPR, int NCH, int OT>
+__device__ __forceinline__ void dequant_row(const kvq_mixed_store& m, const RowWords<NCH>& rw, int t, bool fits,
+                                            int64_t r, int lane, void* out) {
+    const int64_t C = m.C;
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
         const int c0 = 8 * (lane + LPR * j);
@@ -246,30 +293,24 @@ __global__ void __launch_bounds__(kThreads) mixed_dequant_kernel(const kvq_mixed
 #pragma unroll
             for (int e = 0; e < 8; ++e) v[e] = 0.0f;
         } else if (t == 3) {
-            unpack8(*reinterpret_cast<const uint4*>(m.x16 + k * C + c0), v);
+            unpack8(rw.w[j], v);
         } else if (t == 2) {
-            const uint2 w = *reinterpret_cast<const uint2*>(m.q8 + k * C + c0);
-            const float s = m.s8[k], z = (float)m.z8[k];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const int q = (int)(int8_t)(((e < 4 ? w.x : w.y) >> (8 * (e % 4))) & 0xffu);
-                v[e] = ((float)q - z) * s;
+                const int q = (int)(int8_t)(((e < 4 ? rw.w[j].x : rw.w[j].y) >> (8 * (e % 4))) & 0xffu);
+                v[e] = ((float)q - rw.z) * rw.s;
             }
         } else if (t == 1) {
-            const uint32_t w = *reinterpret_cast<const uint32_t*>(m.q4 + k * (C / 2) + c0 / 2);
-            const float s = m.s4[k];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const int q = ((int)((w >> (4 * e)) & 15u) ^ 8) - 8;   // 4-bit two's complement
-                v[e] = (float)q * s;
+                const int q = ((int)((rw.w[j].x >> (4 * e)) & 15u) ^ 8) - 8;   // 4-bit two's complement
+                v[e] = (float)q * rw.s;
             }
         } else {
-            const uint32_t w = *reinterpret_cast<const uint16_t*>(m.q2 + k * (C / 4) + c0 / 4);
-            const float s = m.s2[k];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const int q = ((int)((w >> (2 * e)) & 3u) ^ 2) - 2;    // 2-bit two's complement
-                v[e] = (float)q * s;
+                const int q = ((int)((rw.w[j].x >> (2 * e)) & 3u) ^ 2) - 2;    // 2-bit two's complement
+                v[e] = (float)q * rw.s;
             }
         }
         if constexpr (OT == KVQ_FP32) {
@@ -280,6 +321,53 @@ __global__ void __launch_bounds__(kThreads) mixed_dequant_kernel(const kvq_mixed
             *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + r * C + c0) =
                 make_uint4(pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]), pack_bf2(v[4], v[5]), pack_bf2(v[6], v[7]));
         }
+    }
+}
+
+template <int LPR, int NCH, int OT>
+__global__ void __launch_bounds__(kThreads) mixed_dequant_kernel(const kvq_mixed_store m, void* __restrict__ out) {
+    constexpr int RPB = kThreads / LPR, NR = NCH == 1 ? 4 : 1;
+    const int tid = threadIdx.x, lane = tid % LPR;
+    const int64_t rb = (int64_t)blockIdx.x * RPB * NR + tid / LPR;
+    if constexpr (NCH > 4) {
+        // wide rows (C >= 4096): four chunks at a time, so the words of a row do not all live at once
+        if (rb >= m.N) return;
+        const int t = tag_at(m.tags[rb / 4], (int)(rb % 4));
+        const int64_t k = m.slot[rb];
+        const bool fits = k >= 0 && k < m.cap[t];
+        kvq_mixed_store mq = m;
+#pragma unroll 1
+        for (int j0 = 0; j0 < NCH; j0 += 4) {
+            // a view of chunks j0 .. j0+3 as a 4-chunk row shifted by 8 * LPR * j0 channels
+            RowWords<4> rw;
+            const int64_t shift = (int64_t)8 * LPR * j0;
+            mq.x16 = m.x16 ? m.x16 + shift : nullptr;
+            mq.q8 = m.q8 ? m.q8 + shift : nullptr;
+            mq.q4 = m.q4 ? m.q4 + shift / 2 : nullptr;
+            mq.q2 = m.q2 ? m.q2 + shift / 4 : nullptr;
+            load_row_words<LPR, 4>(mq, t, k, lane, rw);
+            dequant_row<LPR, 4, OT>(mq, rw, t, fits, rb, lane,
+                                    OT == KVQ_FP32 ? (void*)(static_cast<float*>(out) + shift)
+                                                   : (void*)(static_cast<uint16_t*>(out) + shift));
+        }
+        return;
+    }
+    int tg[NR];
+    int64_t kk[NR];
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+        const int64_t r = min(rb + (int64_t)RPB * i, m.N - 1);
+        tg[i] = tag_at(m.tags[r / 4], (int)(r % 4));
+        kk[i] = m.slot[r];
+    }
+    RowWords<NCH> rw[NR];
+#pragma unroll
+    for (int i = 0; i < NR; ++i) load_row_words<LPR, NCH>(m, tg[i], kk[i], lane, rw[i]);
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+        const int64_t r = rb + (int64_t)RPB * i;
+        if (r < m.N)
+            dequant_row<LPR, NCH, OT>(m, rw[i], tg[i], kk[i] >= 0 && kk[i] < m.cap[tg[i]], r, lane, out);
     }
 }
 
@@ -357,7 +445,8 @@ int kvq_mixed_quant(const void* x, const kvq_mixed_store* m, kvq_stream stream) 
     hipStream_t st = static_cast<hipStream_t>(stream);
     const uint16_t* xp = static_cast<const uint16_t*>(x);
 #define KVQ_MQ(LPR, NCH)                                                                                    \
-    hipLaunchKernelGGL((kvq::mixed_quant_kernel<LPR, NCH>), dim3((unsigned)kvq::cdiv(m->N, kvq::kThreads / LPR)), \
+    hipLaunchKernelGGL((kvq::mixed_quant_kernel<LPR, NCH>),                                                 \
+                       dim3((unsigned)kvq::cdiv(m->N, (kvq::kThreads / LPR) * (NCH == 1 ? 4 : 1))),                \
                        dim3(kvq::kThreads), 0, st, xp, *m)
     KVQ_MIXED_DISPATCH(m->C, KVQ_MQ);
 #undef KVQ_MQ
@@ -373,7 +462,7 @@ int kvq_mixed_dequant(const kvq_mixed_store* m, void* out, int ot, kvq_stream st
     hipStream_t st = static_cast<hipStream_t>(stream);
 #define KVQ_MD(LPR, NCH)                                                                                       \
     do {                                                                                                       \
-        const dim3 grid((unsigned)kvq::cdiv(m->N, kvq::kThreads / LPR));                                       \
+        const dim3 grid((unsigned)kvq::cdiv(m->N, (kvq::kThreads / LPR) * (NCH == 1 ? 4 : 1)));               \
         if (ot == KVQ_FP32)                                                                                    \
             hipLaunchKernelGGL((kvq::mixed_dequant_kernel<LPR, NCH, KVQ_FP32>), grid, dim3(kvq::kThreads), 0, st, \
                                *m, out);                                                                       \
