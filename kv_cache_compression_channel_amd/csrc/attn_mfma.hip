@@ -19,7 +19,8 @@
 //                     - sum_t (p s_V)[t][n] * z_V[t][grp(c)],      P' = fp16(p * s_V)
 //           (the middle term is one more MFMA per V group against a constant-64 operand; the
 //           zero-point term is accumulated in fp32 from the unrounded p * s_V, so groups with a
-//           tiny scale and a huge zero point -- constant groups -- keep their value)
+//           tiny scale and a huge zero point -- constant groups -- keep their value; the rotated
+//           cache, whose output is rotated back, uses the fp16 P' there instead, see ROT below)
 //
 // The fp16 range is kept by the softmax reference: p = 2^(logit - ref) with
 // ref = Mlog + E - 15, where Mlog bounds every logit seen so far and 2^E bounds every V scale
@@ -71,6 +72,7 @@ struct MfmaArgs {
     const uint16_t* k_res;
     const uint16_t* v_res;
     const uint16_t* q;
+    const float* qrot;       // ROT mode: rotated queries [B][Hq][D] fp32, already times sm_scale * log2(e)
     float* ws;
     float* lgw;              // base-2 logits [B][Hq][ldl] (token t of head (b, hq) at row * ldl + t), or NULL
     int64_t ldl;
@@ -221,7 +223,12 @@ __device__ void residual_block(const MfmaArgs& a, ResLds& sr, int rb) {
     }
 }
 
-template <int GS, int NQ, bool LG>
+// ROT: the Hadamard-rotated per-token cache.  K is then grouped like V (a bf16 scale and zero per
+// token and g channels), so the query needs no per-group scaling: Q' = q' (fp16 hi + lo, made
+// once), each score MFMA covers 32 consecutive channels (one K group holds whole MFMAs), and
+//   logit = sum_grp s_K[t][grp] * (S'_grp[t][n] - (64 + z_K[t][grp]) * sum_{c in grp} Q'[n][c]).
+// The V side is the same as for the KIVI cache.
+template <int GS, int NQ, bool LG, bool ROT = false>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 attn_mfma_kernel(const MfmaArgs a) {
     constexpr int NG = D / GS;          // V groups per token
@@ -237,7 +244,8 @@ attn_mfma_kernel(const MfmaArgs a) {
         uint8_t v[kWaves][kTile * D / 2];
         float sz[kWaves][2 * kTile * NG * 2];     // (scale, zero) of a tile pair
         uint16_t kp[kWaves][(GS == 32 ? 4 : 2) * D];   // K group scale and zero rows of a tile pair
-        uint32_t qx[kWaves][64][PASS * 8];
+        uint32_t qx[kWaves][ROT ? 1 : 64][PASS * 8];
+        float ksz[kWaves][ROT ? 2 * kTile * NG * 2 : 1];   // ROT: K (scale, zero) of a tile pair
     };
     struct Merge {
         float m[kWaves][16], l[kWaves][16];
@@ -277,7 +285,60 @@ attn_mfma_kernel(const MfmaArgs a) {
         else return (n / NQ) % 4;
     };
     float qv[PASS][8];
-    {
+    // ROT: Q'^T operands (fp16 hi, lo) of MFMA chunk kk = channels 32 kk + 8 G + kPerm[j], the
+    // per-group sums of Q', and the power of two that keeps Q' inside the fp16 range
+    u32x4 rq_hi[ROT ? 4 : 1], rq_lo[ROT ? 4 : 1];
+    float rq_sum[ROT ? NG : 1];
+    float rq_scale = 1.0f;
+    if constexpr (ROT) {
+        const float* qp = a.qrot + (b * a.Hq + h * NQ + n % NQ) * D;
+        float x[4][8];
+        float qmax = 0.0f;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const float4 x0 = *reinterpret_cast<const float4*>(qp + 32 * kk + 8 * G);
+            const float4 x1 = *reinterpret_cast<const float4*>(qp + 32 * kk + 8 * G + 4);
+            const float v8[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                x[kk][j] = v8[kPerm[j]];
+                qmax = vmax2(qmax, __builtin_fabsf(v8[j]));
+            }
+        }
+        qmax = vmax2(qmax, xor_lane<16>(qmax));
+        qmax = vmax2(qmax, xor_lane<32>(qmax));
+        // |Q'| < 2^14 after the scaling (also for tiny queries, which are scaled up)
+        const int tau = qmax > 0.0f ? __builtin_amdgcn_frexp_expf(qmax) - 14 : 0;
+        rq_scale = __builtin_ldexpf(1.0f, tau);
+        float csum[4];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            uint32_t hw[4], lw[4];
+            float sum = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float x0 = __builtin_ldexpf(x[kk][2 * e], -tau), x1 = __builtin_ldexpf(x[kk][2 * e + 1], -tau);
+                hw[e] = pack_h2(x0, x1);
+                const half2v hh = __builtin_bit_cast(half2v, hw[e]);
+                lw[e] = pack_h2(x0 - (float)hh[0], x1 - (float)hh[1]);
+                const half2v ll = __builtin_bit_cast(half2v, lw[e]);
+                sum += ((float)hh[0] + (float)ll[0]) + ((float)hh[1] + (float)ll[1]);
+            }
+            rq_hi[kk] = u32x4{hw[0], hw[1], hw[2], hw[3]};
+            rq_lo[kk] = u32x4{lw[0], lw[1], lw[2], lw[3]};
+            sum += xor_lane<16>(sum);
+            sum += xor_lane<32>(sum);
+            csum[kk] = sum;      // the 32 channels of chunk kk, query n
+        }
+#pragma unroll
+        for (int gI = 0; gI < NG; ++gI) {
+            float t = 0.0f;
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+                if ((32 * kk) / GS == gI) t += csum[kk];
+            rq_sum[gI] = t;
+        }
+    } else {
         const uint16_t* qp = a.q + (b * a.Hq + h * NQ + n % NQ) * D + 32 * G;
 #pragma unroll
         for (int p = 0; p < PASS; ++p) {
@@ -339,9 +400,12 @@ attn_mfma_kernel(const MfmaArgs a) {
     struct SideRegs {
         u32x4 kp;
         uint32_t vs[SW], vz[SW];
+        uint32_t ks[SW], kz[SW];   // ROT: per-token K scale / zero, laid out like V's
     };
     const int last_row = Tq - 1;
     const uint16_t* kpsrc = (G % 2 ? kzero : kscale) + 8 * n;
+    const uint16_t* kspt = a.k_scale + bh * a.ldq * NG;   // ROT: per-token K scale / zero rows
+    const uint16_t* kzpt = a.k_zero + bh * a.ldq * NG;
     // tt0 is at most the last row; rows of the tile past the last row are clamped to it.  Lane
     // offsets are unsigned 32-bit so the loads take the scalar-base + vector-offset form.
     auto fetch_codes = [&](CodeRegs& r, int tt0) {
@@ -353,25 +417,33 @@ attn_mfma_kernel(const MfmaArgs a) {
         r.v[0] = *reinterpret_cast<const u32x4*>(vt + (uint32_t)(min(lane / 4, lim) * (D / 2) + 16 * (lane % 4)));
         r.v[1] = *reinterpret_cast<const u32x4*>(vt + (uint32_t)(min(16 + lane / 4, lim) * (D / 2) + 16 * (lane % 4)));
     };
-    auto fetch_side = [&](SideRegs& r, int tt0) {
+    // per-token (scale, zero) words of token lane of the pair: NG bf16 each
+    auto fetch_pt = [&](const uint16_t* sp, const uint16_t* zp, uint32_t (&os)[SW], uint32_t (&oz)[SW], int tt0) {
         const int lim = last_row - tt0;
-        const uint8_t* st = reinterpret_cast<const uint8_t*>(vsp + (int64_t)tt0 * NG);
-        const uint8_t* zt = reinterpret_cast<const uint8_t*>(vzp + (int64_t)tt0 * NG);
+        const uint8_t* st = reinterpret_cast<const uint8_t*>(sp + (int64_t)tt0 * NG);
+        const uint8_t* zt = reinterpret_cast<const uint8_t*>(zp + (int64_t)tt0 * NG);
         const uint32_t e = (uint32_t)min(lane, lim) * (NG * 2);   // byte offset of token lane's elements
         if constexpr (NG == 1) {   // one bf16 per token: the (b, h) row may be only 2-byte aligned
-            r.vs[0] = *reinterpret_cast<const uint16_t*>(st + e);
-            r.vz[0] = *reinterpret_cast<const uint16_t*>(zt + e);
+            os[0] = *reinterpret_cast<const uint16_t*>(st + e);
+            oz[0] = *reinterpret_cast<const uint16_t*>(zt + e);
         } else if constexpr (NG == 2) {
-            r.vs[0] = *reinterpret_cast<const uint32_t*>(st + e);
-            r.vz[0] = *reinterpret_cast<const uint32_t*>(zt + e);
+            os[0] = *reinterpret_cast<const uint32_t*>(st + e);
+            oz[0] = *reinterpret_cast<const uint32_t*>(zt + e);
         } else {
             const uint2 a2 = *reinterpret_cast<const uint2*>(st + e);
             const uint2 b2 = *reinterpret_cast<const uint2*>(zt + e);
-            r.vs[0] = a2.x; r.vs[1] = a2.y;
-            r.vz[0] = b2.x; r.vz[1] = b2.y;
+            os[0] = a2.x; os[1] = a2.y;
+            oz[0] = b2.x; oz[1] = b2.y;
         }
-        const int gt = GS == 32 ? min(tt0 + kTile * (G / 2), last_row) : tt0;
-        r.kp = *reinterpret_cast<const u32x4*>(kpsrc + (int64_t)(gt / GS) * D);
+    };
+    auto fetch_side = [&](SideRegs& r, int tt0) {
+        fetch_pt(vsp, vzp, r.vs, r.vz, tt0);
+        if constexpr (ROT) {
+            fetch_pt(kspt, kzpt, r.ks, r.kz, tt0);
+        } else {
+            const int gt = GS == 32 ? min(tt0 + kTile * (G / 2), last_row) : tt0;
+            r.kp = *reinterpret_cast<const u32x4*>(kpsrc + (int64_t)(gt / GS) * D);
+        }
     };
     // stage a tile in this wave's LDS (the even tile of a pair also stages the side data: V
     // (scale, zero) as fp32 pairs, K group rows); returns whether this lane holds a V scale at or
@@ -395,7 +467,19 @@ attn_mfma_kernel(const MfmaArgs a) {
                 smax = w == 0 ? vmax2(s0, s1) : vmax3(smax, s0, s1);
             }
         }
-        if (GS == 32 || (new_grp && lane < 32)) reinterpret_cast<u32x4*>(skp)[lane] = r.kp;
+        if constexpr (ROT) {
+            float* kst = sm.lp.ksz[wv];
+            if constexpr (NG == 1) {
+                reinterpret_cast<float2*>(kst)[lane] = make_float2(bf_lo(r.ks[0]), bf_lo(r.kz[0]));
+            } else {
+#pragma unroll
+                for (int w = 0; w < SW; ++w)
+                    reinterpret_cast<float4*>(kst)[lane * SW + w] =
+                        make_float4(bf_lo(r.ks[w]), bf_lo(r.kz[w]), bf_hi(r.ks[w]), bf_hi(r.kz[w]));
+            }
+        } else {
+            if (GS == 32 || (new_grp && lane < 32)) reinterpret_cast<u32x4*>(skp)[lane] = r.kp;
+        }
         return smax >= s_lim;
     };
 
@@ -405,7 +489,7 @@ attn_mfma_kernel(const MfmaArgs a) {
         const uint16_t* tkp = skp + (GS == 32 ? par * 2 * D : 0);   // this tile's K group rows
         const int nvalid = min(kTile, t_hi - t0);
         // ---- K group parameters -> Q'^T operand (fp16 hi + lo) and bias ----
-        if (new_grp) {
+        if (!ROT && new_grp) {
             // pass 1: largest |q * s_K| of this lane's chunks (the fp16 range check)
             auto chunk_scaled = [&](int p, float (&qs)[8]) {
                 const u32x4 sw = *reinterpret_cast<const u32x4*>(tkp + 32 * G + 8 * chunk_of(p));
@@ -473,31 +557,67 @@ attn_mfma_kernel(const MfmaArgs a) {
             c0 = __builtin_fmaf(bpart, lscale, ref);
         }
 
-        // ---- scores: chunk kk of Q' for query n % NQ was computed by lane qsrc(kk), pass qpass(kk) ----
+        // ---- scores ----
         __builtin_amdgcn_wave_barrier();
-        floatx4 sc[2] = {floatx4{0.0f, 0.0f, 0.0f, 0.0f}, floatx4{0.0f, 0.0f, 0.0f, 0.0f}};
-        const u32x4 kraw0 = *reinterpret_cast<const u32x4*>(sk + 16 * lane);
-        const u32x4 kraw1 = *reinterpret_cast<const u32x4*>(sk + 1024 + 16 * lane);
+        float lg[8];   // lane (n, G): tokens 4G+i (half 0) and 16+4G+i (half 1), i = 0..3; lg = logit - ref
+        if constexpr (ROT) {
+            // chunk kk = channels 32 kk .. 32 kk + 31: lane (n, G) takes dword 4 kk + G of token n's row
+            // (staged at byte 16 n + 256 kk + 4 G of the half), one accumulator per K group
+            floatx4 scg[2][NG];
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            const int src = PASS == 4 ? lane : 16 * G + n % NQ + (NQ == 8 ? 8 * (kk % 2) : NQ * kk);
-            const int ps = PASS == 4 ? kk : (NQ == 8 ? kk / 2 : 0);
-            const u32x4 hi = *reinterpret_cast<const u32x4*>(sqx + src * PASS * 8 + 8 * ps);
-            const u32x4 lo = *reinterpret_cast<const u32x4*>(sqx + src * PASS * 8 + 8 * ps + 4);
-            const half8 bh = __builtin_bit_cast(half8, hi), bl = __builtin_bit_cast(half8, lo);
+            for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-                const half8 ak = nib8((hf ? kraw1 : kraw0)[kk]);
-                sc[hf] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak, bh, sc[hf], 0, 0, 0);
-                sc[hf] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak, bl, sc[hf], 0, 0, 0);
+                for (int gI = 0; gI < NG; ++gI) scg[hf][gI] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const int gI = (32 * kk) / GS;
+                const half8 bh = __builtin_bit_cast(half8, rq_hi[kk]), bl = __builtin_bit_cast(half8, rq_lo[kk]);
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf) {
+                    const uint32_t w = *reinterpret_cast<const uint32_t*>(sk + 1024 * hf + 16 * n + 256 * kk + 4 * G);
+                    const half8 ak = nib8(w);
+                    scg[hf][gI] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak, bh, scg[hf][gI], 0, 0, 0);
+                    scg[hf][gI] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak, bl, scg[hf][gI], 0, 0, 0);
+                }
             }
-        }
-        // lane (n, G): tokens 4G+i (half 0) and 16+4G+i (half 1), i = 0..3; lg = logit - ref
-        float lg[8];
+            const float2* tks = reinterpret_cast<const float2*>(sm.lp.ksz[wv] + par * (kTile * NG * 2));
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            lg[i] = __builtin_fmaf(sc[0][i], lscale, -c0);
-            lg[4 + i] = __builtin_fmaf(sc[1][i], lscale, -c0);
+            for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int tl = 16 * hf + 4 * G + i;
+                    float acc = 0.0f;
+#pragma unroll
+                    for (int gI = 0; gI < NG; ++gI) {
+                        const float2 sz = tks[tl * NG + gI];
+                        acc = __builtin_fmaf(sz.x, __builtin_fmaf(-(64.0f + sz.y), rq_sum[gI], scg[hf][gI][i]), acc);
+                    }
+                    lg[4 * hf + i] = __builtin_fmaf(acc, rq_scale, -ref);
+                }
+        } else {
+            // chunk kk of Q' for query n % NQ was computed by lane qsrc(kk), pass qpass(kk)
+            floatx4 sc[2] = {floatx4{0.0f, 0.0f, 0.0f, 0.0f}, floatx4{0.0f, 0.0f, 0.0f, 0.0f}};
+            const u32x4 kraw0 = *reinterpret_cast<const u32x4*>(sk + 16 * lane);
+            const u32x4 kraw1 = *reinterpret_cast<const u32x4*>(sk + 1024 + 16 * lane);
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const int src = PASS == 4 ? lane : 16 * G + n % NQ + (NQ == 8 ? 8 * (kk % 2) : NQ * kk);
+                const int ps = PASS == 4 ? kk : (NQ == 8 ? kk / 2 : 0);
+                const u32x4 hi = *reinterpret_cast<const u32x4*>(sqx + src * PASS * 8 + 8 * ps);
+                const u32x4 lo = *reinterpret_cast<const u32x4*>(sqx + src * PASS * 8 + 8 * ps + 4);
+                const half8 bh = __builtin_bit_cast(half8, hi), bl = __builtin_bit_cast(half8, lo);
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf) {
+                    const half8 ak = nib8((hf ? kraw1 : kraw0)[kk]);
+                    sc[hf] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak, bh, sc[hf], 0, 0, 0);
+                    sc[hf] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak, bl, sc[hf], 0, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                lg[i] = __builtin_fmaf(sc[0][i], lscale, -c0);
+                lg[4 + i] = __builtin_fmaf(sc[1][i], lscale, -c0);
+            }
         }
         if constexpr (LG) {
             // the base-2 logits themselves (lg + ref), for the valid tokens of the real queries
@@ -585,8 +705,21 @@ attn_mfma_kernel(const MfmaArgs a) {
                     const float2 a0 = sz2(hf, i0 * NG + gI), a1 = sz2(hf, i1 * NG + gI);
                     const float ps0 = p[2 * e] * a0.x, ps1 = p[2 * e + 1] * a1.x;
                     w[e] = pack_h2(ps0, ps1);
-                    zsum[gI] = __builtin_fmaf(ps0, a0.y, zsum[gI]);
-                    zsum[gI] = __builtin_fmaf(ps1, a1.y, zsum[gI]);
+                    if constexpr (ROT) {
+                        // the output is rotated back afterwards, which gathers an error shared by a
+                        // group's channels into a few coordinates: the zero-point term takes the same
+                        // fp16 P' the codes are multiplied with, so its rounding cancels inside
+                        // (code - z); below the fp16 normal range (tiny scales of constant groups) P'
+                        // has lost its precision and the unrounded p * s_V is used instead
+                        const half2v hw2 = __builtin_bit_cast(half2v, w[e]);
+                        const float r0 = (float)hw2[0], r1 = (float)hw2[1];
+                        const float u0 = r0 >= 6.103515625e-05f ? r0 : ps0, u1 = r1 >= 6.103515625e-05f ? r1 : ps1;
+                        zsum[gI] = __builtin_fmaf(u0, a0.y, zsum[gI]);
+                        zsum[gI] = __builtin_fmaf(u1, a1.y, zsum[gI]);
+                    } else {
+                        zsum[gI] = __builtin_fmaf(ps0, a0.y, zsum[gI]);
+                        zsum[gI] = __builtin_fmaf(ps1, a1.y, zsum[gI]);
+                    }
                 }
                 bp[gI] = as_half8(w[0], w[1], w[2], w[3]);
             }
@@ -737,6 +870,18 @@ void launch_nq(const MfmaArgs& a, int nq, hipStream_t st) {
     }
 }
 
+template <int GS>
+void launch_nq_rot(const MfmaArgs& a, int nq, hipStream_t st) {
+    const dim3 grid((unsigned)(a.B * a.H * a.nsplit)), blk(kThreads);
+    switch (nq) {
+        case 1: hipLaunchKernelGGL((attn_mfma_kernel<GS, 1, false, true>), grid, blk, 0, st, a); break;
+        case 2: hipLaunchKernelGGL((attn_mfma_kernel<GS, 2, false, true>), grid, blk, 0, st, a); break;
+        case 4: hipLaunchKernelGGL((attn_mfma_kernel<GS, 4, false, true>), grid, blk, 0, st, a); break;
+        case 8: hipLaunchKernelGGL((attn_mfma_kernel<GS, 8, false, true>), grid, blk, 0, st, a); break;
+        default: hipLaunchKernelGGL((attn_mfma_kernel<GS, 16, false, true>), grid, blk, 0, st, a); break;
+    }
+}
+
 template <bool LG>
 void launch_g(const MfmaArgs& a, int64_t g, int nq, hipStream_t st) {
     if (g == 32) launch_nq<32, LG>(a, nq, st);
@@ -776,6 +921,37 @@ void launch_attn_mfma(const kvq_int4_cache* c, const void* q, int64_t Hq, float 
     const int nq = (int)(Hq / c->H);
     if (lgw) launch_g<true>(a, c->g, nq, st);
     else launch_g<false>(a, c->g, nq, st);
+}
+
+// The rotated per-token cache (d = 128): all T tokens on the matrix cores, no bf16 window.
+// qrot: rotated queries [B][Hq][128] fp32 (times sm_scale * log2 e); partials to ws slots
+// 0 .. nsplit - 1 of each (b, hq) in the layout the rotated combine reads.
+void launch_attn_mfma_rot(const kvq_rot_cache* c, const float* qrot, int64_t Hq, float* ws, int nsplit,
+                          int64_t split_len, hipStream_t st) {
+    MfmaArgs a{};
+    a.k_codes = c->k_codes; a.k_scale = c->k_scale; a.k_zero = c->k_zero;
+    a.v_codes = c->v_codes; a.v_scale = c->v_scale; a.v_zero = c->v_zero;
+    a.k_res = nullptr; a.v_res = nullptr;
+    a.R = 0;
+    a.nres = 0;
+    a.q = nullptr;
+    a.qrot = qrot;
+    a.ws = ws;
+    a.lgw = nullptr;
+    a.ldl = 0;
+    a.B = c->B; a.H = c->H; a.Hq = Hq;
+    a.Tq = (int)c->T; a.nKg = 0;
+    a.ldq = c->T;
+    a.ldk = 0;
+    a.ldr = 0;
+    a.split_len = (int)split_len;
+    a.nsplit = nsplit;
+    a.nslot = nsplit;
+    a.qscale = 1.0f;
+    const int nq = (int)(Hq / c->H);
+    if (c->g == 32) launch_nq_rot<32>(a, nq, st);
+    else if (c->g == 64) launch_nq_rot<64>(a, nq, st);
+    else launch_nq_rot<128>(a, nq, st);
 }
 
 }  // namespace kvq

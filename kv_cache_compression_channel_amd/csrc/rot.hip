@@ -20,6 +20,9 @@
 #include "int4_common.h"
 
 namespace kvq {
+void launch_attn_mfma_rot(const kvq_rot_cache* c, const float* qrot, int64_t Hq, float* ws, int nsplit,
+                          int64_t split_len, hipStream_t st);
+
 namespace {
 
 constexpr int kThreads = 256;
@@ -500,10 +503,14 @@ RotGeom geom(const kvq_rot_cache* c) {
     return g;
 }
 
+// Token splits: about 1024 blocks in all; at d = 128 the matrix-core kernel takes the splits
+// (multiples of 512 tokens, so every wave's range starts on a 128-token boundary), otherwise the
+// VALU kernel (multiples of 64).
+bool rot_mfma(const kvq_rot_cache* c) { return c->d == 128; }
 int64_t rot_split_len(const kvq_rot_cache* c) {
-    const int64_t want = cdiv(1024, c->B * c->H);
-    int64_t len = cdiv(cdiv(c->T, want), 64) * 64;
-    return len < 64 ? 64 : len;
+    const int64_t want = cdiv(1024, c->B * c->H), unit = rot_mfma(c) ? 512 : 64;
+    int64_t len = cdiv(cdiv(c->T, want), unit) * unit;
+    return len < unit ? unit : len;
 }
 
 }  // namespace
@@ -595,7 +602,10 @@ int kvq_rot_decode_attn(const kvq_rot_cache* c, const int8_t* k_signs, const int
     if (c->d == 64) kvq::launch_rot_q_combine<64>(a, ks, vs, ot, false, st);
     else if (c->d == 128) kvq::launch_rot_q_combine<128>(a, ks, vs, ot, false, st);
     else kvq::launch_rot_q_combine<256>(a, ks, vs, ot, false, st);
-    KVQ_DISPATCH_DG(c->d, c->g, kvq::launch_rot_attn, a, (int)nq, st);
+    if (kvq::rot_mfma(c))
+        kvq::launch_attn_mfma_rot(c, a.qr, Hq, a.part, a.nsplit, a.split_len, st);
+    else
+        KVQ_DISPATCH_DG(c->d, c->g, kvq::launch_rot_attn, a, (int)nq, st);
     if (c->d == 64) kvq::launch_rot_q_combine<64>(a, ks, vs, ot, true, st);
     else if (c->d == 128) kvq::launch_rot_q_combine<128>(a, ks, vs, ot, true, st);
     else kvq::launch_rot_q_combine<256>(a, ks, vs, ot, true, st);
