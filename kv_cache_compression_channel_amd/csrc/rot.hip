@@ -48,12 +48,11 @@ __device__ __forceinline__ float swz_xor(float x) {
 template <int M, int LPR>
 __device__ __forceinline__ void fwht_cross(float (&v)[8], int lane) {
     if constexpr (M < LPR) {
-        const bool hi = (lane & M) != 0;
+        // low lane of the pair: own + partner; high lane: partner - own.  fma(+-1, own, partner)
+        // rounds exactly like that addition or subtraction.
+        const float sg = (lane & M) ? -1.0f : 1.0f;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const float p = swz_xor<M>(v[k]);
-            v[k] = hi ? (p - v[k]) : (v[k] + p);
-        }
+        for (int k = 0; k < 8; ++k) v[k] = __builtin_fmaf(sg, v[k], swz_xor<M>(v[k]));
         fwht_cross<2 * M, LPR>(v, lane);
     }
 }
