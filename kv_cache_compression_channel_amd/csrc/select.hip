@@ -40,12 +40,12 @@ __global__ void __launch_bounds__(kSumThreads) colsum_kernel(const float* __rest
         for (; t + 8 <= T_obs; t += 8) {
             float4 v[8];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const float4*>(h + (t + u) * T + j);
+            for (int u = 0; u < 8; ++u) v[u] = ld_stream_f4(h + (t + u) * T + j);
 #pragma unroll
             for (int u = 0; u < 8; ++u) { acc.x += v[u].x; acc.y += v[u].y; acc.z += v[u].z; acc.w += v[u].w; }
         }
         for (; t < T_obs; ++t) {
-            const float4 v = *reinterpret_cast<const float4*>(h + t * T + j);
+            const float4 v = ld_stream_f4(h + t * T + j);
             acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
         }
         *reinterpret_cast<float4*>(out + j) = acc;
@@ -263,7 +263,7 @@ __global__ void __launch_bounds__(kSelThreads) h2o_fused_kernel(const float* __r
     int64_t heavy = budget - (T - rs);
     heavy = heavy < 0 ? 0 : (heavy > T ? T : heavy);
 
-    // ---- column sums: one step's eight float4 loads in flight per thread ----
+    // ---- column sums: one step's eight float4 loads in flight per thread (read once: streamed) ----
     float4 acc[kFusedChunks];
 #pragma unroll
     for (int i = 0; i < kFusedChunks; ++i) acc[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
@@ -272,7 +272,7 @@ __global__ void __launch_bounds__(kSelThreads) h2o_fused_kernel(const float* __r
         float4 a[kFusedChunks];
 #pragma unroll
         for (int i = 0; i < kFusedChunks; ++i)
-            if (tok(i) < Ti) a[i] = *reinterpret_cast<const float4*>(hr + t * T + tok(i));
+            if (tok(i) < Ti) a[i] = ld_stream_f4(hr + t * T + tok(i));
 #pragma unroll
         for (int i = 0; i < kFusedChunks; ++i) {
             if (tok(i) < Ti) { acc[i].x += a[i].x; acc[i].y += a[i].y; acc[i].z += a[i].z; acc[i].w += a[i].w; }

@@ -21,8 +21,8 @@ __device__ __forceinline__ void ld(const void* p, int64_t i, double (&v)[VEC]) {
     if constexpr (XT == KVQ_FP32) {
         const float* f = static_cast<const float*>(p) + i;
         if constexpr (VEC == 8) {
-            const float4 a = *reinterpret_cast<const float4*>(f);
-            const float4 b = *reinterpret_cast<const float4*>(f + 4);
+            const float4 a = ld_stream_f4(f);
+            const float4 b = ld_stream_f4(f + 4);
             v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
         } else {
             v[0] = *f;
@@ -30,7 +30,7 @@ __device__ __forceinline__ void ld(const void* p, int64_t i, double (&v)[VEC]) {
     } else {
         const uint16_t* h = static_cast<const uint16_t*>(p) + i;
         if constexpr (VEC == 8) {
-            const uint4 a = *reinterpret_cast<const uint4*>(h);
+            const uint4 a = ld_stream_u4(h);
             v[0] = bf_lo(a.x); v[1] = bf_hi(a.x); v[2] = bf_lo(a.y); v[3] = bf_hi(a.y);
             v[4] = bf_lo(a.z); v[5] = bf_hi(a.z); v[6] = bf_lo(a.w); v[7] = bf_hi(a.w);
         } else {
