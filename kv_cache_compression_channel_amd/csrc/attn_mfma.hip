@@ -412,10 +412,12 @@ attn_mfma_kernel(const MfmaArgs a) {
         const int lim = last_row - tt0;
         const uint8_t* kt = kc + (int64_t)tt0 * (D / 2);
         const uint8_t* vt = vc + (int64_t)tt0 * (D / 2);
-        r.k[0] = *reinterpret_cast<const u32x4*>(kt + (uint32_t)(min(n, lim) * (D / 2) + 16 * G));
-        r.k[1] = *reinterpret_cast<const u32x4*>(kt + (uint32_t)(min(16 + n, lim) * (D / 2) + 16 * G));
-        r.v[0] = *reinterpret_cast<const u32x4*>(vt + (uint32_t)(min(lane / 4, lim) * (D / 2) + 16 * (lane % 4)));
-        r.v[1] = *reinterpret_cast<const u32x4*>(vt + (uint32_t)(min(16 + lane / 4, lim) * (D / 2) + 16 * (lane % 4)));
+        r.k[0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kt + (uint32_t)(min(n, lim) * (D / 2) + 16 * G)));
+        r.k[1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kt + (uint32_t)(min(16 + n, lim) * (D / 2) + 16 * G)));
+        r.v[0] = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4*>(vt + (uint32_t)(min(lane / 4, lim) * (D / 2) + 16 * (lane % 4))));
+        r.v[1] = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4*>(vt + (uint32_t)(min(16 + lane / 4, lim) * (D / 2) + 16 * (lane % 4))));
     };
     // per-token (scale, zero) words of token lane of the pair: NG bf16 each
     auto fetch_pt = [&](const uint16_t* sp, const uint16_t* zp, uint32_t (&os)[SW], uint32_t (&oz)[SW], int tt0) {
@@ -424,14 +426,14 @@ attn_mfma_kernel(const MfmaArgs a) {
         const uint8_t* zt = reinterpret_cast<const uint8_t*>(zp + (int64_t)tt0 * NG);
         const uint32_t e = (uint32_t)min(lane, lim) * (NG * 2);   // byte offset of token lane's elements
         if constexpr (NG == 1) {   // one bf16 per token: the (b, h) row may be only 2-byte aligned
-            os[0] = *reinterpret_cast<const uint16_t*>(st + e);
-            oz[0] = *reinterpret_cast<const uint16_t*>(zt + e);
+            os[0] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(st + e));
+            oz[0] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(zt + e));
         } else if constexpr (NG == 2) {
-            os[0] = *reinterpret_cast<const uint32_t*>(st + e);
-            oz[0] = *reinterpret_cast<const uint32_t*>(zt + e);
+            os[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(st + e));
+            oz[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(zt + e));
         } else {
-            const uint2 a2 = *reinterpret_cast<const uint2*>(st + e);
-            const uint2 b2 = *reinterpret_cast<const uint2*>(zt + e);
+            const uint2 a2 = ld_stream_u2(st + e);
+            const uint2 b2 = ld_stream_u2(zt + e);
             os[0] = a2.x; os[1] = a2.y;
             oz[0] = b2.x; oz[1] = b2.y;
         }

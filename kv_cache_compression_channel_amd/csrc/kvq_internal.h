@@ -56,6 +56,11 @@ __device__ __forceinline__ uint4 ld_stream_u4(const void* p) {
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint2 ld_stream_u2(const void* p) {
+    const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+    return make_uint2(v.x, v.y);
+}
 __device__ __forceinline__ void st_stream_f4(float* p, float4 v) {
     __builtin_nontemporal_store(f32x4_t{v.x, v.y, v.z, v.w}, reinterpret_cast<f32x4_t*>(p));
 }

@@ -10,7 +10,8 @@
 // One launch covers K tiles, V tiles and the residual copy.  A tile is one (b, h) and a
 // block of consecutive tokens (g tokens for K, 64 for V) across all d channels.  Lane
 // layout: d/8 lanes per token row, each owning 8 consecutive channels (one 16-byte load
-// of bf16, one 4-byte store of packed codes); the 256 threads cover 2048/d rows per pass.
+// of bf16, one 4-byte store of packed codes); a block of NT threads (256, or d*g/32 when that is
+// larger, so a K group is at most 4 rows per thread) covers 8*NT/d rows per pass.
 // Block order is (b, token block, h) with h fastest, so concurrently running blocks
 // read neighbouring token rows of the [B][T][H][d] input.
 #include "int4_common.h"
@@ -22,13 +23,18 @@ constexpr int kThreads = 256;
 constexpr int kVTile = 64;   // tokens per V tile
 constexpr int kResTile = 64; // tokens per residual tile
 
+// Threads per quantizer block: enough that a K group is at most 4 rows per thread (16 bytes
+// each), which keeps the tile in registers at no more than about 74 VGPRs.
 template <int D, int G>
-__global__ void __launch_bounds__(kThreads) int4_quant_kernel(const uint16_t* __restrict__ K,
+constexpr int quant_threads() { return D * G / 32 > kThreads ? D * G / 32 : kThreads; }
+
+template <int D, int G, int NT = quant_threads<D, G>()>
+__global__ void __launch_bounds__(NT) int4_quant_kernel(const uint16_t* __restrict__ K,
                                                               const uint16_t* __restrict__ V, I4Geom geo,
                                                               I4Ptrs out) {
     constexpr int LPR = D / 8;            // lanes per token row
-    constexpr int RPP = kThreads / LPR;   // rows per pass
-    constexpr int NW = kThreads / 64;     // waves
+    constexpr int RPP = NT / LPR;         // rows per pass
+    constexpr int NW = NT / 64;           // waves
     constexpr int NGD = D / G;            // V groups per token
     static_assert(G % RPP == 0 && kVTile % RPP == 0, "tile shape");
     constexpr int NP = kVTile * NGD > D ? kVTile * NGD : D;   // parameter slots
@@ -86,7 +92,7 @@ __global__ void __launch_bounds__(kThreads) int4_quant_kernel(const uint16_t* __
             for (int k = 0; k < 8; ++k) { s_mn[wave * D + 8 * lane + k] = mn[k]; s_mx[wave * D + 8 * lane + k] = mx[k]; }
         }
         __syncthreads();
-        for (int c = tid; c < D; c += kThreads) {
+        for (int c = tid; c < D; c += NT) {
             float a = s_mn[c], z = s_mx[c];
 #pragma unroll
             for (int w = 1; w < NW; ++w) { a = vmin2(a, s_mn[w * D + c]); z = vmax2(z, s_mx[w * D + c]); }
@@ -146,7 +152,7 @@ __global__ void __launch_bounds__(kThreads) int4_quant_kernel(const uint16_t* __
             if (lane % LPG == 0) { s_mn[r * NGD + grp] = mn; s_mx[r * NGD + grp] = mx; }
         }
         __syncthreads();
-        for (int p = tid; p < n * NGD; p += kThreads) {
+        for (int p = tid; p < n * NGD; p += NT) {
             const GroupParams gp = group_params(s_mn[p], s_mx[p]);
             const int64_t mi = ((b * H + h) * geo.ldq + t0) * NGD + p;
             out.v_scale[mi] = gp.sb;
@@ -341,7 +347,7 @@ I4Geom geom_of(const kvq_int4_cache* c) {
 template <int D, int G>
 void launch_quant(const uint16_t* K, const uint16_t* V, const I4Geom& g, const I4Ptrs& p, int64_t nblk,
                   hipStream_t st) {
-    hipLaunchKernelGGL((int4_quant_kernel<D, G>), dim3((unsigned)nblk), dim3(kThreads), 0, st, K, V, g, p);
+    hipLaunchKernelGGL((int4_quant_kernel<D, G>), dim3((unsigned)nblk), dim3(quant_threads<D, G>()), 0, st, K, V, g, p);
 }
 
 template <int D, int G>
