@@ -149,6 +149,27 @@ __device__ __forceinline__ float row_min(float v) {
     return v;
 }
 
+// Rows of a block share a wave when a row is narrower than a wave (LPR < 64).  The block's ROWS
+// rows (at most 64) are then sorted by tag, stably, by one wave: s_perm[q] = the row (relative to
+// the block) processed at position q, rows past N last.  The block still reads and writes its
+// own contiguous rows; only their order inside it changes, so a wave runs one precision's code
+// for all its rows but at the tag boundaries.
+template <int ROWS>
+__device__ __forceinline__ void block_tag_sort(const kvq_mixed_store& m, int64_t base, uint8_t* s_perm) {
+    const int tid = threadIdx.x;
+    if (tid < 64) {
+        const int64_t r = base + tid;
+        const int t = (tid < ROWS && r < m.N) ? tag_at(m.tags[r / 4], (int)(r % 4)) : 4;
+        const uint64_t b0 = __ballot(t == 0), b1 = __ballot(t == 1), b2 = __ballot(t == 2), b3 = __ballot(t == 3);
+        const int c0 = __popcll(b0), c1 = __popcll(b1), c2 = __popcll(b2), c3 = __popcll(b3);
+        const uint64_t mine = t == 0 ? b0 : t == 1 ? b1 : t == 2 ? b2 : t == 3 ? b3 : ~(b0 | b1 | b2 | b3);
+        const int off = t == 0 ? 0 : t == 1 ? c0 : t == 2 ? c0 + c1 : t == 3 ? c0 + c1 + c2 : c0 + c1 + c2 + c3;
+        const int pos = off + __popcll(mine & ((1ull << tid) - 1ull));
+        if (tid < ROWS) s_perm[pos] = (uint8_t)tid;
+    }
+    __syncthreads();
+}
+
 // One row: LPR lanes, NCH chunks of 8 channels per lane (C = 8 * LPR * NCH), tag t, pool row k.
 template <int LPR, int NCH>
 __device__ __forceinline__ void quant_row(const kvq_mixed_store& m, const uint4 (&raw)[NCH], int t, int64_t k,
@@ -219,20 +240,29 @@ __device__ __forceinline__ void quant_row(const kvq_mixed_store& m, const uint4 
     }
 }
 
-// Rows of a block: NR passes of RPB consecutive rows (NR = 4 for rows of at most 512 channels);
-// every row's chunks, tag and slot are loaded before any row is processed.  Rows beyond N are
-// skipped as a whole (uniform over the row's lanes).
+// Rows of a block: NR passes of RPB rows (NR = 4 for rows of at most 512 channels), the block's
+// rows in tag order when several rows share a wave; every row's chunks, tag and slot are loaded
+// before any row is processed.  Rows beyond N are skipped as a whole (uniform over the row's lanes).
 template <int LPR, int NCH>
 __global__ void __launch_bounds__(kThreads) mixed_quant_kernel(const uint16_t* __restrict__ x, kvq_mixed_store m) {
     constexpr int RPB = kThreads / LPR, NR = NCH == 1 ? 4 : 1;
-    const int tid = threadIdx.x, lane = tid % LPR;
-    const int64_t rb = (int64_t)blockIdx.x * RPB * NR + tid / LPR;
+    constexpr int ROWS = RPB * NR, RPW = 64 / LPR;   // rows per block, rows per wave per pass
+    constexpr bool SORT = LPR < 64 && ROWS <= 64;
+    __shared__ uint8_t s_perm[SORT ? ROWS : 1];
+    const int tid = threadIdx.x, lane = tid % LPR, lg = tid / LPR;
+    const int64_t base = (int64_t)blockIdx.x * ROWS;
+    if constexpr (SORT) block_tag_sort<ROWS>(m, base, s_perm);
+    // row of pass i of lane group lg; sorted, a wave takes RPW * NR consecutive positions
+    auto row = [&](int i) -> int64_t {
+        if constexpr (SORT) return base + s_perm[(lg / RPW) * (RPW * NR) + i * RPW + lg % RPW];
+        else return base + lg + (int64_t)RPB * i;
+    };
     uint4 raw[NR][NCH];
     int tg[NR];
     int64_t kk[NR];
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
-        const int64_t r = min(rb + (int64_t)RPB * i, m.N - 1);
+        const int64_t r = min(row(i), m.N - 1);
 #pragma unroll
         for (int j = 0; j < NCH; ++j) raw[i][j] = *reinterpret_cast<const uint4*>(x + r * m.C + 8 * (lane + LPR * j));
         tg[i] = tag_at(m.tags[r / 4], (int)(r % 4));
@@ -240,11 +270,11 @@ __global__ void __launch_bounds__(kThreads) mixed_quant_kernel(const uint16_t* _
     }
 #pragma unroll
     for (int i = 0; i < NR; ++i)
-        if (rb + (int64_t)RPB * i < m.N) quant_row<LPR, NCH>(m, raw[i], tg[i], kk[i], lane);
+        if (row(i) < m.N) quant_row<LPR, NCH>(m, raw[i], tg[i], kk[i], lane);
 }
 
-// Dequantization: NR passes of RPB consecutive rows per block as in the quantizer; every row's tag
-// and slot first, then every row's pool words, then the arithmetic and the stores.
+// Dequantization: NR passes of RPB rows per block in the quantizer's order; every row's tag and
+// slot first, then every row's pool words, then the arithmetic and the stores.
 template <int NCH>
 struct RowWords {
     uint4 w[NCH];   // 16-bit rows: 8 bf16; 8 bits: .x .y codes; 4 bits: .x; 2 bits: .x low half
@@ -327,8 +357,12 @@ __device__ __forceinline__ void dequant_row(const kvq_mixed_store& m, const RowW
 template <int LPR, int NCH, int OT>
 __global__ void __launch_bounds__(kThreads) mixed_dequant_kernel(const kvq_mixed_store m, void* __restrict__ out) {
     constexpr int RPB = kThreads / LPR, NR = NCH == 1 ? 4 : 1;
-    const int tid = threadIdx.x, lane = tid % LPR;
-    const int64_t rb = (int64_t)blockIdx.x * RPB * NR + tid / LPR;
+    constexpr int ROWS = RPB * NR, RPW = 64 / LPR;
+    constexpr bool SORT = LPR < 64 && ROWS <= 64;
+    __shared__ uint8_t s_perm[SORT ? ROWS : 1];
+    const int tid = threadIdx.x, lane = tid % LPR, lg = tid / LPR;
+    const int64_t base = (int64_t)blockIdx.x * ROWS;
+    const int64_t rb = base + lg;
     if constexpr (NCH > 4) {
         // wide rows (C >= 4096): four chunks at a time, so the words of a row do not all live at once
         if (rb >= m.N) return;
@@ -352,11 +386,16 @@ __global__ void __launch_bounds__(kThreads) mixed_dequant_kernel(const kvq_mixed
         }
         return;
     }
+    if constexpr (SORT) block_tag_sort<ROWS>(m, base, s_perm);
+    auto row = [&](int i) -> int64_t {
+        if constexpr (SORT) return base + s_perm[(lg / RPW) * (RPW * NR) + i * RPW + lg % RPW];
+        else return rb + (int64_t)RPB * i;
+    };
     int tg[NR];
     int64_t kk[NR];
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
-        const int64_t r = min(rb + (int64_t)RPB * i, m.N - 1);
+        const int64_t r = min(row(i), m.N - 1);
         tg[i] = tag_at(m.tags[r / 4], (int)(r % 4));
         kk[i] = m.slot[r];
     }
@@ -365,7 +404,7 @@ __global__ void __launch_bounds__(kThreads) mixed_dequant_kernel(const kvq_mixed
     for (int i = 0; i < NR; ++i) load_row_words<LPR, NCH>(m, tg[i], kk[i], lane, rw[i]);
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
-        const int64_t r = rb + (int64_t)RPB * i;
+        const int64_t r = row(i);
         if (r < m.N)
             dequant_row<LPR, NCH, OT>(m, rw[i], tg[i], kk[i] >= 0 && kk[i] < m.cap[tg[i]], r, lane, out);
     }
