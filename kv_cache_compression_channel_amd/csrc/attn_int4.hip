@@ -26,6 +26,7 @@ int check_cache_shape(const kvq_int4_cache* c, const char* name);
 void launch_attn_mfma(const kvq_int4_cache* c, const void* q, int64_t Hq, float qscale, float* ws, int nsplit,
                       int64_t split_len, int nslot, float* lgw, int64_t ldl, hipStream_t st);
 int res_splits(int64_t R);
+int mfma_waves(int64_t g, int64_t nq, bool lg);
 
 namespace {
 
@@ -378,20 +379,23 @@ struct SplitPlan {
     int nslot;
 };
 
-#ifndef KVQ_ATTN_BLOCKS
-#define KVQ_ATTN_BLOCKS 1024
-#endif
 
 int64_t split_len_for(int64_t n, int64_t want, int64_t unit) {
     int64_t len = cdiv(cdiv(n, want), unit) * unit;
     return len < unit ? unit : len;
 }
 
-SplitPlan plan_splits(int64_t B, int64_t H, int64_t T, int64_t R, int64_t d, int64_t g) {
+// Workgroups to aim for: the plain matrix-core kernel at 3 waves per SIMD holds 3 workgroups per
+// CU, and 768 of them fill the 256 CUs once; otherwise 1024 (2 rounds at 2 per CU; one round
+// measured the same).  The plan depends on the cache and the heads only, so the variant that also
+// writes logits (2 waves per SIMD) cuts the tokens the same way and its output is the plain
+// kernel's, bit for bit.
+SplitPlan plan_splits(int64_t B, int64_t H, int64_t T, int64_t R, int64_t d, int64_t g, int64_t nq) {
     SplitPlan p{};
     const int64_t Tq = T - R;
-    const int64_t want = cdiv(KVQ_ATTN_BLOCKS, B * H);    // aim for about KVQ_ATTN_BLOCKS blocks
     p.mfma = (d == 128) && Tq > 0;
+    const int64_t blocks = (p.mfma && mfma_waves(g, nq, false) == 3) ? 768 : 1024;
+    const int64_t want = cdiv(blocks, B * H);
     if (p.mfma) {
         p.len_q = split_len_for(Tq, want, 512);
         p.nsplit_q = (int)cdiv(Tq, p.len_q);
@@ -456,7 +460,7 @@ extern "C" {
 
 size_t kvq_decode_attn_int4_ws(const kvq_int4_cache* c, int64_t Hq) {
     if (!c || c->B < 1 || c->H < 1 || c->T < 1 || c->g < 1 || Hq < 1 || c->R < 0 || c->R > c->T) return 0;
-    const kvq::SplitPlan p = kvq::plan_splits(c->B, c->H, c->T, c->R, c->d, c->g);
+    const kvq::SplitPlan p = kvq::plan_splits(c->B, c->H, c->T, c->R, c->d, c->g, Hq / c->H);
     return (size_t)(c->B * Hq * p.nslot * (c->d + 2)) * sizeof(float);
 }
 
@@ -488,7 +492,7 @@ int decode_attn(const char* name, const kvq_int4_cache* c, const void* q, int64_
     KVQ_REQUIRE_ALIGNED(q, "q");
     KVQ_REQUIRE_ALIGNED(out, "out");
     KVQ_REQUIRE_ALIGNED(ws, "ws");
-    const SplitPlan p = plan_splits(c->B, c->H, c->T, c->R, c->d, c->g);
+    const SplitPlan p = plan_splits(c->B, c->H, c->T, c->R, c->d, c->g, nq);
     KVQ_REQUIRE(c->B * c->H * p.nslot < ((int64_t)1 << 31) && c->B * Hq * p.nslot < ((int64_t)1 << 31),
                 "%s: grid too large", name);
     AttnArgs a;

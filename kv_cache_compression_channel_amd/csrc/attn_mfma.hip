@@ -223,13 +223,22 @@ __device__ void residual_block(const MfmaArgs& a, ResLds& sr, int rb) {
     }
 }
 
+// Waves per SIMD the kernel is compiled for.  The plain KIVI kernel with at most 4 query heads
+// per KV head and groups of 64 or 128 fits in 168 VGPRs without spilling, so 3 workgroups share a
+// CU (47 KB of LDS each); the variants that also write logits, the rotated cache's and the
+// others need more registers and run 2 per SIMD.
+template <int GS, int NQ, bool LG, bool ROT>
+constexpr int attn_waves() {
+    return (!LG && !ROT && GS >= 64 && NQ <= 4) ? 3 : 2;
+}
+
 // ROT: the Hadamard-rotated per-token cache.  K is then grouped like V (a bf16 scale and zero per
 // token and g channels), so the query needs no per-group scaling: Q' = q' (fp16 hi + lo, made
 // once), each score MFMA covers 32 consecutive channels (one K group holds whole MFMAs), and
 //   logit = sum_grp s_K[t][grp] * (S'_grp[t][n] - (64 + z_K[t][grp]) * sum_{c in grp} Q'[n][c]).
 // The V side is the same as for the KIVI cache.
 template <int GS, int NQ, bool LG, bool ROT = false>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(attn_waves<GS, NQ, LG, ROT>())))
 attn_mfma_kernel(const MfmaArgs a) {
     constexpr int NG = D / GS;          // V groups per token
     constexpr int BPG = GS / 16;        // MFMA channel blocks per V group
@@ -240,8 +249,8 @@ attn_mfma_kernel(const MfmaArgs a) {
     // per-wave V code tile (32 tokens x 64 bytes), V (scale, zero) pairs in fp32, K group
     // scale/zero rows, the Q' exchange; the merge at the end reuses the same memory
     struct Loop {
-        uint8_t k[kWaves][kTile * D / 2];
-        uint8_t v[kWaves][kTile * D / 2];
+        uint8_t k[kWaves][2 * kTile * D / 2];   // the two tiles of a pair
+        uint8_t v[kWaves][2 * kTile * D / 2];
         float sz[kWaves][2 * kTile * NG * 2];     // (scale, zero) of a tile pair
         uint16_t kp[kWaves][(GS == 32 ? 4 : 2) * D];   // K group scale and zero rows of a tile pair
         uint32_t qx[kWaves][ROT ? 1 : 64][PASS * 8];
@@ -450,11 +459,13 @@ attn_mfma_kernel(const MfmaArgs a) {
     // stage a tile in this wave's LDS (the even tile of a pair also stages the side data: V
     // (scale, zero) as fp32 pairs, K group rows); returns whether this lane holds a V scale at or
     // above the current bound 2^e_s
-    auto stage_codes = [&](const CodeRegs& r) {
-        *reinterpret_cast<u32x4*>(sk + 16 * lane) = r.k[0];
-        *reinterpret_cast<u32x4*>(sk + 16 * lane + 1024) = r.k[1];
-        *reinterpret_cast<u32x4*>(sv + 16 * lane) = r.v[0];
-        *reinterpret_cast<u32x4*>(sv + 16 * lane + 1024) = r.v[1];
+    auto stage_codes = [&](const CodeRegs& r, int par) {
+        uint8_t* skt = sk + par * (kTile * D / 2);
+        uint8_t* svt = sv + par * (kTile * D / 2);
+        *reinterpret_cast<u32x4*>(skt + 16 * lane) = r.k[0];
+        *reinterpret_cast<u32x4*>(skt + 16 * lane + 1024) = r.k[1];
+        *reinterpret_cast<u32x4*>(svt + 16 * lane) = r.v[0];
+        *reinterpret_cast<u32x4*>(svt + 16 * lane + 1024) = r.v[1];
     };
     auto stage_side = [&](const SideRegs& r, bool new_grp) -> bool {
         float smax;
@@ -485,13 +496,11 @@ attn_mfma_kernel(const MfmaArgs a) {
         return smax >= s_lim;
     };
 
-    // ---- one 32-token tile from the staged LDS copy ----
-    auto compute = [&](int t0, bool new_grp, bool big_s, int par) {
-        const float* tsz = ssz + par * (kTile * NG * 2);            // this tile's (scale, zero) pairs
+    // ---- the tiles of a pair from their staged LDS copies (slot par = tile t0 + 32 par) ----
+    // K group parameters -> Q'^T operand (fp16 hi + lo) and bias, for the group of tile par
+    auto setup_group = [&](int par) {
         const uint16_t* tkp = skp + (GS == 32 ? par * 2 * D : 0);   // this tile's K group rows
-        const int nvalid = min(kTile, t_hi - t0);
         // ---- K group parameters -> Q'^T operand (fp16 hi + lo) and bias ----
-        if (!ROT && new_grp) {
             // pass 1: largest |q * s_K| of this lane's chunks (the fp16 range check)
             auto chunk_scaled = [&](int p, float (&qs)[8]) {
                 const u32x4 sw = *reinterpret_cast<const u32x4*>(tkp + 32 * G + 8 * chunk_of(p));
@@ -557,11 +566,12 @@ attn_mfma_kernel(const MfmaArgs a) {
             bpart += xor_lane<16>(bpart);
             bpart += xor_lane<32>(bpart);
             c0 = __builtin_fmaf(bpart, lscale, ref);
-        }
-
-        // ---- scores ----
+    };
+    // scores of tile par -> lg (lane (n, G): tokens 4G+i (half 0) and 16+4G+i (half 1), i = 0..3;
+    // lg = logit - ref)
+    auto score_tile = [&](int par, float (&lg)[8]) {
+        const uint8_t* skt = sk + par * (kTile * D / 2);
         __builtin_amdgcn_wave_barrier();
-        float lg[8];   // lane (n, G): tokens 4G+i (half 0) and 16+4G+i (half 1), i = 0..3; lg = logit - ref
         if constexpr (ROT) {
             // chunk kk = channels 32 kk .. 32 kk + 31: lane (n, G) takes dword 4 kk + G of token n's row
             // (staged at byte 16 n + 256 kk + 4 G of the half), one accumulator per K group
@@ -576,7 +586,7 @@ attn_mfma_kernel(const MfmaArgs a) {
                 const half8 bh = __builtin_bit_cast(half8, rq_hi[kk]), bl = __builtin_bit_cast(half8, rq_lo[kk]);
 #pragma unroll
                 for (int hf = 0; hf < 2; ++hf) {
-                    const uint32_t w = *reinterpret_cast<const uint32_t*>(sk + 1024 * hf + 16 * n + 256 * kk + 4 * G);
+                    const uint32_t w = *reinterpret_cast<const uint32_t*>(skt + 1024 * hf + 16 * n + 256 * kk + 4 * G);
                     const half8 ak = nib8(w);
                     scg[hf][gI] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak, bh, scg[hf][gI], 0, 0, 0);
                     scg[hf][gI] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak, bl, scg[hf][gI], 0, 0, 0);
@@ -599,8 +609,8 @@ attn_mfma_kernel(const MfmaArgs a) {
         } else {
             // chunk kk of Q' for query n % NQ was computed by lane qsrc(kk), pass qpass(kk)
             floatx4 sc[2] = {floatx4{0.0f, 0.0f, 0.0f, 0.0f}, floatx4{0.0f, 0.0f, 0.0f, 0.0f}};
-            const u32x4 kraw0 = *reinterpret_cast<const u32x4*>(sk + 16 * lane);
-            const u32x4 kraw1 = *reinterpret_cast<const u32x4*>(sk + 1024 + 16 * lane);
+            const u32x4 kraw0 = *reinterpret_cast<const u32x4*>(skt + 16 * lane);
+            const u32x4 kraw1 = *reinterpret_cast<const u32x4*>(skt + 1024 + 16 * lane);
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
                 const int src = PASS == 4 ? lane : 16 * G + n % NQ + (NQ == 8 ? 8 * (kk % 2) : NQ * kk);
@@ -621,6 +631,10 @@ attn_mfma_kernel(const MfmaArgs a) {
                 lg[4 + i] = __builtin_fmaf(sc[1][i], lscale, -c0);
             }
         }
+    };
+    // the logits themselves (LG), and the masking of tokens past the wave's range
+    auto finish_logits = [&](int t0, float (&lg)[8]) {
+        const int nvalid = min(kTile, t_hi - t0);
         if constexpr (LG) {
             // the base-2 logits themselves (lg + ref), for the valid tokens of the real queries
             if (n < NQ) {
@@ -640,16 +654,21 @@ attn_mfma_kernel(const MfmaArgs a) {
                 }
             }
         }
-        if (nvalid < kTile) {   // only the last tile of a range is partial
+        if (nvalid < kTile) {   // only the last pair of a range is partial
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 if (4 * G + i >= nvalid) lg[i] = kNegBig;
                 if (16 + 4 * G + i >= nvalid) lg[4 + i] = kNegBig;
             }
         }
-        const float lmax = vmax3(vmax3(lg[0], lg[1], lg[2]), vmax3(lg[3], lg[4], lg[5]), vmax2(lg[6], lg[7]));
+    };
+    // the softmax reference, once for the ntl tiles of a pair
+    auto move_ref = [&](float (&lg)[2][8], int ntl, bool big_s) {
+        float lmax = vmax3(vmax3(lg[0][0], lg[0][1], lg[0][2]), vmax3(lg[0][3], lg[0][4], lg[0][5]), vmax2(lg[0][6], lg[0][7]));
+        if (ntl > 1)
+            lmax = vmax3(lmax, vmax3(vmax3(lg[1][0], lg[1][1], lg[1][2]), vmax3(lg[1][3], lg[1][4], lg[1][5]), lg[1][6]), lg[1][7]);
         if (__any(lmax > thr || big_s)) {
-            // move the reference: largest logit of the tile (+ margin) and largest V scale
+            // move the reference: largest logit of the tiles (+ margin) and largest V scale
             float tmax = vmax2(lmax, xor_lane<16>(lmax));
             tmax = vmax2(tmax, xor_lane<32>(tmax));
             // largest V scale of the tile pair: lane holds token lane's NG scales
@@ -675,7 +694,10 @@ attn_mfma_kernel(const MfmaArgs a) {
                 zsum[gI] *= alpha;
             }
 #pragma unroll
-            for (int i = 0; i < 8; ++i) lg[i] -= d;
+            for (int i = 0; i < 8; ++i) {
+                lg[0][i] -= d;
+                lg[1][i] -= d;
+            }
             ref += d;
             c0 += d;
             e_s = e_new;
@@ -683,6 +705,11 @@ attn_mfma_kernel(const MfmaArgs a) {
             thr = (float)(15 - e_s);
             started = true;
         }
+    };
+    // probabilities, P' and the value MFMAs of tile par
+    auto values_tile = [&](int par, float (&lg)[8]) {
+        const float* tsz = ssz + par * (kTile * NG * 2);            // this tile's (scale, zero) pairs
+        const uint8_t* svt = sv + par * (kTile * D / 2);
         float p[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -740,8 +767,8 @@ attn_mfma_kernel(const MfmaArgs a) {
                 uint32_t P[4][2];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const uint8_t* ra = sv + tok[2 * e] * (D / 2) + boff;
-                    const uint8_t* rb = sv + tok[2 * e + 1] * (D / 2) + boff;
+                    const uint8_t* ra = svt + tok[2 * e] * (D / 2) + boff;
+                    const uint8_t* rb = svt + tok[2 * e + 1] * (D / 2) + boff;
                     if constexpr (PB == 1) {
                         P[e][0] = (uint32_t)*ra | ((uint32_t)*rb << 16);                        // [a 0 b 0]
                     } else if constexpr (PB == 2) {
@@ -774,10 +801,11 @@ attn_mfma_kernel(const MfmaArgs a) {
         }
     };
 
-    // Tile i of the wave starts at t_lo + 32 i.  Each step stages a tile, refills its registers
-    // two tiles ahead and computes it; the loop runs whole pairs, and a tile at or past t_hi (the
-    // odd one of the last pair, at most) is fully masked.  Loads past the wave's last tile
-    // re-read that tile, which is still in cache.
+    // Tile i of the wave starts at t_lo + 32 i.  Each step stages a pair of tiles, refills their
+    // registers a pair ahead and computes the pair: both tiles' scores (their MFMA chains are
+    // independent), one update of the softmax reference for the 64 tokens, then each tile's values.
+    // A tile at or past t_hi (the odd one of the last pair, at most) is fully masked.  Loads past the
+    // wave's last tile re-read that tile, which is still in cache.
     if (t_lo < t_hi) {
         const int ntile = (t_hi - t_lo + kTile - 1) / kTile;
         const int t_last = t_lo + (ntile - 1) * kTile;
@@ -792,27 +820,28 @@ attn_mfma_kernel(const MfmaArgs a) {
         fetch_codes(co, tile_at(1));
         __builtin_amdgcn_sched_barrier(0);
         for (int i = 0; i < ntile; i += 2) {
-            {   // even tile: codes and the pair's side data
-                const int tt = t_lo + i * kTile;
-                const bool new_grp = (tt % GS == 0) || (i == 0);
-                stage_codes(ce);
-                const bool big_s = stage_side(sd, new_grp);
-                fetch_codes(ce, tile_at(i + 2));
-                fetch_side(sd, tile_at(i + 2));
-                __builtin_amdgcn_wave_barrier();
-                compute(tt, new_grp, big_s, 0);
-                __builtin_amdgcn_wave_barrier();     // LDS reads done before the next tile overwrites
-                __builtin_amdgcn_sched_barrier(0);   // keep tiles apart in the schedule (register pressure)
-            }
-            {   // odd tile: its side data came with the even one
-                const int tt = t_lo + (i + 1) * kTile;
-                stage_codes(co);
-                fetch_codes(co, tile_at(i + 3));
-                __builtin_amdgcn_wave_barrier();
-                compute(tt, GS == 32, false, 1);
-                __builtin_amdgcn_wave_barrier();
-                __builtin_amdgcn_sched_barrier(0);
-            }
+            const int tt = t_lo + i * kTile;
+            const bool new_grp = (tt % GS == 0) || (i == 0);
+            stage_codes(ce, 0);
+            const bool big_s = stage_side(sd, new_grp);
+            fetch_codes(ce, tile_at(i + 2));
+            fetch_side(sd, tile_at(i + 2));
+            __builtin_amdgcn_sched_barrier(0);
+            stage_codes(co, 1);
+            fetch_codes(co, tile_at(i + 3));
+            __builtin_amdgcn_wave_barrier();
+            float lg[2][8];
+            if (!ROT && new_grp) setup_group(0);
+            score_tile(0, lg[0]);
+            if (!ROT && GS == 32) setup_group(1);   // the odd tile starts the next group of 32
+            score_tile(1, lg[1]);
+            finish_logits(tt, lg[0]);
+            finish_logits(tt + kTile, lg[1]);
+            move_ref(lg, 2, big_s);
+            values_tile(0, lg[0]);
+            values_tile(1, lg[1]);
+            __builtin_amdgcn_wave_barrier();     // LDS reads done before the next pair overwrites
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 
@@ -894,6 +923,11 @@ void launch_g(const MfmaArgs& a, int64_t g, int nq, hipStream_t st) {
 }  // namespace
 
 int res_splits(int64_t R) { return (int)cdiv(R, kResTile); }
+
+// attn_waves of the instance launch_attn_mfma picks for these arguments (lg: logits written)
+int mfma_waves(int64_t g, int64_t nq, bool lg) {
+    return (!lg && g >= 64 && nq <= 4) ? 3 : 2;
+}
 
 // Launch the INT4 token range [0, Tq) on the matrix cores (d = 128) and the bf16 residual
 // [Tq, T) in blocks of the same grid.  Partials go to ws slots 0 .. nsplit-1 (INT4) and
