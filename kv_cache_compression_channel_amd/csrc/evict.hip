@@ -162,11 +162,8 @@ __global__ void __launch_bounds__(kThreads) int4_evict_kernel(const kvq_int4_cac
             v_values(raw[i], q, x);
             float mn = FLT_MAX, mx = -FLT_MAX;
             minmax8(x, mn, mx);
-#pragma unroll
-            for (int off = 1; off < LPG; off *= 2) {
-                mn = vmin2(mn, __shfl_xor(mn, off));
-                mx = vmax2(mx, __shfl_xor(mx, off));
-            }
+            mn = lane_group_reduce<LPG, false>(mn);
+            mx = lane_group_reduce<LPG, true>(mx);
             if (r < n) {
                 uint8_t* crow = dst.v_codes + (bh * geo.dldq + i0 + r) * (D / 2);
                 const int64_t dmi = (bh * geo.dldq + i0 + r) * NGD + (8 * lane) / G;

@@ -11,6 +11,28 @@
 
 namespace kvq {
 
+// Min or max over aligned groups of L lanes (L a power of two up to 64).  Within a row of 16 lanes
+// DPP lane moves, which are VALU operands and need no LDS: quad permutations [1,0,3,2] and
+// [2,3,0,1], then the half-row mirror (lane i <-> 7 - i) and the row mirror (i <-> 15 - i); after
+// each step every lane holds the value of its 2, 4, 8, 16 lanes.  Across rows, lane exchanges.
+// Every lane of a group ends with the group's value.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+template <int L, bool MAX>
+__device__ __forceinline__ float lane_group_reduce(float v) {
+    static_assert(L >= 1 && L <= 64 && (L & (L - 1)) == 0, "group of 1 to 64 lanes");
+    auto op = [](float a, float b) { return MAX ? vmax2(a, b) : vmin2(a, b); };
+    if constexpr (L >= 2) v = op(v, dpp_move<0xB1>(v));
+    if constexpr (L >= 4) v = op(v, dpp_move<0x4E>(v));
+    if constexpr (L >= 8) v = op(v, dpp_move<0x141>(v));
+    if constexpr (L >= 16) v = op(v, dpp_move<0x140>(v));
+    if constexpr (L >= 32) v = op(v, __shfl_xor(v, 16));
+    if constexpr (L >= 64) v = op(v, __shfl_xor(v, 32));
+    return v;
+}
+
 struct I4Geom {
     int64_t B, T, H, d, g, R, Tq;
     int64_t nKg;   // K groups per (b, h) = ceil(Tq / g)

@@ -135,19 +135,11 @@ __device__ __forceinline__ float rint_q(float x, float s, float r) {
     return n;
 }
 
-// xor-shuffle reductions over the LPR lanes of a row
+// reductions over the LPR lanes of a row
 template <int LPR>
-__device__ __forceinline__ float row_max(float v) {
-#pragma unroll
-    for (int o = 1; o < LPR; o *= 2) v = vmax2(v, __shfl_xor(v, o));
-    return v;
-}
+__device__ __forceinline__ float row_max(float v) { return lane_group_reduce<LPR, true>(v); }
 template <int LPR>
-__device__ __forceinline__ float row_min(float v) {
-#pragma unroll
-    for (int o = 1; o < LPR; o *= 2) v = vmin2(v, __shfl_xor(v, o));
-    return v;
-}
+__device__ __forceinline__ float row_min(float v) { return lane_group_reduce<LPR, false>(v); }
 
 // Rows of a block share a wave when a row is narrower than a wave (LPR < 64).  The block's ROWS
 // rows (at most 64) are then sorted by tag, stably, by one wave: s_perm[q] = the row (relative to

@@ -144,11 +144,8 @@ __global__ void __launch_bounds__(NT) int4_quant_kernel(const uint16_t* __restri
                 unpack8(raw[i], v);
                 minmax8(v, mn, mx);
             }
-#pragma unroll
-            for (int off = 1; off < LPG; off *= 2) {
-                mn = vmin2(mn, __shfl_xor(mn, off));
-                mx = vmax2(mx, __shfl_xor(mx, off));
-            }
+            mn = lane_group_reduce<LPG, false>(mn);
+            mx = lane_group_reduce<LPG, true>(mx);
             if (lane % LPG == 0) { s_mn[r * NGD + grp] = mn; s_mx[r * NGD + grp] = mx; }
         }
         __syncthreads();

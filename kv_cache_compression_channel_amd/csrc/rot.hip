@@ -118,11 +118,8 @@ __global__ void __launch_bounds__(kThreads) rot_quant_kernel(const uint16_t* __r
                 mn = vmin2(mn, v[k]);
                 mx = vmax2(mx, v[k]);
             }
-#pragma unroll
-            for (int off = 1; off < LPG; off *= 2) {
-                mn = vmin2(mn, __shfl_xor(mn, off));
-                mx = vmax2(mx, __shfl_xor(mx, off));
-            }
+            mn = lane_group_reduce<LPG, false>(mn);
+            mx = lane_group_reduce<LPG, true>(mx);
             const GroupParams gp = group_params(mn, mx);
             const bool fast = gp.z >= 0.0f && gp.z <= 15.0f;
             const float ps8[8] = {gp.s, gp.s, gp.s, gp.s, gp.s, gp.s, gp.s, gp.s};
