@@ -38,7 +38,8 @@ __global__ void __launch_bounds__(NT) int4_quant_kernel(const uint16_t* __restri
     constexpr int NGD = D / G;            // V groups per token
     static_assert(G % RPP == 0 && kVTile % RPP == 0, "tile shape");
     constexpr int NP = kVTile * NGD > D ? kVTile * NGD : D;   // parameter slots
-    __shared__ float s_mn[NW * D > NP ? NW * D : NP], s_mx[NW * D > NP ? NW * D : NP];
+    __shared__ __attribute__((aligned(16))) float s_mn[RPP * D > NP ? RPP * D : NP];
+    __shared__ __attribute__((aligned(16))) float s_mx[RPP * D > NP ? RPP * D : NP];
     __shared__ float s_ps[NP], s_pr[NP], s_pz[NP];
 
     const int tid = threadIdx.x, lane = tid % LPR, rg = tid / LPR;
@@ -78,24 +79,21 @@ __global__ void __launch_bounds__(NT) int4_quant_kernel(const uint16_t* __restri
 #pragma unroll
             for (int k = 0; k < 8; ++k) { mn[k] = vmin3(mn[k], v[k], u[k]); mx[k] = vmax3(mx[k], v[k], u[k]); }
         }
-        // rows of the same channel lanes inside the wave: lanes differ by multiples of LPR
-#pragma unroll
-        for (int off = LPR; off < 64; off *= 2) {
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                mn[k] = vmin2(mn[k], __shfl_xor(mn[k], off));
-                mx[k] = vmax2(mx[k], __shfl_xor(mx[k], off));
-            }
-        }
-        if ((tid % 64) < LPR) {
-#pragma unroll
-            for (int k = 0; k < 8; ++k) { s_mn[wave * D + 8 * lane + k] = mn[k]; s_mx[wave * D + 8 * lane + k] = mx[k]; }
+        // every row slot's partials to LDS (two 16-byte stores each), reduced over the RPP slots by
+        // the channel threads: no cross-lane permutes
+        {
+            float4* pm = reinterpret_cast<float4*>(s_mn + rg * D + 8 * lane);
+            float4* px = reinterpret_cast<float4*>(s_mx + rg * D + 8 * lane);
+            pm[0] = make_float4(mn[0], mn[1], mn[2], mn[3]);
+            pm[1] = make_float4(mn[4], mn[5], mn[6], mn[7]);
+            px[0] = make_float4(mx[0], mx[1], mx[2], mx[3]);
+            px[1] = make_float4(mx[4], mx[5], mx[6], mx[7]);
         }
         __syncthreads();
         for (int c = tid; c < D; c += NT) {
             float a = s_mn[c], z = s_mx[c];
 #pragma unroll
-            for (int w = 1; w < NW; ++w) { a = vmin2(a, s_mn[w * D + c]); z = vmax2(z, s_mx[w * D + c]); }
+            for (int w = 1; w < RPP; ++w) { a = vmin2(a, s_mn[w * D + c]); z = vmax2(z, s_mx[w * D + c]); }
             const GroupParams p = group_params(a, z);
             const int64_t mi = ((b * H + h) * geo.ldk + j) * D + c;
             out.k_scale[mi] = p.sb;
