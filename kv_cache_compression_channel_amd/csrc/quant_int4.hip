@@ -27,6 +27,10 @@ constexpr int kResTile = 64; // tokens per residual tile
 // each), which keeps the tile in registers at no more than about 74 VGPRs.
 template <int D, int G>
 constexpr int quant_threads() { return D * G / 32 > kThreads ? D * G / 32 : kThreads; }
+// Tokens per V tile of the quantizer: 64 per 256 threads, so a larger block also takes a larger
+// tile and every thread still quantizes the same number of V elements.
+template <int D, int G>
+constexpr int quant_vtile() { return kVTile * quant_threads<D, G>() / kThreads; }
 
 template <int D, int G, int NT = quant_threads<D, G>()>
 __global__ void __launch_bounds__(NT) int4_quant_kernel(const uint16_t* __restrict__ K,
@@ -36,8 +40,9 @@ __global__ void __launch_bounds__(NT) int4_quant_kernel(const uint16_t* __restri
     constexpr int RPP = NT / LPR;         // rows per pass
     constexpr int NW = NT / 64;           // waves
     constexpr int NGD = D / G;            // V groups per token
-    static_assert(G % RPP == 0 && kVTile % RPP == 0, "tile shape");
-    constexpr int NP = kVTile * NGD > D ? kVTile * NGD : D;   // parameter slots
+    constexpr int VT = quant_vtile<D, G>();   // tokens per V tile
+    static_assert(G % RPP == 0 && VT % RPP == 0, "tile shape");
+    constexpr int NP = VT * NGD > D ? VT * NGD : D;   // parameter slots
     __shared__ __attribute__((aligned(16))) float s_mn[RPP * D > NP ? RPP * D : NP];
     __shared__ __attribute__((aligned(16))) float s_mx[RPP * D > NP ? RPP * D : NP];
     __shared__ float s_ps[NP], s_pr[NP], s_pz[NP];
@@ -124,12 +129,12 @@ __global__ void __launch_bounds__(NT) int4_quant_kernel(const uint16_t* __restri
     bid -= nK;
     if (bid < nV) {
         // ---------------- V: 64 tokens, groups of G channels per token ----------------
-        constexpr int NR = kVTile / RPP;
+        constexpr int NR = VT / RPP;
         constexpr int LPG = G / 8;   // lanes per group
         const Bjh ix = split_bjh((uint32_t)bid, (uint32_t)H, (uint32_t)geo.nVt);
         const int64_t h = ix.h, jt = ix.j, b = ix.b;
-        const int64_t t0 = jt * kVTile;
-        const int n = (int)min<int64_t>(kVTile, Tq - t0);
+        const int64_t t0 = jt * VT;
+        const int n = (int)min<int64_t>(VT, Tq - t0);
         const int grp = (8 * lane) / G;
         uint4 raw[NR];
 #pragma unroll
@@ -339,10 +344,16 @@ I4Geom geom_of(const kvq_int4_cache* c) {
     return g;
 }
 
+// nblk is the grid at 64-token V tiles (what the callers check); the quantizer's own V tiles may be
+// larger, which only shrinks its grid.
 template <int D, int G>
 void launch_quant(const uint16_t* K, const uint16_t* V, const I4Geom& g, const I4Ptrs& p, int64_t nblk,
                   hipStream_t st) {
-    hipLaunchKernelGGL((int4_quant_kernel<D, G>), dim3((unsigned)nblk), dim3(quant_threads<D, G>()), 0, st, K, V, g, p);
+    (void)nblk;
+    I4Geom gq = g;
+    gq.nVt = cdiv(g.Tq, (int64_t)quant_vtile<D, G>());
+    const int64_t n = gq.B * gq.H * (gq.nKg + gq.nVt + gq.nRt);
+    hipLaunchKernelGGL((int4_quant_kernel<D, G>), dim3((unsigned)n), dim3(quant_threads<D, G>()), 0, st, K, V, gq, p);
 }
 
 template <int D, int G>
