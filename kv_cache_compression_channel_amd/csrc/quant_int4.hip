@@ -196,6 +196,11 @@ __global__ void __launch_bounds__(NT) int4_quant_kernel(const uint16_t* __restri
 // Dequantization of one side: x_hat = (q - z) * s rounded once.  q*s and z*s are exact
 // in fp32 (4-bit x 8-bit and 8-bit x 8-bit significands), so fma(q, s, -z*s) rounds the
 // exact value once.  Residual tokens are copied (bf16) or widened (fp32).
+// Tokens per K tile of the dequantizer: one group, but at least 64 tokens (two groups at g = 32),
+// so a block writes as many rows as a V tile's.
+template <int G>
+constexpr int dequant_ktile() { return G < kVTile ? kVTile : G; }
+
 template <int D, int G, bool IS_K, int OT>
 __global__ void __launch_bounds__(kThreads) int4_dequant_kernel(const uint8_t* __restrict__ codes,
                                                                 const uint16_t* __restrict__ scale,
@@ -204,11 +209,13 @@ __global__ void __launch_bounds__(kThreads) int4_dequant_kernel(const uint8_t* _
                                                                 void* __restrict__ out) {
     constexpr int LPR = D / 8;
     constexpr int RPP = kThreads / LPR;
-    constexpr int TILE = IS_K ? G : kVTile;
+    constexpr int TILE = IS_K ? dequant_ktile<G>() : kVTile;
+    constexpr int NGT = IS_K ? TILE / G : 1;   // K groups per tile
     constexpr int NGD = D / G;
+    static_assert(TILE % RPP == 0 && (!IS_K || G % RPP == 0), "tile shape");
     const int tid = threadIdx.x, lane = tid % LPR, rg = tid / LPR;
     const int64_t H = geo.H, T = geo.T, Tq = geo.Tq;
-    const int64_t ntile = IS_K ? geo.nKg : geo.nVt;
+    const int64_t ntile = IS_K ? (Tq + TILE - 1) / TILE : geo.nVt;
     int64_t bid = blockIdx.x;
     const int64_t nQ = geo.B * ntile * H;
 
@@ -230,18 +237,27 @@ __global__ void __launch_bounds__(kThreads) int4_dequant_kernel(const uint8_t* _
         const int64_t h = ix.h, j = ix.j, b = ix.b;
         const int64_t t0 = j * TILE;
         const int n = (int)min<int64_t>(TILE, Tq - t0);
-        float s8[8], zs8[8];
+        float s8[NGT][8], zs8[NGT][8];
         if constexpr (IS_K) {
-            const int64_t mi = ((b * H + h) * geo.ldk + j) * D + 8 * lane;
-            const uint4 sv = *reinterpret_cast<const uint4*>(scale + mi);
-            const uint4 zv = *reinterpret_cast<const uint4*>(zero + mi);
-            float zf[8];
-            unpack8(sv, s8);
-            unpack8(zv, zf);
 #pragma unroll
-            for (int k = 0; k < 8; ++k) zs8[k] = -zf[k] * s8[k];
+            for (int q = 0; q < NGT; ++q) {
+                // a group past the last is never used (its rows are past n); its index is clamped
+                const int64_t jq = min<int64_t>(j * NGT + q, geo.nKg - 1);
+                const int64_t mi = ((b * H + h) * geo.ldk + jq) * D + 8 * lane;
+                const uint4 sv = *reinterpret_cast<const uint4*>(scale + mi);
+                const uint4 zv = *reinterpret_cast<const uint4*>(zero + mi);
+                float zf[8];
+                unpack8(sv, s8[q]);
+                unpack8(zv, zf);
+#pragma unroll
+                for (int k = 0; k < 8; ++k) zs8[q][k] = -zf[k] * s8[q][k];
+            }
         }
-        for (int r = rg; r < n; r += RPP) {
+#pragma unroll
+        for (int i = 0; i < TILE / RPP; ++i) {
+            const int r = rg + RPP * i;
+            if (r >= n) break;
+            const int q = IS_K ? (RPP * i) / G : 0;   // the row's group inside the tile (RPP divides G)
             const int64_t t = t0 + r;
             const uint32_t w =
                 __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(codes + ((b * H + h) * geo.ldq + t) * (D / 2) + 4 * lane));
@@ -257,7 +273,7 @@ __global__ void __launch_bounds__(kThreads) int4_dequant_kernel(const uint8_t* _
             float v[8];
             if constexpr (IS_K) {
 #pragma unroll
-                for (int k = 0; k < 8; ++k) v[k] = __builtin_fmaf(c[k], s8[k], zs8[k]);
+                for (int k = 0; k < 8; ++k) v[k] = __builtin_fmaf(c[k], s8[q][k], zs8[q][k]);
             } else {
                 const int64_t mi = ((b * H + h) * geo.ldq + t) * NGD + (8 * lane) / G;
                 const float s = bf_to_f(scale[mi]);
@@ -358,7 +374,7 @@ void launch_quant(const uint16_t* K, const uint16_t* V, const I4Geom& g, const I
 
 template <int D, int G>
 void launch_dequant(bool is_k, int ot, const kvq_int4_cache* c, const I4Geom& g, void* out, hipStream_t st) {
-    const int64_t nblk = g.B * g.H * ((is_k ? g.nKg : g.nVt) + g.nRt);
+    const int64_t nblk = g.B * g.H * ((is_k ? cdiv(g.Tq, (int64_t)dequant_ktile<G>()) : g.nVt) + g.nRt);
     const dim3 grid((unsigned)nblk), blk(kThreads);
     if (is_k) {
         if (ot == KVQ_FP32)
