@@ -170,6 +170,7 @@ __global__ void __launch_bounds__(kThreads) pc_code_kernel(const void* __restric
     }
     const float lo = (float)qmin, hi = (float)qmax;
     const int64_t r_end = min(g.R, (rc + 1) * kRowsPerChunk);
+#pragma unroll 4
     for (int64_t r = rc * kRowsPerChunk + rl; r < r_end; r += g.rpp) {
         float v[VEC];
         load_x<XT, VEC>(x, s * g.bsx + r * g.ldx + c0, v);
@@ -223,6 +224,7 @@ __global__ void __launch_bounds__(kThreads) pc_dequant_kernel(const int8_t* __re
         zf[k] = zp ? (float)zp[s * g.C + c0 + k] : 0.0f;
     }
     const int64_t r_end = min(g.R, (rc + 1) * kRowsPerChunk);
+#pragma unroll 4
     for (int64_t r = rc * kRowsPerChunk + rl; r < r_end; r += g.rpp) {
         const int64_t e = (s * g.R + r) * g.C + c0;
         float v[VEC];
