@@ -38,7 +38,6 @@ __global__ void __launch_bounds__(NT) int4_quant_kernel(const uint16_t* __restri
                                                               I4Ptrs out) {
     constexpr int LPR = D / 8;            // lanes per token row
     constexpr int RPP = NT / LPR;         // rows per pass
-    constexpr int NW = NT / 64;           // waves
     constexpr int NGD = D / G;            // V groups per token
     constexpr int VT = quant_vtile<D, G>();   // tokens per V tile
     static_assert(G % RPP == 0 && VT % RPP == 0, "tile shape");
@@ -48,7 +47,6 @@ __global__ void __launch_bounds__(NT) int4_quant_kernel(const uint16_t* __restri
     __shared__ float s_ps[NP], s_pr[NP], s_pz[NP];
 
     const int tid = threadIdx.x, lane = tid % LPR, rg = tid / LPR;
-    const int wave = tid / 64;
     const int64_t H = geo.H, Tq = geo.Tq;
     int64_t bid = blockIdx.x;
     const int64_t nK = geo.B * geo.nKg * H, nV = geo.B * geo.nVt * H;

@@ -76,7 +76,6 @@ __global__ void __launch_bounds__(kThreads) pc_minmax_kernel(const void* __restr
     if (c0 < g.C) {
         const int64_t r_end = min(g.R, (rc + 1) * kRowsPerChunk);
         int64_t r = rc * kRowsPerChunk + rl;
-#pragma unroll 2
         for (; r + g.rpp < r_end; r += 2 * g.rpp) {
             float v[VEC], u[VEC];
             load_x<XT, VEC>(x, s * g.bsx + r * g.ldx + c0, v);
