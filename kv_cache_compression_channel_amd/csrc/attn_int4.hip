@@ -250,6 +250,24 @@ __global__ void __launch_bounds__(kThreads) attn_split_kernel(const AttnArgs a) 
     }
 }
 
+// (M, L) of a merged row and its normalised output.
+template <int D, int OT>
+__device__ __forceinline__ void combine_store(int64_t row, int lane, float M, float L, const float (&A)[D / 64],
+                                              void* __restrict__ out, float* __restrict__ ml) {
+    if (ml && lane == 0) *reinterpret_cast<float2*>(ml + 2 * row) = make_float2(M, L);
+#pragma unroll
+    for (int j = 0; j < D / 64; ++j) {
+        const int c = lane + 64 * j;
+        const float o = A[j] / L;
+        if constexpr (OT == KVQ_FP32)
+            static_cast<float*>(out)[row * D + c] = o;
+        else
+            static_cast<uint16_t*>(out)[row * D + c] = f_to_bf(o);
+    }
+}
+
+constexpr int kFewSlots = 16;   // slot counts merged with all loads in flight at once
+
 // Log-sum-exp merge of the split partials (m, l, acc[D]) of one (b, hq) row per wave: lanes
 // read the slots' maxima and sums in parallel, then each lane sums its D/64 channels over the
 // slots with every slot's weight taken from the lane that holds it.
@@ -261,6 +279,36 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(const float* __restri
     const int64_t row = (int64_t)blockIdx.x * 4 + threadIdx.x / 64;   // b * Hq + hq
     if (row >= rows) return;
     const float* base = ws + row * nslot * (D + 2);
+    if (nslot <= kFewSlots) {
+        // every load issued before any reduction: one round trip to memory instead of two; the
+        // sums run in the same order as below, so the result is the same to the bit
+        float ms = kNegBig, ls = 0.0f, x[kFewSlots][CPL];
+        if (lane < nslot) { ms = base[(int64_t)lane * (D + 2)]; ls = base[(int64_t)lane * (D + 2) + 1]; }
+#pragma unroll
+        for (int s = 0; s < kFewSlots; ++s) {
+#pragma unroll
+            for (int j = 0; j < CPL; ++j) x[s][j] = s < nslot ? base[(int64_t)s * (D + 2) + 2 + lane + 64 * j] : 0.0f;
+        }
+        float M = ms;
+#pragma unroll
+        for (int off = 32; off >= 1; off /= 2) M = fmaxf(M, __shfl_xor(M, off));
+        const float f = lane < nslot ? exp2f(ms - M) : 0.0f;
+        float L = lane < nslot ? __builtin_fmaf(ls, f, 0.0f) : 0.0f, A[CPL];
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) A[j] = 0.0f;
+#pragma unroll
+        for (int s = 0; s < kFewSlots; ++s) {
+            if (s < nslot) {
+                const float fk = __shfl(f, s);
+#pragma unroll
+                for (int j = 0; j < CPL; ++j) A[j] = __builtin_fmaf(x[s][j], fk, A[j]);
+            }
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off /= 2) L += __shfl_xor(L, off);
+        combine_store<D, OT>(row, lane, M, L, A, out, ml);
+        return;
+    }
     float M = kNegBig;
     for (int s = lane; s < nslot; s += 64) M = fmaxf(M, base[(int64_t)s * (D + 2)]);
 #pragma unroll
@@ -302,16 +350,7 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(const float* __restri
     }
 #pragma unroll
     for (int off = 32; off >= 1; off /= 2) L += __shfl_xor(L, off);
-    if (ml && lane == 0) *reinterpret_cast<float2*>(ml + 2 * row) = make_float2(M, L);
-#pragma unroll
-    for (int j = 0; j < CPL; ++j) {
-        const int c = lane + 64 * j;
-        const float o = A[j] / L;
-        if constexpr (OT == KVQ_FP32)
-            static_cast<float*>(out)[row * D + c] = o;
-        else
-            static_cast<uint16_t*>(out)[row * D + c] = f_to_bf(o);
-    }
+    combine_store<D, OT>(row, lane, M, L, A, out, ml);
 }
 
 // Decode-time H2O scores: acc[b][h][t] += sum over the NQ query heads n of KV head h of
