@@ -175,8 +175,13 @@ void orc_stats_finalize(const double in[3], int64_t n, double* rmse, double* max
 /* One affine 4-bit group.  [Explainer, quantization section] x ~ s * (q - z) with a
  * bf16 scale and a bf16 zero stored per group; the integer steps are those of
  * [Walkthrough §1.2] with qmin = 0, qmax = 15:
- *   s = (max - min) / 15 (range clipped at 1e-8), stored as bf16 rounded up (READING),
- *   z = round(0 - min / s) with the stored s, stored as bf16 (exact for |z| <= 256),
+ *   s = (max - min) / 15 (range clipped at 1e-8), raised to |min| / 256 when that is
+ *       larger, stored as bf16 rounded up (READING: bf16 holds every integer of
+ *       magnitude <= 256 exactly, so with s >= |min| / 256 the zero point below is
+ *       stored exactly and the 16 levels (k - z) * s cover [min, max]; this keeps the
+ *       lab section's round-trip bound |x - x_hat| <= s / 2 for every group; a group
+ *       that straddles zero always has range >= |min|, so its scale is unchanged),
+ *   z = round(0 - min / s) with the stored s, stored as bf16 (exact: |z| <= 256),
  *   q = clip(round(x / s) + z, 0, 15) with the stored s and z. */
 static void int4_group(const float* v, int64_t n, uint16_t* s_out, uint16_t* z_out, uint8_t* codes) {
     float mn = v[0], mx = v[0];
@@ -186,7 +191,10 @@ static void int4_group(const float* v, int64_t n, uint16_t* s_out, uint16_t* z_o
     }
     float range = mx - mn;
     if (range < RANGE_FLOOR) range = RANGE_FLOOR;
-    const uint16_t sb = bf16_round_up_positive(range / 15.0f);
+    float s32 = range / 15.0f;
+    const float zfloor = fabsf(mn) / 256.0f;
+    if (zfloor > s32) s32 = zfloor;
+    const uint16_t sb = bf16_round_up_positive(s32);
     const float s = orc_bf16_to_f32(sb);
     const float zr = rintf(0.0f - mn / s);
     const uint16_t zb = orc_f32_to_bf16(zr);
@@ -409,10 +417,16 @@ int64_t orc_keep_count(int64_t T, int64_t budget, int64_t window) {
 }
 
 /* Ranking used by TopK: larger score first; equal scores -> lower index first;
- * NaN below every number (READING: the page does not show its TopK helper). */
+ * NaN below every number (READING: the page does not show its TopK helper).  The
+ * recent tokens, whose scores were replaced by -inf, rank below every earlier token,
+ * NaN included (READING: for numeric scores this is what the -inf mask does; it also
+ * keeps |recent ∪ TopK| = min(T, max(budget, |recent|)) when earlier scores are NaN). */
 static const float* g_rank_vals; /* single-threaded oracle: qsort has no context argument */
+static int64_t g_rank_rs;        /* first recent index */
 static int rank_cmp(const void* pa, const void* pb) {
     const int32_t a = *(const int32_t*)pa, b = *(const int32_t*)pb;
+    const int ra = a >= g_rank_rs, rb = b >= g_rank_rs;
+    if (ra != rb) return ra ? 1 : -1;
     const float va = g_rank_vals[a], vb = g_rank_vals[b];
     const int na = isnan(va), nbn = isnan(vb);
     if (na != nbn) return na ? 1 : -1;
@@ -432,6 +446,7 @@ static int select_row(const float* scores, int64_t T, int64_t budget, int64_t wi
     if (heavy > T) heavy = T;
     for (int64_t j = 0; j < T; ++j) order[j] = (int32_t)j;
     g_rank_vals = masked;
+    g_rank_rs = rs;
     qsort(order, (size_t)T, sizeof(int32_t), rank_cmp);
     memset(flag, 0, (size_t)T);
     for (int64_t i = 0; i < heavy; ++i) flag[order[i]] = 1;

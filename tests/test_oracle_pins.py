@@ -424,32 +424,104 @@ def test_attn_gqa_head_map():
     V = np.zeros((B, T, Hkv, d), np.float32)
     for h in range(Hkv):
         V[:, :, h, :] = h + 1
-    # all tokens in the bf16 residual: a constant INT4 group cannot hold a nonzero
-    # constant exactly (see test_int4_constant_group_limit)
+    # all tokens in the bf16 residual
     c = oracle.int4_quant(K, bf16(V), 64, T)
     q = bf16(rng.standard_normal((B, Hq, d)))
     o = oracle.decode_attn(c, q)
     for hq in range(Hq):
         assert np.allclose(o[:, hq], hq // (Hq // Hkv) + 1, rtol=0, atol=1e-12)
-    # the same map with INT4 K in front of the residual
+    # the same map with INT4 tokens in front of the residual: a constant V group is held
+    # exactly (test_int4_constant_group_is_exact), so every row is still its head's constant
     c2 = oracle.int4_quant(K, bf16(V), 64, 16)
     vh = oracle.int4_dequant(c2, "v")
     o2 = oracle.decode_attn(c2, q)
     for hq in range(Hq):
         h = hq // (Hq // Hkv)
-        lo, hi = vh[:, :, h].min(), vh[:, :, h].max()
-        assert np.all((o2[:, hq] >= lo - 1e-12) & (o2[:, hq] <= hi + 1e-12))
-        assert abs(o2[:, hq].mean() - (h + 1)) < 1e-2
+        assert np.all(vh[:, :, h] == h + 1)
+        assert np.allclose(o2[:, hq], h + 1, rtol=0, atol=1e-12)
 
 
-def test_int4_constant_group_limit():
-    # A constant nonzero group has range 0, floored at 1e-8: s is tiny, z = round(-x/s) is
-    # huge and its bf16 rounding (8 significant bits) moves x_hat by up to |x| * 2^-8.
+def test_int4_constant_group_is_exact():
+    # A constant nonzero group has range 0 (floored at 1e-8), so the scale comes from the
+    # zero-point floor |min| / 256: s = 2^-8 for x = 1, z = round(-1 / 2^-8) = -256, held
+    # exactly by bf16, and x_hat = (0 + 256) * 2^-8 = 1 exactly.
     K = np.full((1, 64, 1, 64), 1.0, np.float32)
     c = oracle.int4_quant(bf16(K), bf16(K), 64, 0)
-    xh = oracle.int4_dequant(c, "k")
-    assert np.all(np.abs(xh - 1.0) <= 2.0**-8)
-    assert np.abs(f32(c["k_zero"])).min() > 2**24
+    assert np.all(f32(c["k_scale"]) == 2.0**-8) and np.all(f32(c["k_zero"]) == -256)
+    assert np.all(f32(c["v_scale"]) == 2.0**-8) and np.all(f32(c["v_zero"]) == -256)
+    assert np.all(oracle.int4_dequant(c, "k") == 1.0)
+    assert np.all(oracle.int4_dequant(c, "v") == 1.0)
+
+
+@pytest.mark.parametrize("offset", [100.0, -100.0, 3.0e4, -7.5, 0.37])
+def test_int4_offset_groups_keep_the_round_trip_bound(offset):
+    # Groups far from zero relative to their range (offset +- 0.25 N(0,1)): the stored zero
+    # point is an integer of magnitude <= 256 (exact in bf16), every element stays within
+    # half a stored step of its value, and its code is the nearest of the 16 levels.
+    B, T, H, d, g, R = 1, 256, 2, 128, 64, 0
+    rng = np.random.default_rng(int(abs(offset) * 10))
+    K = (offset + 0.25 * rng.standard_normal((B, T, H, d))).astype(np.float32)
+    V = (offset + 0.25 * rng.standard_normal((B, T, H, d))).astype(np.float32)
+    Kb, Vb = bf16(K), bf16(V)
+    c = oracle.int4_quant(Kb, Vb, g, R)
+    for side, X in (("k", Kb), ("v", Vb)):
+        z = f32(c[side + "_zero"]).astype(np.float64)
+        assert np.all(np.abs(z) <= 256) and np.all(z == np.round(z))
+        x = f32(X).astype(np.float64)
+        xh = oracle.int4_dequant(c, side).astype(np.float64)
+        q, s, zz = _levels_and_ids(c, side)
+        assert np.all(np.abs(x - xh) <= s / 2)
+        levels = (np.arange(16)[None, None, None, None, :] - zz[..., None]) * s[..., None]
+        dist = np.abs(x[..., None] - levels)
+        assert np.all(np.take_along_axis(dist, q[..., None], -1)[..., 0] == dist.min(-1))
+    # a group that straddles zero keeps the plain scale rule: s = smallest bf16 >= range / 15
+    Kz = np.zeros((1, 64, 1, 64), np.float32)
+    Kz[0, :, 0, 0] = np.linspace(-1.0, 2.0, 64)
+    cz = oracle.int4_quant(bf16(Kz), bf16(Kz), 64, 0)
+    r15 = np.float32(np.float32(3.0) / np.float32(15.0))
+    s0 = f32(cz["k_scale"])[0, 0, 0, 0]
+    assert s0 >= r15 and s0 == f32(bf16([s0]))[0] and np.float32(s0 - r15) < r15 * 2.0**-7
+
+
+def _bf16_sign_bit(b):
+    return (np.asarray(b, np.uint16) >> 15) & 1
+
+
+def test_int4_zero_point_sign_bits():
+    # The stored zero point is the IEEE result of round(0 - min / s) (Walkthrough §1.2 with
+    # qmin = 0), evaluated here by numpy in float32: min = +0 or -0 gives 0 - (+-0) = +0
+    # (bits 0x0000); a minimum in (0, s/2] gives a negative quotient that rounds to -0
+    # (bits 0x8000).
+    d, g = 64, 64
+    K = np.zeros((1, 64, 1, d), np.float32)
+    V = np.zeros((1, 64, 1, d), np.float32)
+    K[0, :, 0, 1] = -0.0                               # channel of -0 values
+    K[0, :, 0, 2] = np.linspace(0.01, 1.0, 64)         # min in (0, s/2]
+    K[0, :, 0, 3] = np.linspace(0.0, 1.0, 64)          # min = +0
+    K[0, :, 0, 4] = np.linspace(-1.0, 0.0, 64)         # max = 0, min < 0
+    V[0, 0, 0, :] = -0.0
+    V[0, 1, 0, :] = np.linspace(0.01, 1.0, d)
+    V[0, 2, 0, :] = np.linspace(0.0, 1.0, d)
+    Kb, Vb = bf16(K), bf16(V)
+    c = oracle.int4_quant(Kb, Vb, g, 0)
+    for side, X, zb, sb in (("k", Kb, c["k_zero"][0, 0, 0, :5], c["k_scale"][0, 0, 0, :5]),
+                            ("v", Vb, c["v_zero"][0, 0, :3, 0], c["v_scale"][0, 0, :3, 0])):
+        x = f32(X)[0, :, 0, :]
+        mins = x.min(axis=0)[:5] if side == "k" else x.min(axis=1)[:3]
+        s = f32(sb)
+        with np.errstate(all="ignore"):
+            want = np.round(np.float32(0.0) - mins.astype(np.float32) / s)
+        assert np.array_equal(f32(zb), want)
+        assert np.array_equal(_bf16_sign_bit(zb), np.signbit(want).astype(np.uint16))
+    assert c["k_zero"][0, 0, 0, 0] == 0x0000 and c["k_zero"][0, 0, 0, 1] == 0x0000
+    assert c["k_zero"][0, 0, 0, 2] == 0x8000 and c["k_zero"][0, 0, 0, 3] == 0x0000
+    assert c["v_zero"][0, 0, 0, 0] == 0x0000 and c["v_zero"][0, 0, 1, 0] == 0x8000
+    assert c["v_zero"][0, 0, 2, 0] == 0x0000
+    # per-channel asymmetric INT8: a channel whose minimum is +-0 has zero point qmin exactly
+    xa = np.stack([np.linspace(0.0, 1.0, 16), -np.abs(np.linspace(-0.0, 0.0, 16)),
+                   np.linspace(-0.0, 2.0, 16)], 1).astype(np.float32)
+    qa, sa, za = oracle.quant_asym(xa, -128, 127)
+    assert za.reshape(-1).tolist() == [-128, -128, -128]
 
 
 def test_attn_dominant_logit_picks_its_value():
@@ -549,6 +621,65 @@ def test_select_bruteforce_small():
         heavy = _rank_count_heavy(masked, min(max(0, B - (T - rs)), T))
         want = sorted(set(range(rs, T)) | heavy)
         assert keep == want, (T, B, W, sc.tolist())
+
+
+def _special_better(a, b):
+    """True when score a ranks strictly above score b: IEEE order for numbers (-0 == +0),
+    every number above NaN, NaNs equal to one another."""
+    na, nb = math.isnan(a), math.isnan(b)
+    if na or nb:
+        return nb and not na
+    return a > b
+
+
+def _special_equal(a, b):
+    if math.isnan(a) or math.isnan(b):
+        return math.isnan(a) and math.isnan(b)
+    return a == b
+
+
+def test_select_bruteforce_special_values():
+    # Scores that include NaN, +0, -0, +inf and -inf: a token is heavy when fewer than k
+    # tokens rank above it (larger score, or an equal score at a lower index), with the
+    # recent window's scores replaced by -inf before the TopK (Walkthrough §3.2) and the
+    # window ranked below every earlier token, so that the union always holds
+    # min(T, max(budget, |recent|)) tokens.
+    vals = [math.nan, 0.0, -0.0, math.inf, -math.inf, 0.5, -0.5]
+    rng = np.random.default_rng(33)
+    seen_nan_kept = seen_zero_tie = False
+    for trial in range(600):
+        T = int(rng.integers(1, 13))
+        B = int(rng.integers(0, 15))
+        W = int(rng.integers(0, 6))
+        sc = np.array([vals[i] for i in rng.integers(0, len(vals), T)], np.float32)
+        keep = oracle.select(sc[None], B, W)[0].tolist()
+        rs = max(0, T - W)
+        masked = [float(sc[j]) if j < rs else -math.inf for j in range(T)]
+        k = min(max(0, B - (T - rs)), T)
+        heavy = set()
+        def above_of(j, i):
+            if (j >= rs) != (i >= rs):
+                return i >= rs
+            return _special_better(masked[j], masked[i]) or (_special_equal(masked[j], masked[i]) and j < i)
+
+        for i in range(T):
+            above = sum(1 for j in range(T) if above_of(j, i))
+            if above < k:
+                heavy.add(i)
+        want = sorted(set(range(rs, T)) | heavy)
+        assert keep == want, (T, B, W, sc.tolist())
+        assert len(keep) == min(T, max(B, min(W, T)))
+        seen_nan_kept |= any(math.isnan(masked[i]) for i in heavy)
+        seen_zero_tie |= any(masked[i] == 0.0 and math.copysign(1, masked[i]) < 0 for i in heavy)
+    assert seen_nan_kept and seen_zero_tie
+    # -0 and +0 tie, so the lower index wins whatever the sign; NaN ranks below -inf
+    sc = np.array([[0.0, -0.0, -0.0, 0.0, np.nan, -np.inf]], np.float32)
+    assert oracle.select(sc, 2, 0)[0].tolist() == [0, 1]
+    sc = np.array([[-0.0, 0.0, np.nan, -np.inf]], np.float32)
+    assert oracle.select(sc, 3, 0)[0].tolist() == [0, 1, 3]
+    # a NaN before the window still outranks the window's masked tokens
+    sc = np.array([[np.nan, np.nan, 1.0, 2.0]], np.float32)
+    assert oracle.select(sc, 3, 2)[0].tolist() == [0, 2, 3]
 
 
 def test_select_ties_take_lower_index():
