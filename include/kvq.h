@@ -89,10 +89,13 @@ int kvq_quant_asym(const void* x, int xt, int64_t nb, int64_t R, int64_t C, int6
  *   K is grouped per channel across g consecutive tokens (the last group of a
  *   channel is partial when g does not divide Tq); V is grouped per token across
  *   g consecutive channels.  Per group:
- *     s = smallest bf16 >= max(max - min, fp32(1e-8)) / 15   (stored bf16)
- *     z = round(0 - min / s), stored as bf16 (exact while |z| <= 256)
+ *     s = smallest bf16 >= max(max(max - min, fp32(1e-8)) / 15, |min| / 256)
+ *         (stored bf16; the second bound only binds for a group far from zero
+ *         relative to its range, and makes z below an integer bf16 holds exactly)
+ *     z = round(0 - min / s), stored as bf16 (|z| <= 256, exact)
  *     q = clip(round(x / s) + z, 0, 15), using the stored s and z.
- *   Dequantization: x_hat = (q - z) * s, rounded once (exact in fp32 for |z| < 2^15).
+ *   Every value is then within s / 2 of its dequantized level.
+ *   Dequantization: x_hat = (q - z) * s, rounded once (exact in fp32).
  * Sections (device, caller-allocated, sizes from kvq_int4_cache_sizes), with
  * Q = cap (or Tq when cap is 0) and P = rcap (or R when rcap is 0) rows per (b, h):
  *   [0] k_codes u8   [B][H][Q][d/2]  byte j = code(2j) | code(2j+1) << 4
@@ -331,16 +334,15 @@ uint64_t kvq_int4_bytes(uint64_t N, uint64_t g);
 int kvq_token_ratio(int64_t T, int64_t K, double* out);
 /* [Walkthrough §4] (s_old / s_new) * (T / K); KVQ_EINVAL unless 0 < K <= T and s_new > 0. */
 int kvq_total_gain(double s_old, double s_new, int64_t T, int64_t K, double* out);
-/* [Explainer, "four kinds of smaller"] L * T_stored * C_stored * b + metadata. */
+/* [Explainer, section on the four ways to shrink the cache] L * T_stored * C_stored * b + metadata. */
 uint64_t kvq_kv_bytes(uint64_t L, uint64_t T, uint64_t C, uint64_t b, uint64_t metadata);
 /* [Walkthrough §3.2] size of recent ∪ TopK: min(T, max(budget, min(window, T))); -1 on bad input. */
 int64_t kvq_keep_count(int64_t T, int64_t budget, int64_t window);
 
 /* ======================================================================
- * GQA decode attention over the INT4 cache  [Explainer: "the attention kernel
- * reads the low-bit cache and dequantizes it" (quantization section) and "let the
- * kernel cash in the savings: compact layout, fused dequantization" (evaluation
- * section); GQA head sharing from the GQA section]
+ * GQA decode attention over the INT4 cache  [Explainer, quantization section
+ * (dequantization inside the attention kernel) and evaluation section (fused
+ * dequantization over a compact layout); GQA head sharing from the GQA section]
  *
  * For every batch b and query head hq (one query token each):
  *   h = hq / (Hq / H)   (consecutive query heads share a KV head)
@@ -386,7 +388,9 @@ int kvq_decode_attn_int4_h2o(const kvq_int4_cache* c, const void* q, int64_t Hq,
  * kvq_snapkv_select: scores fp32 [rows][T] given (one-shot observation scores).
  * Both then, per row: recent = [max(0, T - window), T); the recent scores are
  *   replaced by -inf; TopK of the masked scores with k = max(0, budget - |recent|)
- *   (larger first, equal scores -> lower index, NaN below every number); keep =
+ *   (larger first, equal scores -> lower index, NaN below every number, and the
+ *   recent tokens below every earlier token, NaN included, so the union always holds
+ *   kvq_keep_count tokens); keep =
  *   the sorted union of recent and TopK, int32 [rows][kvq_keep_count(T, budget,
  *   window)] (device); when that count is 0, keep may be NULL and nothing is selected.
  * Workspace (device): kvq_select_ws(rows, T) bytes (h2o needs room for the scores
@@ -402,12 +406,14 @@ int kvq_snapkv_select(const float* scores, int64_t rows, int64_t T, int64_t budg
                       int32_t* keep, void* ws, size_t ws_bytes, kvq_stream stream);
 
 /* ======================================================================
- * Compaction of the kept rows  [Explainer, eviction: "keep only the selected KV"]
+ * Compaction of the kept rows  [Explainer, eviction section: only the selected
+ * positions stay in the cache]
  *
  * k_dst[b][k][h][:] = k_src[b][keep[b][h][k]][h][:] (and the same for V when both
  * v pointers are given).  k_src, v_src bf16 [B][T][H][d]; keep int32 [B][H][K] with
  * entries in [0, T) (the output of the selectors with rows = B*H); dst [B][K][H][d].
- * All device.  Indices are trusted (out-of-range indices are undefined behaviour).
+ * All device.  An entry outside [0, T) is clamped into range on the device: the row
+ * it yields is unspecified, but nothing outside k_src / v_src is read.
  * EINVAL: B, T, H, d or K < 1, K > T, d % 8 != 0, NULL k pointers, exactly one
  *   of v_src / v_dst NULL.
  * ====================================================================== */

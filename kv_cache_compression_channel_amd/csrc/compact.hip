@@ -3,7 +3,9 @@
 // selected KV are kept; later queries read only what was kept).
 //
 // dst[b][k][h][:] = src[b][keep[b][h][k]][h][:].  One thread moves 16 bytes; d/8 threads
-// move one 2d-byte row, so reads and writes are whole 128-byte lines for d >= 64.
+// move one 2d-byte row, so reads and writes are whole 128-byte lines for d >= 64.  A keep
+// entry outside [0, T) is clamped into range (two integer operations), so a bad index
+// yields an unspecified row, never an access outside the source.
 #include "kvq_internal.h"
 
 namespace kvq {
@@ -25,7 +27,8 @@ __global__ void __launch_bounds__(kThreads) compact_kernel(const uint16_t* __res
         // destination row order [b][k][h]
         const uint32_t q = row / Hu;
         const int64_t h = row - q * Hu, k = q % Ku, b = q / Ku;
-        const int64_t t = keep[(b * H + h) * K + k];
+        const int32_t tk = keep[(b * H + h) * K + k];
+        const int64_t t = tk < 0 ? 0 : (tk >= T ? T - 1 : (int64_t)tk);
         const int64_t so = ((b * T + t) * H + h) * d + 8 * c;
         const int64_t dof = row * d + 8 * c;
         *reinterpret_cast<uint4*>(kd + dof) = *reinterpret_cast<const uint4*>(ks + so);

@@ -71,7 +71,12 @@ __device__ __forceinline__ void unpack8(const uint4 a, float (&v)[8]) {
 }
 
 // Per-group parameters from the group's min and max:
-//   s = smallest bf16 >= max(max - min, 1e-8) / 15, z = bf16(round(0 - min / s)).
+//   s = smallest bf16 >= max(max(max - min, 1e-8) / 15, |min| / 256),
+//   z = bf16(round(0 - min / s)).
+// bf16 holds every integer of magnitude <= 256 exactly; with s >= |min| / 256 the zero
+// point is one of them, so the levels (k - z) s cover [min, max] and every value of the
+// group lies within s / 2 of its level.  A group that straddles zero has range >= |min|,
+// so only groups far from zero relative to their range take the second bound.
 struct GroupParams {
     float s, r, z;
     uint16_t sb, zb;
@@ -81,7 +86,9 @@ __device__ __forceinline__ GroupParams group_params(float mn, float mx) {
     GroupParams p;
     float range = mx - mn;
     range = vmax2(range, 1e-8f);
-    p.sb = bf_ceil_pos(range / 15.0f);
+    // |min| / 256 is exact (a power-of-two scaling) except below the normal range, where the
+    // product by 2^-8 rounds exactly as the division does
+    p.sb = bf_ceil_pos(vmax2(range / 15.0f, __builtin_fabsf(mn) * 0.00390625f));
     p.s = bf_to_f(p.sb);
     // 0 - m: the backend lowers a subtraction from +0 to a negation, which turns m = +0 into
     // -0; IEEE gives 0 - (+-0) = +0, so the zero quotient is handled explicitly

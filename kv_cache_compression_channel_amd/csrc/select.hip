@@ -12,7 +12,7 @@
 // straight into registers (8 float4 of scores per thread) and selects from there, so the
 // scores never go to memory and back; each block streams its own 4*T_obs*T bytes.
 // Selection: one 1024-thread block per row.  Scores become order-preserving 32-bit keys
-// (NaN lowest, -0 == +0, recent tokens = key(-inf)); an MSB-first radix select (8-bit digits over
+// (recent tokens lowest, then NaN, then numbers in order, -0 == +0); an MSB-first radix select (8-bit digits over
 // the bits where the row's keys differ) finds the k-th largest key t and how many keys
 // equal to t are taken (m); a final in-order scan keeps j when key > t, or key == t and
 // fewer than m equal keys precede it, or j is recent, and writes kept indices with a
@@ -60,11 +60,14 @@ __global__ void __launch_bounds__(kSumThreads) colsum_kernel(const float* __rest
 
 __device__ __forceinline__ uint32_t order_key(float f) {
     const uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return 0u;       // NaN: below every number
+    if ((u & 0x7fffffffu) > 0x7f800000u) return 1u;       // NaN: below every number
     if ((u << 1) == 0u) return 0x80000000u;                // -0 and +0 compare equal
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);    // -inf -> 0x007fffff
 }
-constexpr uint32_t kKeyNegInf = 0x007fffffu;               // order_key(-inf)
+// The recent window's tokens (scores masked to -inf) rank below every earlier token, NaN
+// included: for numeric scores this is the -inf mask itself, and it keeps the union of the
+// window and the TopK at min(T, max(budget, |window|)) tokens for any scores.
+constexpr uint32_t kKeyRecent = 0u;
 
 // Block-wide exclusive prefix of a 0/1 flag; returns the prefix, *total gets the sum.
 __device__ __forceinline__ uint32_t block_prefix(bool flag, uint32_t* sh, uint32_t* total) {
@@ -101,7 +104,7 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(const float* __rest
     const int tid = threadIdx.x, w = tid / 64;
 
     uint32_t kreg[REG ? kRegKeys : 1];
-    auto key_at = [&](int64_t j) -> uint32_t { return j >= rs ? kKeyNegInf : order_key(sc[j]); };
+    auto key_at = [&](int64_t j) -> uint32_t { return j >= rs ? kKeyRecent : order_key(sc[j]); };
     if constexpr (REG) {
 #pragma unroll
         for (int i = 0; i < kRegKeys; ++i) {
@@ -285,7 +288,7 @@ __global__ void __launch_bounds__(kSelThreads) h2o_fused_kernel(const float* __r
     }
     if (K == 0) return;
 
-    // ---- keys: order-preserving, recent tokens = key(-inf), past the end 0 (never counted) ----
+    // ---- keys: order-preserving, recent tokens lowest, past the end 0 (never counted) ----
     uint32_t kreg[kFusedChunks][4];
 #pragma unroll
     for (int i = 0; i < kFusedChunks; ++i) {
@@ -293,7 +296,7 @@ __global__ void __launch_bounds__(kSelThreads) h2o_fused_kernel(const float* __r
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int j = tok(i) + e;
-            kreg[i][e] = j >= Ti ? 0u : (j >= rs ? kKeyNegInf : order_key(v[e]));
+            kreg[i][e] = j >= Ti ? 0u : (j >= rs ? kKeyRecent : order_key(v[e]));
         }
     }
 

@@ -123,3 +123,26 @@ def test_round_trip_bound_on_gpu():
     s = cache.k_scale.float().repeat_interleave(64, dim=2)[:, :, :777].permute(0, 2, 1, 3)
     err = (K.to(DEV).float() - kh).abs()
     assert bool((err <= s / 2).all())
+
+
+@pytest.mark.parametrize("offset", [100.0, -300.0, 3.0e4, 0.37])
+def test_offset_and_constant_groups(offset):
+    """Groups far from zero relative to their range, whose scale comes from the zero-point
+    floor |min| / 256 (so the zero point is an integer bf16 holds exactly), and constant
+    groups: bit-exact sections and dequantization, and every element within half a step."""
+    rng = np.random.default_rng(int(abs(offset)) + 3)
+    B, T, H, d, g, R = 1, 3 * 64 + 29, 2, 128, 64, 13
+    K = (offset + 0.25 * rng.standard_normal((B, T, H, d))).astype(np.float32)
+    V = (offset + 0.25 * rng.standard_normal((B, T, H, d))).astype(np.float32)
+    K[0, 64:128, 0, :40] = 1.5 * offset        # constant K channels over one token group
+    V[0, 7:90:3, 1, :64] = -offset             # constant V groups
+    Kb, Vb = oracle.f32_to_bf16(K), oracle.f32_to_bf16(V)
+    cache = run_and_compare(Kb, Vb, g=g, R=R, check_stats=False)
+    Tq = T - R
+    kz = oracle.bf16_to_f32(u16(cache.k_zero))
+    vz = oracle.bf16_to_f32(u16(cache.v_zero))
+    assert np.abs(kz).max() <= 256 and np.abs(vz).max() <= 256
+    kh = np_(kvq.dequant_int4(cache, "k", torch.float32))[:, :Tq]
+    torch.cuda.synchronize()
+    s = np_(cache.k_scale.float()).repeat(g, axis=2)[:, :, :Tq].transpose(0, 2, 1, 3)
+    assert np.all(np.abs(oracle.bf16_to_f32(Kb)[:, :Tq].astype(np.float64) - kh) <= s / 2)

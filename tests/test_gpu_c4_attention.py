@@ -150,3 +150,22 @@ def test_repeatable():
     b = kvq.decode_attn_int4(cache, q.to(DEV))
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("d,g,T,R,nslot", [
+    (128, 64, 14 * 512 + 128, 128, 16),        # the combine's all-loads-first path, full
+    (128, 64, 14 * 512 + 129, 128, 17),        # one slot past it: the general path
+    (128, 64, 32768, 128, 66),                 # batch-1 long context: more than 64 slots
+    (128, 64, 65536 + 77, 128, 130),           # two passes of the 64-slot loop, ragged
+    (64, 32, 5000, 0, 79),                     # VALU split kernel, more than 64 slots
+    (256, 128, 9000, 64, 71),
+])
+def test_combine_slot_counts(d, g, T, R, nslot):
+    """One (batch, KV head) row with a long context, so the split plan gives the combine
+    launch nslot partials per query row: both of its paths (at most 16 slots, loads issued
+    first; more, in 64-slot passes) against the oracle, and bf16 = RNE(fp32)."""
+    B, H, Hq = 1, 1, 4
+    probe = kvq.Int4Cache.empty(B, T, H, d, g, R, "cpu")
+    got_slots = kvq.decode_attn_ws_bytes(probe, Hq) // (B * Hq * (d + 2) * 4)
+    assert got_slots == nslot, f"split plan gives {got_slots} slots, the case wants {nslot}"
+    run_attn(B=B, T=T, H=H, Hq=Hq, d=d, g=g, R=R, seed=T % 97)

@@ -64,6 +64,22 @@ def test_special_values_snapkv():
     s[2, 200:300] = 0.0
     check_snapkv(s, 1000, 128)
     check_snapkv(s, 3990, 0)
+    # NaN scores before the window are needed to fill the budget: the window's masked tokens
+    # rank below them, so the union still holds the full keep count
+    check_snapkv(s, 3990, 128)
+    check_snapkv(s, 3500, 600)
+    n = torch.full((2, 700), float("nan"))
+    n[0, ::3] = torch.arange(0, 700, 3, dtype=torch.float32)
+    check_snapkv(n, 300, 50)
+    check_snapkv(n, 690, 64)
+    # a NaN in the history makes its token's H2O score NaN (fused path and the general one)
+    hist = synth.attention_history(3, 4, 2048, seed=9)
+    hist[0, 2, ::5] = float("nan")
+    hist[2, 0, :1500] = float("nan")
+    check_h2o(hist, 1900, 128)
+    hist = synth.attention_history(2, 3, 2050, seed=10)
+    hist[1, 1, 3::4] = float("nan")
+    check_h2o(hist, 2000, 100)
 
 
 def test_long_rows_beyond_register_path():
@@ -93,6 +109,25 @@ def test_compact_small():
         kd2, _ = kvq.compact(K2.to(DEV), None, kp.to(DEV))
         torch.cuda.synchronize()
         assert_bits_equal(u16(kd2), oracle.compact(u16(K2), kp.numpy()), f"compact d={dd}")
+
+
+def test_compact_out_of_range_indices_are_clamped():
+    """Keep entries below 0 or at / past T move the row of the nearest valid index (the
+    documented clamp), so a bad index never reads outside the source."""
+    B, T, H, d = 2, 77, 3, 128
+    K = synth.normal_bf16((B, T, H, d), seed=12)
+    V = synth.normal_bf16((B, T, H, d), seed=13)
+    keep = torch.randint(0, T, (B, H, 20), dtype=torch.int32)
+    keep[0, 0, 3] = -1
+    keep[0, 1, 0] = -(2 ** 31)
+    keep[1, 2, 19] = T
+    keep[1, 0, 7] = 2 ** 31 - 1
+    say("compact clamp", dict(B=B, T=T, H=H, d=d))
+    kd, vd = kvq.compact(K.to(DEV), V.to(DEV), keep.to(DEV))
+    torch.cuda.synchronize()
+    kc = keep.clamp(0, T - 1).numpy()
+    assert_bits_equal(u16(kd), oracle.compact(u16(K), kc), "compact K, clamped indices")
+    assert_bits_equal(u16(vd), oracle.compact(u16(V), kc), "compact V, clamped indices")
 
 
 def test_config5_full_size_sampled_rows():
