@@ -420,6 +420,20 @@ int kvq_snapkv_select(const float* scores, int64_t rows, int64_t T, int64_t budg
 int kvq_compact(const void* k_src, const void* v_src_or_null, int64_t B, int64_t T, int64_t H, int64_t d,
                 const int32_t* keep, int64_t K, void* k_dst, void* v_dst_or_null, kvq_stream stream);
 
+/* ======================================================================
+ * Streaming bandwidth probe  [a measurement helper, not a step of the method]
+ *
+ * Moves read_bytes from src and write_bytes to dst with the 16-byte loads and stores
+ * the kernels above use (non-temporal when nt != 0), so that a kernel's time can be
+ * read against what this device sustains for the same read:write mix.  In each round
+ * every thread issues its loads, then stores a value that depends on them.  The ratio
+ * read_bytes : write_bytes must be 1:0 (read only), 0:1 (write only), 1:1, 2:1, 1:2,
+ * 32:9 (a bf16 -> 4-bit g=64 quantizer's mix) or 9:32 (its dequantizer's).  dst is
+ * always required: a read-only probe stores at most 16 bytes there.  Both device.
+ * EINVAL: another ratio, sizes not multiples of 16, nothing to move, NULL pointers.
+ * ====================================================================== */
+int kvq_bw_probe(const void* src, uint64_t read_bytes, void* dst, uint64_t write_bytes, int nt, kvq_stream stream);
+
 #ifdef __cplusplus
 }
 #endif

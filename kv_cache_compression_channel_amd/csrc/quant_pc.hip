@@ -110,21 +110,9 @@ __global__ void __launch_bounds__(kThreads) pc_minmax_kernel(const void* __restr
     }
 }
 
-// Pass 2: per (slice, channel) scale / zero point (Walkthrough §1.1, §1.2).
+// Scale and zero point of one channel from its min and max (Walkthrough §1.1, §1.2).
 template <bool SYM>
-__global__ void __launch_bounds__(kThreads) pc_params_kernel(const float2* __restrict__ part, int64_t nb,
-                                                             int64_t nrc, int64_t C, int qmin, int qmax,
-                                                             float* __restrict__ scale, int8_t* __restrict__ zp,
-                                                             PcParams* __restrict__ prm) {
-    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    if (i >= nb * C) return;
-    const int64_t s = i / C, c = i % C;
-    float mn = FLT_MAX, mx = -FLT_MAX;
-    for (int64_t k = 0; k < nrc; ++k) {
-        const float2 p = part[(s * nrc + k) * C + c];
-        mn = vmin2(mn, p.x);
-        mx = vmax2(mx, p.y);
-    }
+__device__ __forceinline__ PcParams pc_param_of(float mn, float mx, int qmin, int qmax) {
     PcParams P;
     int z = 0;
     if constexpr (SYM) {
@@ -142,8 +130,56 @@ __global__ void __launch_bounds__(kThreads) pc_params_kernel(const float2* __res
     P.r = 1.0f / P.s;
     P.zf = (float)z;
     P.fast = (vmax2(fabsf(mn), fabsf(mx)) * P.r <= 250.0f) ? 1.0f : 0.0f;
+    return P;
+}
+
+// Codes of 8 values of one row: q = clip(round(x / s) + zp, qmin, qmax), packed low byte first.
+template <int VEC>
+__device__ __forceinline__ void pc_codes(const float (&v)[VEC], const float (&ps)[VEC], const float (&pr)[VEC],
+                                         const float (&pz)[VEC], bool fast, float lo, float hi,
+                                         int8_t (&o)[VEC]) {
+    float n[VEC];
+    if (fast) {
+        rint_div_n<VEC>(v, ps, pr, n);
+    } else {
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) n[k] = __builtin_rintf(v[k] / ps[k]);
+    }
+#pragma unroll
+    for (int k = 0; k < VEC; ++k) {
+        // n and zf are integers: the fp32 sum is exact whenever the result can land in
+        // [qmin, qmax] (Sterbenz), and far outside otherwise, so the clip is exact.
+        o[k] = (int8_t)(int)vclamp(n[k] + pz[k], lo, hi);
+    }
+}
+
+__device__ __forceinline__ uint2 pack8_i8(const int8_t (&o)[8]) {
+    uint2 w;
+    w.x = (uint32_t)(uint8_t)o[0] | ((uint32_t)(uint8_t)o[1] << 8) | ((uint32_t)(uint8_t)o[2] << 16) |
+          ((uint32_t)(uint8_t)o[3] << 24);
+    w.y = (uint32_t)(uint8_t)o[4] | ((uint32_t)(uint8_t)o[5] << 8) | ((uint32_t)(uint8_t)o[6] << 16) |
+          ((uint32_t)(uint8_t)o[7] << 24);
+    return w;
+}
+
+// Pass 2: per (slice, channel) scale / zero point (Walkthrough §1.1, §1.2).
+template <bool SYM>
+__global__ void __launch_bounds__(kThreads) pc_params_kernel(const float2* __restrict__ part, int64_t nb,
+                                                             int64_t nrc, int64_t C, int qmin, int qmax,
+                                                             float* __restrict__ scale, int8_t* __restrict__ zp,
+                                                             PcParams* __restrict__ prm) {
+    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (i >= nb * C) return;
+    const int64_t s = i / C, c = i % C;
+    float mn = FLT_MAX, mx = -FLT_MAX;
+    for (int64_t k = 0; k < nrc; ++k) {
+        const float2 p = part[(s * nrc + k) * C + c];
+        mn = vmin2(mn, p.x);
+        mx = vmax2(mx, p.y);
+    }
+    const PcParams P = pc_param_of<SYM>(mn, mx, qmin, qmax);
     scale[i] = P.s;
-    if (zp) zp[i] = (int8_t)z;
+    if (zp) zp[i] = (int8_t)P.zf;
     prm[i] = P;
 }
 
@@ -175,27 +211,10 @@ __global__ void __launch_bounds__(kThreads) pc_code_kernel(const void* __restric
         float v[VEC];
         load_x<XT, VEC>(x, s * g.bsx + r * g.ldx + c0, v);
         int8_t o[VEC];
-        float n[VEC];
-        if (fast) {
-            rint_div_n<VEC>(v, ps, pr, n);
-        } else {
-#pragma unroll
-            for (int k = 0; k < VEC; ++k) n[k] = __builtin_rintf(v[k] / ps[k]);
-        }
-#pragma unroll
-        for (int k = 0; k < VEC; ++k) {
-            // n and zf are integers: the fp32 sum is exact whenever the result can land in
-            // [qmin, qmax] (Sterbenz), and far outside otherwise, so the clip is exact.
-            o[k] = (int8_t)(int)vclamp(n[k] + pz[k], lo, hi);
-        }
+        pc_codes<VEC>(v, ps, pr, pz, fast, lo, hi, o);
         int8_t* dst = q + (s * g.R + r) * g.C + c0;
         if constexpr (VEC == 8) {
-            uint2 w;
-            w.x = (uint32_t)(uint8_t)o[0] | ((uint32_t)(uint8_t)o[1] << 8) | ((uint32_t)(uint8_t)o[2] << 16) |
-                  ((uint32_t)(uint8_t)o[3] << 24);
-            w.y = (uint32_t)(uint8_t)o[4] | ((uint32_t)(uint8_t)o[5] << 8) | ((uint32_t)(uint8_t)o[6] << 16) |
-                  ((uint32_t)(uint8_t)o[7] << 24);
-            *reinterpret_cast<uint2*>(dst) = w;
+            *reinterpret_cast<uint2*>(dst) = pack8_i8(o);
         } else {
             dst[0] = o[0];
         }

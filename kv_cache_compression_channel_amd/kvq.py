@@ -31,6 +31,7 @@ EXPORTED = [
     "kvq_select_ws", "kvq_h2o_select", "kvq_snapkv_select", "kvq_compact",
     "kvq_rot_cache_sizes", "kvq_rot_quant_int4", "kvq_rot_dequant", "kvq_rot_decode_attn_ws", "kvq_rot_decode_attn",
     "kvq_mixed_plan_ws", "kvq_mixed_plan", "kvq_mixed_quant", "kvq_mixed_dequant", "kvq_mixed_bytes",
+    "kvq_bw_probe",
 ]
 
 
@@ -132,6 +133,7 @@ def lib():
     L.kvq_h2o_select.argtypes = [P, I64, I64, I64, I64, I64, P, P, P, SZ, P]
     L.kvq_snapkv_select.argtypes = [P, I64, I64, I64, I64, P, P, SZ, P]
     L.kvq_compact.argtypes = [P, P, I64, I64, I64, I64, P, I64, P, P, P]
+    L.kvq_bw_probe.argtypes = [P, C.c_uint64, P, C.c_uint64, I, P]
     _lib = L
     return L
 
@@ -189,28 +191,46 @@ def quant_pc_ws_bytes(nb, R, Cc) -> int:
     return int(lib().kvq_quant_pc_ws(nb, R, Cc))
 
 
-def quant_sym(x: torch.Tensor, bits: int = 8, ws=None, with_zp: bool = True):
+def _pc_outs(x: torch.Tensor, nb, R, Cc, out, need_zp: bool):
+    """Caller-supplied (q, scale, zp) checked for shape and dtype, or new ones."""
+    if out is None:
+        q = torch.empty((nb, R, Cc), dtype=torch.int8, device=x.device)
+        s = torch.empty((nb, Cc), dtype=torch.float32, device=x.device)
+        z = torch.empty((nb, Cc), dtype=torch.int8, device=x.device) if need_zp else None
+        return q, s, z
+    q, s, z = out
+    _need_cuda(q, s, z)
+    if q.dtype != torch.int8 or q.numel() != nb * R * Cc or not q.is_contiguous():
+        raise ValueError("q must be a contiguous int8 tensor of nb * R * C elements")
+    if s.dtype != torch.float32 or s.numel() != nb * Cc or not s.is_contiguous():
+        raise ValueError("scale must be a contiguous fp32 tensor of nb * C elements")
+    if z is not None and (z.dtype != torch.int8 or z.numel() != nb * Cc or not z.is_contiguous()):
+        raise ValueError("zp must be a contiguous int8 tensor of nb * C elements")
+    if need_zp and z is None:
+        raise ValueError("the asymmetric quantizer needs a zp tensor")
+    return q, s, z
+
+
+def quant_sym(x: torch.Tensor, bits: int = 8, ws=None, with_zp: bool = True, out=None):
     """x: [nb][R][C] (or [R][C]) fp32/bf16 on the GPU, rows = tokens, columns = channels.
-    Returns (q int8 [nb][R][C], scale fp32 [nb][C], zp int8 [nb][C] of zeros or None)."""
+    Returns (q int8 [nb][R][C], scale fp32 [nb][C], zp int8 [nb][C] of zeros or None).
+    out: optional caller-owned (q, scale, zp) to write into (zp may be None)."""
     _need_cuda(x)
     x3, ldx, bsx = _pc_view(x)
     nb, R, Cc = x3.shape
-    q = torch.empty((nb, R, Cc), dtype=torch.int8, device=x.device)
-    s = torch.empty((nb, Cc), dtype=torch.float32, device=x.device)
-    z = torch.empty((nb, Cc), dtype=torch.int8, device=x.device) if with_zp else None
+    q, s, z = _pc_outs(x, nb, R, Cc, out, with_zp)
     w, wb = _ws(quant_pc_ws_bytes(nb, R, Cc), x.device, ws)
     _check(lib().kvq_quant_sym(_p(x3), _dt(x3), nb, R, Cc, ldx, bsx, bits, _p(q), _p(s), _p(z), _p(w), wb,
                                _stream(x)))
     return q, s, z
 
 
-def quant_asym(x: torch.Tensor, qmin: int = -128, qmax: int = 127, ws=None):
+def quant_asym(x: torch.Tensor, qmin: int = -128, qmax: int = 127, ws=None, out=None):
+    """As quant_sym, with codes in [qmin, qmax] and an int8 zero point per channel."""
     _need_cuda(x)
     x3, ldx, bsx = _pc_view(x)
     nb, R, Cc = x3.shape
-    q = torch.empty((nb, R, Cc), dtype=torch.int8, device=x.device)
-    s = torch.empty((nb, Cc), dtype=torch.float32, device=x.device)
-    z = torch.empty((nb, Cc), dtype=torch.int8, device=x.device)
+    q, s, z = _pc_outs(x, nb, R, Cc, out, True)
     w, wb = _ws(quant_pc_ws_bytes(nb, R, Cc), x.device, ws)
     _check(lib().kvq_quant_asym(_p(x3), _dt(x3), nb, R, Cc, ldx, bsx, qmin, qmax, _p(q), _p(s),
                                 _p(z), _p(w), wb, _stream(x)))
@@ -690,3 +710,17 @@ def compact(k_src: torch.Tensor, v_src: torch.Tensor | None, keep: torch.Tensor,
         v_dst = torch.empty((B, K, H, d), dtype=v_src.dtype, device=v_src.device)
     _check(lib().kvq_compact(_p(k_src), _p(v_src), B, T, H, d, _p(keep), K, _p(k_dst), _p(v_dst), _stream(k_src)))
     return k_dst, v_dst
+
+
+# ------------------------------------------------------- bandwidth probe --
+
+def bw_probe(src: torch.Tensor | None, read_bytes: int, dst: torch.Tensor, write_bytes: int, nt: bool = True):
+    """Stream read_bytes of src and write_bytes into dst (device buffers) in one of the probe's
+    read:write mixes; see kvq_bw_probe."""
+    _need_cuda(dst)
+    if src is not None and src.numel() * src.element_size() < read_bytes:
+        raise ValueError("src is smaller than read_bytes")
+    if dst.numel() * dst.element_size() < max(write_bytes, 16):
+        raise ValueError("dst is smaller than write_bytes (or 16 bytes)")
+    _check(lib().kvq_bw_probe(_p(src) if src is not None else None, read_bytes, _p(dst), write_bytes, int(nt),
+                              _stream(dst)))

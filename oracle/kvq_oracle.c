@@ -421,8 +421,10 @@ int64_t orc_keep_count(int64_t T, int64_t budget, int64_t window) {
  * recent tokens, whose scores were replaced by -inf, rank below every earlier token,
  * NaN included (READING: for numeric scores this is what the -inf mask does; it also
  * keeps |recent ∪ TopK| = min(T, max(budget, |recent|)) when earlier scores are NaN). */
-static const float* g_rank_vals; /* single-threaded oracle: qsort has no context argument */
-static int64_t g_rank_rs;        /* first recent index */
+/* qsort has no context argument: the ranking context is per thread, so independent rows may be
+ * selected on several threads at once */
+static _Thread_local const float* g_rank_vals;
+static _Thread_local int64_t g_rank_rs;        /* first recent index */
 static int rank_cmp(const void* pa, const void* pb) {
     const int32_t a = *(const int32_t*)pa, b = *(const int32_t*)pb;
     const int ra = a >= g_rank_rs, rb = b >= g_rank_rs;

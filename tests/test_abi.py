@@ -315,6 +315,16 @@ def test_select_and_compact_validation(L):
     assert cp(FAKE, None, 1, 10, 1, 128, FAKE, 0, FAKE, None, None) == kvq.KVQ_EINVAL   # K 0
 
 
+def test_bw_probe_validation(L):
+    bw = L.kvq_bw_probe
+    assert bw(FAKE, 64, None, 0, 1, None) == kvq.KVQ_EINVAL            # no sink
+    assert bw(None, 64, FAKE, 0, 1, None) == kvq.KVQ_EINVAL            # no source
+    assert bw(FAKE, 0, FAKE, 0, 1, None) == kvq.KVQ_EINVAL             # nothing to move
+    assert bw(FAKE, 24, FAKE, 0, 1, None) == kvq.KVQ_EINVAL            # not a multiple of 16
+    assert bw(FAKE, 48, FAKE, 16, 1, None) == kvq.KVQ_EINVAL           # 3:1 is not a probe mix
+    assert bw(MISALIGNED, 64, FAKE, 0, 1, None) == kvq.KVQ_EALIGN
+
+
 def test_library_has_no_oracle_dependency():
     """The product library and binding never load the oracle."""
     import subprocess

@@ -117,3 +117,34 @@ def test_exact_half_quotients():
     # asym with s = 1 and an odd zero point (-1)
     col = np.array([-127, 128, 0.5, 2.5, -3.5, 5.5] * 40, np.float32)[:, None]
     _check_pc(torch.from_numpy(col).to(DEV), col, "asym")
+
+
+@pytest.mark.parametrize("shape", [(2, 8192, 4096), (4, 1, 2048), (8, 128, 1024), (8, 129, 1024),
+                                   (3, 5000, 2752), (2, 4999, 4096)])
+def test_bf16_wide_slices(shape):
+    """bf16 slices with thousands of channels, as the full-model cache uses them: row counts of
+    one, below, at and past a 128- and 256-row chunk, and a whole 8192-token slice pair, with
+    all-zero, constant, all-positive and exact-half channels."""
+    x = synth.normal_bf16(shape, seed=sum(shape) + 1)
+    xf = x.float()
+    xf[0, :, 5] = 0.0                                   # all-zero channel
+    xf[-1, :, 33] = 2.5                                 # constant channel
+    xf[0, :, 64] = xf[0, :, 64].abs() + 1.0             # all positive
+    # absmax 127/16 gives s = 1/16 exactly; every other value sits on a half step (k + 0.5) / 16
+    xf[-1, :, 100] = (torch.arange(shape[1]) % 20 - 10 + 0.5) / 16
+    xf[-1, 0, 100] = 127 / 16
+    x = xf.to(torch.bfloat16)
+    _check_pc(x.to(DEV), u16(x), "sym", bits=8)
+    _check_pc(x.to(DEV), u16(x), "asym")
+    if shape[1] <= 1000:
+        _check_pc(x.to(DEV), u16(x), "sym", bits=3)
+        _check_pc(x.to(DEV), u16(x), "asym", qmin=0, qmax=15)
+
+
+def test_bf16_wide_strided_view():
+    big = synth.normal_bf16((2, 300, 4160), seed=31)
+    xg = big.to(DEV)[:, 3:260, 32:4128]                 # [2][257][4096], ldx = 4160
+    assert xg.stride() == (300 * 4160, 4160, 1)
+    host = np.ascontiguousarray(u16(big)[:, 3:260, 32:4128])
+    _check_pc(xg, host, "sym", bits=8)
+    _check_pc(xg, host, "asym")
