@@ -12,24 +12,42 @@
 namespace kvq {
 
 // Min or max over aligned groups of L lanes (L a power of two up to 64).  Within a row of 16 lanes
-// DPP lane moves, which are VALU operands and need no LDS: quad permutations [1,0,3,2] and
-// [2,3,0,1], then the half-row mirror (lane i <-> 7 - i) and the row mirror (i <-> 15 - i); after
-// each step every lane holds the value of its 2, 4, 8, 16 lanes.  Across rows, lane exchanges.
-// Every lane of a group ends with the group's value.
-template <int CTRL>
-__device__ __forceinline__ float dpp_move(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
-}
+// each step is one VALU instruction with a DPP source operand, v_min/v_max(permuted v, v): quad
+// permutations [1,0,3,2] and [2,3,0,1], then the half-row mirror (lane i <-> 7 - i) and the row
+// mirror (i <-> 15 - i); after each step every lane holds the value of its 2, 4, 8, 16 lanes.  The
+// two wait states a DPP read needs after a VALU write of its source are issued with the step.
+// Across rows, lane exchanges.  Every lane of a group ends with the group's value.
+#define KVQ_DPP_STEP(OP, PAT)                                                                        \
+    __device__ __forceinline__ float dpp_##OP##_##PAT(float v) {                                     \
+        float r;                                                                                     \
+        asm("s_nop 1\n\tv_" #OP "_f32_dpp %0, %1, %1 " KVQ_DPP_PAT_##PAT " row_mask:0xf bank_mask:0xf" \
+            : "=v"(r)                                                                                \
+            : "v"(v));                                                                               \
+        return r;                                                                                    \
+    }
+#define KVQ_DPP_PAT_q1032 "quad_perm:[1,0,3,2]"
+#define KVQ_DPP_PAT_q2301 "quad_perm:[2,3,0,1]"
+#define KVQ_DPP_PAT_hmir "row_half_mirror"
+#define KVQ_DPP_PAT_mir "row_mirror"
+KVQ_DPP_STEP(min, q1032)
+KVQ_DPP_STEP(min, q2301)
+KVQ_DPP_STEP(min, hmir)
+KVQ_DPP_STEP(min, mir)
+KVQ_DPP_STEP(max, q1032)
+KVQ_DPP_STEP(max, q2301)
+KVQ_DPP_STEP(max, hmir)
+KVQ_DPP_STEP(max, mir)
+#undef KVQ_DPP_STEP
+
 template <int L, bool MAX>
 __device__ __forceinline__ float lane_group_reduce(float v) {
     static_assert(L >= 1 && L <= 64 && (L & (L - 1)) == 0, "group of 1 to 64 lanes");
-    auto op = [](float a, float b) { return MAX ? vmax2(a, b) : vmin2(a, b); };
-    if constexpr (L >= 2) v = op(v, dpp_move<0xB1>(v));
-    if constexpr (L >= 4) v = op(v, dpp_move<0x4E>(v));
-    if constexpr (L >= 8) v = op(v, dpp_move<0x141>(v));
-    if constexpr (L >= 16) v = op(v, dpp_move<0x140>(v));
-    if constexpr (L >= 32) v = op(v, __shfl_xor(v, 16));
-    if constexpr (L >= 64) v = op(v, __shfl_xor(v, 32));
+    if constexpr (L >= 2) v = MAX ? dpp_max_q1032(v) : dpp_min_q1032(v);
+    if constexpr (L >= 4) v = MAX ? dpp_max_q2301(v) : dpp_min_q2301(v);
+    if constexpr (L >= 8) v = MAX ? dpp_max_hmir(v) : dpp_min_hmir(v);
+    if constexpr (L >= 16) v = MAX ? dpp_max_mir(v) : dpp_min_mir(v);
+    if constexpr (L >= 32) v = MAX ? vmax2(v, __shfl_xor(v, 16)) : vmin2(v, __shfl_xor(v, 16));
+    if constexpr (L >= 64) v = MAX ? vmax2(v, __shfl_xor(v, 32)) : vmin2(v, __shfl_xor(v, 32));
     return v;
 }
 
@@ -90,13 +108,22 @@ __device__ __forceinline__ GroupParams group_params(float mn, float mx) {
     // product by 2^-8 rounds exactly as the division does
     p.sb = bf_ceil_pos(vmax2(range / 15.0f, __builtin_fabsf(mn) * 0.00390625f));
     p.s = bf_to_f(p.sb);
-    // 0 - m: the backend lowers a subtraction from +0 to a negation, which turns m = +0 into
-    // -0; IEEE gives 0 - (+-0) = +0, so the zero quotient is handled explicitly
-    const float m = mn / p.s;
-    const float zr = (m == 0.0f) ? 0.0f : __builtin_rintf(-m);
+    // r only feeds the fast code path, whose tolerance covers the 1-ulp hardware reciprocal (see
+    // codes8); the stored values come from IEEE operations.
+    p.r = __builtin_amdgcn_rcpf(p.s);
+    // z = round(0 - fl(mn / s)), |mn / s| <= 256.  y = mn * r lies within 8e-5 of the quotient, as
+    // does fl(mn / s), so unless -y is within 1e-3 of a half-integer both round alike (and to
+    // zeros of the same sign while |y| is far above the subnormal range); otherwise the IEEE
+    // division decides.  0 - m: the backend lowers a subtraction from +0 to a negation, which
+    // turns m = +0 into -0; IEEE gives 0 - (+-0) = +0, so the zero quotient is explicit.
+    const float y = mn * p.r;
+    float zr = __builtin_rintf(-y);
+    if (__builtin_fabsf(-y - zr) > 0.499f || __builtin_fabsf(y) < 1e-30f) {
+        const float m = mn / p.s;
+        zr = (m == 0.0f) ? 0.0f : __builtin_rintf(-m);
+    }
     p.zb = f_to_bf(zr);
     p.z = bf_to_f(p.zb);
-    p.r = 1.0f / p.s;
     return p;
 }
 

@@ -114,13 +114,12 @@ __global__ void __launch_bounds__(NT) int4_quant_kernel(const uint16_t* __restri
 #pragma unroll
         for (int i = 0; i < NR; ++i) {
             const int r = rg + RPP * i;
-            if (r < n) {
-                float v[8], q[8];
-                unpack8(raw[i], v);
-                codes8<false>(v, ps, pr, pz, fast, q);
+            float v[8], q[8];
+            unpack8(raw[i], v);
+            codes8<false>(v, ps, pr, pz, fast, q);
+            if (n == G || r < n)
                 *reinterpret_cast<uint32_t*>(out.k_codes + ((b * H + h) * geo.ldq + t0 + r) * (D / 2) + 4 * lane) =
                     pack_codes(q);
-            }
         }
         return;
     }
@@ -135,16 +134,19 @@ __global__ void __launch_bounds__(NT) int4_quant_kernel(const uint16_t* __restri
         const int n = (int)min<int64_t>(VT, Tq - t0);
         const int grp = (8 * lane) / G;
         uint4 raw[NR];
+        // every row's load issued before any is used: rows past the tile's end load its last row
+        // again (their parameters are never read and their codes never stored)
 #pragma unroll
         for (int i = 0; i < NR; ++i) {
             const int r = rg + RPP * i;
-            float mn = FLT_MAX, mx = -FLT_MAX;
-            if (r < n) {
-                raw[i] = ld_stream_u4(V + b * geo.sb + (t0 + r) * geo.st + h * geo.sh + 8 * lane);
-                float v[8];
-                unpack8(raw[i], v);
-                minmax8(v, mn, mx);
-            }
+            raw[i] = ld_stream_u4(V + b * geo.sb + (t0 + (r < n ? r : n - 1)) * geo.st + h * geo.sh + 8 * lane);
+        }
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+            const int r = rg + RPP * i;
+            float mn = FLT_MAX, mx = -FLT_MAX, v[8];
+            unpack8(raw[i], v);
+            minmax8(v, mn, mx);
             mn = lane_group_reduce<LPG, false>(mn);
             mx = lane_group_reduce<LPG, true>(mx);
             if (lane % LPG == 0) { s_mn[r * NGD + grp] = mn; s_mx[r * NGD + grp] = mx; }
@@ -161,17 +163,16 @@ __global__ void __launch_bounds__(NT) int4_quant_kernel(const uint16_t* __restri
 #pragma unroll
         for (int i = 0; i < NR; ++i) {
             const int r = rg + RPP * i;
-            if (r < n) {
-                const float ps = s_ps[r * NGD + grp], pr = s_pr[r * NGD + grp], pz = s_pz[r * NGD + grp];
-                const bool fast = pz >= 0.0f && pz <= 15.0f;
-                const float ps8[8] = {ps, ps, ps, ps, ps, ps, ps, ps}, pr8[8] = {pr, pr, pr, pr, pr, pr, pr, pr};
-                const float pz8[8] = {pz, pz, pz, pz, pz, pz, pz, pz};
-                float v[8], q[8];
-                unpack8(raw[i], v);
-                codes8<true>(v, ps8, pr8, pz8, fast, q);
+            const float ps = s_ps[r * NGD + grp], pr = s_pr[r * NGD + grp], pz = s_pz[r * NGD + grp];
+            const bool fast = pz >= 0.0f && pz <= 15.0f;
+            const float ps8[8] = {ps, ps, ps, ps, ps, ps, ps, ps}, pr8[8] = {pr, pr, pr, pr, pr, pr, pr, pr};
+            const float pz8[8] = {pz, pz, pz, pz, pz, pz, pz, pz};
+            float v[8], q[8];
+            unpack8(raw[i], v);
+            codes8<true>(v, ps8, pr8, pz8, fast, q);
+            if (n == VT || r < n)
                 *reinterpret_cast<uint32_t*>(out.v_codes + ((b * H + h) * geo.ldq + t0 + r) * (D / 2) + 4 * lane) =
                     pack_codes(q);
-            }
         }
         return;
     }
