@@ -146,3 +146,43 @@ def test_offset_and_constant_groups(offset):
     torch.cuda.synchronize()
     s = np_(cache.k_scale.float()).repeat(g, axis=2)[:, :, :Tq].transpose(0, 2, 1, 3)
     assert np.all(np.abs(oracle.bf16_to_f32(Kb)[:, :Tq].astype(np.float64) - kh) <= s / 2)
+
+
+def test_scale_rounding_boundaries():
+    """Groups whose range / 15 is exactly a bf16 value m * 2^k (m <= 16, so the endpoints are bf16
+    too), with the top value moved by -2..2 bf16 ulps: the scale's round-up is then decided by the
+    last bits of the fp32 quotient.  Plus groups far from zero whose |min| / 256 bound is close to
+    range / 15.  Every scale and zero bit-exact against the oracle."""
+    rng = np.random.default_rng(23)
+    B, T, H, d, g = 1, 64, 4, 128, 64
+
+    def bump(x, k):
+        """x moved by k bf16 ulps (x bf16-exact)."""
+        b = oracle.f32_to_bf16(np.array([x], np.float32)).astype(np.int64)[0]
+        b = b + k if x >= 0 else b - k
+        return float(oracle.bf16_to_f32(np.array([b], np.uint16))[0])
+
+    K = np.zeros((B, T, H, d), np.float32)
+    V = rng.standard_normal((B, T, H, d)).astype(np.float32)
+    for idx in range(H * d):
+        h, c = divmod(idx, d)
+        m, k = int(rng.integers(1, 17)), int(rng.integers(-20, 10))
+        bstep = m * 2.0 ** k
+        j = int(rng.choice([0, 1, 2, 4, 8]))
+        lo, hi = -j * bstep, (15 - j) * bstep
+        nud = int(rng.integers(-2, 3))
+        col = np.linspace(lo, hi, T).astype(np.float32)
+        col[-1] = bump(hi, nud)
+        K[0, :, h, c] = col
+        row = np.linspace(lo, hi, g).astype(np.float32)
+        row[-1] = bump(hi, -nud)
+        V[0, idx % T, h, :g] = row
+    Kb, Vb = oracle.f32_to_bf16(K), oracle.f32_to_bf16(V)
+    run_and_compare(Kb, Vb, g=g, R=0, check_stats=False)
+    # far from zero: |min| / 256 close to range / 15
+    K2 = np.zeros((1, 64, 1, d), np.float32)
+    for c in range(d):
+        base = float(2.0 ** rng.integers(-4, 8))
+        K2[0, :, 0, c] = base + np.linspace(0, base * 15 / 256 * float(rng.uniform(0.9, 1.1)), 64)
+    K2b = oracle.f32_to_bf16(K2)
+    run_and_compare(K2b, K2b, g=64, R=0, check_stats=False)
