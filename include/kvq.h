@@ -360,6 +360,25 @@ int kvq_decode_attn_int4(const kvq_int4_cache* c, const void* q, int64_t Hq, flo
                          int ot, void* ws, size_t ws_bytes, kvq_stream stream);
 
 /* ======================================================================
+ * Decode attention without a workspace  [for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops]
+ *
+ * The same operation, arguments and result as kvq_decode_attn_int4 (bit for bit), with the
+ * split partials kept in a scratch array of KVQ_ATTN_SCRATCH_BYTES that the library holds
+ * on each GPU it runs on, from its load until the process ends.  The call allocates nothing
+ * (no hipMalloc, hipFree or allocating routine); its first call on a device takes the
+ * array's address on that device.  Nothing in the scratch has to start at zero.  Every call
+ * on a GPU shares that GPU's array: calls that overlap in time on one GPU (other streams,
+ * other host threads) race and corrupt each other's output -- serialize them.
+ * EINVAL: as kvq_decode_attn_int4, and kvq_decode_attn_int4_ws(c, Hq) above
+ *         KVQ_ATTN_SCRATCH_BYTES (checked before anything is launched).
+ * EHIP: the device or the scratch address could not be queried.
+ * ====================================================================== */
+#define KVQ_ATTN_SCRATCH_BYTES (16u << 20)
+int kvq_decode_attn_int4_noalloc(const kvq_int4_cache* c, const void* q, int64_t Hq, float sm_scale, void* out,
+                                 int ot, kvq_stream stream);
+
+/* ======================================================================
  * Decode attention with running H2O scores  [Walkthrough §3.1: a token's score
  * is the attention it has received, summed over the observed steps; applied one
  * decode step at a time; the attention itself as kvq_decode_attn_int4]

@@ -18,6 +18,7 @@
 // Lane layout (VALU path): d/8 lanes per token, 8 channels per lane; a wave takes
 // 512/d tokens per step; dot products are finished with butterfly shuffles.
 #include <cmath>
+#include <mutex>
 
 #include "kvq_internal.h"
 
@@ -581,6 +582,58 @@ int kvq_decode_attn_int4(const kvq_int4_cache* c, const void* q, int64_t Hq, flo
                          void* ws, size_t ws_bytes, kvq_stream stream) {
     return kvq::decode_attn("kvq_decode_attn_int4", c, q, Hq, sm_scale, out, ot, nullptr, 0, ws, ws_bytes,
                             kvq_decode_attn_int4_ws(c, Hq), static_cast<hipStream_t>(stream));
+}
+
+// Scratch of the allocation-free entry point: the split partials, in a fixed array each GPU holds
+// from the library's load until the process ends.  In host code the name is a stand-in, not a
+// device address: the address is taken once per device with hipGetSymbolAddress.
+static __device__ __attribute__((aligned(256))) uint8_t scratch[KVQ_ATTN_SCRATCH_BYTES];
+
+}  // extern "C"
+
+namespace kvq {
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of the scratch array (its address taken on the first call on that
+// device, with the device current).
+int scratch_of_current_device(const char* name, void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(KVQ_EHIP, "%s: hipGetDevice: %s", name, hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(KVQ_EINVAL, "%s: device %d out of range", name, dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(KVQ_EHIP, "%s: hipGetSymbolAddress(scratch): %s", name, hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return KVQ_OK;
+}
+
+}  // namespace
+}  // namespace kvq
+
+extern "C" {
+
+int kvq_decode_attn_int4_noalloc(const kvq_int4_cache* c, const void* q, int64_t Hq, float sm_scale, void* out,
+                                 int ot, kvq_stream stream) {
+    const char* name = "kvq_decode_attn_int4_noalloc";
+    const size_t need = kvq_decode_attn_int4_ws(c, Hq);
+    KVQ_REQUIRE(need <= (size_t)KVQ_ATTN_SCRATCH_BYTES,
+                "%s: the split partials need %zu bytes, more than the %u-byte scratch (use kvq_decode_attn_int4 "
+                "with a workspace)", name, need, (unsigned)KVQ_ATTN_SCRATCH_BYTES);
+    void* ws = nullptr;
+    const int rc = kvq::scratch_of_current_device(name, &ws);
+    if (rc) return rc;
+    return kvq::decode_attn(name, c, q, Hq, sm_scale, out, ot, nullptr, 0, ws, (size_t)KVQ_ATTN_SCRATCH_BYTES, need,
+                            static_cast<hipStream_t>(stream));
 }
 
 size_t kvq_decode_attn_int4_h2o_ws(const kvq_int4_cache* c, int64_t Hq) {

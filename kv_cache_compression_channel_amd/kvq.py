@@ -31,7 +31,7 @@ EXPORTED = [
     "kvq_select_ws", "kvq_h2o_select", "kvq_snapkv_select", "kvq_compact",
     "kvq_rot_cache_sizes", "kvq_rot_quant_int4", "kvq_rot_dequant", "kvq_rot_decode_attn_ws", "kvq_rot_decode_attn",
     "kvq_mixed_plan_ws", "kvq_mixed_plan", "kvq_mixed_quant", "kvq_mixed_dequant", "kvq_mixed_bytes",
-    "kvq_bw_probe",
+    "kvq_bw_probe", "kvq_decode_attn_int4_noalloc",
 ]
 
 
@@ -134,6 +134,7 @@ def lib():
     L.kvq_snapkv_select.argtypes = [P, I64, I64, I64, I64, P, P, SZ, P]
     L.kvq_compact.argtypes = [P, P, I64, I64, I64, I64, P, I64, P, P, P]
     L.kvq_bw_probe.argtypes = [P, C.c_uint64, P, C.c_uint64, I, P]
+    L.kvq_decode_attn_int4_noalloc.argtypes = [P, P, I64, C.c_float, P, I, P]
     _lib = L
     return L
 
@@ -642,6 +643,26 @@ def decode_attn_int4(cache: Int4Cache, q: torch.Tensor, sm_scale: float = 1.0, o
     w, wb = _ws(int(lib().kvq_decode_attn_int4_ws(C.byref(desc), Hq)), q.device, ws)
     _check(lib().kvq_decode_attn_int4(C.byref(desc), _p(q), Hq, float(sm_scale), _p(out), _dt(out), _p(w), wb,
                                       _stream(q)))
+    return out
+
+
+ATTN_SCRATCH_BYTES = 16 << 20   # KVQ_ATTN_SCRATCH_BYTES
+
+
+def decode_attn_int4_noalloc(cache: Int4Cache, q: torch.Tensor, sm_scale: float = 1.0, out=None,
+                             out_dtype=torch.bfloat16):
+    """decode_attn_int4 with the split partials in the library's per-device scratch array instead of a
+    workspace (the library call allocates nothing; out is allocated here unless given).  Calls that
+    overlap on one GPU race."""
+    _need_cuda(q)
+    if q.dtype != torch.bfloat16 or not q.is_contiguous():
+        raise TypeError("q must be a contiguous bfloat16 [B][Hq][d] tensor")
+    B, Hq, d = q.shape
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=out_dtype, device=q.device)
+    desc = cache.desc()
+    _check(lib().kvq_decode_attn_int4_noalloc(C.byref(desc), _p(q), Hq, float(sm_scale), _p(out), _dt(out),
+                                              _stream(q)))
     return out
 
 
