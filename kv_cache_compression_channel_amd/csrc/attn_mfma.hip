@@ -15,12 +15,12 @@
 //           (K scales and zeros are per channel over a token group, so they fold into Q'; Q' is
 //           split into two fp16 parts, two MFMAs each, so it carries ~22 significant bits; the
 //           bias is formed in fp32 from the unrounded q')
-//   values  O[c][n] = sum_t (64 + code_V[t][c]) * P'[t][n]  -  sum_t 64 * P'[t][n]
-//                     - sum_t (p s_V)[t][n] * z_V[t][grp(c)],      P' = fp16(p * s_V)
-//           (the middle term is one more MFMA per V group against a constant-64 operand; the
-//           zero-point term is accumulated in fp32 from the unrounded p * s_V, so groups with a
-//           tiny scale and a huge zero point -- constant groups -- keep their value; the rotated
-//           cache, whose output is rotated back, uses the fp16 P' there instead, see ROT below)
+//   values  O[c][n] = sum_t (64 + code_V[t][c]) * P'[t][n]  -  sum_t (64 + z_V[t][grp(c)]) * P'[t][n],
+//                     P' = fp16(p * s_V)
+//           (the second term is one more MFMA per V group, whose A operand holds fp16(64 + z_V)
+//           of each token -- exact, as a stored zero point is an integer of magnitude <= 256 --
+//           so both terms carry the same rounded weight and its rounding cancels inside
+//           (code - z); the rotated cache keeps its own form of the zero-point term, see ROT)
 //
 // The fp16 range is kept by the softmax reference: p = 2^(logit - ref) with
 // ref = Mlog + E - 15, where Mlog bounds every logit seen so far and 2^E bounds every V scale
@@ -255,6 +255,7 @@ attn_mfma_kernel(const MfmaArgs a) {
         uint16_t kp[kWaves][(GS == 32 ? 4 : 2) * D];   // K group scale and zero rows of a tile pair
         uint32_t qx[kWaves][ROT ? 1 : 64][PASS * 8];
         float ksz[kWaves][ROT ? 2 * kTile * NG * 2 : 1];   // ROT: K (scale, zero) of a tile pair
+        uint16_t zf[kWaves][ROT ? 1 : 2 * NG * kTile];     // fp16(64 + z_V), [tile][group][token]
     };
     struct Merge {
         float m[kWaves][16], l[kWaves][16];
@@ -480,6 +481,16 @@ attn_mfma_kernel(const MfmaArgs a) {
                 smax = w == 0 ? vmax2(s0, s1) : vmax3(smax, s0, s1);
             }
         }
+        if constexpr (!ROT) {
+            // fp16(64 + z_V) of token lane % 32 of tile lane / 32, every group (exact: |z| <= 256)
+            uint16_t* zt = sm.lp.zf[wv] + (lane / kTile) * (NG * kTile) + lane % kTile;
+#pragma unroll
+            for (int gI = 0; gI < NG; ++gI) {
+                const uint32_t zw = r.vz[gI / 2];
+                const float z = (gI % 2) ? bf_hi(zw) : bf_lo(zw);
+                zt[gI * kTile] = __builtin_bit_cast(uint16_t, (_Float16)(64.0f + z));
+            }
+        }
         if constexpr (ROT) {
             float* kst = sm.lp.ksz[wv];
             if constexpr (NG == 1) {
@@ -691,7 +702,7 @@ attn_mfma_kernel(const MfmaArgs a) {
 #pragma unroll
             for (int gI = 0; gI < NG; ++gI) {
                 acc_off[gI] *= alpha;
-                zsum[gI] *= alpha;
+                if constexpr (ROT) zsum[gI] *= alpha;
             }
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
@@ -745,9 +756,6 @@ attn_mfma_kernel(const MfmaArgs a) {
                         const float u0 = r0 >= 6.103515625e-05f ? r0 : ps0, u1 = r1 >= 6.103515625e-05f ? r1 : ps1;
                         zsum[gI] = __builtin_fmaf(u0, a0.y, zsum[gI]);
                         zsum[gI] = __builtin_fmaf(u1, a1.y, zsum[gI]);
-                    } else {
-                        zsum[gI] = __builtin_fmaf(ps0, a0.y, zsum[gI]);
-                        zsum[gI] = __builtin_fmaf(ps1, a1.y, zsum[gI]);
                     }
                 }
                 bp[gI] = as_half8(w[0], w[1], w[2], w[3]);
@@ -759,6 +767,7 @@ attn_mfma_kernel(const MfmaArgs a) {
             const int tok[8] = {4 * G, 4 * G + 1, 4 * G + 2, 4 * G + 3,
                                 16 + 4 * G, 16 + 4 * G + 1, 16 + 4 * G + 2, 16 + 4 * G + 3};
             const half8 c64 = as_half8(kMagic, kMagic, kMagic, kMagic);
+            const uint16_t* tzf = sm.lp.zf[wv] + par * (NG * kTile);
 #pragma unroll
             for (int gI = 0; gI < NG; ++gI) {
                 // this lane's piece of group gI: PB bytes at byte offset (GS/2)*gI + PB*n
@@ -796,7 +805,16 @@ attn_mfma_kernel(const MfmaArgs a) {
                     acc_o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(w[0], w[1], w[2], w[3]), bp[gI],
                                                                        acc_o[nb], 0, 0, 0);
                 }
-                acc_off[gI] = __builtin_amdgcn_mfma_f32_16x16x32_f16(c64, bp[gI], acc_off[gI], 0, 0, 0);
+                if constexpr (ROT) {
+                    acc_off[gI] = __builtin_amdgcn_mfma_f32_16x16x32_f16(c64, bp[gI], acc_off[gI], 0, 0, 0);
+                } else {
+                    // sum_t P'[t][n] * (64 + z_V[t][gI]) in one MFMA: every row of A is the token slots'
+                    // fp16(64 + z), in the order of bp's slots (tokens 4G..4G+3, then 16+4G..16+4G+3)
+                    const uint2 z0 = *reinterpret_cast<const uint2*>(tzf + gI * kTile + 4 * G);
+                    const uint2 z1 = *reinterpret_cast<const uint2*>(tzf + gI * kTile + 16 + 4 * G);
+                    acc_off[gI] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(z0.x, z0.y, z1.x, z1.y), bp[gI],
+                                                                         acc_off[gI], 0, 0, 0);
+                }
             }
         }
     };
@@ -848,10 +866,12 @@ attn_mfma_kernel(const MfmaArgs a) {
     // ---------------- finish the wave: sums over the 4 lane groups, offset and zero terms ----------------
     l_part += xor_lane<16>(l_part);
     l_part += xor_lane<32>(l_part);
+    if constexpr (ROT) {
 #pragma unroll
-    for (int gI = 0; gI < NG; ++gI) {
-        zsum[gI] += xor_lane<16>(zsum[gI]);
-        zsum[gI] += xor_lane<32>(zsum[gI]);
+        for (int gI = 0; gI < NG; ++gI) {
+            zsum[gI] += xor_lane<16>(zsum[gI]);
+            zsum[gI] += xor_lane<32>(zsum[gI]);
+        }
     }
     __syncthreads();   // every wave is done with the loop buffers before the merge reuses them
     // acc_o[nb][i] is channel row m = 4G + i of block nb, query n
