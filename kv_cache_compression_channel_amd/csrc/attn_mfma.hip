@@ -267,18 +267,22 @@ attn_mfma_kernel(const MfmaArgs a) {
         ResLds rs;
     } sm;
 
-    const int nres_blocks = (int)(a.B * a.H) * a.nres;
-    if ((int)blockIdx.x < nres_blocks) {      // uniform per block
-        residual_block<NQ, LG>(a, sm.rs, (int)blockIdx.x);
+    // Block order: the INT4 splits split-major (block = split * B*H + (b, h)), then the bf16
+    // residual blocks.  Blocks go to the XCDs round-robin, so split-major order gives every XCD
+    // the same share of the short last splits, and the residual blocks, dispatched last, take
+    // the slots those splits free instead of delaying a long split at the start.
+    const int nq_blocks = (int)(a.B * a.H) * a.nsplit;
+    if ((int)blockIdx.x >= nq_blocks) {      // uniform per block
+        residual_block<NQ, LG>(a, sm.rs, (int)blockIdx.x - nq_blocks);
         return;
     }
-    const int blk = (int)blockIdx.x - nres_blocks;
+    const int blk = (int)blockIdx.x;
 
     const int tid = threadIdx.x, lane = tid % 64;
     const int wv = __builtin_amdgcn_readfirstlane(tid / 64);
     const int n = lane % 16, G = lane / 16;
-    const int64_t bh = blk / a.nsplit;
-    const int split = blk % a.nsplit;
+    const int64_t bh = blk % (a.B * a.H);
+    const int split = (int)(blk / (a.B * a.H));
     const int64_t b = bh / a.H, h = bh % a.H;
     const int Tq = a.Tq;
     // this wave's contiguous token range inside the split
