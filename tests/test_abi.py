@@ -340,3 +340,28 @@ def test_library_has_no_oracle_dependency():
             if f.endswith((".py", ".hip", ".h", ".cpp")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"import oracle|from oracle|liboracle|\borc_", text), f
+
+
+def _gpu_visible():
+    import torch
+    return torch.cuda.device_count() > 0
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="needs a host with no GPU: the arguments are fake pointers that "
+                                           "pass validation, so on a GPU they would reach a kernel")
+def test_hip_errors_map_to_EHIP(L):
+    """With no device, every call that gets past its argument checks fails in the HIP runtime:
+    the status is KVQ_EHIP and kvq_last_error names the entry point and the runtime's message.
+    Covers launches (the probe, INT4 dequantization) and the device query of the
+    no-allocation attention."""
+    L.kvq_last_error.restype = C.c_char_p
+    assert L.kvq_bw_probe(FAKE, 4096, FAKE, 4096, 0, None) == kvq.KVQ_EHIP
+    assert L.kvq_last_error().startswith(b"kvq_bw_probe")
+    d = _desc(H=8)
+    qd = kvq.QDesc(kvq.KVQ_FMT_INT4_K, C.cast(C.pointer(d), C.c_void_p))
+    assert L.kvq_dequant(C.byref(qd), FAKE, 0, None) == kvq.KVQ_EHIP
+    assert L.kvq_decode_attn_int4_noalloc(C.byref(d), FAKE, 32, 1.0, FAKE, 1, None) == kvq.KVQ_EHIP
+    msg = L.kvq_last_error()
+    assert b"kvq_decode_attn_int4_noalloc" in msg and len(msg) > len(b"kvq_decode_attn_int4_noalloc: ")
+    # a host-only call after the failures still succeeds
+    assert kvq.keep_count(32768, 2048, 256) == 2048

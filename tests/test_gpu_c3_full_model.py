@@ -62,6 +62,29 @@ def test_int4_sweep_sampled(cache_kv, g):
     assert full[2] >= kmax and full[0] > 0
 
 
+@pytest.mark.parametrize("g", [32, 64, 128])
+def test_int4_whole_slice_every_head(cache_kv, g):
+    """One whole (b, l) slice, all 32 heads, every section and both dequantized sides
+    element by element (the sampled test above covers one head of three slices)."""
+    K, V = cache_kv
+    b, l = 2, 5
+    s = b * LAYERS + l
+    say("C3 int4 whole slice", (b, l), "g", g)
+    cache = kvq.group_quant_int4(K, V, g=g, R=0)
+    kh = kvq.dequant_int4(cache, "k", torch.bfloat16)
+    vh = kvq.dequant_int4(cache, "v", torch.bfloat16)
+    torch.cuda.synchronize()
+    Kb, Vb = u16(K[s:s + 1]), u16(V[s:s + 1])
+    want = oracle.int4_quant(Kb, Vb, g, 0)
+    for sec in ("k_codes", "k_scale", "k_zero", "v_codes", "v_scale", "v_zero"):
+        t = getattr(cache, sec)[s:s + 1]
+        got = u16(t) if t.dtype == torch.bfloat16 else np_(t)
+        assert_bits_equal(got, want[sec], f"{sec} slice {(b, l)} g={g}")
+    for side, Xh in (("k", kh), ("v", vh)):
+        assert_bits_equal(u16(Xh[s:s + 1]), oracle.f32_to_bf16(oracle.int4_dequant(want, side)),
+                          f"{side} dequant slice {(b, l)} g={g}")
+
+
 def gpu_slice(a: np.ndarray) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(DEV)
 
@@ -73,7 +96,7 @@ def test_int8_per_channel_sampled(cache_kv):
     q, s, _ = kvq.quant_sym(x, bits=8, with_zp=True)
     xh = kvq.dequant_pc(q, s, None, torch.bfloat16)
     torch.cuda.synchronize()
-    for b, l, _h in SAMPLES[:2]:
+    for b, l, _h in SAMPLES:
         sl = b * LAYERS + l
         xb = u16(x[sl:sl + 1])
         oq, os_, _ = oracle.quant_sym(xb, 8)
