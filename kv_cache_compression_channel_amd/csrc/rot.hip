@@ -77,66 +77,127 @@ struct RotGeom {
     int64_t B, T, H;
     float c;        // fp32(1 / sqrt(d))
     uint32_t rows;  // B * T * H
+    uint32_t ntt;   // token tiles of kRowsPerBlock per (b, h)
 };
+
+// Block u of the quantizer and dequantizer grids: (b, token tile, h) with h fastest, so blocks
+// running together touch neighbouring [B][T][H] input rows; the index arithmetic is done once
+// per block instead of per row.
+struct RotTile {
+    int64_t in0;    // [B][T][H] row of the tile's first token
+    int64_t out0;   // [B][H][T] row of the tile's first token
+    int n;          // tokens in the tile
+};
+__device__ __forceinline__ RotTile rot_tile(const RotGeom& geo, uint32_t u) {
+    const uint32_t H = (uint32_t)geo.H;
+    const uint32_t q = u / H, h = u - q * H;
+    const uint32_t b = q / geo.ntt, tt = q - b * geo.ntt;
+    const int64_t t0 = (int64_t)tt * kRowsPerBlock;
+    RotTile r;
+    r.in0 = ((int64_t)b * geo.T + t0) * geo.H + h;
+    r.out0 = ((int64_t)b * geo.H + h) * geo.T + t0;
+    r.n = (int)min<int64_t>(kRowsPerBlock, geo.T - t0);
+    return r;
+}
 
 // ---------------- quantization: K and V rows of the [B][T][H][d] input ----------------
 // Each thread loads the K and V pieces of all its rows first (rows past the end repeat the last
-// row and are not stored, so every lane takes part in every shuffle), then rotates and quantizes.
+// row and are not stored, so every lane takes part in every shuffle), then rotates them.  The
+// sign flips are applied to the bf16 pairs before widening (one xor per pair of coordinates).
+// Group parameters are computed once per group rather than in each of its lanes: the group's
+// first lane puts the group's (min, max) in its wave's LDS table, lane j of the wave computes
+// the parameters of table entries j, j + 64, ... (and stores the bf16 scale and zero), and every
+// lane reads back the entries of its own groups.  The table is private to the wave, so no block
+// barrier is needed.  Rows are taken in batches of SB sides (K and V together when d <= 128),
+// which bounds the rotated values held in registers to SB * NR rows of 8.
 template <int D, int G>
 __global__ void __launch_bounds__(kThreads) rot_quant_kernel(const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
                                                             RotGeom geo, SignBits ks, SignBits vs, kvq_rot_cache out) {
     constexpr int LPR = D / 8, RPP = kThreads / LPR, LPG = G / 8, NGD = D / G, NR = kRowsPerBlock / RPP;
+    constexpr int RW = 64 / LPR;              // rows of a wave in one pass
+    constexpr int GW = RW * NGD;              // groups of a wave in one row of each of its lanes
+    constexpr int SB = D <= 128 ? 2 : 1;      // sides per batch
+    constexpr int NRS = SB * NR;              // rows per lane in a batch
+    constexpr int NPAIR = NRS * GW;           // groups of a wave in a batch
+    __shared__ float2 s_mm[kWaves][NPAIR];
+    __shared__ float4 s_prm[kWaves][NPAIR];
     const int tid = threadIdx.x, lane = tid % LPR, rg = tid / LPR;
-    const uint32_t r0 = blockIdx.x * kRowsPerBlock;
+    const int wl = tid % 64, wv = tid / 64;
+    const int gw = wl / LPG;                  // this lane's group in the wave's table row
+    const RotTile tl = rot_tile(geo, blockIdx.x);
+    const int64_t rs_in = geo.H * D;          // elements between consecutive tokens of the input
     uint4 raw[2][NR];
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
-        const uint32_t r = min(r0 + rg + RPP * i, geo.rows - 1);
-        raw[0][i] = *reinterpret_cast<const uint4*>(K + (int64_t)r * D + 8 * lane);
-        raw[1][i] = *reinterpret_cast<const uint4*>(V + (int64_t)r * D + 8 * lane);
+        const int u = min(rg + RPP * i, tl.n - 1);
+        const int64_t e = (tl.in0 * D + 8 * lane) + u * rs_in;
+        raw[0][i] = *reinterpret_cast<const uint4*>(K + e);
+        raw[1][i] = *reinterpret_cast<const uint4*>(V + e);
     }
-    const uint32_t sgn[2] = {sign8(ks, 8 * lane), sign8(vs, 8 * lane)};
+    // bf16 pair j of the lane holds coordinates 8 lane + 2j (bits 0..15) and + 2j + 1 (bits 16..31)
+    uint32_t sm[2][4];
 #pragma unroll
-    for (int i = 0; i < NR; ++i) {
-        const uint32_t r = r0 + rg + RPP * i;
-        const bool live = r < geo.rows;
-        const uint32_t rc = live ? r : geo.rows - 1;
-        const uint32_t q1 = rc / (uint32_t)geo.H;
-        const int64_t h = rc - q1 * (uint32_t)geo.H, t = q1 % (uint32_t)geo.T, b = q1 / (uint32_t)geo.T;
-        const int64_t o = (b * geo.H + h) * geo.T + t;          // [B][H][T] output row
+    for (int side = 0; side < 2; ++side) {
+        const uint32_t s8 = sign8(side ? vs : ks, 8 * lane);
 #pragma unroll
-        for (int side = 0; side < 2; ++side) {
-            float v[8];
-            unpack8(raw[side][i], v);
+        for (int j = 0; j < 4; ++j) sm[side][j] = ((s8 >> (2 * j)) & 1u) << 15 | ((s8 >> (2 * j + 1)) & 1u) << 31;
+    }
 #pragma unroll
-            for (int k = 0; k < 8; ++k) v[k] = ((sgn[side] >> k) & 1u) ? -v[k] : v[k];
-            fwht_row<LPR>(v, lane);
-            float mn = FLT_MAX, mx = -FLT_MAX;
+    for (int s0 = 0; s0 < 2; s0 += SB) {
+        float v[NRS][8];
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                v[k] = v[k] * geo.c;
-                mn = vmin2(mn, v[k]);
-                mx = vmax2(mx, v[k]);
-            }
+        for (int rs = 0; rs < NRS; ++rs) {
+            const int side = s0 + rs / NR, i = rs % NR;
+            uint4 w = raw[side][i];
+            w.x ^= sm[side][0]; w.y ^= sm[side][1]; w.z ^= sm[side][2]; w.w ^= sm[side][3];
+            unpack8(w, v[rs]);
+            fwht_row<LPR>(v[rs], lane);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) v[rs][k] = v[rs][k] * geo.c;
+            float mn = vmin3(v[rs][0], v[rs][1], v[rs][2]), mx = vmax3(v[rs][0], v[rs][1], v[rs][2]);
+            mn = vmin3(mn, v[rs][3], v[rs][4]); mx = vmax3(mx, v[rs][3], v[rs][4]);
+            mn = vmin3(mn, v[rs][5], v[rs][6]); mx = vmax3(mx, v[rs][5], v[rs][6]);
+            mn = vmin2(mn, v[rs][7]); mx = vmax2(mx, v[rs][7]);
             mn = lane_group_reduce<LPG, false>(mn);
             mx = lane_group_reduce<LPG, true>(mx);
-            const GroupParams gp = group_params(mn, mx);
-            const bool fast = gp.z >= 0.0f && gp.z <= 15.0f;
-            const float ps8[8] = {gp.s, gp.s, gp.s, gp.s, gp.s, gp.s, gp.s, gp.s};
-            const float pr8[8] = {gp.r, gp.r, gp.r, gp.r, gp.r, gp.r, gp.r, gp.r};
-            const float pz8[8] = {gp.z, gp.z, gp.z, gp.z, gp.z, gp.z, gp.z, gp.z};
-            float q[8];
-            codes8<true>(v, ps8, pr8, pz8, fast, q);
-            if (live) {
-                const int64_t mi = o * NGD + (8 * lane) / G;
-                if (lane % LPG == 0) {
+            if (wl % LPG == 0) s_mm[wv][rs * GW + gw] = make_float2(mn, mx);
+        }
+        __builtin_amdgcn_wave_barrier();
+        // one group per lane: parameters, and the bf16 scale / zero of the group
+#pragma unroll
+        for (int p0 = 0; p0 < NPAIR; p0 += 64) {
+            const int p = p0 + wl;
+            if (NPAIR % 64 == 0 || p < NPAIR) {
+                const float2 m = s_mm[wv][p];
+                const GroupParams gp = group_params(m.x, m.y);
+                s_prm[wv][p] = make_float4(gp.s, gp.r, gp.z, 0.0f);
+                const int rs = p / GW, gq = p % GW;
+                const int side = s0 + rs / NR, i = rs % NR;
+                const int u = wv * RW + gq / NGD + RPP * i;
+                if (u < tl.n) {
+                    const int64_t mi = (tl.out0 + u) * NGD + gq % NGD;
                     (side ? out.v_scale : out.k_scale)[mi] = gp.sb;
                     (side ? out.v_zero : out.k_zero)[mi] = gp.zb;
                 }
-                *reinterpret_cast<uint32_t*>((side ? out.v_codes : out.k_codes) + o * (D / 2) + 4 * lane) =
-                    pack_codes(q);
             }
         }
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int rs = 0; rs < NRS; ++rs) {
+            const int side = s0 + rs / NR, i = rs % NR;
+            const float4 pp = s_prm[wv][rs * GW + gw];
+            const bool fast = pp.z >= 0.0f && pp.z <= 15.0f;
+            const float ps8[8] = {pp.x, pp.x, pp.x, pp.x, pp.x, pp.x, pp.x, pp.x};
+            const float pr8[8] = {pp.y, pp.y, pp.y, pp.y, pp.y, pp.y, pp.y, pp.y};
+            const float pz8[8] = {pp.z, pp.z, pp.z, pp.z, pp.z, pp.z, pp.z, pp.z};
+            float q[8];
+            codes8<true>(v[rs], ps8, pr8, pz8, fast, q);
+            const int u = rg + RPP * i;
+            if (u < tl.n)
+                *reinterpret_cast<uint32_t*>((side ? out.v_codes : out.k_codes) + (tl.out0 + u) * (D / 2) + 4 * lane) =
+                    pack_codes(q);
+        }
+        __builtin_amdgcn_wave_barrier();   // the table is reused by the next batch
     }
 }
 
@@ -149,16 +210,13 @@ __global__ void __launch_bounds__(kThreads) rot_dequant_kernel(const uint8_t* __
                                                               SignBits sg, void* __restrict__ out) {
     constexpr int LPR = D / 8, RPP = kThreads / LPR, NGD = D / G, NR = kRowsPerBlock / RPP;
     const int tid = threadIdx.x, lane = tid % LPR, rg = tid / LPR;
-    const uint32_t r0 = blockIdx.x * kRowsPerBlock;
+    const RotTile tl = rot_tile(geo, blockIdx.x);
     const uint32_t sb = sign8(sg, 8 * lane);
     uint32_t w[NR];
     uint16_t sc[NR], zr[NR];
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
-        const uint32_t rc = min(r0 + rg + RPP * i, geo.rows - 1);   // [B][T][H] output row
-        const uint32_t q1 = rc / (uint32_t)geo.H;
-        const int64_t h = rc - q1 * (uint32_t)geo.H, t = q1 % (uint32_t)geo.T, b = q1 / (uint32_t)geo.T;
-        const int64_t o = (b * geo.H + h) * geo.T + t;
+        const int64_t o = tl.out0 + min(rg + RPP * i, tl.n - 1);   // [B][H][T] cache row
         w[i] = *reinterpret_cast<const uint32_t*>(codes + o * (D / 2) + 4 * lane);
         const int64_t mi = o * NGD + (8 * lane) / G;
         sc[i] = scale[mi];
@@ -166,7 +224,7 @@ __global__ void __launch_bounds__(kThreads) rot_dequant_kernel(const uint8_t* __
     }
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
-        const uint32_t r = r0 + rg + RPP * i;
+        const int u = rg + RPP * i;
         const float s = bf_to_f(sc[i]), zs = -bf_to_f(zr[i]) * s;
         const uint32_t lo = w[i] & 0x0f0f0f0fu, hi = (w[i] >> 4) & 0x0f0f0f0fu;
         float v[8];
@@ -181,13 +239,14 @@ __global__ void __launch_bounds__(kThreads) rot_dequant_kernel(const uint8_t* __
             const float x = v[k] * geo.c;
             v[k] = ((sb >> k) & 1u) ? -x : x;
         }
-        if (r >= geo.rows) continue;
+        if (u >= tl.n) continue;
+        const int64_t r = tl.in0 + u * geo.H;                          // [B][T][H] output row
         if constexpr (OT == KVQ_FP32) {
-            float* p = static_cast<float*>(out) + (int64_t)r * D + 8 * lane;
+            float* p = static_cast<float*>(out) + r * D + 8 * lane;
             *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
             *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
         } else {
-            *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + (int64_t)r * D + 8 * lane) =
+            *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + r * D + 8 * lane) =
                 make_uint4(pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]), pack_bf2(v[4], v[5]), pack_bf2(v[6], v[7]));
         }
     }
@@ -418,7 +477,7 @@ __global__ void __launch_bounds__(256) rot_combine_kernel(const RotAttnArgs a, S
 template <int D, int G>
 void launch_rot_quant(const void* K, const void* V, const RotGeom& geo, const SignBits& ks, const SignBits& vs,
                       const kvq_rot_cache& c, hipStream_t st) {
-    const unsigned nblk = (unsigned)cdiv(geo.rows, kRowsPerBlock);
+    const unsigned nblk = (unsigned)(geo.B * geo.ntt * geo.H);
     hipLaunchKernelGGL((rot_quant_kernel<D, G>), dim3(nblk), dim3(kThreads), 0, st, static_cast<const uint16_t*>(K),
                        static_cast<const uint16_t*>(V), geo, ks, vs, c);
 }
@@ -426,7 +485,7 @@ void launch_rot_quant(const void* K, const void* V, const RotGeom& geo, const Si
 template <int D, int G>
 void launch_rot_dequant(const kvq_rot_cache& c, int side, const RotGeom& geo, const SignBits& sg, void* out, int ot,
                         hipStream_t st) {
-    const unsigned nblk = (unsigned)cdiv(geo.rows, kRowsPerBlock);
+    const unsigned nblk = (unsigned)(geo.B * geo.ntt * geo.H);
     const uint8_t* codes = side ? c.v_codes : c.k_codes;
     const uint16_t* sc = side ? c.v_scale : c.k_scale;
     const uint16_t* zr = side ? c.v_zero : c.k_zero;
@@ -496,6 +555,7 @@ RotGeom geom(const kvq_rot_cache* c) {
     g.B = c->B; g.T = c->T; g.H = c->H;
     g.c = (float)(1.0 / std::sqrt((double)c->d));
     g.rows = (uint32_t)(c->B * c->T * c->H);
+    g.ntt = (uint32_t)cdiv(c->T, kRowsPerBlock);
     return g;
 }
 
