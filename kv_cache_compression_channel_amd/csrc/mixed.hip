@@ -142,25 +142,48 @@ template <int LPR>
 __device__ __forceinline__ float row_min(float v) { return lane_group_reduce<LPR, false>(v); }
 
 // Rows of a block share a wave when a row is narrower than a wave (LPR < 64).  The block's ROWS
-// rows (at most 64) are then sorted by tag, stably, by one wave: s_perm[q] = the row (relative to
-// the block) processed at position q, rows past N last.  The block still reads and writes its
-// own contiguous rows; only their order inside it changes, so a wave runs one precision's code
+// rows (at most 64) are then sorted by tag, stably, by one wave: position q of the sorted order
+// holds row ts.perm[q] of the block with its tag ts.tag[q] and pool slot ts.slot[q] (rows past N
+// last, as tag 0 with slot -1).  The wave loads the rows' tags and slots together, so the block
+// waits on memory once before the pool words.  The block still reads and writes its own
+// contiguous rows; only their order inside it changes, so a wave runs one precision's code
 // for all its rows but at the tag boundaries.
+// Blocks of more than 64 rows are sorted in runs of 64, one wave per run (a wave's positions
+// never straddle two runs).
 template <int ROWS>
-__device__ __forceinline__ void block_tag_sort(const kvq_mixed_store& m, int64_t base, uint8_t* s_perm) {
-    const int tid = threadIdx.x;
-    if (tid < 64) {
-        const int64_t r = base + tid;
-        const int t = (tid < ROWS && r < m.N) ? tag_at(m.tags[r / 4], (int)(r % 4)) : 4;
+struct TagSortLds {
+    uint8_t perm[ROWS], tag[ROWS];
+    int32_t slot[ROWS];
+};
+template <int ROWS>
+__device__ __forceinline__ void block_tag_sort(const kvq_mixed_store& m, int64_t base, TagSortLds<ROWS>& ts) {
+    static_assert(ROWS <= 64 || (ROWS % 64 == 0 && ROWS / 64 <= kThreads / 64), "one wave per run of 64 rows");
+    const int tid = threadIdx.x, lane = tid % 64, run = tid / 64;
+    if (run * 64 < ROWS) {
+        const int rl = run * 64 + lane;   // row of the block
+        const int64_t r = base + rl;
+        const bool valid = rl < ROWS && r < m.N;
+        const int t = valid ? tag_at(m.tags[r / 4], (int)(r % 4)) : 4;
+        const int32_t k = valid ? m.slot[r] : -1;
         const uint64_t b0 = __ballot(t == 0), b1 = __ballot(t == 1), b2 = __ballot(t == 2), b3 = __ballot(t == 3);
         const int c0 = __popcll(b0), c1 = __popcll(b1), c2 = __popcll(b2), c3 = __popcll(b3);
         const uint64_t mine = t == 0 ? b0 : t == 1 ? b1 : t == 2 ? b2 : t == 3 ? b3 : ~(b0 | b1 | b2 | b3);
         const int off = t == 0 ? 0 : t == 1 ? c0 : t == 2 ? c0 + c1 : t == 3 ? c0 + c1 + c2 : c0 + c1 + c2 + c3;
-        const int pos = off + __popcll(mine & ((1ull << tid) - 1ull));
-        if (tid < ROWS) s_perm[pos] = (uint8_t)tid;
+        const int pos = run * 64 + off + __popcll(mine & ((1ull << lane) - 1ull));
+        if (rl < ROWS) {
+            ts.perm[pos] = (uint8_t)rl;
+            ts.tag[pos] = (uint8_t)(valid ? t : 0);
+            ts.slot[pos] = k;
+        }
     }
     __syncthreads();
 }
+
+// Rows per lane group (NR) of the quantizer and dequantizer: rows of at most 512 channels take
+// four passes, so a block waits on memory for all of its rows at once (eight passes measured
+// slower: the dequantizer's registers then allow 5 waves per SIMD instead of 8).
+template <int LPR, int NCH>
+constexpr int mixed_passes() { return NCH == 1 ? 4 : 1; }
 
 // One row: LPR lanes, NCH chunks of 8 channels per lane (C = 8 * LPR * NCH), tag t, pool row k.
 template <int LPR, int NCH>
@@ -237,16 +260,17 @@ __device__ __forceinline__ void quant_row(const kvq_mixed_store& m, const uint4 
 // before any row is processed.  Rows beyond N are skipped as a whole (uniform over the row's lanes).
 template <int LPR, int NCH>
 __global__ void __launch_bounds__(kThreads) mixed_quant_kernel(const uint16_t* __restrict__ x, kvq_mixed_store m) {
-    constexpr int RPB = kThreads / LPR, NR = NCH == 1 ? 4 : 1;
+    constexpr int RPB = kThreads / LPR, NR = mixed_passes<LPR, NCH>();
     constexpr int ROWS = RPB * NR, RPW = 64 / LPR;   // rows per block, rows per wave per pass
-    constexpr bool SORT = LPR < 64 && ROWS <= 64;
-    __shared__ uint8_t s_perm[SORT ? ROWS : 1];
+    constexpr bool SORT = LPR < 64;
+    __shared__ TagSortLds<SORT ? ROWS : 1> s_ts;
     const int tid = threadIdx.x, lane = tid % LPR, lg = tid / LPR;
     const int64_t base = (int64_t)blockIdx.x * ROWS;
-    if constexpr (SORT) block_tag_sort<ROWS>(m, base, s_perm);
-    // row of pass i of lane group lg; sorted, a wave takes RPW * NR consecutive positions
+    if constexpr (SORT) block_tag_sort<ROWS>(m, base, s_ts);
+    // sorted position of pass i of lane group lg: a wave takes RPW * NR consecutive positions
+    auto pos = [&](int i) -> int { return (lg / RPW) * (RPW * NR) + i * RPW + lg % RPW; };
     auto row = [&](int i) -> int64_t {
-        if constexpr (SORT) return base + s_perm[(lg / RPW) * (RPW * NR) + i * RPW + lg % RPW];
+        if constexpr (SORT) return base + s_ts.perm[pos(i)];
         else return base + lg + (int64_t)RPB * i;
     };
     uint4 raw[NR][NCH];
@@ -257,8 +281,13 @@ __global__ void __launch_bounds__(kThreads) mixed_quant_kernel(const uint16_t* _
         const int64_t r = min(row(i), m.N - 1);
 #pragma unroll
         for (int j = 0; j < NCH; ++j) raw[i][j] = *reinterpret_cast<const uint4*>(x + r * m.C + 8 * (lane + LPR * j));
-        tg[i] = tag_at(m.tags[r / 4], (int)(r % 4));
-        kk[i] = m.slot[r];
+        if constexpr (SORT) {
+            tg[i] = s_ts.tag[pos(i)];
+            kk[i] = s_ts.slot[pos(i)];
+        } else {
+            tg[i] = tag_at(m.tags[r / 4], (int)(r % 4));
+            kk[i] = m.slot[r];
+        }
     }
 #pragma unroll
     for (int i = 0; i < NR; ++i)
@@ -348,10 +377,10 @@ __device__ __forceinline__ void dequant_row(const kvq_mixed_store& m, const RowW
 
 template <int LPR, int NCH, int OT>
 __global__ void __launch_bounds__(kThreads) mixed_dequant_kernel(const kvq_mixed_store m, void* __restrict__ out) {
-    constexpr int RPB = kThreads / LPR, NR = NCH == 1 ? 4 : 1;
+    constexpr int RPB = kThreads / LPR, NR = mixed_passes<LPR, NCH>();
     constexpr int ROWS = RPB * NR, RPW = 64 / LPR;
-    constexpr bool SORT = LPR < 64 && ROWS <= 64;
-    __shared__ uint8_t s_perm[SORT ? ROWS : 1];
+    constexpr bool SORT = LPR < 64;
+    __shared__ TagSortLds<SORT ? ROWS : 1> s_ts;
     const int tid = threadIdx.x, lane = tid % LPR, lg = tid / LPR;
     const int64_t base = (int64_t)blockIdx.x * ROWS;
     const int64_t rb = base + lg;
@@ -378,18 +407,24 @@ __global__ void __launch_bounds__(kThreads) mixed_dequant_kernel(const kvq_mixed
         }
         return;
     }
-    if constexpr (SORT) block_tag_sort<ROWS>(m, base, s_perm);
+    if constexpr (SORT) block_tag_sort<ROWS>(m, base, s_ts);
+    auto pos = [&](int i) -> int { return (lg / RPW) * (RPW * NR) + i * RPW + lg % RPW; };
     auto row = [&](int i) -> int64_t {
-        if constexpr (SORT) return base + s_perm[(lg / RPW) * (RPW * NR) + i * RPW + lg % RPW];
+        if constexpr (SORT) return base + s_ts.perm[pos(i)];
         else return rb + (int64_t)RPB * i;
     };
     int tg[NR];
     int64_t kk[NR];
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
-        const int64_t r = min(row(i), m.N - 1);
-        tg[i] = tag_at(m.tags[r / 4], (int)(r % 4));
-        kk[i] = m.slot[r];
+        if constexpr (SORT) {
+            tg[i] = s_ts.tag[pos(i)];
+            kk[i] = s_ts.slot[pos(i)];
+        } else {
+            const int64_t r = min(row(i), m.N - 1);
+            tg[i] = tag_at(m.tags[r / 4], (int)(r % 4));
+            kk[i] = m.slot[r];
+        }
     }
     RowWords<NCH> rw[NR];
 #pragma unroll
@@ -477,7 +512,7 @@ int kvq_mixed_quant(const void* x, const kvq_mixed_store* m, kvq_stream stream) 
     const uint16_t* xp = static_cast<const uint16_t*>(x);
 #define KVQ_MQ(LPR, NCH)                                                                                    \
     hipLaunchKernelGGL((kvq::mixed_quant_kernel<LPR, NCH>),                                                 \
-                       dim3((unsigned)kvq::cdiv(m->N, (kvq::kThreads / LPR) * (NCH == 1 ? 4 : 1))),                \
+                       dim3((unsigned)kvq::cdiv(m->N, (kvq::kThreads / LPR) * kvq::mixed_passes<LPR, NCH>())),                \
                        dim3(kvq::kThreads), 0, st, xp, *m)
     KVQ_MIXED_DISPATCH(m->C, KVQ_MQ);
 #undef KVQ_MQ
@@ -493,7 +528,7 @@ int kvq_mixed_dequant(const kvq_mixed_store* m, void* out, int ot, kvq_stream st
     hipStream_t st = static_cast<hipStream_t>(stream);
 #define KVQ_MD(LPR, NCH)                                                                                       \
     do {                                                                                                       \
-        const dim3 grid((unsigned)kvq::cdiv(m->N, (kvq::kThreads / LPR) * (NCH == 1 ? 4 : 1)));               \
+        const dim3 grid((unsigned)kvq::cdiv(m->N, (kvq::kThreads / LPR) * kvq::mixed_passes<LPR, NCH>()));               \
         if (ot == KVQ_FP32)                                                                                    \
             hipLaunchKernelGGL((kvq::mixed_dequant_kernel<LPR, NCH, KVQ_FP32>), grid, dim3(kvq::kThreads), 0, st, \
                                *m, out);                                                                       \
