@@ -444,14 +444,20 @@ int kvq_compact(const void* k_src, const void* v_src_or_null, int64_t B, int64_t
  *
  * Moves read_bytes from src and write_bytes to dst with the 16-byte loads and stores
  * the kernels above use (non-temporal when nt != 0), so that a kernel's time can be
- * read against what this device sustains for the same read:write mix.  In each round
- * every thread issues its loads, then stores a value that depends on them.  The ratio
- * read_bytes : write_bytes must be 1:0 (read only), 0:1 (write only), 1:1, 2:1, 1:2,
- * 32:9 (a bf16 -> 4-bit g=64 quantizer's mix) or 9:32 (its dequantizer's).  dst is
- * always required: a read-only probe stores at most 16 bytes there.  Both device.
- * EINVAL: another ratio, sizes not multiples of 16, nothing to move, NULL pointers.
+ * read against what this device sustains for the same read:write mix.  Each workgroup
+ * moves one tile: every thread issues its loads, then stores a value that depends on
+ * them.  The ratio read_bytes : write_bytes must be 1:0 (read only), 0:1 (write only),
+ * 1:1, 2:1, 1:2, 32:9 (a bf16 -> 4-bit g=64 quantizer's mix) or 9:32 (its
+ * dequantizer's).  depth (1, 2, 4 or 8) multiplies the mix's accesses per thread (1:1
+ * at depth 4: four loads and four stores; 32:9 and 9:32 take depth 1 only); thread t of
+ * workgroup u makes its i-th store the 16 bytes (a ^ i, a, a, a) at chunk
+ * (u * nstores + i) * 256 + t, a = t for a write-only probe.  dst is always required: a
+ * read-only probe stores at most 16 bytes there.  Both device.
+ * EINVAL: another ratio, another depth, sizes not multiples of 16, nothing to move,
+ *   NULL pointers.
  * ====================================================================== */
-int kvq_bw_probe(const void* src, uint64_t read_bytes, void* dst, uint64_t write_bytes, int nt, kvq_stream stream);
+int kvq_bw_probe(const void* src, uint64_t read_bytes, void* dst, uint64_t write_bytes, int nt, int depth,
+                 kvq_stream stream);
 
 #ifdef __cplusplus
 }

@@ -6,7 +6,9 @@
 // One kernel shape for every mix, shaped like the library's streaming kernels: each
 // workgroup moves one tile and exits -- every thread issues its A loads (each instruction a
 // contiguous 4 KiB per workgroup), then B stores of a value that depends on them (as a
-// quantizer's output depends on its input), so no load can be dropped.
+// quantizer's output depends on its input), so no load can be dropped.  The depth scales A and
+// B together: on MI355X short tiles (one or two accesses per thread) stream stores markedly
+// faster than eight (6.8 against 5.7 TB/s write-only), so a ceiling is the best over depths.
 #include "kvq_internal.h"
 
 namespace kvq {
@@ -65,10 +67,21 @@ void launch_bw_nt(const void* src, int64_t r16, void* dst, int64_t w16, int nt, 
     else launch_bw<A, B, false>(src, r16, dst, w16, st);
 }
 
+// the base pattern (A, B) times depth 1, 2, 4 or 8
+template <int A, int B>
+void launch_bw_depth(const void* src, int64_t r16, void* dst, int64_t w16, int nt, int depth, hipStream_t st) {
+    switch (depth) {
+        case 1: launch_bw_nt<A, B>(src, r16, dst, w16, nt, st); break;
+        case 2: launch_bw_nt<2 * A, 2 * B>(src, r16, dst, w16, nt, st); break;
+        case 4: launch_bw_nt<4 * A, 4 * B>(src, r16, dst, w16, nt, st); break;
+        default: launch_bw_nt<8 * A, 8 * B>(src, r16, dst, w16, nt, st); break;
+    }
+}
+
 }  // namespace
 }  // namespace kvq
 
-extern "C" int kvq_bw_probe(const void* src, uint64_t read_bytes, void* dst, uint64_t write_bytes, int nt,
+extern "C" int kvq_bw_probe(const void* src, uint64_t read_bytes, void* dst, uint64_t write_bytes, int nt, int depth,
                             kvq_stream stream) {
     KVQ_REQUIRE(dst, "kvq_bw_probe: NULL dst (a read-only probe needs a 16-byte sink)");
     KVQ_REQUIRE(read_bytes == 0 || src, "kvq_bw_probe: NULL src");
@@ -76,19 +89,23 @@ extern "C" int kvq_bw_probe(const void* src, uint64_t read_bytes, void* dst, uin
     KVQ_REQUIRE(read_bytes + write_bytes > 0, "kvq_bw_probe: nothing to move");
     // the grid (one workgroup per 4 KiB x the larger part of the mix) must fit 32 bits
     KVQ_REQUIRE(read_bytes < ((uint64_t)1 << 42) && write_bytes < ((uint64_t)1 << 42), "kvq_bw_probe: too large");
+    KVQ_REQUIRE(depth == 1 || depth == 2 || depth == 4 || depth == 8, "kvq_bw_probe: depth must be 1, 2, 4 or 8");
     KVQ_REQUIRE_ALIGNED(src, "src");
     KVQ_REQUIRE_ALIGNED(dst, "dst");
     const int64_t r16 = (int64_t)(read_bytes / 16), w16 = (int64_t)(write_bytes / 16);
     hipStream_t st = static_cast<hipStream_t>(stream);
     const uint64_t r = read_bytes, w = write_bytes;
-    // loads and stores per thread and round: at least 8 loads (or stores) in flight per lane
-    if (w == 0) kvq::launch_bw_nt<8, 0>(src, r16, dst, w16, nt, st);
-    else if (r == 0) kvq::launch_bw_nt<0, 8>(src, r16, dst, w16, nt, st);
-    else if (r == w) kvq::launch_bw_nt<8, 8>(src, r16, dst, w16, nt, st);
-    else if (r == 2 * w) kvq::launch_bw_nt<8, 4>(src, r16, dst, w16, nt, st);
-    else if (2 * r == w) kvq::launch_bw_nt<4, 8>(src, r16, dst, w16, nt, st);
-    else if (9 * r == 32 * w) kvq::launch_bw_nt<32, 9>(src, r16, dst, w16, nt, st);
-    else if (32 * r == 9 * w) kvq::launch_bw_nt<9, 32>(src, r16, dst, w16, nt, st);
-    else return kvq::fail(KVQ_EINVAL, "kvq_bw_probe: read:write must be 1:0, 0:1, 1:1, 2:1, 1:2, 32:9 or 9:32");
+    if (w == 0) kvq::launch_bw_depth<1, 0>(src, r16, dst, w16, nt, depth, st);
+    else if (r == 0) kvq::launch_bw_depth<0, 1>(src, r16, dst, w16, nt, depth, st);
+    else if (r == w) kvq::launch_bw_depth<1, 1>(src, r16, dst, w16, nt, depth, st);
+    else if (r == 2 * w) kvq::launch_bw_depth<2, 1>(src, r16, dst, w16, nt, depth, st);
+    else if (2 * r == w) kvq::launch_bw_depth<1, 2>(src, r16, dst, w16, nt, depth, st);
+    else if (9 * r == 32 * w || 32 * r == 9 * w) {
+        KVQ_REQUIRE(depth == 1, "kvq_bw_probe: the 32:9 and 9:32 mixes take depth 1 (32 + 9 accesses per thread)");
+        if (9 * r == 32 * w) kvq::launch_bw_nt<32, 9>(src, r16, dst, w16, nt, st);
+        else kvq::launch_bw_nt<9, 32>(src, r16, dst, w16, nt, st);
+    } else {
+        return kvq::fail(KVQ_EINVAL, "kvq_bw_probe: read:write must be 1:0, 0:1, 1:1, 2:1, 1:2, 32:9 or 9:32");
+    }
     return kvq::launch_status("kvq_bw_probe");
 }

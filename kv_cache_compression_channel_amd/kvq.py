@@ -133,7 +133,7 @@ def lib():
     L.kvq_h2o_select.argtypes = [P, I64, I64, I64, I64, I64, P, P, P, SZ, P]
     L.kvq_snapkv_select.argtypes = [P, I64, I64, I64, I64, P, P, SZ, P]
     L.kvq_compact.argtypes = [P, P, I64, I64, I64, I64, P, I64, P, P, P]
-    L.kvq_bw_probe.argtypes = [P, C.c_uint64, P, C.c_uint64, I, P]
+    L.kvq_bw_probe.argtypes = [P, C.c_uint64, P, C.c_uint64, I, I, P]
     L.kvq_decode_attn_int4_noalloc.argtypes = [P, P, I64, C.c_float, P, I, P]
     _lib = L
     return L
@@ -735,13 +735,14 @@ def compact(k_src: torch.Tensor, v_src: torch.Tensor | None, keep: torch.Tensor,
 
 # ------------------------------------------------------- bandwidth probe --
 
-def bw_probe(src: torch.Tensor | None, read_bytes: int, dst: torch.Tensor, write_bytes: int, nt: bool = True):
+def bw_probe(src: torch.Tensor | None, read_bytes: int, dst: torch.Tensor, write_bytes: int, nt: bool = True,
+             depth: int = 8):
     """Stream read_bytes of src and write_bytes into dst (device buffers) in one of the probe's
-    read:write mixes; see kvq_bw_probe."""
+    read:write mixes, depth times the mix's accesses per thread; see kvq_bw_probe."""
     _need_cuda(dst)
     if src is not None and src.numel() * src.element_size() < read_bytes:
         raise ValueError("src is smaller than read_bytes")
     if dst.numel() * dst.element_size() < max(write_bytes, 16):
         raise ValueError("dst is smaller than write_bytes (or 16 bytes)")
     _check(lib().kvq_bw_probe(_p(src) if src is not None else None, read_bytes, _p(dst), write_bytes, int(nt),
-                              _stream(dst)))
+                              int(depth), _stream(dst)))

@@ -317,12 +317,15 @@ def test_select_and_compact_validation(L):
 
 def test_bw_probe_validation(L):
     bw = L.kvq_bw_probe
-    assert bw(FAKE, 64, None, 0, 1, None) == kvq.KVQ_EINVAL            # no sink
-    assert bw(None, 64, FAKE, 0, 1, None) == kvq.KVQ_EINVAL            # no source
-    assert bw(FAKE, 0, FAKE, 0, 1, None) == kvq.KVQ_EINVAL             # nothing to move
-    assert bw(FAKE, 24, FAKE, 0, 1, None) == kvq.KVQ_EINVAL            # not a multiple of 16
-    assert bw(FAKE, 48, FAKE, 16, 1, None) == kvq.KVQ_EINVAL           # 3:1 is not a probe mix
-    assert bw(MISALIGNED, 64, FAKE, 0, 1, None) == kvq.KVQ_EALIGN
+    assert bw(FAKE, 64, None, 0, 1, 8, None) == kvq.KVQ_EINVAL            # no sink
+    assert bw(None, 64, FAKE, 0, 1, 8, None) == kvq.KVQ_EINVAL            # no source
+    assert bw(FAKE, 0, FAKE, 0, 1, 8, None) == kvq.KVQ_EINVAL             # nothing to move
+    assert bw(FAKE, 24, FAKE, 0, 1, 8, None) == kvq.KVQ_EINVAL            # not a multiple of 16
+    assert bw(FAKE, 48, FAKE, 16, 1, 8, None) == kvq.KVQ_EINVAL           # 3:1 is not a probe mix
+    for depth in (0, 3, 16):
+        assert bw(FAKE, 64, FAKE, 0, 1, depth, None) == kvq.KVQ_EINVAL    # depth 1, 2, 4 or 8
+    assert bw(FAKE, 32 * 16, FAKE, 9 * 16, 1, 2, None) == kvq.KVQ_EINVAL  # 32:9 takes depth 1
+    assert bw(MISALIGNED, 64, FAKE, 0, 1, 8, None) == kvq.KVQ_EALIGN
 
 
 def test_library_has_no_oracle_dependency():
@@ -355,7 +358,7 @@ def test_hip_errors_map_to_EHIP(L):
     Covers launches (the probe, INT4 dequantization) and the device query of the
     no-allocation attention."""
     L.kvq_last_error.restype = C.c_char_p
-    assert L.kvq_bw_probe(FAKE, 4096, FAKE, 4096, 0, None) == kvq.KVQ_EHIP
+    assert L.kvq_bw_probe(FAKE, 4096, FAKE, 4096, 0, 8, None) == kvq.KVQ_EHIP
     assert L.kvq_last_error().startswith(b"kvq_bw_probe")
     d = _desc(H=8)
     qd = kvq.QDesc(kvq.KVQ_FMT_INT4_K, C.cast(C.pointer(d), C.c_void_p))
