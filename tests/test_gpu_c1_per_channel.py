@@ -124,7 +124,7 @@ def test_exact_half_quotients():
 def test_bf16_wide_slices(shape):
     """bf16 slices with thousands of channels, as the full-model cache uses them: row counts of
     one, below, at and past a 128- and 256-row chunk, and a whole 8192-token slice pair, with
-    all-zero, constant, all-positive and exact-half channels."""
+    all-zero, constant, all-positive, exact-half and far-from-zero channels."""
     x = synth.normal_bf16(shape, seed=sum(shape) + 1)
     xf = x.float()
     xf[0, :, 5] = 0.0                                   # all-zero channel
@@ -133,6 +133,7 @@ def test_bf16_wide_slices(shape):
     # absmax 127/16 gives s = 1/16 exactly; every other value sits on a half step (k + 0.5) / 16
     xf[-1, :, 100] = (torch.arange(shape[1]) % 20 - 10 + 0.5) / 16
     xf[-1, 0, 100] = 127 / 16
+    xf[0, :, 200] = 100 + 0.25 * xf[0, :, 200]         # far from zero: |x / s| > 250 under asym
     x = xf.to(torch.bfloat16)
     _check_pc(x.to(DEV), u16(x), "sym", bits=8)
     _check_pc(x.to(DEV), u16(x), "asym")
