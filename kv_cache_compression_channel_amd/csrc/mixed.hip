@@ -26,6 +26,45 @@ constexpr int kPlanRows = 1024;   // rows per plan block (one tag byte per threa
 
 __device__ __forceinline__ int tag_at(uint32_t byte, int i) { return (int)((byte >> (2 * i)) & 3u); }
 
+// The store descriptor in scalar registers.  It arrives in kernel-argument memory, where a
+// per-lane index (the capacity of a row's tag) or a per-lane choice between two of its pointers
+// (the scale array of a 2- or 4-bit row) compiles to a load from that memory, and then a load
+// through the pointer it returns, in front of every pool access: two dependent round trips per
+// row.  Values passed through readfirstlane are plain registers to the compiler.
+__device__ __forceinline__ uint32_t sgpr32(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ int64_t sgpr64(int64_t v) {
+    const uint64_t u = (uint64_t)v;
+    return (int64_t)(((uint64_t)sgpr32((uint32_t)(u >> 32)) << 32) | sgpr32((uint32_t)u));
+}
+// (through a global-address-space pointer, so accesses stay global loads and stores)
+template <typename T>
+__device__ __forceinline__ T* sgprp(T* p) {
+    typedef __attribute__((address_space(1))) T gT;
+    return (T*)(gT*)(uintptr_t)sgpr64(reinterpret_cast<int64_t>(p));
+}
+__device__ __forceinline__ kvq_mixed_store store_in_sregs(const kvq_mixed_store& a) {
+    kvq_mixed_store m;
+    m.N = sgpr64(a.N);
+    m.C = sgpr64(a.C);
+    m.tags = sgprp(a.tags);
+    m.slot = sgprp(a.slot);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) m.cap[i] = sgpr64(a.cap[i]);
+    m.q2 = sgprp(a.q2);
+    m.s2 = sgprp(a.s2);
+    m.q4 = sgprp(a.q4);
+    m.s4 = sgprp(a.s4);
+    m.q8 = sgprp(a.q8);
+    m.s8 = sgprp(a.s8);
+    m.z8 = sgprp(a.z8);
+    m.x16 = sgprp(a.x16);
+    return m;
+}
+// Capacity of tag t's pool, selected among the four values.
+__device__ __forceinline__ int64_t cap_of(const kvq_mixed_store& m, int t) {
+    return t == 0 ? m.cap[0] : t == 1 ? m.cap[1] : t == 2 ? m.cap[2] : m.cap[3];
+}
+
 // Inclusive scan over the block of a 64-bit word of four 16-bit counters (sums stay below 2^16).
 __device__ __forceinline__ uint64_t block_scan_u64(uint64_t v, uint64_t* s_w) {
     const int tid = threadIdx.x, lane = tid % 64, w = tid / 64;
@@ -163,8 +202,14 @@ __device__ __forceinline__ void block_tag_sort(const kvq_mixed_store& m, int64_t
         const int rl = run * 64 + lane;   // row of the block
         const int64_t r = base + rl;
         const bool valid = rl < ROWS && r < m.N;
-        const int t = valid ? tag_at(m.tags[r / 4], (int)(r % 4)) : 4;
-        const int32_t k = valid ? m.slot[r] : -1;
+        // both loads before either value is used: one round trip
+        uint32_t byte = 0;
+        int32_t k = -1;
+        if (valid) {
+            byte = m.tags[r / 4];
+            k = m.slot[r];
+        }
+        const int t = valid ? tag_at(byte, (int)(r % 4)) : 4;
         const uint64_t b0 = __ballot(t == 0), b1 = __ballot(t == 1), b2 = __ballot(t == 2), b3 = __ballot(t == 3);
         const int c0 = __popcll(b0), c1 = __popcll(b1), c2 = __popcll(b2), c3 = __popcll(b3);
         const uint64_t mine = t == 0 ? b0 : t == 1 ? b1 : t == 2 ? b2 : t == 3 ? b3 : ~(b0 | b1 | b2 | b3);
@@ -190,7 +235,7 @@ template <int LPR, int NCH>
 __device__ __forceinline__ void quant_row(const kvq_mixed_store& m, const uint4 (&raw)[NCH], int t, int64_t k,
                                           int lane) {
     const int64_t C = m.C;
-    const bool fits = k >= 0 && k < m.cap[t];
+    const bool fits = k >= 0 && k < cap_of(m, t);
     if (t == 3) {
         if (!fits) return;
 #pragma unroll
@@ -259,7 +304,9 @@ __device__ __forceinline__ void quant_row(const kvq_mixed_store& m, const uint4 
 // rows in tag order when several rows share a wave; every row's chunks, tag and slot are loaded
 // before any row is processed.  Rows beyond N are skipped as a whole (uniform over the row's lanes).
 template <int LPR, int NCH>
-__global__ void __launch_bounds__(kThreads) mixed_quant_kernel(const uint16_t* __restrict__ x, kvq_mixed_store m) {
+__global__ void __launch_bounds__(kThreads) mixed_quant_kernel(const uint16_t* __restrict__ x,
+                                                              const kvq_mixed_store m_arg) {
+    const kvq_mixed_store m = store_in_sregs(m_arg);
     constexpr int RPB = kThreads / LPR, NR = mixed_passes<LPR, NCH>();
     constexpr int ROWS = RPB * NR, RPW = 64 / LPR;   // rows per block, rows per wave per pass
     constexpr bool SORT = LPR < 64;
@@ -305,7 +352,7 @@ struct RowWords {
 template <int LPR, int NCH>
 __device__ __forceinline__ void load_row_words(const kvq_mixed_store& m, int t, int64_t k, int lane, RowWords<NCH>& rw) {
     const int64_t C = m.C;
-    const bool fits = k >= 0 && k < m.cap[t];
+    const bool fits = k >= 0 && k < cap_of(m, t);
     const int64_t kc = fits ? k : 0;
     rw.s = 0.0f;
     rw.z = 0.0f;
@@ -376,7 +423,9 @@ __device__ __forceinline__ void dequant_row(const kvq_mixed_store& m, const RowW
 }
 
 template <int LPR, int NCH, int OT>
-__global__ void __launch_bounds__(kThreads) mixed_dequant_kernel(const kvq_mixed_store m, void* __restrict__ out) {
+__global__ void __launch_bounds__(kThreads) mixed_dequant_kernel(const kvq_mixed_store m_arg,
+                                                                void* __restrict__ out) {
+    const kvq_mixed_store m = store_in_sregs(m_arg);
     constexpr int RPB = kThreads / LPR, NR = mixed_passes<LPR, NCH>();
     constexpr int ROWS = RPB * NR, RPW = 64 / LPR;
     constexpr bool SORT = LPR < 64;
@@ -389,7 +438,7 @@ __global__ void __launch_bounds__(kThreads) mixed_dequant_kernel(const kvq_mixed
         if (rb >= m.N) return;
         const int t = tag_at(m.tags[rb / 4], (int)(rb % 4));
         const int64_t k = m.slot[rb];
-        const bool fits = k >= 0 && k < m.cap[t];
+        const bool fits = k >= 0 && k < cap_of(m, t);
         kvq_mixed_store mq = m;
 #pragma unroll 1
         for (int j0 = 0; j0 < NCH; j0 += 4) {
@@ -433,7 +482,7 @@ __global__ void __launch_bounds__(kThreads) mixed_dequant_kernel(const kvq_mixed
     for (int i = 0; i < NR; ++i) {
         const int64_t r = row(i);
         if (r < m.N)
-            dequant_row<LPR, NCH, OT>(m, rw[i], tg[i], kk[i] >= 0 && kk[i] < m.cap[tg[i]], r, lane, out);
+            dequant_row<LPR, NCH, OT>(m, rw[i], tg[i], kk[i] >= 0 && kk[i] < cap_of(m, tg[i]), r, lane, out);
     }
 }
 

@@ -34,8 +34,15 @@ struct SignBits {
     uint32_t w[8];   // bit c of the d-bit mask: coordinate c is negated
 };
 
-__device__ __forceinline__ uint32_t sign8(const SignBits& s, int c0) {   // bits c0 .. c0+7 (c0 % 8 == 0)
-    return (s.w[c0 / 32] >> (c0 % 32)) & 0xffu;
+// Bits c0 .. c0+7 (c0 % 8 == 0).  The word is picked by a select over the eight values: an index
+// that differs between lanes would read the argument from kernel-argument memory, once per lane,
+// in front of the first use.
+__device__ __forceinline__ uint32_t sign8(const SignBits& s, int c0) {
+    const int wi = c0 / 32;
+    uint32_t w = __builtin_amdgcn_readfirstlane(s.w[0]);
+#pragma unroll
+    for (int i = 1; i < 8; ++i) w = wi == i ? __builtin_amdgcn_readfirstlane(s.w[i]) : w;
+    return (w >> (c0 % 32)) & 0xffu;
 }
 
 // x from the lane whose index differs in bit pattern M (M < 32): ds_swizzle's bit mode, which
@@ -466,7 +473,7 @@ __global__ void __launch_bounds__(256) rot_combine_kernel(const RotAttnArgs a, S
     for (int j = 0; j < CPL; ++j) {
         const int c = lane + 64 * j;
         float x = v[j] * a.c;
-        if ((vs.w[c / 32] >> (c % 32)) & 1u) x = -x;
+        if ((sign8(vs, c & ~7) >> (c % 8)) & 1u) x = -x;
         if constexpr (OT == KVQ_FP32)
             static_cast<float*>(a.out)[row * D + c] = x;
         else
