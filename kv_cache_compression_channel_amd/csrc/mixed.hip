@@ -379,6 +379,61 @@ __device__ __forceinline__ void load_row_words(const kvq_mixed_store& m, int t, 
     }
 }
 
+// Rows of one chunk per lane (C <= 512): one 16-byte load per lane whatever the tag.  Each lane
+// loads the aligned 16 bytes of its row that hold its 8 codes (the lanes of a 2-, 4- or 8-bit row
+// share chunks, and the wave's load still touches each line once) and picks its bytes out with
+// selects.  The tag then decides addresses and arithmetic only: loads in branches of their own
+// per tag would share registers, and each would wait for the one before it.  The loads of every
+// row are issued (row_words_load) before any value is used (row_words_finish).
+struct RawWords {
+    uint4 w;
+    float s;
+    int z;
+    bool fits;
+};
+// safe: a readable 16-byte-aligned address of at least 16 bytes; rows that do not fit their pool
+// (or whose tag has no scale or zero point) load from it, so no load is conditional and none
+// needs a merge with a default value (which would make the next load wait for it)
+__device__ __forceinline__ RawWords row_words_load(const kvq_mixed_store& m, int t, int64_t k, int lane,
+                                                   uintptr_t safe) {
+    typedef __attribute__((address_space(1))) const u32x4_t gu4;
+    typedef __attribute__((address_space(1))) const float gf32;
+    typedef __attribute__((address_space(1))) const int8_t gi8;
+    const bool fits = k >= 0 && k < cap_of(m, t);
+    const int sh = t == 0 ? 1 : t == 1 ? 2 : t == 2 ? 3 : 4;   // log2 of the bits per value
+    const int64_t rowbytes = (m.C << sh) >> 3;
+    const int boff = lane << sh;                                 // first byte of the lane's codes
+    // the candidates pass through empty asm statements: a select among fields of one struct may
+    // otherwise be rebuilt as an indexed load from a stack copy of it
+    uint64_t q2 = (uintptr_t)m.q2, q4 = (uintptr_t)m.q4, q8 = (uintptr_t)m.q8, x16 = (uintptr_t)m.x16;
+    uint64_t s2 = (uintptr_t)m.s2, s4 = (uintptr_t)m.s4, s8 = (uintptr_t)m.s8, z8 = (uintptr_t)m.z8;
+    asm volatile("" : "+s"(q2), "+s"(q4), "+s"(q8), "+s"(x16));
+    asm volatile("" : "+s"(s2), "+s"(s4), "+s"(s8), "+s"(z8));
+    const uintptr_t base = t == 0 ? q2 : t == 1 ? q4 : t == 2 ? q8 : x16;
+    const uintptr_t sbase = t == 0 ? s2 : t == 1 ? s4 : s8;
+    const uintptr_t wa = fits ? base + k * rowbytes + (boff & ~15) : safe;
+    const uintptr_t sa = fits && t < 3 ? sbase + 4 * k : safe;
+    const uintptr_t za = fits && t == 2 ? z8 + k : safe;
+    RawWords r;
+    const u32x4_t w = *reinterpret_cast<gu4*>(wa);
+    r.w = make_uint4(w.x, w.y, w.z, w.w);
+    r.s = *reinterpret_cast<gf32*>(sa);
+    r.z = *reinterpret_cast<gi8*>(za);
+    r.fits = fits;
+    return r;
+}
+__device__ __forceinline__ void row_words_finish(const RawWords& r, int t, int lane, RowWords<1>& rw) {
+    const int sh = t == 0 ? 1 : t == 1 ? 2 : t == 2 ? 3 : 4;
+    const int o = (lane << sh) & 15;   // 0 for 16-bit rows, 0 or 8 for 8-bit, a multiple of 4 or 2 below
+    const uint4 w = r.fits ? r.w : make_uint4(0u, 0u, 0u, 0u);
+    const uint32_t d0 = o < 4 ? w.x : o < 8 ? w.y : o < 12 ? w.z : w.w;
+    const uint32_t d1 = o < 8 ? w.y : w.w;
+    rw.w[0] = t == 3 ? w : t == 2 ? make_uint4(d0, d1, 0u, 0u)
+            : make_uint4(t == 1 ? d0 : (d0 >> (8 * (o & 3))) & 0xffffu, 0u, 0u, 0u);
+    rw.s = r.fits && t < 3 ? r.s : 0.0f;
+    rw.z = r.fits && t == 2 ? (float)r.z : 0.0f;
+}
+
 template <int LPR, int NCH, int OT>
 __device__ __forceinline__ void dequant_row(const kvq_mixed_store& m, const RowWords<NCH>& rw, int t, bool fits,
                                             int64_t r, int lane, void* out) {
@@ -476,8 +531,16 @@ __global__ void __launch_bounds__(kThreads) mixed_dequant_kernel(const kvq_mixed
         }
     }
     RowWords<NCH> rw[NR];
+    if constexpr (NCH == 1) {
+        RawWords raw[NR];
 #pragma unroll
-    for (int i = 0; i < NR; ++i) load_row_words<LPR, NCH>(m, tg[i], kk[i], lane, rw[i]);
+        for (int i = 0; i < NR; ++i) raw[i] = row_words_load(m, tg[i], kk[i], lane, (uintptr_t)out);
+#pragma unroll
+        for (int i = 0; i < NR; ++i) row_words_finish(raw[i], tg[i], lane, rw[i]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < NR; ++i) load_row_words<LPR, NCH>(m, tg[i], kk[i], lane, rw[i]);
+    }
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
         const int64_t r = row(i);

@@ -106,3 +106,34 @@ def test_full_decode_cache_rows():
                               w.view(np.uint32) if w.dtype == np.float32 else w, f"row {r} tag {t}: {f}")
         assert_bits_equal(np_(out[int(r)]).view(np.uint32), oracle.mixed_dequant(one)[0].view(np.uint32),
                           f"row {r}: dequant")
+
+
+def test_rows_past_capacity():
+    """Pools smaller than the plan's counts, one of them absent: rows whose slot is past their
+    pool's capacity are not stored and dequantize to zeros; the others are exact."""
+    rng = np.random.default_rng(11)
+    N, Cc = 777, 128
+    x = bf16_rows(rng.standard_normal((N, Cc)))
+    tags = rng.integers(0, 4, N).astype(np.uint8)
+    packed = oracle.pack_tags(tags)
+    tg = torch.from_numpy(packed).to(DEV)
+    slot, counts = kvq.mixed_plan(tg, N)
+    cap = [int(c) // 2 for c in counts.cpu()]
+    cap[1] = 0
+    say("mixed past capacity", dict(N=N, C=Cc, cap=cap))
+    st = kvq.mixed_quant(x.to(DEV), kvq.mixed_store_empty(N, Cc, tg, slot, cap, DEV))
+    o32 = kvq.mixed_dequant(st, torch.float32)
+    o16 = kvq.mixed_dequant(st, torch.bfloat16)
+    torch.cuda.synchronize()
+    want = oracle.mixed_quant(u16(x), packed)
+    ref = oracle.mixed_dequant(want)
+    fits = np_(slot) < np.array(cap)[tags]
+    got = np_(o32)
+    assert_bits_equal(got[fits].view(np.uint32), ref[fits].view(np.uint32), "rows that fit")
+    assert not got[~fits].any(), "rows past capacity dequantize to zeros"
+    assert_bits_equal(u16(o16), oracle.f32_to_bf16(got), "bf16 = RNE of fp32")
+    for f, t in (("q2", 0), ("s2", 0), ("q8", 2), ("s8", 2), ("z8", 2)):
+        g, w = np_(getattr(st, f)), want[f][:cap[t]]
+        assert_bits_equal(g.view(np.uint32) if g.dtype == np.float32 else g,
+                          w.view(np.uint32) if w.dtype == np.float32 else w, f"pool {f}")
+    assert_bits_equal(u16(st.x16), want["x16"][:cap[3]], "pool x16")
