@@ -245,6 +245,10 @@ __device__ __forceinline__ void quant_row(const kvq_mixed_store& m, const uint4 
     float v[NCH][8];
 #pragma unroll
     for (int j = 0; j < NCH; ++j) unpack8(raw[j], v[j]);
+    // Codes leave as bytes of offset binary (q + 2^(bits-1), made by v_cvt_pk_u8_f32 from exact
+    // integers) and become two's complement with one xor per word.  The reciprocal only feeds the
+    // fast paths of rint_q / rint_div, whose window (|x * r - x / s| below 1e-4 while
+    // |x / s| < 256) also covers the hardware reciprocal's 1-ulp error.
     if (t == 2) {
         float mn = FLT_MAX, mx = -FLT_MAX;
 #pragma unroll
@@ -255,7 +259,7 @@ __device__ __forceinline__ void quant_row(const kvq_mixed_store& m, const uint4 
         const float s = range / 255.0f;
         const float zr = __builtin_rintf(-128.0f - mn / s);
         const float z = vclamp(zr, -128.0f, 127.0f);
-        const float rs = 1.0f / s;
+        const float rs = __builtin_amdgcn_rcpf(s);
         if (!fits) return;
         if (lane == 0) {
             m.s8[k] = s;
@@ -263,18 +267,21 @@ __device__ __forceinline__ void quant_row(const kvq_mixed_store& m, const uint4 
         }
 #pragma unroll
         for (int j = 0; j < NCH; ++j) {
+            float u[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) u[e] = vclamp(rint_q(v[j][e], s, rs) + z, -128.0f, 127.0f) + 128.0f;
             uint32_t w0 = 0, w1 = 0;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int q = (int)vclamp(rint_q(v[j][e], s, rs) + z, -128.0f, 127.0f);
-                if (e < 4) w0 |= ((uint32_t)q & 0xffu) << (8 * e);
-                else w1 |= ((uint32_t)q & 0xffu) << (8 * (e - 4));
+            for (int e = 0; e < 4; ++e) {
+                w0 = __builtin_amdgcn_cvt_pk_u8_f32(u[e], e, w0);
+                w1 = __builtin_amdgcn_cvt_pk_u8_f32(u[e + 4], e, w1);
             }
-            *reinterpret_cast<uint2*>(m.q8 + k * C + 8 * (lane + LPR * j)) = make_uint2(w0, w1);
+            *reinterpret_cast<uint2*>(m.q8 + k * C + 8 * (lane + LPR * j)) =
+                make_uint2(w0 ^ 0x80808080u, w1 ^ 0x80808080u);
         }
         return;
     }
-    // 2 or 4 bits, symmetric
+    // 2 or 4 bits, symmetric: |x / s| <= qmax, so rint_div's fast path always applies
     float am = 0.0f;
 #pragma unroll
     for (int j = 0; j < NCH; ++j)
@@ -283,20 +290,30 @@ __device__ __forceinline__ void quant_row(const kvq_mixed_store& m, const uint4 
     am = row_max<LPR>(am);
     const float qmax = t == 0 ? 1.0f : 7.0f;
     const float s = vmax2(am, 1e-8f) / qmax;
-    const float rs = 1.0f / s;
+    const float rs = __builtin_amdgcn_rcpf(s);
     if (!fits) return;
     if (lane == 0) (t == 0 ? m.s2 : m.s4)[k] = s;
+    const float off = qmax + 1.0f;   // 2 or 8
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
-        uint32_t w = 0;
+        float u[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int q = (int)vclamp(rint_q(v[j][e], s, rs), -qmax, qmax);
-            w |= t == 0 ? ((uint32_t)q & 3u) << (2 * e) : ((uint32_t)q & 15u) << (4 * e);
+        for (int e = 0; e < 8; ++e) u[e] = vclamp(rint_div(v[j][e], s, rs), -qmax, qmax) + off;
+        uint32_t even = 0, odd = 0;   // bytes: elements 0 2 4 6 and 1 3 5 7
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            even = __builtin_amdgcn_cvt_pk_u8_f32(u[2 * e], e, even);
+            odd = __builtin_amdgcn_cvt_pk_u8_f32(u[2 * e + 1], e, odd);
         }
         const int c0 = 8 * (lane + LPR * j);
-        if (t == 0) *reinterpret_cast<uint16_t*>(m.q2 + k * (C / 4) + c0 / 4) = (uint16_t)w;
-        else *reinterpret_cast<uint32_t*>(m.q4 + k * (C / 2) + c0 / 2) = w;
+        if (t == 0) {
+            // byte i = c(2i) | c(2i+1) << 2; then the four 4-bit bytes close up into 16 bits
+            const uint32_t b = even | (odd << 2);
+            const uint32_t b2 = (b | (b >> 4)) & 0x00ff00ffu;
+            *reinterpret_cast<uint16_t*>(m.q2 + k * (C / 4) + c0 / 4) = (uint16_t)((b2 | (b2 >> 8)) ^ 0xaaaau);
+        } else {
+            *reinterpret_cast<uint32_t*>(m.q4 + k * (C / 2) + c0 / 2) = (even | (odd << 4)) ^ 0x88888888u;
+        }
     }
 }
 
