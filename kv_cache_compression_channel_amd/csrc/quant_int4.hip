@@ -253,14 +253,28 @@ __global__ void __launch_bounds__(kThreads) int4_dequant_kernel(const uint8_t* _
                 for (int k = 0; k < 8; ++k) zs8[q][k] = -zf[k] * s8[q][k];
             }
         }
+        // Every row's words are loaded before any is used (one round trip per block): rows past n
+        // (the last tile's tail) load row n - 1 again and are not stored.
+        constexpr int NRW = TILE / RPP;
+        uint32_t wr[NRW];
+        uint16_t sr[NRW], zr[NRW];
 #pragma unroll
-        for (int i = 0; i < TILE / RPP; ++i) {
+        for (int i = 0; i < NRW; ++i) {
+            const int64_t t = t0 + min(rg + RPP * i, n - 1);
+            wr[i] = __builtin_nontemporal_load(
+                reinterpret_cast<const uint32_t*>(codes + ((b * H + h) * geo.ldq + t) * (D / 2) + 4 * lane));
+            if constexpr (!IS_K) {
+                const int64_t mi = ((b * H + h) * geo.ldq + t) * NGD + (8 * lane) / G;
+                sr[i] = scale[mi];
+                zr[i] = zero[mi];
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < NRW; ++i) {
             const int r = rg + RPP * i;
-            if (r >= n) break;
             const int q = IS_K ? (RPP * i) / G : 0;   // the row's group inside the tile (RPP divides G)
             const int64_t t = t0 + r;
-            const uint32_t w =
-                __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(codes + ((b * H + h) * geo.ldq + t) * (D / 2) + 4 * lane));
+            const uint32_t w = wr[i];
             // nibbles 2e and 2e+1 sit in byte e of w & 0x0f0f0f0f and of (w >> 4) & 0x0f0f0f0f;
             // each byte converts with one v_cvt_f32_ubyte<e>
             const uint32_t lo = w & 0x0f0f0f0fu, hi = (w >> 4) & 0x0f0f0f0fu;
@@ -275,13 +289,12 @@ __global__ void __launch_bounds__(kThreads) int4_dequant_kernel(const uint8_t* _
 #pragma unroll
                 for (int k = 0; k < 8; ++k) v[k] = __builtin_fmaf(c[k], s8[q][k], zs8[q][k]);
             } else {
-                const int64_t mi = ((b * H + h) * geo.ldq + t) * NGD + (8 * lane) / G;
-                const float s = bf_to_f(scale[mi]);
-                const float zs = -bf_to_f(zero[mi]) * s;
+                const float s = bf_to_f(sr[i]);
+                const float zs = -bf_to_f(zr[i]) * s;
 #pragma unroll
                 for (int k = 0; k < 8; ++k) v[k] = __builtin_fmaf(c[k], s, zs);
             }
-            store8(t, b, h, v);
+            if (r < n) store8(t, b, h, v);
         }
         return;
     }
