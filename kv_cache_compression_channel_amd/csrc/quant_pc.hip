@@ -24,6 +24,8 @@ constexpr int kRowsPerChunk = 256;
 // made the code pass 5% and the dequantizer 3-5% faster (256-row chunks against 32 and 64).
 constexpr int kCodeRows = 32;
 constexpr int kDqRows = 64;
+// Row loads a thread issues before it uses any: every pass waits on memory once per batch.
+constexpr int kBatch = 8;
 
 struct PcParams {
     float s;     // scale
@@ -80,20 +82,23 @@ __global__ void __launch_bounds__(kThreads) pc_minmax_kernel(const void* __restr
 #pragma unroll
     for (int k = 0; k < VEC; ++k) { mn[k] = FLT_MAX; mx[k] = -FLT_MAX; }
     if (c0 < g.C) {
+        // kBatch rows' loads in flight per step; rows past the chunk's end repeat its last row,
+        // which leaves min and max as they are
         const int64_t r_end = min(g.R, (rc + 1) * kRowsPerChunk);
-        int64_t r = rc * kRowsPerChunk + rl;
-        for (; r + g.rpp < r_end; r += 2 * g.rpp) {
-            float v[VEC], u[VEC];
-            load_x<XT, VEC>(x, s * g.bsx + r * g.ldx + c0, v);
-            load_x<XT, VEC>(x, s * g.bsx + (r + g.rpp) * g.ldx + c0, u);
+        for (int64_t r0 = rc * kRowsPerChunk + rl; r0 < r_end; r0 += kBatch * g.rpp) {
+            float v[kBatch][VEC];
 #pragma unroll
-            for (int k = 0; k < VEC; ++k) { mn[k] = vmin3(mn[k], v[k], u[k]); mx[k] = vmax3(mx[k], v[k], u[k]); }
-        }
-        if (r < r_end) {
-            float v[VEC];
-            load_x<XT, VEC>(x, s * g.bsx + r * g.ldx + c0, v);
+            for (int u = 0; u < kBatch; ++u) {
+                const int64_t r = min(r0 + u * g.rpp, r_end - 1);
+                load_x<XT, VEC>(x, s * g.bsx + r * g.ldx + c0, v[u]);
+            }
 #pragma unroll
-            for (int k = 0; k < VEC; ++k) { mn[k] = vmin2(mn[k], v[k]); mx[k] = vmax2(mx[k], v[k]); }
+            for (int u = 0; u < kBatch; u += 2)
+#pragma unroll
+                for (int k = 0; k < VEC; ++k) {
+                    mn[k] = vmin3(mn[k], v[u][k], v[u + 1][k]);
+                    mx[k] = vmax3(mx[k], v[u][k], v[u + 1][k]);
+                }
         }
     }
 #pragma unroll
@@ -212,17 +217,27 @@ __global__ void __launch_bounds__(kThreads) pc_code_kernel(const void* __restric
     }
     const float lo = (float)qmin, hi = (float)qmax;
     const int64_t r_end = min(g.R, (rc + 1) * kCodeRows);
-#pragma unroll 4
-    for (int64_t r = rc * kCodeRows + rl; r < r_end; r += g.rpp) {
-        float v[VEC];
-        load_x<XT, VEC>(x, s * g.bsx + r * g.ldx + c0, v);
-        int8_t o[VEC];
-        pc_codes<VEC>(v, ps, pr, pz, fast, lo, hi, o);
-        int8_t* dst = q + (s * g.R + r) * g.C + c0;
-        if constexpr (VEC == 8) {
-            *reinterpret_cast<uint2*>(dst) = pack8_i8(o);
-        } else {
-            dst[0] = o[0];
+    // every row of the chunk (at most kCodeRows / 4: rpp >= 4) loaded before any is coded; rows
+    // past the end load the last row again and are not stored
+    constexpr int NRT = kCodeRows / 4;
+    float v[NRT][VEC];
+#pragma unroll
+    for (int u = 0; u < NRT; ++u) {
+        const int64_t r = min(rc * kCodeRows + rl + u * g.rpp, r_end - 1);
+        load_x<XT, VEC>(x, s * g.bsx + r * g.ldx + c0, v[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < NRT; ++u) {
+        const int64_t r = rc * kCodeRows + rl + u * g.rpp;
+        if (r < r_end) {
+            int8_t o[VEC];
+            pc_codes<VEC>(v[u], ps, pr, pz, fast, lo, hi, o);
+            int8_t* dst = q + (s * g.R + r) * g.C + c0;
+            if constexpr (VEC == 8) {
+                *reinterpret_cast<uint2*>(dst) = pack8_i8(o);
+            } else {
+                dst[0] = o[0];
+            }
         }
     }
 }
@@ -242,26 +257,50 @@ __global__ void __launch_bounds__(kThreads) pc_dequant_kernel(const int8_t* __re
     const int lane = threadIdx.x % g.lpr, rl = threadIdx.x / g.lpr;
     const int64_t c0 = (cb * g.lpr + lane) * VEC;
     if (c0 >= g.C) return;
+    // the channel parameters as two 16-byte and one 8-byte load (one branch on zp, uniform)
     float sc[VEC], zf[VEC];
+    if constexpr (VEC == 8) {
+        const float4 a = *reinterpret_cast<const float4*>(scale + s * g.C + c0);
+        const float4 b = *reinterpret_cast<const float4*>(scale + s * g.C + c0 + 4);
+        sc[0] = a.x; sc[1] = a.y; sc[2] = a.z; sc[3] = a.w; sc[4] = b.x; sc[5] = b.y; sc[6] = b.z; sc[7] = b.w;
+        uint2 z = make_uint2(0u, 0u);
+        if (zp) z = *reinterpret_cast<const uint2*>(zp + s * g.C + c0);
 #pragma unroll
-    for (int k = 0; k < VEC; ++k) {
-        sc[k] = scale[s * g.C + c0 + k];
-        zf[k] = zp ? (float)zp[s * g.C + c0 + k] : 0.0f;
+        for (int k = 0; k < 4; ++k) {
+            zf[k] = (float)(int8_t)(z.x >> (8 * k));
+            zf[k + 4] = (float)(int8_t)(z.y >> (8 * k));
+        }
+    } else {
+        sc[0] = scale[s * g.C + c0];
+        zf[0] = zp ? (float)zp[s * g.C + c0] : 0.0f;
     }
     const int64_t r_end = min(g.R, (rc + 1) * kDqRows);
-#pragma unroll 4
-    for (int64_t r = rc * kDqRows + rl; r < r_end; r += g.rpp) {
+    for (int64_t r0 = rc * kDqRows + rl; r0 < r_end; r0 += kBatch * g.rpp) {
+    // kBatch rows' codes loaded before any is used; rows past the end load the last row again and
+    // are not stored
+    uint2 wq[kBatch];
+    int8_t wq1[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+        const int64_t e = (s * g.R + min(r0 + u * g.rpp, r_end - 1)) * g.C + c0;
+        if constexpr (VEC == 8) wq[u] = *reinterpret_cast<const uint2*>(q + e);
+        else wq1[u] = q[e];
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+        const int64_t r = r0 + u * g.rpp;
+        if (r >= r_end) continue;
         const int64_t e = (s * g.R + r) * g.C + c0;
         float v[VEC];
         if constexpr (VEC == 8) {
-            const uint2 w = *reinterpret_cast<const uint2*>(q + e);
+            const uint2 w = wq[u];
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 v[k] = ((float)(int8_t)(w.x >> (8 * k)) - zf[k]) * sc[k];
                 v[k + 4] = ((float)(int8_t)(w.y >> (8 * k)) - zf[k + 4]) * sc[k + 4];
             }
         } else {
-            v[0] = ((float)q[e] - zf[0]) * sc[0];
+            v[0] = ((float)wq1[u] - zf[0]) * sc[0];
         }
         if constexpr (OT == KVQ_FP32) {
             float* o = static_cast<float*>(out) + e;
@@ -280,6 +319,7 @@ __global__ void __launch_bounds__(kThreads) pc_dequant_kernel(const int8_t* __re
                 o[0] = f_to_bf(v[0]);
             }
         }
+    }
     }
 }
 
