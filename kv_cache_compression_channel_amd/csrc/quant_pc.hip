@@ -17,7 +17,12 @@ namespace kvq {
 namespace {
 
 constexpr int kThreads = 256;
+// Rows per min/max chunk: at least kRowsPerChunk (the workspace is sized for that), grown by
+// doubling while the grid keeps at least kMinMaxBlocks workgroups (4 per CU).  On the full-model
+// cache ([128][8192][4096] bf16) whole 8192-row slices per chunk took the quantizer from 7.34 to
+// 7.03 ms against 256-row chunks: fewer, longer workgroups and 32x fewer partials.
 constexpr int kRowsPerChunk = 256;
+constexpr int64_t kMinMaxBlocks = 1024;
 // The code and dequantization passes need no partials, so they take shorter row chunks than the
 // min/max pass: a workgroup then issues 8 (code) or 16 (dequantization) stores per thread instead
 // of 64, and the workgroups in flight write a more compact window of the output.  On MI355X that
@@ -39,6 +44,7 @@ struct PcGeom {
     int lpr;   // lanes per row (power of two, <= 64)
     int rpp;   // rows per pass = kThreads / lpr
     int64_t ncb, nrc;  // column blocks, row chunks
+    int64_t rpc;       // rows per chunk of the min/max pass
 };
 
 template <int XT, int VEC>
@@ -84,8 +90,8 @@ __global__ void __launch_bounds__(kThreads) pc_minmax_kernel(const void* __restr
     if (c0 < g.C) {
         // kBatch rows' loads in flight per step; rows past the chunk's end repeat its last row,
         // which leaves min and max as they are
-        const int64_t r_end = min(g.R, (rc + 1) * kRowsPerChunk);
-        for (int64_t r0 = rc * kRowsPerChunk + rl; r0 < r_end; r0 += kBatch * g.rpp) {
+        const int64_t r_end = min(g.R, (rc + 1) * g.rpc);
+        for (int64_t r0 = rc * g.rpc + rl; r0 < r_end; r0 += kBatch * g.rpp) {
             float v[kBatch][VEC];
 #pragma unroll
             for (int u = 0; u < kBatch; ++u) {
@@ -331,7 +337,7 @@ PcGeom geom_of(int64_t nb, int64_t R, int64_t C, int64_t ldx, int64_t bsx, bool 
     const int64_t cols = vec8 ? C / 8 : C;
     int lpr = 1;
     while (lpr < 64 && lpr < cols) lpr *= 2;
-    return PcGeom{nb, R, C, ldx, nb == 1 ? 0 : bsx, lpr, kThreads / lpr, cdiv(cols, lpr), nrc_of(R)};
+    return PcGeom{nb, R, C, ldx, nb == 1 ? 0 : bsx, lpr, kThreads / lpr, cdiv(cols, lpr), nrc_of(R), kRowsPerChunk};
 }
 
 size_t ws_bytes_for(int64_t nb, int64_t R, int64_t C) {
@@ -388,7 +394,11 @@ int quant_pc(const void* x, int xt, int64_t nb, int64_t R, int64_t C, int64_t ld
     KVQ_REQUIRE_ALIGNED(zp, "zp");
     KVQ_REQUIRE_ALIGNED(ws, "ws");
     const bool vec8 = (C % 8 == 0) && (ldx % 8 == 0) && (nb == 1 || bsx % 8 == 0);
-    const PcGeom g = geom_of(nb, R, C, ldx, bsx, vec8);
+    PcGeom g = geom_of(nb, R, C, ldx, bsx, vec8);
+    while (g.rpc < R && g.nb * cdiv(R, 2 * g.rpc) * g.ncb >= kMinMaxBlocks) {
+        g.rpc *= 2;
+        g.nrc = cdiv(R, g.rpc);
+    }
     KVQ_REQUIRE(g.nb * g.nrc * g.ncb < ((int64_t)1 << 31), "%s: grid too large", name);
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (xt == KVQ_FP32) return launch_pc<KVQ_FP32>(x, g, vec8, sym, qmin, qmax, q, scale, zp, ws, st);

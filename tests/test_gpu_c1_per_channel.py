@@ -120,11 +120,12 @@ def test_exact_half_quotients():
 
 
 @pytest.mark.parametrize("shape", [(2, 8192, 4096), (4, 1, 2048), (8, 128, 1024), (8, 129, 1024),
-                                   (3, 5000, 2752), (2, 4999, 4096)])
+                                   (3, 5000, 2752), (2, 4999, 4096), (32, 2000, 4096)])
 def test_bf16_wide_slices(shape):
     """bf16 slices with thousands of channels, as the full-model cache uses them: row counts of
-    one, below, at and past a 128- and 256-row chunk, and a whole 8192-token slice pair, with
-    all-zero, constant, all-positive, exact-half and far-from-zero channels."""
+    one, below, at and past a 128- and 256-row chunk, a whole 8192-token slice pair, and enough
+    slices that the min/max pass takes 512-row chunks (the last one ragged), with all-zero,
+    constant, all-positive, exact-half and far-from-zero channels."""
     x = synth.normal_bf16(shape, seed=sum(shape) + 1)
     xf = x.float()
     xf[0, :, 5] = 0.0                                   # all-zero channel
