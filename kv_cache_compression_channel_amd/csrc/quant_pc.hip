@@ -311,16 +311,16 @@ __global__ void __launch_bounds__(kThreads) pc_dequant_kernel(const int8_t* __re
         if constexpr (OT == KVQ_FP32) {
             float* o = static_cast<float*>(out) + e;
             if constexpr (VEC == 8) {
-                *reinterpret_cast<float4*>(o) = make_float4(v[0], v[1], v[2], v[3]);
-                *reinterpret_cast<float4*>(o + 4) = make_float4(v[4], v[5], v[6], v[7]);
+                st_stream_f4(o, make_float4(v[0], v[1], v[2], v[3]));
+                st_stream_f4(o + 4, make_float4(v[4], v[5], v[6], v[7]));
             } else {
                 o[0] = v[0];
             }
         } else {
             uint16_t* o = static_cast<uint16_t*>(out) + e;
             if constexpr (VEC == 8) {
-                *reinterpret_cast<uint4*>(o) = make_uint4(pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]),
-                                                          pack_bf2(v[4], v[5]), pack_bf2(v[6], v[7]));
+                st_stream_u4(o, make_uint4(pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]), pack_bf2(v[4], v[5]),
+                                           pack_bf2(v[6], v[7])));
             } else {
                 o[0] = f_to_bf(v[0]);
             }
