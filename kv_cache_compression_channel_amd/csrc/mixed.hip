@@ -144,20 +144,56 @@ __global__ void __launch_bounds__(1024) mixed_scan_kernel(uint64_t* __restrict__
     }
 }
 
+// Slots of one block's rows.  off != NULL: the block's offset in each pool comes from the scan
+// kernel.  off == NULL (at most kSelfPrefixBlocks blocks): every block sums the count words of the
+// blocks before it itself (at most that many 8-byte words, from L2), which saves the scan launch
+// between the count and slot passes; block 0 sums all of them and writes the totals.
+constexpr int64_t kSelfPrefixBlocks = 4096;
 __global__ void __launch_bounds__(kThreads) mixed_slot_kernel(const uint8_t* __restrict__ tags, int64_t N,
-                                                             const uint4* __restrict__ off, int32_t* __restrict__ slot) {
+                                                             const uint4* __restrict__ off,
+                                                             const uint64_t* __restrict__ blk, int64_t nblk,
+                                                             int64_t* __restrict__ counts, int32_t* __restrict__ slot) {
     __shared__ uint64_t s_w[kThreads / 64];
-    const int64_t r0 = (int64_t)blockIdx.x * kPlanRows + 4 * threadIdx.x;
+    __shared__ uint32_t s_pre[kThreads / 64][4];
+    const int tid = threadIdx.x, lane = tid % 64, wv = tid / 64;
+    if (!off) {
+        const int64_t upto = blockIdx.x == 0 ? nblk : (int64_t)blockIdx.x;
+        uint32_t acc[4] = {0u, 0u, 0u, 0u};
+        for (int64_t i = tid; i < upto; i += kThreads) {
+            const uint64_t v = blk[i];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) acc[k] += (uint32_t)((v >> (16 * k)) & 0xffffu);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+#pragma unroll
+            for (int o = 32; o >= 1; o /= 2) acc[k] += __shfl_xor(acc[k], o);
+            if (lane == 0) s_pre[wv][k] = acc[k];
+        }
+    }
+    const int64_t r0 = (int64_t)blockIdx.x * kPlanRows + 4 * tid;
     uint32_t byte = 0;
     uint64_t c = 0;
     if (r0 < N) {
         byte = tags[r0 / 4];
         for (int i = 0; i < 4 && r0 + i < N; ++i) c += (uint64_t)1 << (16 * tag_at(byte, i));
     }
-    uint64_t ex = block_scan_u64(c, s_w) - c;   // rows of each tag before this thread's rows
+    uint64_t ex = block_scan_u64(c, s_w) - c;   // rows of each tag before this thread's rows (its barrier also
+                                                // orders the s_pre writes above)
+    uint32_t ob[4];
+    if (off) {
+        const uint4 o = off[blockIdx.x];
+        ob[0] = o.x; ob[1] = o.y; ob[2] = o.z; ob[3] = o.w;
+    } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            uint32_t t = 0;
+            for (int w = 0; w < kThreads / 64; ++w) t += s_pre[w][k];
+            ob[k] = blockIdx.x == 0 ? 0u : t;
+            if (blockIdx.x == 0 && tid == 0) counts[k] = t;
+        }
+    }
     if (r0 >= N) return;
-    const uint4 o = off[blockIdx.x];
-    const uint32_t ob[4] = {o.x, o.y, o.z, o.w};
     for (int i = 0; i < 4 && r0 + i < N; ++i) {
         const int t = tag_at(byte, i);
         slot[r0 + i] = (int32_t)(ob[t] + (uint32_t)((ex >> (16 * t)) & 0xffffu));
@@ -626,9 +662,11 @@ int kvq_mixed_plan(const uint8_t* tags, int64_t N, int32_t* slot, int64_t* count
     KVQ_REQUIRE(kvq::cdiv(nblk * 8, 16) * 16 + nblk * 16 <= (int64_t)ws_bytes, "kvq_mixed_plan: workspace too small");
     hipStream_t st = static_cast<hipStream_t>(stream);
     hipLaunchKernelGGL(kvq::mixed_count_kernel, dim3((unsigned)nblk), dim3(kvq::kThreads), 0, st, tags, N, blk);
-    hipLaunchKernelGGL(kvq::mixed_scan_kernel, dim3(1), dim3(1024), 0, st, blk, off, nblk, counts);
+    const bool self_prefix = nblk <= kvq::kSelfPrefixBlocks;
+    if (!self_prefix) hipLaunchKernelGGL(kvq::mixed_scan_kernel, dim3(1), dim3(1024), 0, st, blk, off, nblk, counts);
     hipLaunchKernelGGL(kvq::mixed_slot_kernel, dim3((unsigned)nblk), dim3(kvq::kThreads), 0, st, tags, N,
-                       static_cast<const uint4*>(off), slot);
+                       self_prefix ? nullptr : static_cast<const uint4*>(off), static_cast<const uint64_t*>(blk), nblk,
+                       counts, slot);
     return kvq::launch_status("kvq_mixed_plan");
 }
 

@@ -137,3 +137,18 @@ def test_rows_past_capacity():
         assert_bits_equal(g.view(np.uint32) if g.dtype == np.float32 else g,
                           w.view(np.uint32) if w.dtype == np.float32 else w, f"pool {f}")
     assert_bits_equal(u16(st.x16), want["x16"][:cap[3]], "pool x16")
+
+
+@pytest.mark.parametrize("N", [4096 * 1024, 4096 * 1024 + 1])
+def test_plan_at_the_prefix_path_boundary(N):
+    """The plan with 4096 blocks of 1024 rows (each block sums the counts before it) and one row
+    more (a separate scan launch): slots and counts against the oracle."""
+    rng = np.random.default_rng(N % 1000)
+    tags = rng.choice(4, N, p=[0.3, 0.4, 0.2, 0.1]).astype(np.uint8)
+    packed = oracle.pack_tags(tags)
+    say("mixed plan", dict(N=N))
+    slot, counts = kvq.mixed_plan(torch.from_numpy(packed).to(DEV), N)
+    torch.cuda.synchronize()
+    want_slot, want_counts = oracle.mixed_plan(packed, N)
+    assert_bits_equal(np_(slot), want_slot, f"N={N}: slots")
+    assert [int(v) for v in counts.cpu()] == [int(v) for v in want_counts], f"N={N}: counts"
