@@ -136,6 +136,9 @@ __device__ __forceinline__ GroupParams group_params(float mn, float mx) {
 // behind one branch per 8 elements; groups with z outside [0, 15] always take it:
 // rint(x/s) + z is then an fp32 sum of two integers, exact whenever the result can
 // fall in [0, 15] (Sterbenz) and far outside otherwise.
+// The clip is needed on the fallback only: for x in [min, max] of the group, x/s + z lies in
+// [-0.5 - 2e-5, 15.5 + 2e-5] (s >= range / 15 up to rounding, |min/s + z| <= 0.5 + 2e-5), so a
+// w that rounds outside [0, 15] lies within 1e-4 of -0.5 or 15.5 and has taken the fallback.
 template <bool UNIFORM>
 __device__ __forceinline__ void codes8(const float (&x)[8], const float (&s)[8], const float (&r)[8],
                                        const float (&z)[8], bool fast, float (&q)[8]) {
@@ -153,10 +156,11 @@ __device__ __forceinline__ void codes8(const float (&x)[8], const float (&s)[8],
             const float w = __builtin_fmaf(x[k], r[k], z[k]);
             if (!fast || __builtin_fabsf(w - __builtin_rintf(w)) > 0.4999f)
                 n[k] = __builtin_rintf(x[k] / s[k]) + z[k];
+            n[k] = vclamp(n[k], 0.0f, 15.0f);
         }
     }
 #pragma unroll
-    for (int k = 0; k < 8; ++k) q[k] = vclamp(n[k], 0.0f, 15.0f);
+    for (int k = 0; k < 8; ++k) q[k] = n[k];
 }
 
 // 8 codes (as floats in [0, 15]) -> one dword, byte j = code(2j) | code(2j+1) << 4.
