@@ -330,11 +330,13 @@ __device__ __forceinline__ void quant_row(const kvq_mixed_store& m, const uint4 
     if (!fits) return;
     if (lane == 0) (t == 0 ? m.s2 : m.s4)[k] = s;
     const float off = qmax + 1.0f;   // 2 or 8
+    // no clip: |x| <= max|x| and s = fl(max|x| / qmax) (or the floor's larger s) give
+    // |x / s| <= qmax (1 + 2^-23), which rounds into [-qmax, qmax]
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
         float u[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) u[e] = vclamp(rint_div(v[j][e], s, rs), -qmax, qmax) + off;
+        for (int e = 0; e < 8; ++e) u[e] = rint_div(v[j][e], s, rs) + off;
         uint32_t even = 0, odd = 0;   // bytes: elements 0 2 4 6 and 1 3 5 7
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
