@@ -56,6 +56,10 @@ constexpr int D = 128;
 constexpr float kNegBig = -3.0e38f;
 constexpr float kMargin = 2.0f;     // head-room put above the largest logit when the reference moves
 constexpr int kEmin = -64, kEmax = 64;
+// Buffer resource word 3 for raw byte-addressed loads (32-bit data format, no swizzle or thread
+// offset), and the non-temporal cache policy of a buffer load.
+constexpr int kBufferFormat = 0x00020000;
+constexpr int kLoadNT = 2;
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
@@ -97,6 +101,16 @@ __device__ __forceinline__ uint32_t pack_h2(float a, float b) {
     return __builtin_bit_cast(uint32_t, h);
 }
 
+// The fp16 pair (a - h.lo, b - h.hi) for h = pack_h2(a, b): each difference is exact in fp32 and
+// v_fma_mix{lo,hi}_f16 (h's half taken as fp16, times -1, plus the fp32 value) round it once to
+// fp16, which is what converting the fp32 difference gives -- in two instructions instead of five.
+__device__ __forceinline__ uint32_t residual_h2(uint32_t h, float a, float b) {
+    uint32_t r = 0;
+    asm("v_fma_mixlo_f16 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "+v"(r) : "v"(h), "v"(a));
+    asm("v_fma_mixhi_f16 %0, %1, -1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "+v"(r) : "v"(h), "v"(b));
+    return r;
+}
+
 // fp16 0x5400 | (n << 4) = 64 + n for a nibble n in mantissa bits 4..7.
 constexpr uint32_t kMagic = 0x54005400u;
 constexpr uint32_t kNib = 0x00f000f0u;
@@ -111,14 +125,34 @@ __device__ __forceinline__ half8 nib8(uint32_t w) {
     return as_half8(nib_pair(w << 4), nib_pair(w >> 4), nib_pair(w), nib_pair(w >> 8));
 }
 
-// Butterfly exchange across lanes: xor distances below 32 go through ds_swizzle's bit mode.
+// Butterfly exchange across lanes at xor distances below 32: ds_swizzle's bit mode.
 template <int OFF>
 __device__ __forceinline__ float xor_lane(float x) {
-    if constexpr (OFF < 32) {
-        return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x1f | (OFF << 10)));
-    } else {
-        return __shfl_xor(x, OFF);
-    }
+    static_assert(OFF >= 1 && OFF < 32, "xor distance below 32");
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x1f | (OFF << 10)));
+}
+// x[lane] + x[lane ^ 32] and max(x[lane], x[lane ^ 32]) in every lane: v_permlane32_swap trades
+// the upper half of one copy of x for the lower half of another, after which each lane holds
+// both operands (which of the two registers holds which does not change a sum or a maximum).
+__device__ __forceinline__ float add_halves(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float max_halves(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return vmax2(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+// Sum over the lanes lane ^ j for j in [0, 2 * END) stepping by OFF, OFF ... END powers of two
+// below 32 (every lane ends with the sum of its group)
+template <int OFF, int END>
+__device__ __forceinline__ float add_lanes(float x) {
+    if constexpr (OFF < END) return add_lanes<2 * OFF, END>(x + xor_lane<OFF>(x));
+    else return x;
+}
+template <int OFF, int END>
+__device__ __forceinline__ float max_lanes(float x) {
+    if constexpr (OFF < END) return max_lanes<2 * OFF, END>(vmax2(x, xor_lane<OFF>(x)));
+    else return x;
 }
 
 // ---- the bf16 residual window: one block per (b, h, split of up to kResTile tokens) ----
@@ -319,8 +353,7 @@ attn_mfma_kernel(const MfmaArgs a) {
                 qmax = vmax2(qmax, __builtin_fabsf(v8[j]));
             }
         }
-        qmax = vmax2(qmax, xor_lane<16>(qmax));
-        qmax = vmax2(qmax, xor_lane<32>(qmax));
+        qmax = max_halves(vmax2(qmax, xor_lane<16>(qmax)));
         // |Q'| < 2^14 after the scaling (also for tiny queries, which are scaled up)
         const int tau = qmax > 0.0f ? __builtin_amdgcn_frexp_expf(qmax) - 14 : 0;
         rq_scale = __builtin_ldexpf(1.0f, tau);
@@ -340,8 +373,7 @@ attn_mfma_kernel(const MfmaArgs a) {
             }
             rq_hi[kk] = u32x4{hw[0], hw[1], hw[2], hw[3]};
             rq_lo[kk] = u32x4{lw[0], lw[1], lw[2], lw[3]};
-            sum += xor_lane<16>(sum);
-            sum += xor_lane<32>(sum);
+            sum = add_halves(sum + xor_lane<16>(sum));
             csum[kk] = sum;      // the 32 channels of chunk kk, query n
         }
 #pragma unroll
@@ -404,9 +436,10 @@ attn_mfma_kernel(const MfmaArgs a) {
     // token lane of the pair, and the K group scale and zero rows (both groups of the pair when
     // g = 32: lane group G holds row G % 2 of the pair's group G / 2).
     // Every lane issues the same loads for every tile, whatever the position: rows past the
-    // end of the cache are clamped to its last row (their logits are masked, so their values
-    // never count).  With no load behind a branch, the wait before staging a tile leaves the
-    // loads of the tile behind it in flight.
+    // end of the cache read as zero (their logits are masked and their V scales are zero, so
+    // they never count; the largest V scale of a pair is unchanged, as the pair holds the last
+    // row).  With no load behind a branch, the wait before staging a tile leaves the loads of the
+    // tile behind it in flight.
     constexpr int SW = NG >= 2 ? NG / 2 : 1;   // dwords of V scale (and of zero) per lane per pair
     struct CodeRegs {
         u32x4 k[2], v[2];
@@ -420,36 +453,41 @@ attn_mfma_kernel(const MfmaArgs a) {
     const uint16_t* kpsrc = (G % 2 ? kzero : kscale) + 8 * n;
     const uint16_t* kspt = a.k_scale + bh * a.ldq * NG;   // ROT: per-token K scale / zero rows
     const uint16_t* kzpt = a.k_zero + bh * a.ldq * NG;
-    // tt0 is at most the last row; rows of the tile past the last row are clamped to it.  Lane
-    // offsets are unsigned 32-bit so the loads take the scalar-base + vector-offset form.
-    auto fetch_codes = [&](CodeRegs& r, int tt0) {
-        const int lim = last_row - tt0;
-        const uint8_t* kt = kc + (int64_t)tt0 * (D / 2);
-        const uint8_t* vt = vc + (int64_t)tt0 * (D / 2);
-        r.k[0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kt + (uint32_t)(min(n, lim) * (D / 2) + 16 * G)));
-        r.k[1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kt + (uint32_t)(min(16 + n, lim) * (D / 2) + 16 * G)));
-        r.v[0] = __builtin_nontemporal_load(
-            reinterpret_cast<const u32x4*>(vt + (uint32_t)(min(lane / 4, lim) * (D / 2) + 16 * (lane % 4))));
-        r.v[1] = __builtin_nontemporal_load(
-            reinterpret_cast<const u32x4*>(vt + (uint32_t)(min(16 + lane / 4, lim) * (D / 2) + 16 * (lane % 4))));
+    // Tile loads go through buffer resources that cover the rows [tt0, min(Tq, tt0 + n)) of a
+    // section: a row at or past Tq reads as zero (a buffer load past the resource's size returns
+    // zeros and touches no memory), so no lane clamps its row, and the lane offsets below stay
+    // the same for every tile (the tile's position is in the resource, a scalar).
+    auto rows_rsrc = [&](const void* base, int tt0, int nrow, int row_bytes) {
+        const uint32_t size = (uint32_t)min(Tq - tt0, nrow) * (uint32_t)row_bytes;
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)size, kBufferFormat);
     };
-    // per-token (scale, zero) words of token lane of the pair: NG bf16 each
+    const uint32_t off_k = (uint32_t)(n * (D / 2) + 16 * G);   // K: token n (+16), bytes 16G..16G+15
+    const uint32_t off_v = (uint32_t)(16 * lane);              // V: 16-byte unit lane of the tile (+1 KB)
+    auto fetch_codes = [&](CodeRegs& r, int tt0) {
+        const auto rk = rows_rsrc(kc + (int64_t)tt0 * (D / 2), tt0, kTile, D / 2);
+        const auto rv = rows_rsrc(vc + (int64_t)tt0 * (D / 2), tt0, kTile, D / 2);
+        r.k[0] = __builtin_amdgcn_raw_buffer_load_b128(rk, off_k, 0, kLoadNT);
+        r.k[1] = __builtin_amdgcn_raw_buffer_load_b128(rk, off_k + 16 * (D / 2), 0, kLoadNT);
+        r.v[0] = __builtin_amdgcn_raw_buffer_load_b128(rv, off_v, 0, kLoadNT);
+        r.v[1] = __builtin_amdgcn_raw_buffer_load_b128(rv, off_v + 16 * (D / 2), 0, kLoadNT);
+    };
+    // per-token (scale, zero) words of token lane of the pair: NG bf16 each (the (b, h) row of a
+    // one-group-per-token section may be only 2-byte aligned, hence 2-byte loads for NG = 1)
     auto fetch_pt = [&](const uint16_t* sp, const uint16_t* zp, uint32_t (&os)[SW], uint32_t (&oz)[SW], int tt0) {
-        const int lim = last_row - tt0;
-        const uint8_t* st = reinterpret_cast<const uint8_t*>(sp + (int64_t)tt0 * NG);
-        const uint8_t* zt = reinterpret_cast<const uint8_t*>(zp + (int64_t)tt0 * NG);
-        const uint32_t e = (uint32_t)min(lane, lim) * (NG * 2);   // byte offset of token lane's elements
-        if constexpr (NG == 1) {   // one bf16 per token: the (b, h) row may be only 2-byte aligned
-            os[0] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(st + e));
-            oz[0] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(zt + e));
+        const auto rs = rows_rsrc(sp + (int64_t)tt0 * NG, tt0, 2 * kTile, NG * 2);
+        const auto rz = rows_rsrc(zp + (int64_t)tt0 * NG, tt0, 2 * kTile, NG * 2);
+        const uint32_t e = (uint32_t)lane * (NG * 2);   // byte offset of token lane's elements
+        if constexpr (NG == 1) {
+            os[0] = __builtin_amdgcn_raw_buffer_load_b16(rs, e, 0, kLoadNT);
+            oz[0] = __builtin_amdgcn_raw_buffer_load_b16(rz, e, 0, kLoadNT);
         } else if constexpr (NG == 2) {
-            os[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(st + e));
-            oz[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(zt + e));
+            os[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, e, 0, kLoadNT);
+            oz[0] = __builtin_amdgcn_raw_buffer_load_b32(rz, e, 0, kLoadNT);
         } else {
-            const uint2 a2 = ld_stream_u2(st + e);
-            const uint2 b2 = ld_stream_u2(zt + e);
-            os[0] = a2.x; os[1] = a2.y;
-            oz[0] = b2.x; oz[1] = b2.y;
+            const auto a2 = __builtin_amdgcn_raw_buffer_load_b64(rs, e, 0, kLoadNT);
+            const auto b2 = __builtin_amdgcn_raw_buffer_load_b64(rz, e, 0, kLoadNT);
+            os[0] = a2[0]; os[1] = a2[1];
+            oz[0] = b2[0]; oz[1] = b2[1];
         }
     };
     auto fetch_side = [&](SideRegs& r, int tt0) {
@@ -531,17 +569,15 @@ attn_mfma_kernel(const MfmaArgs a) {
                 float qs[8];
                 chunk_scaled(p, qs);
 #pragma unroll
-                for (int j = 0; j < 8; j += 2) qmax = vmax3(qmax, __builtin_fabsf(qs[j]), __builtin_fabsf(qs[j + 1]));
+                for (int j = 0; j < 8; j += 2) qmax = vmax3_abs(qmax, qs[j], qs[j + 1]);
             }
             lscale = a.qscale;
             int tau = 0;
             if (__any(qmax >= 16384.0f)) {
                 // out of the fp16 range: scale this query's Q' by 2^-tau, tau from the largest
                 // |q * s_K| over its 128 channels (lanes that hold the same query)
-#pragma unroll
-                for (int off = NQ; off < 4 * NQ && off < 16; off *= 2) qmax = vmax2(qmax, __shfl_xor(qmax, off));
-                qmax = vmax2(qmax, xor_lane<16>(qmax));
-                qmax = vmax2(qmax, xor_lane<32>(qmax));
+                qmax = max_lanes<NQ, (4 * NQ < 16 ? 4 * NQ : 16)>(qmax);
+                qmax = max_halves(vmax2(qmax, xor_lane<16>(qmax)));
                 tau = __builtin_amdgcn_frexp_expf(qmax) - 14;
                 lscale = __builtin_ldexpf(a.qscale, tau);
             }
@@ -568,18 +604,15 @@ attn_mfma_kernel(const MfmaArgs a) {
                 for (int e = 0; e < 4; ++e) {
                     const float x0 = qs[kPerm[2 * e]], x1 = qs[kPerm[2 * e + 1]];
                     hw[e] = pack_h2(x0, x1);
-                    const half2v hh = __builtin_bit_cast(half2v, hw[e]);
-                    lw[e] = pack_h2(x0 - (float)hh[0], x1 - (float)hh[1]);
+                    lw[e] = residual_h2(hw[e], x0, x1);
                 }
                 *reinterpret_cast<u32x4*>(sqx + lane * PASS * 8 + 8 * p) = u32x4{hw[0], hw[1], hw[2], hw[3]};
                 *reinterpret_cast<u32x4*>(sqx + lane * PASS * 8 + 8 * p + 4) = u32x4{lw[0], lw[1], lw[2], lw[3]};
             }
             float bpart = __builtin_fmaf(64.0f, bsum, bz);
             // bias: sum over the distinct chunks of this query, then over the 4 lane groups
-#pragma unroll
-            for (int off = NQ; off < 4 * NQ && off < 16; off *= 2) bpart += __shfl_xor(bpart, off);
-            bpart += xor_lane<16>(bpart);
-            bpart += xor_lane<32>(bpart);
+            bpart = add_lanes<NQ, (4 * NQ < 16 ? 4 * NQ : 16)>(bpart);
+            bpart = add_halves(bpart + xor_lane<16>(bpart));
             c0 = __builtin_fmaf(bpart, lscale, ref);
     };
     // scores of tile par -> lg (lane (n, G): tokens 4G+i (half 0) and 16+4G+i (half 1), i = 0..3;
@@ -684,18 +717,12 @@ attn_mfma_kernel(const MfmaArgs a) {
             lmax = vmax3(lmax, vmax3(vmax3(lg[1][0], lg[1][1], lg[1][2]), vmax3(lg[1][3], lg[1][4], lg[1][5]), lg[1][6]), lg[1][7]);
         if (__any(lmax > thr || big_s)) {
             // move the reference: largest logit of the tiles (+ margin) and largest V scale
-            float tmax = vmax2(lmax, xor_lane<16>(lmax));
-            tmax = vmax2(tmax, xor_lane<32>(tmax));
+            const float tmax = max_halves(vmax2(lmax, xor_lane<16>(lmax)));
             // largest V scale of the tile pair: lane holds token lane's NG scales
             float sm2 = ssz[2 * NG * lane];
 #pragma unroll
             for (int gI = 1; gI < NG; ++gI) sm2 = vmax2(sm2, ssz[2 * (NG * lane + gI)]);
-            sm2 = vmax2(sm2, xor_lane<1>(sm2));
-            sm2 = vmax2(sm2, xor_lane<2>(sm2));
-            sm2 = vmax2(sm2, xor_lane<4>(sm2));
-            sm2 = vmax2(sm2, xor_lane<8>(sm2));
-            sm2 = vmax2(sm2, xor_lane<16>(sm2));
-            sm2 = vmax2(sm2, xor_lane<32>(sm2));
+            sm2 = max_halves(max_lanes<1, 32>(sm2));
             int e_new = max(e_s, __builtin_amdgcn_frexp_expf(sm2));   // sm2 < 2^frexp_exp
             e_new = min(max(e_new, kEmin), kEmax);
             const float d = vmax2(thr, tmax + kMargin) + (float)(e_new - 15);
@@ -868,13 +895,11 @@ attn_mfma_kernel(const MfmaArgs a) {
     }
 
     // ---------------- finish the wave: sums over the 4 lane groups, offset and zero terms ----------------
-    l_part += xor_lane<16>(l_part);
-    l_part += xor_lane<32>(l_part);
+    l_part = add_halves(l_part + xor_lane<16>(l_part));
     if constexpr (ROT) {
 #pragma unroll
         for (int gI = 0; gI < NG; ++gI) {
-            zsum[gI] += xor_lane<16>(zsum[gI]);
-            zsum[gI] += xor_lane<32>(zsum[gI]);
+            zsum[gI] = add_halves(zsum[gI] + xor_lane<16>(zsum[gI]));
         }
     }
     __syncthreads();   // every wave is done with the loop buffers before the merge reuses them
