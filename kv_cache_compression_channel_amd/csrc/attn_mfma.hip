@@ -105,8 +105,8 @@ __device__ __forceinline__ uint32_t pack_h2(float a, float b) {
 // v_fma_mix{lo,hi}_f16 (h's half taken as fp16, times -1, plus the fp32 value) round it once to
 // fp16, which is what converting the fp32 difference gives -- in two instructions instead of five.
 __device__ __forceinline__ uint32_t residual_h2(uint32_t h, float a, float b) {
-    uint32_t r = 0;
-    asm("v_fma_mixlo_f16 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "+v"(r) : "v"(h), "v"(a));
+    uint32_t r;   // the high half is written by the second instruction
+    asm("v_fma_mixlo_f16 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h), "v"(a));
     asm("v_fma_mixhi_f16 %0, %1, -1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "+v"(r) : "v"(h), "v"(b));
     return r;
 }
@@ -573,7 +573,8 @@ attn_mfma_kernel(const MfmaArgs a) {
             }
             lscale = a.qscale;
             int tau = 0;
-            if (__any(qmax >= 16384.0f)) {
+            const bool big = __any(qmax >= 16384.0f);   // uniform: the scaling below is a scalar branch
+            if (big) {
                 // out of the fp16 range: scale this query's Q' by 2^-tau, tau from the largest
                 // |q * s_K| over its 128 channels (lanes that hold the same query)
                 qmax = max_lanes<NQ, (4 * NQ < 16 ? 4 * NQ : 16)>(qmax);
@@ -588,7 +589,7 @@ attn_mfma_kernel(const MfmaArgs a) {
             for (int p = 0; p < PASS; ++p) {
                 float qs[8];
                 chunk_scaled(p, qs);
-                if (tau != 0) {
+                if (big) {
 #pragma unroll
                     for (int j = 0; j < 8; ++j) qs[j] = __builtin_ldexpf(qs[j], -tau);
                 }
@@ -597,7 +598,8 @@ attn_mfma_kernel(const MfmaArgs a) {
                 for (int e = 0; e < 4; ++e) {
                     bz = __builtin_fmaf(qs[2 * e], bf_lo(zw[e]), bz);
                     bz = __builtin_fmaf(qs[2 * e + 1], bf_hi(zw[e]), bz);
-                    bsum += qs[2 * e] + qs[2 * e + 1];
+                    // the first pair starts the sum (an addition of +0 would cost an instruction)
+                    bsum = (p == 0 && e == 0) ? qs[0] + qs[1] : bsum + (qs[2 * e] + qs[2 * e + 1]);
                 }
                 uint32_t hw[4], lw[4];
 #pragma unroll

@@ -47,28 +47,52 @@ struct PcGeom {
     int64_t rpc;       // rows per chunk of the min/max pass
 };
 
+// The raw bits of VEC consecutive values of x (fp32 or bf16) and their conversion to fp32, kept
+// apart so that a thread can issue every row's load before it converts any.
+struct XRaw {
+    uint4 a, b;
+};
 template <int XT, int VEC>
-__device__ __forceinline__ void load_x(const void* x, int64_t off, float (&v)[VEC]) {
+__device__ __forceinline__ XRaw load_raw(const void* x, int64_t off) {
+    XRaw r;
     if constexpr (XT == KVQ_FP32) {
         const float* p = static_cast<const float*>(x) + off;
         if constexpr (VEC == 8) {
-            const float4 a = *reinterpret_cast<const float4*>(p);
-            const float4 b = *reinterpret_cast<const float4*>(p + 4);
-            v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-            v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+            r.a = *reinterpret_cast<const uint4*>(p);
+            r.b = *reinterpret_cast<const uint4*>(p + 4);
         } else {
-            v[0] = *p;
+            r.a.x = __float_as_uint(*p);
         }
     } else {
         const uint16_t* p = static_cast<const uint16_t*>(x) + off;
+        if constexpr (VEC == 8) r.a = *reinterpret_cast<const uint4*>(p);
+        else r.a.x = *p;
+    }
+    return r;
+}
+template <int XT, int VEC>
+__device__ __forceinline__ void unpack_raw(const XRaw& r, float (&v)[VEC]) {
+    if constexpr (XT == KVQ_FP32) {
         if constexpr (VEC == 8) {
-            const uint4 a = *reinterpret_cast<const uint4*>(p);
-            v[0] = bf_lo(a.x); v[1] = bf_hi(a.x); v[2] = bf_lo(a.y); v[3] = bf_hi(a.y);
-            v[4] = bf_lo(a.z); v[5] = bf_hi(a.z); v[6] = bf_lo(a.w); v[7] = bf_hi(a.w);
+            v[0] = __uint_as_float(r.a.x); v[1] = __uint_as_float(r.a.y);
+            v[2] = __uint_as_float(r.a.z); v[3] = __uint_as_float(r.a.w);
+            v[4] = __uint_as_float(r.b.x); v[5] = __uint_as_float(r.b.y);
+            v[6] = __uint_as_float(r.b.z); v[7] = __uint_as_float(r.b.w);
         } else {
-            v[0] = bf_to_f(*p);
+            v[0] = __uint_as_float(r.a.x);
+        }
+    } else {
+        if constexpr (VEC == 8) {
+            v[0] = bf_lo(r.a.x); v[1] = bf_hi(r.a.x); v[2] = bf_lo(r.a.y); v[3] = bf_hi(r.a.y);
+            v[4] = bf_lo(r.a.z); v[5] = bf_hi(r.a.z); v[6] = bf_lo(r.a.w); v[7] = bf_hi(r.a.w);
+        } else {
+            v[0] = bf_to_f((uint16_t)r.a.x);
         }
     }
+}
+template <int XT, int VEC>
+__device__ __forceinline__ void load_x(const void* x, int64_t off, float (&v)[VEC]) {
+    unpack_raw<XT, VEC>(load_raw<XT, VEC>(x, off), v);
 }
 
 // Pass 1: min and max of every channel over one chunk of rows.
@@ -92,19 +116,24 @@ __global__ void __launch_bounds__(kThreads) pc_minmax_kernel(const void* __restr
         // which leaves min and max as they are
         const int64_t r_end = min(g.R, (rc + 1) * g.rpc);
         for (int64_t r0 = rc * g.rpc + rl; r0 < r_end; r0 += kBatch * g.rpp) {
-            float v[kBatch][VEC];
+            XRaw raw[kBatch];
 #pragma unroll
             for (int u = 0; u < kBatch; ++u) {
                 const int64_t r = min(r0 + u * g.rpp, r_end - 1);
-                load_x<XT, VEC>(x, s * g.bsx + r * g.ldx + c0, v[u]);
+                raw[u] = load_raw<XT, VEC>(x, s * g.bsx + r * g.ldx + c0);
             }
+            __builtin_amdgcn_sched_barrier(0);   // the batch's loads all issued before the first use
 #pragma unroll
-            for (int u = 0; u < kBatch; u += 2)
+            for (int u = 0; u < kBatch; u += 2) {
+                float v0[VEC], v1[VEC];
+                unpack_raw<XT, VEC>(raw[u], v0);
+                unpack_raw<XT, VEC>(raw[u + 1], v1);
 #pragma unroll
                 for (int k = 0; k < VEC; ++k) {
-                    mn[k] = vmin3(mn[k], v[u][k], v[u + 1][k]);
-                    mx[k] = vmax3(mx[k], v[u][k], v[u + 1][k]);
+                    mn[k] = vmin3(mn[k], v0[k], v1[k]);
+                    mx[k] = vmax3(mx[k], v0[k], v1[k]);
                 }
+            }
         }
     }
 #pragma unroll
@@ -213,37 +242,41 @@ __global__ void __launch_bounds__(kThreads) pc_code_kernel(const void* __restric
     const int lane = threadIdx.x % g.lpr, rl = threadIdx.x / g.lpr;
     const int64_t c0 = (cb * g.lpr + lane) * VEC;
     if (c0 >= g.C) return;
+    PcParams P[VEC];
+#pragma unroll
+    for (int k = 0; k < VEC; ++k) P[k] = prm[s * g.C + c0 + k];
+    const float lo = (float)qmin, hi = (float)qmax;
+    const int64_t r_end = min(g.R, (rc + 1) * kCodeRows);
+    // every row of the chunk (at most kCodeRows / 4: rpp >= 4) loaded before any is coded.  A row
+    // past the end takes the last row for its load and its store alike (the same codes to the same
+    // bytes), so no load or store sits behind a branch.
+    constexpr int NRT = kCodeRows / 4;
+    XRaw raw[NRT];
+    int64_t rr[NRT];
+#pragma unroll
+    for (int u = 0; u < NRT; ++u) {
+        rr[u] = min(rc * kCodeRows + rl + u * g.rpp, r_end - 1);
+        raw[u] = load_raw<XT, VEC>(x, s * g.bsx + rr[u] * g.ldx + c0);
+    }
+    __builtin_amdgcn_sched_barrier(0);   // every load issued before the first use
     float ps[VEC], pr[VEC], pz[VEC];
     bool fast = true;
 #pragma unroll
     for (int k = 0; k < VEC; ++k) {
-        const PcParams P = prm[s * g.C + c0 + k];
-        ps[k] = P.s; pr[k] = P.r; pz[k] = P.zf;
-        fast = fast && (P.fast != 0.0f);
-    }
-    const float lo = (float)qmin, hi = (float)qmax;
-    const int64_t r_end = min(g.R, (rc + 1) * kCodeRows);
-    // every row of the chunk (at most kCodeRows / 4: rpp >= 4) loaded before any is coded; rows
-    // past the end load the last row again and are not stored
-    constexpr int NRT = kCodeRows / 4;
-    float v[NRT][VEC];
-#pragma unroll
-    for (int u = 0; u < NRT; ++u) {
-        const int64_t r = min(rc * kCodeRows + rl + u * g.rpp, r_end - 1);
-        load_x<XT, VEC>(x, s * g.bsx + r * g.ldx + c0, v[u]);
+        ps[k] = P[k].s; pr[k] = P[k].r; pz[k] = P[k].zf;
+        fast = fast && (P[k].fast != 0.0f);
     }
 #pragma unroll
     for (int u = 0; u < NRT; ++u) {
-        const int64_t r = rc * kCodeRows + rl + u * g.rpp;
-        if (r < r_end) {
-            int8_t o[VEC];
-            pc_codes<VEC>(v[u], ps, pr, pz, fast, lo, hi, o);
-            int8_t* dst = q + (s * g.R + r) * g.C + c0;
-            if constexpr (VEC == 8) {
-                *reinterpret_cast<uint2*>(dst) = pack8_i8(o);
-            } else {
-                dst[0] = o[0];
-            }
+        float v[VEC];
+        unpack_raw<XT, VEC>(raw[u], v);
+        int8_t o[VEC];
+        pc_codes<VEC>(v, ps, pr, pz, fast, lo, hi, o);
+        int8_t* dst = q + (s * g.R + rr[u]) * g.C + c0;
+        if constexpr (VEC == 8) {
+            *reinterpret_cast<uint2*>(dst) = pack8_i8(o);
+        } else {
+            dst[0] = o[0];
         }
     }
 }
@@ -282,21 +315,22 @@ __global__ void __launch_bounds__(kThreads) pc_dequant_kernel(const int8_t* __re
     }
     const int64_t r_end = min(g.R, (rc + 1) * kDqRows);
     for (int64_t r0 = rc * kDqRows + rl; r0 < r_end; r0 += kBatch * g.rpp) {
-    // kBatch rows' codes loaded before any is used; rows past the end load the last row again and
-    // are not stored
+    // kBatch rows' codes loaded before any is used.  A row past the end takes the last row, for
+    // its load and its store alike: it writes that row's values to that row again (the same
+    // bytes), so no load or store sits behind a branch (a conditional store lets the compiler
+    // sink the row's load into the branch, where it waits on its own).
+    int64_t e[kBatch];
     uint2 wq[kBatch];
     int8_t wq1[kBatch];
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
-        const int64_t e = (s * g.R + min(r0 + u * g.rpp, r_end - 1)) * g.C + c0;
-        if constexpr (VEC == 8) wq[u] = *reinterpret_cast<const uint2*>(q + e);
-        else wq1[u] = q[e];
+        e[u] = (s * g.R + min(r0 + u * g.rpp, r_end - 1)) * g.C + c0;
+        if constexpr (VEC == 8) wq[u] = *reinterpret_cast<const uint2*>(q + e[u]);
+        else wq1[u] = q[e[u]];
     }
+    __builtin_amdgcn_sched_barrier(0);   // every load of the batch issued before the first store
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
-        const int64_t r = r0 + u * g.rpp;
-        if (r >= r_end) continue;
-        const int64_t e = (s * g.R + r) * g.C + c0;
         float v[VEC];
         if constexpr (VEC == 8) {
             const uint2 w = wq[u];
@@ -309,7 +343,7 @@ __global__ void __launch_bounds__(kThreads) pc_dequant_kernel(const int8_t* __re
             v[0] = ((float)wq1[u] - zf[0]) * sc[0];
         }
         if constexpr (OT == KVQ_FP32) {
-            float* o = static_cast<float*>(out) + e;
+            float* o = static_cast<float*>(out) + e[u];
             if constexpr (VEC == 8) {
                 st_stream_f4(o, make_float4(v[0], v[1], v[2], v[3]));
                 st_stream_f4(o + 4, make_float4(v[4], v[5], v[6], v[7]));
@@ -317,7 +351,7 @@ __global__ void __launch_bounds__(kThreads) pc_dequant_kernel(const int8_t* __re
                 o[0] = v[0];
             }
         } else {
-            uint16_t* o = static_cast<uint16_t*>(out) + e;
+            uint16_t* o = static_cast<uint16_t*>(out) + e[u];
             if constexpr (VEC == 8) {
                 st_stream_u4(o, make_uint4(pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]), pack_bf2(v[4], v[5]),
                                            pack_bf2(v[6], v[7])));
