@@ -253,8 +253,10 @@ __global__ void __launch_bounds__(kThreads) int4_dequant_kernel(const uint8_t* _
                 for (int k = 0; k < 8; ++k) zs8[q][k] = -zf[k] * s8[q][k];
             }
         }
-        // Every row's words are loaded before any is used (one round trip per block): rows past n
-        // (the last tile's tail) load row n - 1 again and are not stored.
+        // Every row's words are loaded before any is used (one round trip per block).  A row past n
+        // (the last tile's tail) takes row n - 1 for its loads and its store alike and writes that
+        // row's values again (a K row past n has the parameters of row n - 1's group: a group of
+        // the tile past the last one repeats the last), so no load or store sits behind a branch.
         constexpr int NRW = TILE / RPP;
         uint32_t wr[NRW];
         uint16_t sr[NRW], zr[NRW];
@@ -269,11 +271,12 @@ __global__ void __launch_bounds__(kThreads) int4_dequant_kernel(const uint8_t* _
                 zr[i] = zero[mi];
             }
         }
+        __builtin_amdgcn_sched_barrier(0);   // every load issued before the first store
 #pragma unroll
         for (int i = 0; i < NRW; ++i) {
             const int r = rg + RPP * i;
             const int q = IS_K ? (RPP * i) / G : 0;   // the row's group inside the tile (RPP divides G)
-            const int64_t t = t0 + r;
+            const int64_t t = t0 + min(r, n - 1);
             const uint32_t w = wr[i];
             // nibbles 2e and 2e+1 sit in byte e of w & 0x0f0f0f0f and of (w >> 4) & 0x0f0f0f0f;
             // each byte converts with one v_cvt_f32_ubyte<e>
@@ -294,7 +297,7 @@ __global__ void __launch_bounds__(kThreads) int4_dequant_kernel(const uint8_t* _
 #pragma unroll
                 for (int k = 0; k < 8; ++k) v[k] = __builtin_fmaf(c[k], s, zs);
             }
-            if (r < n) store8(t, b, h, v);
+            store8(t, b, h, v);
         }
         return;
     }

@@ -106,10 +106,15 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(const float* __rest
     uint32_t kreg[REG ? kRegKeys : 1];
     auto key_at = [&](int64_t j) -> uint32_t { return j >= rs ? kKeyRecent : order_key(sc[j]); };
     if constexpr (REG) {
+        // every score loaded (past the end: the last one again), then keyed, so that no load sits
+        // behind a per-key branch and waits for the loads before it
+        float sv[kRegKeys];
+#pragma unroll
+        for (int i = 0; i < kRegKeys; ++i) sv[i] = sc[min((int64_t)i * kSelThreads + tid, T - 1)];
 #pragma unroll
         for (int i = 0; i < kRegKeys; ++i) {
             const int64_t j = (int64_t)i * kSelThreads + tid;
-            kreg[i] = j < T ? key_at(j) : 0u;
+            kreg[i] = j >= T ? 0u : (j >= rs ? kKeyRecent : order_key(sv[i]));
         }
     }
 
