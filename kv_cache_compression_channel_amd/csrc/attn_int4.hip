@@ -290,9 +290,7 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(const float* __restri
 #pragma unroll
             for (int j = 0; j < CPL; ++j) x[s][j] = s < nslot ? base[(int64_t)s * (D + 2) + 2 + lane + 64 * j] : 0.0f;
         }
-        float M = ms;
-#pragma unroll
-        for (int off = 32; off >= 1; off /= 2) M = fmaxf(M, __shfl_xor(M, off));
+        const float M = max_lanes_desc<16>(max_halves(ms));
         const float f = lane < nslot ? exp2f(ms - M) : 0.0f;
         float L = lane < nslot ? __builtin_fmaf(ls, f, 0.0f) : 0.0f, A[CPL];
 #pragma unroll
@@ -300,20 +298,18 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(const float* __restri
 #pragma unroll
         for (int s = 0; s < kFewSlots; ++s) {
             if (s < nslot) {
-                const float fk = __shfl(f, s);
+                const float fk = lane_value(f, s);
 #pragma unroll
                 for (int j = 0; j < CPL; ++j) A[j] = __builtin_fmaf(x[s][j], fk, A[j]);
             }
         }
-#pragma unroll
-        for (int off = 32; off >= 1; off /= 2) L += __shfl_xor(L, off);
+        L = add_lanes_desc<16>(add_halves(L));
         combine_store<D, OT>(row, lane, M, L, A, out, ml);
         return;
     }
     float M = kNegBig;
     for (int s = lane; s < nslot; s += 64) M = fmaxf(M, base[(int64_t)s * (D + 2)]);
-#pragma unroll
-    for (int off = 32; off >= 1; off /= 2) M = fmaxf(M, __shfl_xor(M, off));
+    M = max_lanes_desc<16>(max_halves(M));
     float L = 0.0f, A[CPL];
 #pragma unroll
     for (int j = 0; j < CPL; ++j) A[j] = 0.0f;
@@ -349,8 +345,7 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(const float* __restri
             for (int j = 0; j < CPL; ++j) A[j] = __builtin_fmaf(sp[lane + 64 * j], fk, A[j]);
         }
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off /= 2) L += __shfl_xor(L, off);
+    L = add_lanes_desc<16>(add_halves(L));
     combine_store<D, OT>(row, lane, M, L, A, out, ml);
 }
 

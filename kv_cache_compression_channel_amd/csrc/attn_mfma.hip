@@ -125,36 +125,6 @@ __device__ __forceinline__ half8 nib8(uint32_t w) {
     return as_half8(nib_pair(w << 4), nib_pair(w >> 4), nib_pair(w), nib_pair(w >> 8));
 }
 
-// Butterfly exchange across lanes at xor distances below 32: ds_swizzle's bit mode.
-template <int OFF>
-__device__ __forceinline__ float xor_lane(float x) {
-    static_assert(OFF >= 1 && OFF < 32, "xor distance below 32");
-    return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x1f | (OFF << 10)));
-}
-// x[lane] + x[lane ^ 32] and max(x[lane], x[lane ^ 32]) in every lane: v_permlane32_swap trades
-// the upper half of one copy of x for the lower half of another, after which each lane holds
-// both operands (which of the two registers holds which does not change a sum or a maximum).
-__device__ __forceinline__ float add_halves(float x) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-__device__ __forceinline__ float max_halves(float x) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return vmax2(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-// Sum over the lanes lane ^ j for j in [0, 2 * END) stepping by OFF, OFF ... END powers of two
-// below 32 (every lane ends with the sum of its group)
-template <int OFF, int END>
-__device__ __forceinline__ float add_lanes(float x) {
-    if constexpr (OFF < END) return add_lanes<2 * OFF, END>(x + xor_lane<OFF>(x));
-    else return x;
-}
-template <int OFF, int END>
-__device__ __forceinline__ float max_lanes(float x) {
-    if constexpr (OFF < END) return max_lanes<2 * OFF, END>(vmax2(x, xor_lane<OFF>(x)));
-    else return x;
-}
-
 // ---- the bf16 residual window: one block per (b, h, split of up to kResTile tokens) ----
 // Plain fp32 arithmetic from an LDS copy of the rows: logits q . k (q pre-scaled by
 // sm_scale log2 e), base-2 softmax over the split, p-weighted sum of the V rows.  Writes the
@@ -218,13 +188,9 @@ __device__ void residual_block(const MfmaArgs& a, ResLds& sr, int rb) {
     // softmax over the split: one wave per query, lanes over tokens
     for (int n = wv; n < NQ; n += kWaves) {
         const float x = lane < nt ? sr.p[n][lane] : kNegBig;
-        float m = x;
-#pragma unroll
-        for (int off = 32; off >= 1; off /= 2) m = vmax2(m, __shfl_xor(m, off));
+        const float m = max_lanes_desc<16>(max_halves(x));
         const float pv = lane < nt ? exp2f(x - m) : 0.0f;
-        float l = pv;
-#pragma unroll
-        for (int off = 32; off >= 1; off /= 2) l += __shfl_xor(l, off);
+        const float l = add_lanes_desc<16>(add_halves(pv));
         sr.p[n][lane] = pv;
         if (lane == 0) { sr.m[n] = m; sr.l[n] = l; }
     }

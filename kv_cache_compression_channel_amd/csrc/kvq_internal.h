@@ -116,6 +116,52 @@ __device__ __forceinline__ float vmax2(float a, float b) {
 }
 __device__ __forceinline__ float vclamp(float x, float lo, float hi) { return __builtin_amdgcn_fmed3f(x, lo, hi); }
 
+// Butterfly exchange across lanes at xor distances below 32: ds_swizzle's bit mode.
+template <int OFF>
+__device__ __forceinline__ float xor_lane(float x) {
+    static_assert(OFF >= 1 && OFF < 32, "xor distance below 32");
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x1f | (OFF << 10)));
+}
+// x[lane] + x[lane ^ 32] and max(x[lane], x[lane ^ 32]) in every lane: v_permlane32_swap trades
+// the upper half of one copy of x for the lower half of another, after which each lane holds
+// both operands (which of the two registers holds which does not change a sum or a maximum).
+__device__ __forceinline__ float add_halves(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float max_halves(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return vmax2(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+// Sum over the lanes lane ^ j for j in [0, 2 * END) stepping by OFF, OFF ... END powers of two
+// below 32 (every lane ends with the sum of its group)
+template <int OFF, int END>
+__device__ __forceinline__ float add_lanes(float x) {
+    if constexpr (OFF < END) return add_lanes<2 * OFF, END>(x + xor_lane<OFF>(x));
+    else return x;
+}
+template <int OFF, int END>
+__device__ __forceinline__ float max_lanes(float x) {
+    if constexpr (OFF < END) return max_lanes<2 * OFF, END>(vmax2(x, xor_lane<OFF>(x)));
+    else return x;
+}
+// The same reductions with the distances in descending order (32 first, then OFF, OFF/2, ... 1):
+// the order of a plain xor-shuffle loop from 32 down to 1, so sums keep its rounding.
+template <int OFF>
+__device__ __forceinline__ float add_lanes_desc(float x) {
+    if constexpr (OFF >= 1) return add_lanes_desc<OFF / 2>(x + xor_lane<OFF>(x));
+    else return x;
+}
+template <int OFF>
+__device__ __forceinline__ float max_lanes_desc(float x) {
+    if constexpr (OFF >= 1) return max_lanes_desc<OFF / 2>(vmax2(x, xor_lane<OFF>(x)));
+    else return x;
+}
+// v[src] of a wave-uniform lane index src, in every lane (one v_readlane_b32, no LDS)
+__device__ __forceinline__ float lane_value(float v, int src) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), src));
+}
+
 // min and max of 8 values folded into running (mn, mx).
 __device__ __forceinline__ void minmax8(const float (&v)[8], float& mn, float& mx) {
     mn = vmin3(vmin3(vmin3(mn, v[0], v[1]), v[2], v[3]), vmin3(v[4], v[5], v[6]), v[7]);
