@@ -23,12 +23,13 @@ constexpr int kThreads = 256;
 // 7.03 ms against 256-row chunks: fewer, longer workgroups and 32x fewer partials.
 constexpr int kRowsPerChunk = 256;
 constexpr int64_t kMinMaxBlocks = 1024;
-// The code and dequantization passes need no partials, so they take shorter row chunks than the
-// min/max pass: a workgroup then issues 8 (code) or 16 (dequantization) stores per thread instead
-// of 64, and the workgroups in flight write a more compact window of the output.  On MI355X that
-// made the code pass 5% and the dequantizer 3-5% faster (256-row chunks against 32 and 64).
+// The code and dequantization passes need no partials, so they take short row chunks: a
+// workgroup then issues 8 stores per thread (one batch of loads, then its stores) instead of 64,
+// and the workgroups in flight write a compact window of the output.  On MI355X that made the
+// code pass 5% faster (256-row chunks against 32), and the dequantizer 3-5% (256 against 64)
+// and then 10% more (64 against 32, once its loads no longer waited behind store branches).
 constexpr int kCodeRows = 32;
-constexpr int kDqRows = 64;
+constexpr int kDqRows = 32;
 // Row loads a thread issues before it uses any: every pass waits on memory once per batch.
 constexpr int kBatch = 8;
 
