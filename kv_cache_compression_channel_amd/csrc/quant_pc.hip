@@ -24,14 +24,16 @@ constexpr int kThreads = 256;
 constexpr int kRowsPerChunk = 256;
 constexpr int64_t kMinMaxBlocks = 1024;
 // The code and dequantization passes need no partials, so they take short row chunks: a
-// workgroup then issues 8 stores per thread (one batch of loads, then its stores) instead of 64,
-// and the workgroups in flight write a compact window of the output.  On MI355X that made the
-// code pass 5% faster (256-row chunks against 32), and the dequantizer 3-5% (256 against 64)
-// and then 10% more (64 against 32, once its loads no longer waited behind store branches).
+// workgroup then issues one batch of loads and then its stores (8 stores per thread in the code
+// pass, 4 in the dequantizer) instead of 64, and the workgroups in flight write a compact window
+// of the output.  On MI355X that made the code pass 5% faster (256-row chunks against 32), and
+// the dequantizer 3-5% (256 against 64), then 10% (64 against 32, once its loads no longer
+// waited behind store branches) and 1% more (32 against 16).
 constexpr int kCodeRows = 32;
-constexpr int kDqRows = 32;
+constexpr int kDqRows = 16;
 // Row loads a thread issues before it uses any: every pass waits on memory once per batch.
 constexpr int kBatch = 8;
+constexpr int kDqBatch = 4;   // the dequantizer's batch: its 16-row chunk at 4 rows per pass
 
 struct PcParams {
     float s;     // scale
@@ -315,23 +317,23 @@ __global__ void __launch_bounds__(kThreads) pc_dequant_kernel(const int8_t* __re
         zf[0] = zp ? (float)zp[s * g.C + c0] : 0.0f;
     }
     const int64_t r_end = min(g.R, (rc + 1) * kDqRows);
-    for (int64_t r0 = rc * kDqRows + rl; r0 < r_end; r0 += kBatch * g.rpp) {
-    // kBatch rows' codes loaded before any is used.  A row past the end takes the last row, for
+    for (int64_t r0 = rc * kDqRows + rl; r0 < r_end; r0 += kDqBatch * g.rpp) {
+    // kDqBatch rows' codes loaded before any is used.  A row past the end takes the last row, for
     // its load and its store alike: it writes that row's values to that row again (the same
     // bytes), so no load or store sits behind a branch (a conditional store lets the compiler
     // sink the row's load into the branch, where it waits on its own).
-    int64_t e[kBatch];
-    uint2 wq[kBatch];
-    int8_t wq1[kBatch];
+    int64_t e[kDqBatch];
+    uint2 wq[kDqBatch];
+    int8_t wq1[kDqBatch];
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
+    for (int u = 0; u < kDqBatch; ++u) {
         e[u] = (s * g.R + min(r0 + u * g.rpp, r_end - 1)) * g.C + c0;
         if constexpr (VEC == 8) wq[u] = *reinterpret_cast<const uint2*>(q + e[u]);
         else wq1[u] = q[e[u]];
     }
     __builtin_amdgcn_sched_barrier(0);   // every load of the batch issued before the first store
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
+    for (int u = 0; u < kDqBatch; ++u) {
         float v[VEC];
         if constexpr (VEC == 8) {
             const uint2 w = wq[u];
