@@ -93,10 +93,6 @@ __device__ __forceinline__ void unpack_raw(const XRaw& r, float (&v)[VEC]) {
         }
     }
 }
-template <int XT, int VEC>
-__device__ __forceinline__ void load_x(const void* x, int64_t off, float (&v)[VEC]) {
-    unpack_raw<XT, VEC>(load_raw<XT, VEC>(x, off), v);
-}
 
 // Pass 1: min and max of every channel over one chunk of rows.
 template <int XT, int VEC>
