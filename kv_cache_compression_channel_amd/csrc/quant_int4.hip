@@ -199,26 +199,33 @@ __global__ void __launch_bounds__(NT) int4_quant_kernel(const uint16_t* __restri
 // Short tiles stream the stores best: 32 tokens (two rows per thread at d = 128) measured 1-3%
 // faster than 64 at g = 32/64/128 and a third faster than 16 (one row per thread).
 constexpr int kDqTile = 32;
+// With many heads (d = 128, H a multiple of 4 and at least 32), a tile spans 4 heads and 8
+// tokens instead: each wave writes one token's four heads, 1 KB contiguous.  On the full-model
+// cache (32 heads) that measured 2-7% faster at g = 32/64/128 (16 tokens: 2-3%); on the decode
+// cache (8 heads) the same tiles were 8-11% slower, so fewer heads keep one-head tiles.
+constexpr int kDqHeads = 4;
+constexpr int kDqTileH = 8;
+constexpr int64_t kDqHeadsMinH = 32;
 template <int D>
 constexpr int dequant_tile() { return kDqTile > kThreads / (D / 8) ? kDqTile : kThreads / (D / 8); }
 
-template <int D, int G, bool IS_K, int OT>
+template <int D, int G, bool IS_K, int OT, int HPT>
 __global__ void __launch_bounds__(kThreads) int4_dequant_kernel(const uint8_t* __restrict__ codes,
                                                                 const uint16_t* __restrict__ scale,
                                                                 const uint16_t* __restrict__ zero,
                                                                 const uint16_t* __restrict__ res, I4Geom geo,
                                                                 void* __restrict__ out) {
     constexpr int LPR = D / 8;
-    constexpr int RPP = kThreads / LPR;
-    constexpr int TILE = dequant_tile<D>();   // at least one row per thread
+    constexpr int RPP = kThreads / (LPR * HPT);
+    constexpr int TILE = HPT > 1 ? kDqTileH : dequant_tile<D>();   // at least one row per thread
     constexpr int NGT = IS_K && TILE > G ? TILE / G : 1;   // K groups per tile (a tile may hold part of one)
     constexpr int NGD = D / G;
     static_assert(TILE % RPP == 0 && (!IS_K || G % RPP == 0), "tile shape");
-    const int tid = threadIdx.x, lane = tid % LPR, rg = tid / LPR;
+    const int tid = threadIdx.x, lane = tid % LPR, rg = tid / (LPR * HPT), hl = (tid / LPR) % HPT;
     const int64_t H = geo.H, T = geo.T, Tq = geo.Tq;
     const int64_t ntile = (Tq + TILE - 1) / TILE;
     int64_t bid = blockIdx.x;
-    const int64_t nQ = geo.B * ntile * H;
+    const int64_t nQ = geo.B * ntile * (H / HPT);
 
     auto store8 = [&](int64_t t, int64_t b, int64_t h, const float (&v)[8]) {
         const int64_t o = ((b * T + t) * H + h) * D + 8 * lane;
@@ -234,8 +241,8 @@ __global__ void __launch_bounds__(kThreads) int4_dequant_kernel(const uint8_t* _
     };
 
     if (bid < nQ) {
-        const Bjh ix = split_bjh((uint32_t)bid, (uint32_t)H, (uint32_t)ntile);
-        const int64_t h = ix.h, j = ix.j, b = ix.b;
+        const Bjh ix = split_bjh((uint32_t)bid, (uint32_t)(H / HPT), (uint32_t)ntile);
+        const int64_t h = ix.h * HPT + hl, j = ix.j, b = ix.b;
         const int64_t t0 = j * TILE;
         const int n = (int)min<int64_t>(TILE, Tq - t0);
         float s8[NGT][8], zs8[NGT][8];
@@ -307,7 +314,8 @@ __global__ void __launch_bounds__(kThreads) int4_dequant_kernel(const uint8_t* _
     const int64_t h = ix.h, jr = ix.j, b = ix.b;
     const int64_t r0 = jr * kResTile;
     const int n = (int)min<int64_t>(kResTile, geo.R - r0);
-    for (int r = rg; r < n; r += RPP) {
+    constexpr int RPP1 = kThreads / LPR;
+    for (int r = tid / LPR; r < n; r += RPP1) {
         const uint4 a = *reinterpret_cast<const uint4*>(res + ((b * H + h) * geo.ldr + r0 + r) * D + 8 * lane);
         if constexpr (OT == KVQ_BF16) {
             *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + ((b * T + Tq + r0 + r) * H + h) * D + 8 * lane) = a;
@@ -389,26 +397,31 @@ void launch_quant(const uint16_t* K, const uint16_t* V, const I4Geom& g, const I
     hipLaunchKernelGGL((int4_quant_kernel<D, G>), dim3((unsigned)n), dim3(quant_threads<D, G>()), 0, st, K, V, gq, p);
 }
 
-template <int D, int G>
-void launch_dequant(bool is_k, int ot, const kvq_int4_cache* c, const I4Geom& g, void* out, hipStream_t st) {
-    const int64_t nblk =
-        g.B * g.H * (cdiv(g.Tq, (int64_t)dequant_tile<D>()) + g.nRt);
+template <int D, int G, int HPT>
+void launch_dequant_h(bool is_k, int ot, const kvq_int4_cache* c, const I4Geom& g, void* out, hipStream_t st) {
+    constexpr int TILE = HPT > 1 ? kDqTileH : dequant_tile<D>();
+    const int64_t nblk = g.B * (cdiv(g.Tq, (int64_t)TILE) * (g.H / HPT) + g.H * g.nRt);
     const dim3 grid((unsigned)nblk), blk(kThreads);
     if (is_k) {
         if (ot == KVQ_FP32)
-            hipLaunchKernelGGL((int4_dequant_kernel<D, G, true, KVQ_FP32>), grid, blk, 0, st, c->k_codes, c->k_scale,
+            hipLaunchKernelGGL((int4_dequant_kernel<D, G, true, KVQ_FP32, HPT>), grid, blk, 0, st, c->k_codes, c->k_scale,
                                c->k_zero, c->k_res, g, out);
         else
-            hipLaunchKernelGGL((int4_dequant_kernel<D, G, true, KVQ_BF16>), grid, blk, 0, st, c->k_codes, c->k_scale,
+            hipLaunchKernelGGL((int4_dequant_kernel<D, G, true, KVQ_BF16, HPT>), grid, blk, 0, st, c->k_codes, c->k_scale,
                                c->k_zero, c->k_res, g, out);
     } else {
         if (ot == KVQ_FP32)
-            hipLaunchKernelGGL((int4_dequant_kernel<D, G, false, KVQ_FP32>), grid, blk, 0, st, c->v_codes, c->v_scale,
+            hipLaunchKernelGGL((int4_dequant_kernel<D, G, false, KVQ_FP32, HPT>), grid, blk, 0, st, c->v_codes, c->v_scale,
                                c->v_zero, c->v_res, g, out);
         else
-            hipLaunchKernelGGL((int4_dequant_kernel<D, G, false, KVQ_BF16>), grid, blk, 0, st, c->v_codes, c->v_scale,
+            hipLaunchKernelGGL((int4_dequant_kernel<D, G, false, KVQ_BF16, HPT>), grid, blk, 0, st, c->v_codes, c->v_scale,
                                c->v_zero, c->v_res, g, out);
     }
+}
+template <int D, int G>
+void launch_dequant(bool is_k, int ot, const kvq_int4_cache* c, const I4Geom& g, void* out, hipStream_t st) {
+    if (D == 128 && g.H % kDqHeads == 0 && g.H >= kDqHeadsMinH) launch_dequant_h<D, G, kDqHeads>(is_k, ot, c, g, out, st);
+    else launch_dequant_h<D, G, 1>(is_k, ot, c, g, out, st);
 }
 
 

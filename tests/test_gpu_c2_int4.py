@@ -65,6 +65,15 @@ def test_all_shapes_ragged(d, g):
     run_and_compare(u16(K), u16(V), g=g, R=21)
 
 
+@pytest.mark.parametrize("g", [32, 64, 128])
+@pytest.mark.parametrize("T,R", [(3 * 64 + 37, 21), (5, 3), (8 * 40, 0)])
+def test_many_heads_ragged(g, T, R):
+    """32 KV heads at d = 128: the dequantizer's tiles then span four heads and 8 tokens (a K tile
+    holds part of a group); ragged token counts, a residual window, and fewer tokens than a tile."""
+    K, V, _ = synth.kv_layer(1, T, 32, 128, seed=T * 3 + g)
+    run_and_compare(u16(K), u16(V), g=g, R=R, check_stats=False)
+
+
 @pytest.mark.parametrize("T,R", [(1, 0), (1, 1), (64, 64), (200, 0), (200, 199), (130, 2), (8192 + 5, 512)])
 def test_residual_extents(T, R):
     K, V, _ = synth.kv_layer(1, T, 2, 128, seed=T * 7 + R)
