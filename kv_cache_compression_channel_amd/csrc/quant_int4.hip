@@ -8,7 +8,9 @@
 // of the Walkthrough (KV Compression 公式到源码对照) §1.2 with qmin = 0, qmax = 15.
 //
 // One launch covers K tiles, V tiles and the residual copy.  A tile is one (b, h) and a
-// block of consecutive tokens (g tokens for K, 64 for V) across all d channels.  Lane
+// block of consecutive tokens (g tokens for K, or two groups of 32 at g = 32 and d <= 128; 64 for
+// V) across all d channels.  The per-row K minima and maxima meet in LDS as bf16 pairs (one dword
+// per channel and row slot), which keeps a block within 19 KB and the CU at 7 blocks.  Lane
 // layout: d/8 lanes per token row, each owning 8 consecutive channels (one 16-byte load
 // of bf16, one 4-byte store of packed codes); a block of NT threads (256, or d*g/32 when that is
 // larger, so a K group is at most 4 rows per thread) covers 8*NT/d rows per pass.
@@ -31,6 +33,10 @@ constexpr int quant_threads() { return D * G / 32 > kThreads ? D * G / 32 : kThr
 // tile and every thread still quantizes the same number of V elements.
 template <int D, int G>
 constexpr int quant_vtile() { return kVTile * quant_threads<D, G>() / kThreads; }
+// K groups per quantizer block: two at g = 32 (d <= 128), so each thread still carries four rows
+// (two at d = 64) and every thread of the block takes a channel of the cross-row reduction.
+template <int D, int G>
+constexpr int quant_kgroups() { return G == 32 && D <= 128 ? 2 : 1; }
 
 template <int D, int G, int NT = quant_threads<D, G>()>
 __global__ void __launch_bounds__(NT) int4_quant_kernel(const uint16_t* __restrict__ K,
@@ -41,108 +47,136 @@ __global__ void __launch_bounds__(NT) int4_quant_kernel(const uint16_t* __restri
     constexpr int NGD = D / G;            // V groups per token
     constexpr int VT = quant_vtile<D, G>();   // tokens per V tile
     static_assert(G % RPP == 0 && VT % RPP == 0, "tile shape");
-    constexpr int NP = VT * NGD > D ? VT * NGD : D;   // parameter slots
-    __shared__ __attribute__((aligned(16))) float s_mn[RPP * D > NP ? RPP * D : NP];
-    __shared__ __attribute__((aligned(16))) float s_mx[RPP * D > NP ? RPP * D : NP];
+    constexpr int GPB = quant_kgroups<D, G>();   // K groups per block
+    constexpr int KT = G * GPB;                  // tokens per K tile
+    constexpr int NRG = G / RPP;                 // rows per thread per K group
+    constexpr int NR = KT / RPP;                 // rows per thread per K tile
+    constexpr int NP = VT * NGD > GPB * D ? VT * NGD : GPB * D;   // parameter slots
+    constexpr int NKS = GPB * RPP * D;            // K: one dword per (group, row slot, channel)
+    constexpr int NVS = VT * NGD;                 // V: one min and one max per group
+    constexpr int NS = NKS > 2 * NVS ? NKS : 2 * NVS;
+    // K and V blocks use the one array: a K slot holds the bf16 min (high half) and bf16 max (low
+    // half) of its channel, a V block keeps fp32 group minima, then maxima
+    __shared__ __attribute__((aligned(16))) uint32_t s_red[NS];
     __shared__ float s_ps[NP], s_pr[NP], s_pz[NP];
+    float* const s_mn = reinterpret_cast<float*>(s_red);
+    float* const s_mx = s_mn + NVS;
 
     const int tid = threadIdx.x, lane = tid % LPR, rg = tid / LPR;
     const int64_t H = geo.H, Tq = geo.Tq;
     int64_t bid = blockIdx.x;
-    const int64_t nK = geo.B * geo.nKg * H, nV = geo.B * geo.nVt * H;
+    const int64_t nKb = (geo.nKg + GPB - 1) / GPB;   // K tiles per (b, h)
+    const int64_t nK = geo.B * nKb * H, nV = geo.B * geo.nVt * H;
 
     if (bid < nK) {
-        // ---------------- K: one group of G tokens, every channel ----------------
-        constexpr int NR = G / RPP;
-        const Bjh ix = split_bjh((uint32_t)bid, (uint32_t)H, (uint32_t)geo.nKg);
-        const int64_t h = ix.h, j = ix.j, b = ix.b;
-        const int64_t t0 = j * G;
-        const int n = (int)min<int64_t>(G, Tq - t0);
+        // ---------------- K: GPB groups of G tokens, every channel ----------------
+        const Bjh ix = split_bjh((uint32_t)bid, (uint32_t)H, (uint32_t)nKb);
+        const int64_t h = ix.h, jb = ix.j, b = ix.b;
+        const int64_t t0 = jb * KT;
+        const int n = (int)min<int64_t>(KT, Tq - t0);
         uint4 raw[NR];
-        float mn[8], mx[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) { mn[k] = FLT_MAX; mx[k] = -FLT_MAX; }
-        if (n == G) {
+        if (n == KT) {
 #pragma unroll
             for (int i = 0; i < NR; ++i)
                 raw[i] = ld_stream_u4(K + b * geo.sb + (t0 + rg + RPP * i) * geo.st + h * geo.sh + 8 * lane);
         } else {
 #pragma unroll
             for (int i = 0; i < NR; ++i) {
-                const int r = rg + RPP * i;
-                // rows past the group repeat row 0 of this lane, which leaves min and max unchanged
-                raw[i] = ld_stream_u4(K + b * geo.sb + (t0 + (r < n ? r : 0)) * geo.st + h * geo.sh + 8 * lane);
+                // rows past the tile's end repeat its last row, which lies in the same group or an
+                // earlier one: the last group's min and max are unchanged, and groups wholly past
+                // the end are never stored
+                const int r = min(rg + RPP * i, n - 1);
+                raw[i] = ld_stream_u4(K + b * geo.sb + (t0 + r) * geo.st + h * geo.sh + 8 * lane);
             }
         }
+        // per group: min and max over this thread's rows, then every row slot's partials to LDS
+        // (two 16-byte stores each), reduced over the RPP slots by the channel threads: no
+        // cross-lane permutes
 #pragma unroll
-        for (int i = 0; i < NR; i += 2) {
-            float v[8], u[8];
-            unpack8(raw[i], v);
-            if (i + 1 < NR) unpack8(raw[i + 1], u); else unpack8(raw[i], u);
+        for (int gi = 0; gi < GPB; ++gi) {
+            float mn[8], mx[8];
 #pragma unroll
-            for (int k = 0; k < 8; ++k) { mn[k] = vmin3(mn[k], v[k], u[k]); mx[k] = vmax3(mx[k], v[k], u[k]); }
-        }
-        // every row slot's partials to LDS (two 16-byte stores each), reduced over the RPP slots by
-        // the channel threads: no cross-lane permutes
-        {
-            float4* pm = reinterpret_cast<float4*>(s_mn + rg * D + 8 * lane);
-            float4* px = reinterpret_cast<float4*>(s_mx + rg * D + 8 * lane);
-            pm[0] = make_float4(mn[0], mn[1], mn[2], mn[3]);
-            pm[1] = make_float4(mn[4], mn[5], mn[6], mn[7]);
-            px[0] = make_float4(mx[0], mx[1], mx[2], mx[3]);
-            px[1] = make_float4(mx[4], mx[5], mx[6], mx[7]);
+            for (int k = 0; k < 8; ++k) { mn[k] = FLT_MAX; mx[k] = -FLT_MAX; }
+#pragma unroll
+            for (int i = gi * NRG; i < (gi + 1) * NRG; i += 2) {
+                float v[8], u[8];
+                unpack8(raw[i], v);
+                if (i + 1 < (gi + 1) * NRG) unpack8(raw[i + 1], u); else unpack8(raw[i], u);
+#pragma unroll
+                for (int k = 0; k < 8; ++k) { mn[k] = vmin3(mn[k], v[k], u[k]); mx[k] = vmax3(mx[k], v[k], u[k]); }
+            }
+            // the input is bf16, so each min and max is a bf16 value (low 16 bits zero): one
+            // v_perm_b32 puts both top halves in one dword
+            uint32_t w[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                w[k] = __builtin_amdgcn_perm(__float_as_uint(mn[k]), __float_as_uint(mx[k]), 0x07060302u);
+            uint4* pk = reinterpret_cast<uint4*>(s_red + (gi * RPP + rg) * D + 8 * lane);
+            pk[0] = make_uint4(w[0], w[1], w[2], w[3]);
+            pk[1] = make_uint4(w[4], w[5], w[6], w[7]);
         }
         __syncthreads();
-        for (int c = tid; c < D; c += NT) {
-            float a = s_mn[c], z = s_mx[c];
+        for (int c = tid; c < GPB * D; c += NT) {
+            const int gi = c / D, cc = c % D;
+            if constexpr (GPB > 1)
+                if (gi * G >= n) continue;
+            const uint32_t* pk = s_red + gi * RPP * D + cc;
+            float a = __uint_as_float(pk[0] & 0xffff0000u), z = __uint_as_float(pk[0] << 16);
 #pragma unroll
-            for (int w = 1; w < RPP; ++w) { a = vmin2(a, s_mn[w * D + c]); z = vmax2(z, s_mx[w * D + c]); }
+            for (int w = 1; w < RPP; w += 2) {
+                const uint32_t u0 = pk[w * D], u1 = pk[(w + 1 < RPP ? w + 1 : w) * D];
+                a = vmin3(a, __uint_as_float(u0 & 0xffff0000u), __uint_as_float(u1 & 0xffff0000u));
+                z = vmax3(z, __uint_as_float(u0 << 16), __uint_as_float(u1 << 16));
+            }
             const GroupParams p = group_params(a, z);
-            const int64_t mi = ((b * H + h) * geo.ldk + j) * D + c;
+            const int64_t mi = ((b * H + h) * geo.ldk + jb * GPB + gi) * D + cc;
             out.k_scale[mi] = p.sb;
             out.k_zero[mi] = p.zb;
             s_ps[c] = p.s; s_pr[c] = p.r; s_pz[c] = p.z;
         }
         __syncthreads();
-        float ps[8], pr[8], pz[8];
-        bool fast = true;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            ps[k] = s_ps[8 * lane + k]; pr[k] = s_pr[8 * lane + k]; pz[k] = s_pz[8 * lane + k];
-            fast = fast && pz[k] >= 0.0f && pz[k] <= 15.0f;
-        }
+        for (int gi = 0; gi < GPB; ++gi) {
+            float ps[8], pr[8], pz[8];
+            bool fast = true;
 #pragma unroll
-        for (int i = 0; i < NR; ++i) {
-            const int r = rg + RPP * i;
-            float v[8], q[8];
-            unpack8(raw[i], v);
-            codes8<false>(v, ps, pr, pz, fast, q);
-            if (n == G || r < n)
-                *reinterpret_cast<uint32_t*>(out.k_codes + ((b * H + h) * geo.ldq + t0 + r) * (D / 2) + 4 * lane) =
-                    pack_codes(q);
+            for (int k = 0; k < 8; ++k) {
+                ps[k] = s_ps[gi * D + 8 * lane + k]; pr[k] = s_pr[gi * D + 8 * lane + k]; pz[k] = s_pz[gi * D + 8 * lane + k];
+                fast = fast && pz[k] >= 0.0f && pz[k] <= 15.0f;
+            }
+#pragma unroll
+            for (int i = gi * NRG; i < (gi + 1) * NRG; ++i) {
+                const int r = rg + RPP * i;
+                float v[8], q[8];
+                unpack8(raw[i], v);
+                codes8<false>(v, ps, pr, pz, fast, q);
+                if (n == KT || r < n)
+                    *reinterpret_cast<uint32_t*>(out.k_codes + ((b * H + h) * geo.ldq + t0 + r) * (D / 2) + 4 * lane) =
+                        pack_codes(q);
+            }
         }
         return;
     }
     bid -= nK;
     if (bid < nV) {
         // ---------------- V: 64 tokens, groups of G channels per token ----------------
-        constexpr int NR = VT / RPP;
+        constexpr int NRV = VT / RPP;
         constexpr int LPG = G / 8;   // lanes per group
         const Bjh ix = split_bjh((uint32_t)bid, (uint32_t)H, (uint32_t)geo.nVt);
         const int64_t h = ix.h, jt = ix.j, b = ix.b;
         const int64_t t0 = jt * VT;
         const int n = (int)min<int64_t>(VT, Tq - t0);
         const int grp = (8 * lane) / G;
-        uint4 raw[NR];
+        uint4 raw[NRV];
         // every row's load issued before any is used: rows past the tile's end load its last row
         // again (their parameters are never read and their codes never stored)
 #pragma unroll
-        for (int i = 0; i < NR; ++i) {
+        for (int i = 0; i < NRV; ++i) {
             const int r = rg + RPP * i;
             raw[i] = ld_stream_u4(V + b * geo.sb + (t0 + (r < n ? r : n - 1)) * geo.st + h * geo.sh + 8 * lane);
         }
 #pragma unroll
-        for (int i = 0; i < NR; ++i) {
+        for (int i = 0; i < NRV; ++i) {
             const int r = rg + RPP * i;
             float mn = FLT_MAX, mx = -FLT_MAX, v[8];
             unpack8(raw[i], v);
@@ -161,7 +195,7 @@ __global__ void __launch_bounds__(NT) int4_quant_kernel(const uint16_t* __restri
         }
         __syncthreads();
 #pragma unroll
-        for (int i = 0; i < NR; ++i) {
+        for (int i = 0; i < NRV; ++i) {
             const int r = rg + RPP * i;
             const float ps = s_ps[r * NGD + grp], pr = s_pr[r * NGD + grp], pz = s_pz[r * NGD + grp];
             const bool fast = pz >= 0.0f && pz <= 15.0f;
@@ -385,15 +419,15 @@ I4Geom geom_of(const kvq_int4_cache* c) {
     return g;
 }
 
-// nblk is the grid at 64-token V tiles (what the callers check); the quantizer's own V tiles may be
-// larger, which only shrinks its grid.
+// nblk is the grid at one K group and 64 tokens per tile (what the callers check); the quantizer's
+// own K and V tiles may be larger, which only shrinks its grid.
 template <int D, int G>
 void launch_quant(const uint16_t* K, const uint16_t* V, const I4Geom& g, const I4Ptrs& p, int64_t nblk,
                   hipStream_t st) {
     (void)nblk;
     I4Geom gq = g;
     gq.nVt = cdiv(g.Tq, (int64_t)quant_vtile<D, G>());
-    const int64_t n = gq.B * gq.H * (gq.nKg + gq.nVt + gq.nRt);
+    const int64_t n = gq.B * gq.H * (cdiv(gq.nKg, (int64_t)quant_kgroups<D, G>()) + gq.nVt + gq.nRt);
     hipLaunchKernelGGL((int4_quant_kernel<D, G>), dim3((unsigned)n), dim3(quant_threads<D, G>()), 0, st, K, V, gq, p);
 }
 

@@ -74,6 +74,15 @@ def test_many_heads_ragged(g, T, R):
     run_and_compare(u16(K), u16(V), g=g, R=R, check_stats=False)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("T", [31, 32, 33, 63, 64, 65, 96, 97])
+def test_two_group_k_tiles(d, T):
+    """At g = 32 (d <= 128) a quantizer block covers two K groups: a tile that ends inside its
+    first group, exactly at its end, inside the second, or at the tile's end."""
+    K, V, _ = synth.kv_layer(1, T, 2, d, seed=T * 5 + d)
+    run_and_compare(u16(K), u16(V), g=32, R=0, check_stats=False)
+
+
 @pytest.mark.parametrize("T,R", [(1, 0), (1, 1), (64, 64), (200, 0), (200, 199), (130, 2), (8192 + 5, 512)])
 def test_residual_extents(T, R):
     K, V, _ = synth.kv_layer(1, T, 2, 128, seed=T * 7 + R)
